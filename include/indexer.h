@@ -1,0 +1,202 @@
+/*
+ * Lightning-indexer score + top-k for MI355X (gfx950): the C ABI.
+ *
+ * Pages this library implements (cited by title and section):
+ *  [listing] "nvfp4-megamoe-kernel -- dsv4/kernels/indexer/indexer_score_topk.cu":
+ *            header comment (eq. 16), NVFP4 notes, dequant_fp4_scalar, heap_insert,
+ *            the main kernel (paged pool, block table, valid lengths, final sort)
+ *            and its PyTorch binding (argument list and shapes).
+ *  [commits] "nvfp4-megamoe-kernel -- commit graph of dsv4/kernels/indexer":
+ *            79ef87f9a9 (E2M1 encoding table), e74c84458c (E2M1 magnitude LUT),
+ *            c2f705a21a (score_topk launcher: q in BF16 or FP32).
+ *  [qsa.rs]  "metrale_model_layers/layers/ops/qsa.rs": doc comments and argument
+ *            lists of qsa_block_pool, qsa_qprep_rows, qsa_score_rows(_tc), and the
+ *            module comment on per-row prefill selection passes.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device pointers the caller allocates; the library never
+ *    allocates, frees or synchronises.  All work is enqueued on `stream`
+ *    (NULL = the null stream) and the call returns without waiting.
+ *  - Inputs are read-only and must not alias outputs.  Outputs are overwritten
+ *    completely (including -1 / -inf padding).
+ *  - Return value: IDX_OK or an IDX_ERR_* code.  Argument checks run on the host
+ *    before any HIP call; on failure nothing is launched and
+ *    indexer_last_error() describes the problem.  Device faults surface at the
+ *    caller's next synchronisation.  A call with no rows to process returns
+ *    IDX_OK without launching anything ([qsa.rs] qsa_block_pool: no launch when
+ *    there is no work).
+ *  - Out-of-range data (a valid length beyond the table, a page id outside the
+ *    pool) is undefined behaviour; callers must validate such data.
+ */
+#ifndef SALB_INDEXER_H
+#define SALB_INDEXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define IDX_OK 0
+#define IDX_ERR_NULL 1         /* a required pointer is NULL */
+#define IDX_ERR_SHAPE 2        /* inconsistent or out-of-range sizes */
+#define IDX_ERR_WORKSPACE 3    /* workspace missing or smaller than the *_workspace_size() value */
+#define IDX_ERR_UNSUPPORTED 4  /* a size or mode this build does not implement */
+#define IDX_ERR_HIP 5          /* a HIP runtime call failed (message in indexer_last_error) */
+
+/* element type of q */
+#define IDX_DTYPE_F32 0
+#define IDX_DTYPE_BF16 1
+
+/* arithmetic of the dot products */
+#define IDX_PREC_FP32 0   /* fp32 vector FMAs; scores within ~1e-5 relative of the exact value */
+#define IDX_PREC_MFMA 1   /* fp16 matrix cores with fp32 accumulation; q rounded to 11 bits
+                             after a per-head power-of-two prescale, NVFP4 code values exact */
+
+/* Human-readable description of the last error on the calling thread ("" if none). */
+const char* indexer_last_error(void);
+
+/*
+ * indexer_score_rows -- the lightning-indexer scores of every (query, key) pair.
+ *
+ * [listing] header comment (eq. 16) and main kernel:
+ *     scores[t, s] = sum_h w[t,h] * ReLU( q[t,h,:] . k[t,s,:] )    for s < valid_lens[t]
+ *     scores[t, s] = -inf                                          for valid_lens[t] <= s < n_cols
+ * with one key vector per logical entry s, shared by all heads:
+ *     p = block_table[t * bt_stride + s / epb],  e = p * epb + s % epb,
+ *     k[t,s,d] = E2M1(nibble d of keys_fp4[e]) * E4M3(key_scale[e, d/16]) * key_gscale[p]
+ * nibble d is the low nibble of byte d/2 for even d and the high nibble for odd d
+ * ([listing] dequant_fp4_scalar); E2M1 magnitudes are 0, .5, 1, 1.5, 2, 3, 4, 6 with
+ * bit 3 as sign ([commits] 79ef87f9a9, e74c84458c); E4M3 is the OCP FP8 format.
+ *
+ *  q           [T, H, D] fp32 or bf16 (q_dtype), contiguous
+ *  w           [T, H] fp32, contiguous (any sign)
+ *  keys_fp4    [n_pages, epb, D/2] uint8, contiguous
+ *  key_scale   [n_pages, epb, D/16] uint8 (E4M3 bytes), contiguous
+ *  key_gscale  [n_pages] fp32 (any sign)
+ *  block_table [T, max_lb] int32 with row stride bt_stride >= max_lb; entries at
+ *              logical blocks >= ceil(valid_lens[t]/epb) are never read
+ *  valid_lens  [T] int32, each in [0, min(n_cols, max_lb*epb)]
+ *  scores      [T, n_cols] fp32 output with row stride score_stride >= n_cols
+ * Supported: D in {64, 128, 256}; 1 <= H <= 64; 1 <= epb <= 65536; n_cols < 2^24.
+ * precision: IDX_PREC_FP32 or IDX_PREC_MFMA.
+ */
+int indexer_score_rows(const void* q, int q_dtype, const float* w,
+                       const uint8_t* keys_fp4, const uint8_t* key_scale, const float* key_gscale,
+                       const int32_t* block_table, int64_t bt_stride, const int32_t* valid_lens,
+                       int T, int H, int D, int epb, int max_lb, int n_pages,
+                       int precision, float* scores, int64_t score_stride, int n_cols,
+                       hipStream_t stream);
+
+/*
+ * indexer_topk_select -- per-row top-k of a score matrix.
+ *
+ * For each row r, the candidates are the entries s in [0, valid_r); they are
+ * ranked by score descending, equal scores by increasing index (the order of the
+ * [listing]'s heap comparator and final selection sort; -0.0 equals 0.0, NaN
+ * ranks below every number).  The first K_r = min(top_k, valid_r) ranked indices
+ * go to topk_idx[r, 0:K_r] and the remaining slots hold -1 ([listing]: heap
+ * pre-filled with -1); topk_scores (optional, may be NULL) receives the matching
+ * scores and -inf in padded slots.
+ *
+ * valid_r is valid_lens[r] if valid_lens != NULL; otherwise, if ratio > 0,
+ * min(n_cols, floor((first_pos + r + 1) / ratio)) -- the count of complete
+ * blocks of a prefill row at position first_pos + r ([qsa.rs] qsa_score_rows);
+ * otherwise n_cols.
+ *
+ *  scores      [rows, n_cols] fp32, row stride score_stride >= n_cols
+ *  topk_idx    [rows, top_k] int32 output (logical indices s)
+ *  topk_scores [rows, top_k] fp32 output or NULL
+ *  workspace   device scratch of indexer_topk_workspace_size(...) bytes
+ * Supported: 1 <= top_k <= 16384, n_cols < 2^24.
+ */
+size_t indexer_topk_workspace_size(int rows, int n_cols, int top_k);
+int indexer_topk_select(const float* scores, int64_t score_stride, const int32_t* valid_lens,
+                        int64_t first_pos, int ratio, int rows, int n_cols, int top_k,
+                        int32_t* topk_idx, float* topk_scores,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * indexer_score_topk -- the fused hot path: Selected[t] = TopK(I[t, :], top_k)
+ * ([listing] header comment, eq. 16; main kernel and its binding).
+ *
+ * Arguments as for indexer_score_rows (with n_cols = max_lb * epb) and
+ * indexer_topk_select; the scores live only in the workspace.
+ *  topk_idx    [T, top_k] int32 output: logical entry indices s, -1 padded
+ *  topk_scores [T, top_k] fp32 output or NULL
+ *  workspace   device scratch of indexer_score_topk_workspace_size(...) bytes
+ */
+size_t indexer_score_topk_workspace_size(int T, int max_lb, int epb, int top_k);
+int indexer_score_topk(const void* q, int q_dtype, const float* w,
+                       const uint8_t* keys_fp4, const uint8_t* key_scale, const float* key_gscale,
+                       const int32_t* block_table, int64_t bt_stride, const int32_t* valid_lens,
+                       int T, int H, int D, int epb, int max_lb, int n_pages, int top_k,
+                       int precision, int32_t* topk_idx, float* topk_scores,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * qsa_block_pool -- pooled QSA block keys ([qsa.rs] qsa_block_pool).
+ *
+ * For b in [first_block, first_block + n_new):
+ *     m = mean(raw_keys[ratio*b .. ratio*b + ratio - 1, :])
+ *     n = m / sqrt(mean(m^2) + eps) * (1 + k_norm_w)
+ *     block_keys[b, :] = RoPE(n, position ratio*b) on dims [0, rot)
+ * RoPE pairs dim i with i + rot/2 (i < rot/2) at angle pos * theta^(-2i/rot),
+ * the angle formed in fp64; dims >= rot are copied.
+ *  raw_keys   [>= ratio*(first_block+n_new), hd] bf16 (uint16 bit patterns)
+ *  k_norm_w   [hd] fp32
+ *  block_keys [>= first_block+n_new, hd] fp32 output (only the n_new rows are written)
+ * Supported: hd in {64, 128, 256}, rot even and <= hd, ratio >= 1.
+ */
+int qsa_block_pool(const uint16_t* raw_keys, const float* k_norm_w, float* block_keys,
+                   uint32_t first_block, uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot,
+                   float theta, float eps, hipStream_t stream);
+
+/*
+ * qsa_qprep_rows -- prefill query prep ([qsa.rs] qsa_qprep_rows, qsa_qprep).
+ *
+ * For row r and head h: x = qk[r, h*hd .. h*hd+hd-1];
+ *     q_out[r, h, :] = RoPE(x / sqrt(mean(x^2) + eps) * (1 + q_norm_w), first_pos + r)
+ *  qk       [rows, qkw] bf16 (uint16 bit patterns), qkw >= n_heads*hd
+ *  q_norm_w [hd] fp32
+ *  q_out    [rows, n_heads, hd] fp32 output
+ */
+int qsa_qprep_rows(const uint16_t* qk, const float* q_norm_w, float* q_out,
+                   uint32_t rows, uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t hd,
+                   uint32_t rot, float theta, float eps, hipStream_t stream);
+
+/*
+ * qsa_score_rows -- QSA block scores ([qsa.rs] qsa_score, qsa_score_rows, qsa_score_rows_tc):
+ *     scores[r, b] = sum_h ReLU(q[r,h,:] . block_keys[b,:]) / sqrt(hd)   for b < nb_r
+ *     scores[r, b] = -inf                                              for nb_r <= b < n_blocks_max
+ * with nb_r = min(n_blocks_max, floor((first_pos + r + 1) / ratio)).
+ *  q          [rows, n_heads, hd] fp32
+ *  block_keys [n_blocks_max, hd] fp32
+ *  scores     [rows, n_blocks_max] fp32 output, row stride score_stride >= n_blocks_max
+ * Supported: hd in {64, 128, 256}, 1 <= n_heads <= 64; precision IDX_PREC_FP32 or IDX_PREC_MFMA.
+ */
+int qsa_score_rows(const float* q, const float* block_keys, float* scores,
+                   uint32_t rows, uint32_t n_blocks_max, uint32_t first_pos, uint32_t score_stride,
+                   uint32_t ratio, uint32_t n_heads, uint32_t hd, int precision, hipStream_t stream);
+
+/*
+ * indexer_debug_dequant -- test hook for the NVFP4 decoders used by the scorers.
+ *
+ * For the first n logical entries of one block-table row (addressing as in
+ * indexer_score_rows), writes out[s, d] (fp32, [n, D]):
+ *   mode 0: the exact code value E2M1 * E4M3 from the fp32 decoder,
+ *   mode 1: the fp32 rounding of code value * key_gscale[p] from the fp32 decoder,
+ *   mode 2: the code value from the fp16 matrix-core operand decoder, widened to fp32.
+ */
+int indexer_debug_dequant(const uint8_t* keys_fp4, const uint8_t* key_scale, const float* key_gscale,
+                          const int32_t* block_table_row, int n, int D, int epb, int n_pages,
+                          int mode, float* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SALB_INDEXER_H */

@@ -1,0 +1,16 @@
+"""MI355X (gfx950) lightning-indexer score + top-k: a C-ABI HIP library with a thin
+PyTorch binding.  The binding only marshals arguments; every step runs in the
+hand-written HIP kernels of libsalb_indexer.so."""
+
+from .ops import (  # noqa: F401
+    indexer_debug_dequant,
+    indexer_score_rows,
+    indexer_score_topk,
+    indexer_score_topk_workspace_size,
+    indexer_topk_select,
+    indexer_topk_workspace_size,
+    qsa_block_pool,
+    qsa_qprep_rows,
+    qsa_score_rows,
+)
+from ._lib import IndexerError, load  # noqa: F401

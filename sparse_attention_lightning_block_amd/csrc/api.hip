@@ -1,0 +1,273 @@
+// C ABI of the gfx950 indexer library: argument checks, workspace layout, dispatch.
+// Every check runs on the host before any HIP call; see include/indexer.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/indexer.h"
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return IDX_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(IDX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int kMaxCols = 1 << 24;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Checks shared by the paged scorers.
+int check_paged(const void* q, int q_dtype, const float* w, const uint8_t* keys, const uint8_t* scale,
+                const float* gscale, const int32_t* bt, int64_t bt_stride, const int32_t* valid_lens, int T, int H,
+                int D, int epb, int max_lb, int n_pages, int precision) {
+  if (T < 0) return fail(IDX_ERR_SHAPE, "T = %d must be >= 0", T);
+  if (!q || !w || !keys || !scale || !gscale || !bt || !valid_lens)
+    return fail(IDX_ERR_NULL, "q, w, keys_fp4, key_scale, key_gscale, block_table and valid_lens are required");
+  if (q_dtype != IDX_DTYPE_F32 && q_dtype != IDX_DTYPE_BF16) return fail(IDX_ERR_UNSUPPORTED, "q_dtype %d", q_dtype);
+  if (precision != IDX_PREC_FP32 && precision != IDX_PREC_MFMA)
+    return fail(IDX_ERR_UNSUPPORTED, "precision %d", precision);
+  if (D != 64 && D != 128 && D != 256) return fail(IDX_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128, 256)", D);
+  if (H < 1 || H > 64) return fail(IDX_ERR_UNSUPPORTED, "n_heads %d (supported: 1..64)", H);
+  if (epb < 1 || epb > 65536) return fail(IDX_ERR_SHAPE, "entries_per_block %d (supported: 1..65536)", epb);
+  if (max_lb < 1) return fail(IDX_ERR_SHAPE, "max_lb %d must be >= 1", max_lb);
+  if (n_pages < 1) return fail(IDX_ERR_SHAPE, "n_pages %d must be >= 1", n_pages);
+  if (bt_stride < max_lb) return fail(IDX_ERR_SHAPE, "bt_stride %lld < max_lb %d", (long long)bt_stride, max_lb);
+  if ((int64_t)max_lb * epb >= kMaxCols)
+    return fail(IDX_ERR_UNSUPPORTED, "max_lb * epb = %lld (supported: < 2^24)", (long long)max_lb * epb);
+  if (!aligned(keys, 16)) return fail(IDX_ERR_SHAPE, "keys_fp4 must be 16-byte aligned");
+  if (!aligned(scale, 4)) return fail(IDX_ERR_SHAPE, "key_scale must be 4-byte aligned");
+  if (!aligned(q, q_dtype == IDX_DTYPE_F32 ? 4 : 2) || !aligned(w, 4) || !aligned(gscale, 4) || !aligned(bt, 4) ||
+      !aligned(valid_lens, 4))
+    return fail(IDX_ERR_SHAPE, "q, w, key_gscale, block_table and valid_lens must be naturally aligned");
+  return IDX_OK;
+}
+
+salb::ScoreArgs make_args(const void* q, int q_dtype, const float* w, const uint8_t* keys, const uint8_t* scale,
+                          const float* gscale, const int32_t* bt, int64_t bt_stride, const int32_t* valid_lens,
+                          int T, int H, int D, int epb, int max_lb) {
+  salb::ScoreArgs a{};
+  a.q = q;
+  a.q_bf16 = q_dtype == IDX_DTYPE_BF16;
+  a.w = w;
+  a.keys = keys;
+  a.kscale = scale;
+  a.gscale = gscale;
+  a.bt = bt;
+  a.bt_stride = bt_stride;
+  a.valid_lens = valid_lens;
+  a.T = T;
+  a.H = H;
+  a.D = D;
+  a.epb = epb;
+  a.max_lb = max_lb;
+  a.epb_magic = salb::host_epb_magic(epb);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* indexer_last_error(void) { return g_err.c_str(); }
+
+int indexer_score_rows(const void* q, int q_dtype, const float* w, const uint8_t* keys_fp4,
+                       const uint8_t* key_scale, const float* key_gscale, const int32_t* block_table,
+                       int64_t bt_stride, const int32_t* valid_lens, int T, int H, int D, int epb, int max_lb,
+                       int n_pages, int precision, float* scores, int64_t score_stride, int n_cols,
+                       hipStream_t stream) {
+  int rc = check_paged(q, q_dtype, w, keys_fp4, key_scale, key_gscale, block_table, bt_stride, valid_lens, T, H, D,
+                       epb, max_lb, n_pages, precision);
+  if (rc) return rc;
+  if (!scores) return fail(IDX_ERR_NULL, "scores is required");
+  if (n_cols < 0 || n_cols >= kMaxCols) return fail(IDX_ERR_SHAPE, "n_cols %d out of range [0, 2^24)", n_cols);
+  if (score_stride < n_cols) return fail(IDX_ERR_SHAPE, "score_stride < n_cols");
+  if (!aligned(scores, 4)) return fail(IDX_ERR_SHAPE, "scores must be 4-byte aligned");
+  if (T == 0 || n_cols == 0) return ok();
+  salb::ScoreArgs a = make_args(q, q_dtype, w, keys_fp4, key_scale, key_gscale, block_table, bt_stride, valid_lens,
+                                T, H, D, epb, max_lb);
+  a.scores = scores;
+  a.score_stride = score_stride;
+  a.n_cols = n_cols;
+  a.write_tail = 1;
+  hipError_t e = salb::launch_score_rows(a, precision, stream);
+  if (e != hipSuccess) return hip_fail(e, "score kernel launch");
+  return ok();
+}
+
+size_t indexer_topk_workspace_size(int rows, int n_cols, int top_k) {
+  if (rows <= 0 || n_cols <= 0 || top_k <= 0 || n_cols >= kMaxCols) return 0;
+  return salb::select_workspace_bytes(rows, n_cols, top_k);
+}
+
+static int check_select(int rows, int n_cols, int top_k, int64_t score_stride, int ratio) {
+  if (rows < 0) return fail(IDX_ERR_SHAPE, "rows %d must be >= 0", rows);
+  if (n_cols < 0 || n_cols >= kMaxCols) return fail(IDX_ERR_SHAPE, "n_cols %d out of range [0, 2^24)", n_cols);
+  if (top_k < 1 || top_k > 16384) return fail(IDX_ERR_UNSUPPORTED, "top_k %d (supported: 1..16384)", top_k);
+  if (score_stride < n_cols) return fail(IDX_ERR_SHAPE, "score_stride < n_cols");
+  if (ratio < 0) return fail(IDX_ERR_SHAPE, "ratio %d must be >= 0", ratio);
+  return IDX_OK;
+}
+
+int indexer_topk_select(const float* scores, int64_t score_stride, const int32_t* valid_lens, int64_t first_pos,
+                        int ratio, int rows, int n_cols, int top_k, int32_t* topk_idx, float* topk_scores,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_select(rows, n_cols, top_k, score_stride, ratio);
+  if (rc) return rc;
+  if (!topk_idx) return fail(IDX_ERR_NULL, "topk_idx is required");
+  if (rows == 0) return ok();
+  if (!scores && n_cols > 0) return fail(IDX_ERR_NULL, "scores is required");
+  salb::SelectPlan p;
+  if (!salb::plan_select(rows, n_cols > 0 ? n_cols : 1, top_k, &p))
+    return fail(IDX_ERR_UNSUPPORTED, "top_k %d does not fit the device's LDS for rows of %d entries", top_k, n_cols);
+  if (p.bytes > 0 && (!workspace || workspace_bytes < p.bytes))
+    return fail(IDX_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", p.bytes, workspace_bytes);
+  if (workspace && !aligned(workspace, 256)) return fail(IDX_ERR_SHAPE, "workspace must be 256-byte aligned");
+  if (n_cols == 0) {
+    // no candidates: every slot is padding
+    p.n_cols = 0;
+  }
+  hipError_t e = salb::launch_select(p, scores, score_stride, valid_lens, first_pos, ratio, topk_idx, topk_scores,
+                                     workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "select kernel launch");
+  return ok();
+}
+
+size_t indexer_score_topk_workspace_size(int T, int max_lb, int epb, int top_k) {
+  if (T <= 0 || max_lb <= 0 || epb <= 0 || top_k <= 0) return 0;
+  const int64_t n_cols = (int64_t)max_lb * epb;
+  if (n_cols >= kMaxCols) return 0;
+  const size_t stride = round_up((size_t)n_cols, 64);
+  const size_t scores = round_up((size_t)T * stride * 4, 256);
+  return scores + salb::select_workspace_bytes(T, (int)n_cols, top_k);
+}
+
+int indexer_score_topk(const void* q, int q_dtype, const float* w, const uint8_t* keys_fp4,
+                       const uint8_t* key_scale, const float* key_gscale, const int32_t* block_table,
+                       int64_t bt_stride, const int32_t* valid_lens, int T, int H, int D, int epb, int max_lb,
+                       int n_pages, int top_k, int precision, int32_t* topk_idx, float* topk_scores,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_paged(q, q_dtype, w, keys_fp4, key_scale, key_gscale, block_table, bt_stride, valid_lens, T, H, D,
+                       epb, max_lb, n_pages, precision);
+  if (rc) return rc;
+  const int n_cols = max_lb * epb;
+  rc = check_select(T, n_cols, top_k, n_cols, 0);
+  if (rc) return rc;
+  if (!topk_idx) return fail(IDX_ERR_NULL, "topk_idx is required");
+  if (T == 0) return ok();
+  salb::SelectPlan p;
+  if (!salb::plan_select(T, n_cols, top_k, &p))
+    return fail(IDX_ERR_UNSUPPORTED, "top_k %d does not fit the device's LDS for rows of %d entries", top_k, n_cols);
+  const size_t stride = round_up((size_t)n_cols, 64);
+  const size_t score_bytes = round_up((size_t)T * stride * 4, 256);
+  const size_t need = score_bytes + p.bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(IDX_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(IDX_ERR_SHAPE, "workspace must be 256-byte aligned");
+  float* sc = static_cast<float*>(workspace);
+  salb::ScoreArgs a = make_args(q, q_dtype, w, keys_fp4, key_scale, key_gscale, block_table, bt_stride, valid_lens,
+                                T, H, D, epb, max_lb);
+  a.scores = sc;
+  a.score_stride = (int64_t)stride;
+  a.n_cols = n_cols;
+  a.write_tail = 0;
+  hipError_t e = salb::launch_score_rows(a, precision, stream);
+  if (e != hipSuccess) return hip_fail(e, "score kernel launch");
+  e = salb::launch_select(p, sc, (int64_t)stride, valid_lens, 0, 0, topk_idx, topk_scores,
+                          static_cast<unsigned char*>(workspace) + score_bytes, stream);
+  if (e != hipSuccess) return hip_fail(e, "select kernel launch");
+  return ok();
+}
+
+int qsa_block_pool(const uint16_t* raw_keys, const float* k_norm_w, float* block_keys, uint32_t first_block,
+                   uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot, float theta, float eps,
+                   hipStream_t stream) {
+  if (!raw_keys || !k_norm_w || !block_keys) return fail(IDX_ERR_NULL, "raw_keys, k_norm_w and block_keys are required");
+  if (hd != 64 && hd != 128 && hd != 256) return fail(IDX_ERR_UNSUPPORTED, "hd %u (supported: 64, 128, 256)", hd);
+  if (rot > hd || (rot & 1)) return fail(IDX_ERR_SHAPE, "rot %u must be even and <= hd", rot);
+  if (ratio < 1) return fail(IDX_ERR_SHAPE, "ratio must be >= 1");
+  if ((uint64_t)first_block + n_new > 0x7fffffffull) return fail(IDX_ERR_SHAPE, "block range too large");
+  if (!aligned(raw_keys, 16) || !aligned(block_keys, 4) || !aligned(k_norm_w, 4))
+    return fail(IDX_ERR_SHAPE, "raw_keys must be 16-byte aligned");
+  if (n_new == 0) return ok();
+  hipError_t e = salb::launch_block_pool(raw_keys, k_norm_w, block_keys, first_block, n_new, ratio, hd, rot, theta,
+                                         eps, stream);
+  if (e != hipSuccess) return hip_fail(e, "block pool launch");
+  return ok();
+}
+
+int qsa_qprep_rows(const uint16_t* qk, const float* q_norm_w, float* q_out, uint32_t rows, uint32_t first_pos,
+                   uint32_t qkw, uint32_t n_heads, uint32_t hd, uint32_t rot, float theta, float eps,
+                   hipStream_t stream) {
+  if (!qk || !q_norm_w || !q_out) return fail(IDX_ERR_NULL, "qk, q_norm_w and q_out are required");
+  if (hd != 64 && hd != 128 && hd != 256) return fail(IDX_ERR_UNSUPPORTED, "hd %u (supported: 64, 128, 256)", hd);
+  if (rot > hd || (rot & 1)) return fail(IDX_ERR_SHAPE, "rot %u must be even and <= hd", rot);
+  if (n_heads < 1 || n_heads > 65535) return fail(IDX_ERR_SHAPE, "n_heads %u out of range", n_heads);
+  if ((uint64_t)n_heads * hd > qkw) return fail(IDX_ERR_SHAPE, "qkw %u < n_heads * hd", qkw);
+  if (rows == 0) return ok();
+  hipError_t e = salb::launch_qprep_rows(qk, q_norm_w, q_out, rows, first_pos, qkw, n_heads, hd, rot, theta, eps,
+                                         stream);
+  if (e != hipSuccess) return hip_fail(e, "query prep launch");
+  return ok();
+}
+
+int qsa_score_rows(const float* q, const float* block_keys, float* scores, uint32_t rows, uint32_t n_blocks_max,
+                   uint32_t first_pos, uint32_t score_stride, uint32_t ratio, uint32_t n_heads, uint32_t hd,
+                   int precision, hipStream_t stream) {
+  if (!q || !block_keys || !scores) return fail(IDX_ERR_NULL, "q, block_keys and scores are required");
+  if (hd != 64 && hd != 128 && hd != 256) return fail(IDX_ERR_UNSUPPORTED, "hd %u (supported: 64, 128, 256)", hd);
+  if (n_heads < 1 || n_heads > 64) return fail(IDX_ERR_UNSUPPORTED, "n_heads %u (supported: 1..64)", n_heads);
+  if (ratio < 1) return fail(IDX_ERR_SHAPE, "ratio must be >= 1");
+  if (score_stride < n_blocks_max) return fail(IDX_ERR_SHAPE, "score_stride < n_blocks_max");
+  if (n_blocks_max >= (uint32_t)kMaxCols) return fail(IDX_ERR_UNSUPPORTED, "n_blocks_max must be < 2^24");
+  if (precision != IDX_PREC_FP32 && precision != IDX_PREC_MFMA)
+    return fail(IDX_ERR_UNSUPPORTED, "precision %d", precision);
+  if (!aligned(q, 16) || !aligned(block_keys, 16) || !aligned(scores, 4))
+    return fail(IDX_ERR_SHAPE, "q and block_keys must be 16-byte aligned");
+  if (rows == 0 || n_blocks_max == 0) return ok();
+  hipError_t e = salb::launch_qsa_score(q, block_keys, scores, rows, n_blocks_max, first_pos, score_stride, ratio,
+                                        n_heads, hd, precision, stream);
+  if (e != hipSuccess) return hip_fail(e, "QSA score launch");
+  return ok();
+}
+
+int indexer_debug_dequant(const uint8_t* keys_fp4, const uint8_t* key_scale, const float* key_gscale,
+                          const int32_t* block_table_row, int n, int D, int epb, int n_pages, int mode, float* out,
+                          hipStream_t stream) {
+  if (!keys_fp4 || !key_scale || !key_gscale || !block_table_row || !out)
+    return fail(IDX_ERR_NULL, "all pointers are required");
+  if (D != 64 && D != 128 && D != 256) return fail(IDX_ERR_UNSUPPORTED, "head_dim %d", D);
+  if (epb < 1 || epb > 65536 || n_pages < 1) return fail(IDX_ERR_SHAPE, "epb / n_pages out of range");
+  if (n < 0 || n >= kMaxCols) return fail(IDX_ERR_SHAPE, "n out of range");
+  if (mode < 0 || mode > 2) return fail(IDX_ERR_UNSUPPORTED, "mode %d", mode);
+  if (!aligned(keys_fp4, 16) || !aligned(key_scale, 4)) return fail(IDX_ERR_SHAPE, "misaligned key arrays");
+  if (n == 0) return ok();
+  hipError_t e = salb::launch_debug_dequant(keys_fp4, key_scale, key_gscale, block_table_row, n, D, epb, mode, out,
+                                            stream);
+  if (e != hipSuccess) return hip_fail(e, "dequant launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Shared device/host helpers for the gfx950 indexer library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace salb {
+
+typedef _Float16 half2v __attribute__((__vector_size__(2 * sizeof(_Float16))));
+typedef _Float16 half8v __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef float float4v __attribute__((__vector_size__(4 * sizeof(float))));
+typedef float float2v __attribute__((__vector_size__(2 * sizeof(float))));
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;  // MI355X: 8 XCDs; workgroup b is dispatched to XCD b % 8
+
+// ---------------------------------------------------------------------------
+// Total order used by every top-k: score descending, ties by lower index.
+// A float maps to a 32-bit key whose unsigned order is the float order, with
+// -0.0 merged into +0.0 and NaN mapped to the smallest key.  The 64-bit
+// composite (key << 32) | ~index is unique per entry and its unsigned order is
+// exactly the selection order.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t ord_key(float v) {
+  uint32_t b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0u;
+  if ((b & 0x7fffffffu) > 0x7f800000u) return 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float ord_to_float(uint32_t k) {
+  uint32_t b = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(b);
+}
+
+__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
+  return ((uint64_t)key << 32) | (uint32_t)(~idx);
+}
+
+// Exact floor(s / epb) for s < 2^24 and epb <= 2^16: m = ceil(2^40 / epb).
+__device__ __forceinline__ uint32_t div_epb(uint32_t s, uint64_t magic) {
+  return (uint32_t)(((uint64_t)s * magic) >> 40);
+}
+
+inline uint64_t host_epb_magic(int epb) {
+  return (((uint64_t)1 << 40) + (uint64_t)epb - 1) / (uint64_t)epb;
+}
+
+// Reverse of the XCD round-robin: blocks b with equal b % 8 share an XCD (and its
+// L2).  Work item (chunk, row) is assigned so that each XCD walks chunks
+// c = xcd, xcd + 8, ... and, for each of them, all rows: rows that read the same
+// pages (shared block tables) do so from the same L2 at about the same time.
+struct XcdTile {
+  int chunk;
+  int row;
+};
+
+__device__ __forceinline__ XcdTile xcd_tile(int b, int rows) {
+  int xcd = b & (kXcds - 1);
+  int j = b >> 3;
+  XcdTile t;
+  t.row = j % rows;
+  t.chunk = (j / rows) * kXcds + xcd;
+  return t;
+}
+
+}  // namespace salb

@@ -1,0 +1,68 @@
+// Internal interfaces between the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace salb {
+
+struct ScoreArgs {
+  const void* q;
+  int q_bf16;
+  const float* w;
+  const uint8_t* keys;
+  const uint8_t* kscale;
+  const float* gscale;
+  const int32_t* bt;
+  int64_t bt_stride;
+  const int32_t* valid_lens;
+  int T, H, D, epb, max_lb;
+  uint64_t epb_magic;
+  float* scores;
+  int64_t score_stride;
+  int n_cols;
+  int write_tail;  // 1: s in [valid, n_cols) gets -inf
+  // filled by the launcher
+  int chunk;       // keys per workgroup
+  int n_chunks;
+  int pid_cap;     // LDS slots for the chunk's block-table entries
+};
+
+hipError_t launch_score_rows(ScoreArgs a, int precision, hipStream_t st);
+hipError_t launch_debug_dequant(const uint8_t* keys, const uint8_t* kscale, const float* gscale,
+                                const int32_t* bt_row, int n, int D, int epb, int mode, float* out,
+                                hipStream_t st);
+
+// Per-row top-k (topk.hip).
+struct SelectPlan {
+  int rows, n_cols, top_k;
+  int seg;          // entries per first-level workgroup (score mode)
+  int nseg;         // first-level segments per row
+  int kseg;         // candidates kept per segment: min(top_k, seg)
+  int cap;          // candidate capacity of a merging workgroup
+  int levels;       // merge levels after the first (the last one writes the final result)
+  size_t bytes;     // workspace bytes
+  size_t lds_score; // dynamic LDS of a score-mode workgroup
+  size_t lds_cand;  // dynamic LDS of a candidate-mode workgroup
+};
+
+bool plan_select(int rows, int n_cols, int top_k, SelectPlan* p);
+hipError_t launch_select(const SelectPlan& p, const float* scores, int64_t score_stride,
+                         const int32_t* valid_lens, int64_t first_pos, int ratio, int32_t* out_idx,
+                         float* out_scores, void* ws, hipStream_t st);
+int max_lds_bytes();
+size_t select_workspace_bytes(int rows, int n_cols, int top_k);  // 0 if unsupported
+
+// QSA (qsa.hip).
+hipError_t launch_block_pool(const uint16_t* raw, const float* kw, float* out, uint32_t first_block,
+                             uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot, float theta,
+                             float eps, hipStream_t st);
+hipError_t launch_qprep_rows(const uint16_t* qk, const float* qw, float* out, uint32_t rows,
+                             uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t hd, uint32_t rot,
+                             float theta, float eps, hipStream_t st);
+hipError_t launch_qsa_score(const float* q, const float* keys, float* scores, uint32_t rows, uint32_t nb,
+                            uint32_t first_pos, uint32_t stride, uint32_t ratio, uint32_t n_heads, uint32_t hd,
+                            int precision, hipStream_t st);
+
+}  // namespace salb

@@ -1,0 +1,172 @@
+"""Thin PyTorch binding of the C ABI: each function marshals tensors into the C call
+of the same name (pointers, sizes, the current HIP stream) and allocates outputs
+and workspaces with torch.  All computation happens in the HIP library."""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import IDX_DTYPE_BF16, IDX_DTYPE_F32, IDX_PREC_FP32, IDX_PREC_MFMA, check
+
+PRECISION = {"fp32": IDX_PREC_FP32, "mfma": IDX_PREC_MFMA}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, dims=None) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dims")
+    return t
+
+
+def _q_dtype(q: torch.Tensor) -> int:
+    return IDX_DTYPE_BF16 if q.dtype == torch.bfloat16 else IDX_DTYPE_F32
+
+
+def indexer_score_rows(q, w, keys_fp4, key_scale, key_gscale, block_table, valid_lens, *, n_cols: int,
+                       precision: str = "mfma", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """scores [T, n_cols] fp32: I[t, s] for s < valid_lens[t], -inf beyond."""
+    _dev(q, "q", (torch.float32, torch.bfloat16), 3)
+    _dev(w, "w", torch.float32, 2)
+    _dev(keys_fp4, "keys_fp4", torch.uint8, 3)
+    _dev(key_scale, "key_scale", torch.uint8, 3)
+    _dev(key_gscale, "key_gscale", torch.float32, 1)
+    _dev(block_table, "block_table", torch.int32, 2)
+    _dev(valid_lens, "valid_lens", torch.int32, 1)
+    T, H, D = q.shape
+    P, epb, _ = keys_fp4.shape
+    if out is None:
+        out = torch.empty((T, n_cols), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32, 2)
+    check(_lib.load().indexer_score_rows(
+        _ptr(q), _q_dtype(q), _ptr(w), _ptr(keys_fp4), _ptr(key_scale), _ptr(key_gscale), _ptr(block_table),
+        block_table.stride(0), _ptr(valid_lens), T, H, D, epb, block_table.shape[1], P, PRECISION[precision],
+        _ptr(out), out.stride(0), n_cols, _stream()))
+    return out
+
+
+def indexer_topk_workspace_size(rows: int, n_cols: int, top_k: int) -> int:
+    return int(_lib.load().indexer_topk_workspace_size(rows, n_cols, top_k))
+
+
+def indexer_topk_select(scores, top_k: int, *, valid_lens: Optional[torch.Tensor] = None, first_pos: int = 0,
+                        ratio: int = 0, with_scores: bool = False, workspace: Optional[torch.Tensor] = None,
+                        out_idx: Optional[torch.Tensor] = None, out_scores: Optional[torch.Tensor] = None):
+    """(idx [rows, top_k] int32, scores [rows, top_k] fp32 or None)."""
+    _dev(scores, "scores", torch.float32, 2)
+    rows, n_cols = scores.shape
+    dev = scores.device
+    if valid_lens is not None:
+        _dev(valid_lens, "valid_lens", torch.int32, 1)
+    if out_idx is None:
+        out_idx = torch.empty((rows, top_k), dtype=torch.int32, device=dev)
+    if with_scores and out_scores is None:
+        out_scores = torch.empty((rows, top_k), dtype=torch.float32, device=dev)
+    if workspace is None:
+        nbytes = indexer_topk_workspace_size(rows, n_cols, top_k)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    check(_lib.load().indexer_topk_select(
+        _ptr(scores), scores.stride(0), _ptr(valid_lens), first_pos, ratio, rows, n_cols, top_k, _ptr(out_idx),
+        _ptr(out_scores), _ptr(workspace), workspace.numel(), _stream()))
+    return out_idx, out_scores
+
+
+def indexer_score_topk_workspace_size(T: int, max_lb: int, epb: int, top_k: int) -> int:
+    return int(_lib.load().indexer_score_topk_workspace_size(T, max_lb, epb, top_k))
+
+
+def indexer_score_topk(q, w, keys_fp4, key_scale, key_gscale, block_table, valid_lens, *, top_k: int,
+                       precision: str = "mfma", with_scores: bool = False,
+                       workspace: Optional[torch.Tensor] = None, out_idx: Optional[torch.Tensor] = None,
+                       out_scores: Optional[torch.Tensor] = None):
+    """(idx [T, top_k] int32, scores [T, top_k] fp32 or None) = TopK of the indexer scores."""
+    _dev(q, "q", (torch.float32, torch.bfloat16), 3)
+    _dev(w, "w", torch.float32, 2)
+    _dev(keys_fp4, "keys_fp4", torch.uint8, 3)
+    _dev(key_scale, "key_scale", torch.uint8, 3)
+    _dev(key_gscale, "key_gscale", torch.float32, 1)
+    _dev(block_table, "block_table", torch.int32, 2)
+    _dev(valid_lens, "valid_lens", torch.int32, 1)
+    T, H, D = q.shape
+    P, epb, _ = keys_fp4.shape
+    max_lb = block_table.shape[1]
+    dev = q.device
+    if out_idx is None:
+        out_idx = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    if with_scores and out_scores is None:
+        out_scores = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(indexer_score_topk_workspace_size(T, max_lb, epb, top_k), 1), dtype=torch.uint8,
+                                device=dev)
+    check(_lib.load().indexer_score_topk(
+        _ptr(q), _q_dtype(q), _ptr(w), _ptr(keys_fp4), _ptr(key_scale), _ptr(key_gscale), _ptr(block_table),
+        block_table.stride(0), _ptr(valid_lens), T, H, D, epb, max_lb, P, top_k, PRECISION[precision], _ptr(out_idx),
+        _ptr(out_scores), _ptr(workspace), workspace.numel(), _stream()))
+    return out_idx, out_scores
+
+
+def qsa_block_pool(raw_keys, k_norm_w, block_keys, *, first_block: int, n_new: int, ratio: int, rot: int,
+                   theta: float, eps: float) -> torch.Tensor:
+    """Writes block_keys[first_block : first_block + n_new] (fp32) from bf16 raw keys."""
+    _dev(raw_keys, "raw_keys", torch.bfloat16, 2)
+    _dev(k_norm_w, "k_norm_w", torch.float32, 1)
+    _dev(block_keys, "block_keys", torch.float32, 2)
+    hd = raw_keys.shape[1]
+    if (first_block + n_new) * ratio > raw_keys.shape[0] or first_block + n_new > block_keys.shape[0]:
+        raise ValueError("block range exceeds the raw keys or the block-key table")
+    check(_lib.load().qsa_block_pool(_ptr(raw_keys), _ptr(k_norm_w), _ptr(block_keys), first_block, n_new, ratio, hd,
+                                     rot, theta, eps, _stream()))
+    return block_keys
+
+
+def qsa_qprep_rows(qk, q_norm_w, *, n_heads: int, hd: int, first_pos: int, rot: int, theta: float, eps: float,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Prepared queries [rows, n_heads, hd] fp32 from bf16 projection rows qk [rows, qkw]."""
+    _dev(qk, "qk", torch.bfloat16, 2)
+    _dev(q_norm_w, "q_norm_w", torch.float32, 1)
+    rows, qkw = qk.shape
+    if out is None:
+        out = torch.empty((rows, n_heads, hd), dtype=torch.float32, device=qk.device)
+    _dev(out, "out", torch.float32, 3)
+    check(_lib.load().qsa_qprep_rows(_ptr(qk), _ptr(q_norm_w), _ptr(out), rows, first_pos, qkw, n_heads, hd, rot,
+                                     theta, eps, _stream()))
+    return out
+
+
+def qsa_score_rows(q, block_keys, *, first_pos: int, ratio: int, n_blocks_max: Optional[int] = None,
+                   precision: str = "mfma", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """scores [rows, n_blocks_max] fp32 with -inf past each row's complete blocks."""
+    _dev(q, "q", torch.float32, 3)
+    _dev(block_keys, "block_keys", torch.float32, 2)
+    rows, n_heads, hd = q.shape
+    nb = block_keys.shape[0] if n_blocks_max is None else n_blocks_max
+    if out is None:
+        out = torch.empty((rows, nb), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32, 2)
+    check(_lib.load().qsa_score_rows(_ptr(q), _ptr(block_keys), _ptr(out), rows, nb, first_pos, out.stride(0), ratio,
+                                     n_heads, hd, PRECISION[precision], _stream()))
+    return out
+
+
+def indexer_debug_dequant(keys_fp4, key_scale, key_gscale, block_table_row, n: int, mode: int) -> torch.Tensor:
+    """[n, D] fp32 decoder output for one block-table row (mode 0 code, 1 code*gscale, 2 fp16 operand)."""
+    P, epb, half = keys_fp4.shape
+    out = torch.empty((n, 2 * half), dtype=torch.float32, device=keys_fp4.device)
+    check(_lib.load().indexer_debug_dequant(_ptr(keys_fp4), _ptr(key_scale), _ptr(key_gscale),
+                                            _ptr(block_table_row), n, 2 * half, epb, P, mode, _ptr(out), _stream()))
+    return out

@@ -1,0 +1,84 @@
+"""The C-ABI library loads, exports every symbol include/indexer.h declares, and its host
+argument checks reject bad calls before any HIP call (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_lightning_block_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "indexer.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="HIP library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_matches_binding():
+    names = declared_functions()
+    assert names == sorted(_lib.SIGNATURES), names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _score_rows(lib, **over):
+    args = dict(q=8, q_dtype=0, w=16, keys=256, scale=512, gscale=1024, bt=2048, bt_stride=4, valid=4096, T=1, H=4,
+                D=64, epb=16, max_lb=4, P=4, prec=1, scores=8192, stride=64, n_cols=64)
+    args.update(over)
+    return lib.indexer_score_rows(args["q"], args["q_dtype"], args["w"], args["keys"], args["scale"], args["gscale"],
+                                  args["bt"], args["bt_stride"], args["valid"], args["T"], args["H"], args["D"],
+                                  args["epb"], args["max_lb"], args["P"], args["prec"], args["scores"], args["stride"],
+                                  args["n_cols"], None)
+
+
+def test_argument_checks_without_gpu():
+    lib = _lib.load()
+    assert _score_rows(lib, q=None) == _lib.IDX_ERR_NULL
+    assert b"required" in lib.indexer_last_error()
+    assert _score_rows(lib, D=96) == _lib.IDX_ERR_UNSUPPORTED
+    assert _score_rows(lib, H=65) == _lib.IDX_ERR_UNSUPPORTED
+    assert _score_rows(lib, epb=0) == _lib.IDX_ERR_SHAPE
+    assert _score_rows(lib, bt_stride=3) == _lib.IDX_ERR_SHAPE
+    assert _score_rows(lib, prec=7) == _lib.IDX_ERR_UNSUPPORTED
+    assert _score_rows(lib, keys=264) == _lib.IDX_ERR_SHAPE       # misaligned key pool
+    assert _score_rows(lib, stride=10) == _lib.IDX_ERR_SHAPE
+    assert _score_rows(lib, T=0) == _lib.IDX_OK                   # no work: no launch
+    assert lib.indexer_last_error() == b""
+    # select
+    assert lib.indexer_topk_select(16, 64, None, 0, 0, 2, 64, 0, 32, None, None, 0, None) == _lib.IDX_ERR_UNSUPPORTED
+    assert lib.indexer_topk_select(16, 64, None, 0, 0, 2, 64, 8, None, None, None, 0, None) == _lib.IDX_ERR_NULL
+    assert lib.indexer_topk_select(16, 60, None, 0, 0, 2, 64, 8, 32, None, None, 0, None) == _lib.IDX_ERR_SHAPE
+    assert lib.indexer_topk_select(16, 64, None, 0, 0, 0, 64, 8, 32, None, None, 0, None) == _lib.IDX_OK
+    # fused: workspace too small is reported before any launch
+    rc = lib.indexer_score_topk(8, 0, 16, 256, 512, 1024, 2048, 4, 4096, 1, 4, 64, 16, 4, 4, 8, 1, 8192, None, 256, 16,
+                                None)
+    assert rc == _lib.IDX_ERR_WORKSPACE
+    # QSA
+    assert lib.qsa_block_pool(None, 16, 32, 0, 1, 16, 128, 64, 1e4, 1e-6, None) == _lib.IDX_ERR_NULL
+    assert lib.qsa_block_pool(16, 16, 32, 0, 1, 16, 100, 64, 1e4, 1e-6, None) == _lib.IDX_ERR_UNSUPPORTED
+    assert lib.qsa_block_pool(16, 16, 32, 0, 0, 16, 128, 64, 1e4, 1e-6, None) == _lib.IDX_OK
+    assert lib.qsa_qprep_rows(16, 16, 32, 4, 0, 100, 1, 128, 64, 1e4, 1e-6, None) == _lib.IDX_ERR_SHAPE
+    assert lib.qsa_score_rows(16, 32, 48, 4, 64, 0, 32, 16, 8, 128, 1, None) == _lib.IDX_ERR_SHAPE
+    assert lib.indexer_debug_dequant(16, 16, 16, 16, 4, 64, 16, 4, 3, 64, None) == _lib.IDX_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes_are_device_independent():
+    lib = _lib.load()
+    small = lib.indexer_topk_workspace_size(4, 4096, 512)
+    assert small == 0 or small == 256        # one segment: no candidate buffers
+    big = lib.indexer_topk_workspace_size(32, 262144, 2048)
+    assert big >= 2 * 32 * (262144 // 32768) * 2048 * 8
+    fused = lib.indexer_score_topk_workspace_size(32, 4096, 64, 2048)
+    assert fused >= 32 * 262144 * 4 + big
+    assert lib.indexer_topk_workspace_size(0, 10, 10) == 0

@@ -1,0 +1,193 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.  Needs an MI355X."""
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_lightning_block_amd as salb
+from oracle import indexer, nvfp4
+from tests.parity import check_scores, check_topk, oracle_rows, to_dev
+from workloads import make
+from workloads.configs import csa, e4m3_encode_rne
+
+pytestmark = pytest.mark.gpu
+
+
+def _row(t):
+    return t.cpu().numpy()
+
+
+# ------------------------------------------------------------------ dequant
+
+def _exhaustive_pool():
+    """Every byte in every nibble position and every scale byte (NaN codes excluded)."""
+    scales = np.array([c for c in range(256) if (c & 0x7f) != 0x7f], dtype=np.uint8)   # 254 codes
+    D, epb = 64, 16
+    n = len(scales) * 8                   # 8 keys per scale code, 32 bytes each = all 256 byte values
+    keys = np.zeros((n, D // 2), dtype=np.uint8)
+    sc = np.zeros((n, D // 16), dtype=np.uint8)
+    for i, s in enumerate(scales):
+        for j in range(8):
+            keys[i * 8 + j] = np.arange(32 * j, 32 * j + 32, dtype=np.uint8)
+            sc[i * 8 + j] = s
+    P = n // epb
+    g = np.linspace(0.5, 2.0, P).astype(np.float32)
+    return keys.reshape(P, epb, D // 2), sc.reshape(P, epb, D // 16), g, epb
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_dequant_bit_exact_exhaustive(mode):
+    keys, sc, g, epb = _exhaustive_pool()
+    P = keys.shape[0]
+    bt = np.random.default_rng(0).permutation(P).astype(np.int32)
+    n = P * epb
+    out = salb.indexer_debug_dequant(torch.from_numpy(keys).cuda(), torch.from_numpy(sc).cuda(),
+                                     torch.from_numpy(g).cuda(), torch.from_numpy(bt).cuda(), n, mode)
+    c, gg = nvfp4.dequant_row(keys, sc, g, bt, n, epb)
+    ref = nvfp4.dequant_f32(c, gg) if mode == 1 else c.astype(np.float32)
+    got = out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))   # bit-exact, -0.0 included
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_dequant_bit_exact_configs(cfg):
+    w = make(cfg, reduced=1 if cfg != 1 else 0)
+    d = to_dev(w)
+    for t in range(min(w.T, 2)):
+        n = int(w.valid_lens[t])
+        c, gg = nvfp4.dequant_row(w.keys_fp4, w.key_scale, w.key_gscale, w.block_table[t], n, w.epb)
+        for mode, ref in ((0, c.astype(np.float32)), (1, nvfp4.dequant_f32(c, gg)), (2, c.astype(np.float32))):
+            got = salb.indexer_debug_dequant(d["keys_fp4"], d["key_scale"], d["key_gscale"], d["block_table"][t], n,
+                                             mode).cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (cfg, t, mode)
+
+
+# ------------------------------------------------------------------ scores
+
+CASES = [(1, 0), (2, 1), (3, 1), (4, 1)]
+
+
+@pytest.mark.parametrize("precision", ["fp32", "mfma"])
+@pytest.mark.parametrize("cfg,reduced", CASES)
+def test_score_rows(cfg, reduced, precision):
+    w = make(cfg, reduced)
+    d = to_dev(w)
+    n_cols = w.max_lb * w.epb
+    out = salb.indexer_score_rows(**d, n_cols=n_cols, precision=precision)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref, amag = oracle_rows(w)
+    for t in range(w.T):
+        v = int(w.valid_lens[t])
+        check_scores(got[t], ref[t], amag[t], precision, f"cfg{cfg} t{t}")
+        assert np.all(np.isneginf(got[t, v:])), "tail must be -inf"
+
+
+@pytest.mark.parametrize("precision", ["fp32", "mfma"])
+@pytest.mark.parametrize("cfg,reduced", CASES)
+def test_score_topk(cfg, reduced, precision):
+    w = make(cfg, reduced)
+    d = to_dev(w)
+    idx, val = salb.indexer_score_topk(**d, top_k=w.top_k, precision=precision, with_scores=True)
+    torch.cuda.synchronize()
+    gi, gv = idx.cpu().numpy(), val.cpu().numpy()
+    ref, amag = oracle_rows(w)
+    for t in range(w.T):
+        check_topk(gi[t], gv[t], ref[t], amag[t], w.top_k, precision, f"cfg{cfg} t{t}")
+
+
+def test_tiny_config_exact_topk_fp32():
+    """Config 1 on the FP32 path: the selected sets equal the oracle's exactly except within tolerance;
+    the short row (valid 17 < k) selects every key, zero scores ordered by index."""
+    w = make(1)
+    d = to_dev(w)
+    idx, val = salb.indexer_score_topk(**d, top_k=w.top_k, precision="fp32", with_scores=True)
+    gi = _row(idx)
+    ref, _ = oracle_rows(w)
+    o_idx, _ = indexer.topk(ref[3], w.top_k)
+    assert gi[3].tolist() == o_idx.tolist()
+
+
+def test_determinism():
+    w = make(2, reduced=1)
+    d = to_dev(w)
+    a = salb.indexer_score_topk(**d, top_k=w.top_k, precision="mfma", with_scores=True)
+    b = salb.indexer_score_topk(**d, top_k=w.top_k, precision="mfma", with_scores=True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
+
+
+@pytest.mark.parametrize("precision", ["fp32", "mfma"])
+def test_edge_valid_lens_and_tables(precision):
+    """valid_len in {0, 1, < k, not a multiple of epb, = capacity}; per-row tables; -1 in unread slots;
+    a duplicated page (equal scores: the lower index wins)."""
+    T, epb, max_lb, k = 6, 64, 40, 100
+    w = csa("edges", [77], T=T, H=64, D=128, epb=epb, P=64, max_lb=max_lb, top_k=k,
+            valid_lens=np.array([0, 1, 99, 1000, max_lb * epb, 333]), dist="gauss", w_scale=1 / 64, table="per_row")
+    bt = w.block_table.copy()
+    for t in range(T):
+        used = -(-int(w.valid_lens[t]) // epb)
+        bt[t, used:] = -1
+    bt[5, 3] = bt[5, 1]          # duplicate page inside row 5's valid range (333 > 4*64)
+    w.block_table = bt
+    d = to_dev(w)
+    idx, val = salb.indexer_score_topk(**d, top_k=k, precision=precision, with_scores=True)
+    rows = salb.indexer_score_rows(**d, n_cols=max_lb * epb, precision=precision)
+    torch.cuda.synchronize()
+    gi, gv, gr = _row(idx), _row(val), _row(rows)
+    ref, amag = oracle_rows(w)
+    for t in range(T):
+        check_scores(gr[t], ref[t], amag[t], precision, f"edge t{t}")
+        check_topk(gi[t], gv[t], ref[t], amag[t], k, precision, f"edge t{t}")
+    assert np.all(gi[0] == -1)
+    assert gi[1][0] == 0 and np.all(gi[1][1:] == -1)
+    # duplicated page: bit-equal scores at both logical positions
+    assert np.array_equal(gr[5, 3 * epb:4 * epb], gr[5, 1 * epb:2 * epb])
+
+
+def test_epb_not_multiple_of_16():
+    w = csa("odd_epb", [78], T=3, H=16, D=64, epb=7, P=50, max_lb=40, top_k=20,
+            valid_lens=np.array([280, 45, 7]), dist="tiny", table="per_row")
+    d = to_dev(w)
+    ref, amag = oracle_rows(w)
+    for precision in ("fp32", "mfma"):
+        rows = salb.indexer_score_rows(**d, n_cols=280, precision=precision)
+        idx, val = salb.indexer_score_topk(**d, top_k=20, precision=precision, with_scores=True)
+        gr, gi, gv = _row(rows), _row(idx), _row(val)
+        for t in range(3):
+            check_scores(gr[t], ref[t], amag[t], precision, f"odd epb t{t} {precision}")
+            check_topk(gi[t], gv[t], ref[t], amag[t], 20, precision, f"odd epb t{t} {precision}")
+
+
+# ------------------------------------------------------------------ select on given scores
+
+@pytest.mark.parametrize("n_cols,k", [(1000, 32), (4096, 512), (70000, 2048), (300000, 2048), (40000, 256)])
+def test_topk_select_exact(n_cols, k):
+    """Selection alone on fixed fp32 scores is exact: indices equal the oracle's, ties included."""
+    rng = np.random.default_rng(n_cols)
+    rows = 3
+    s = rng.standard_normal((rows, n_cols)).astype(np.float32)
+    s[0, ::7] = 1.5                      # heavy ties
+    s[1] = np.round(s[1] * 4) / 4         # coarse values: ties at the threshold
+    s[2, : n_cols // 2] = 0.0
+    s[2, 5] = -0.0
+    valid = np.array([n_cols, n_cols - 17, max(0, k - 5)], dtype=np.int32)
+    idx, val = salb.indexer_topk_select(torch.from_numpy(s).cuda(), k, valid_lens=torch.from_numpy(valid).cuda(),
+                                        with_scores=True)
+    gi, gv = _row(idx), _row(val)
+    for r in range(rows):
+        o_idx, o_val = indexer.topk(s[r, : valid[r]].astype(np.float64), k)
+        assert gi[r].tolist() == o_idx.tolist(), r
+        kk = min(k, int(valid[r]))
+        assert np.array_equal(gv[r][:kk], o_val[:kk].astype(np.float32))
+
+
+def test_topk_select_causal_rule():
+    rng = np.random.default_rng(9)
+    rows, nb, ratio, first = 5, 64, 16, 900
+    s = rng.standard_normal((rows, nb)).astype(np.float32)
+    idx, _ = salb.indexer_topk_select(torch.from_numpy(s).cuda(), 10, first_pos=first, ratio=ratio)
+    gi = _row(idx)
+    for r in range(rows):
+        v = min(nb, (first + r + 1) // ratio)
+        o_idx, _ = indexer.topk(s[r, :v].astype(np.float64), 10)
+        assert gi[r].tolist() == o_idx.tolist()
