@@ -26,6 +26,8 @@ FLAGS = [
     "-Wno-unused-result",
     # packed fp32 instructions stay off: only scalar and fp16-packed VALU forms are emitted
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results straight into VGPRs: the epilogue reads them without accvgpr copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

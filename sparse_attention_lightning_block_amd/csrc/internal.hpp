@@ -27,6 +27,7 @@ struct ScoreArgs {
   int chunk;       // keys per workgroup
   int n_chunks;
   int pid_cap;     // LDS slots for the chunk's block-table entries
+  int swizzle;     // 1: chunk-major XCD grouping (see score_tile)
 };
 
 hipError_t launch_score_rows(ScoreArgs a, int precision, hipStream_t st);

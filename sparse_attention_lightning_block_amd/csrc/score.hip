@@ -32,47 +32,6 @@ namespace salb {
 
 // ------------------------------------------------------------------ helpers
 
-template <int D>
-struct KeySlice {
-  // One lane's share of one key for the MFMA operand: D/4 consecutive dims
-  // (D/8 bytes of codes) and their D/64 scale bytes.
-  static constexpr int kWords = D / 32;
-  uint32_t w[kWords];
-  uint32_t sc;
-};
-
-template <int D>
-__device__ __forceinline__ void load_slice(KeySlice<D>& ks, const uint8_t* __restrict__ keys,
-                                           const uint8_t* __restrict__ kscale, int64_t e, int quarter) {
-  const uint8_t* kp = keys + e * (D / 2) + quarter * (D / 8);
-  const uint8_t* sp = kscale + e * (D / 16) + quarter * (D / 64);
-  if constexpr (D == 64) {
-    u32x2 v = *reinterpret_cast<const u32x2*>(kp);
-    ks.w[0] = v[0];
-    ks.w[1] = v[1];
-    ks.sc = *sp;
-  } else if constexpr (D == 128) {
-    u32x4 v = *reinterpret_cast<const u32x4*>(kp);
-    ks.w[0] = v[0];
-    ks.w[1] = v[1];
-    ks.w[2] = v[2];
-    ks.w[3] = v[3];
-    ks.sc = *reinterpret_cast<const uint16_t*>(sp);
-  } else {
-    u32x4 v0 = *reinterpret_cast<const u32x4*>(kp);
-    u32x4 v1 = *reinterpret_cast<const u32x4*>(kp + 16);
-    ks.w[0] = v0[0];
-    ks.w[1] = v0[1];
-    ks.w[2] = v0[2];
-    ks.w[3] = v0[3];
-    ks.w[4] = v1[0];
-    ks.w[5] = v1[1];
-    ks.w[6] = v1[2];
-    ks.w[7] = v1[3];
-    ks.sc = *reinterpret_cast<const uint32_t*>(sp);
-  }
-}
-
 __device__ __forceinline__ float load_q(const void* q, int bf16, int64_t i) {
   if (bf16) {
     uint32_t b = reinterpret_cast<const uint16_t*>(q)[i];
@@ -92,18 +51,260 @@ __device__ __forceinline__ int prescale_exp(float mx) {
 
 // ------------------------------------------------------------------ MFMA scorer
 
-template <int MT, int D>
-__global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
-  constexpr int HP = MT * 16;     // padded head count
-  constexpr int QLD = D + 8;      // padded LDS row (halves)
-  constexpr int KW = D / 32;      // K-steps of 32 dims
-  extern __shared__ __align__(16) unsigned char smem[];
-  _Float16* qh = reinterpret_cast<_Float16*>(smem);                       // [HP][QLD]
-  float* wsc = reinterpret_cast<float*>(smem + HP * QLD * 2);              // [HP]
-  int* pid = reinterpret_cast<int*>(wsc + HP);                             // [pid_cap]
-  float* pgs = reinterpret_cast<float*>(pid + a.pid_cap);                  // [pid_cap]
+// ReLU through the integer max: a negative float (sign bit set) is a negative int32,
+// so max(bits, 0) gives +0.0 for it and leaves non-negative values unchanged.  One
+// VALU op, with no NaN canonicalisation.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-  const XcdTile tile = xcd_tile(blockIdx.x, a.T);
+// Raw bytes of one lane's slice of one key: D/8 code bytes and D/64 scale bytes.
+template <int D>
+struct Raw {
+  uint32_t w[D / 32];
+  uint32_t sc;
+};
+
+template <int D>
+__device__ __forceinline__ void load_raw(Raw<D>& r, const uint8_t* codes, const uint8_t* scales) {
+  if constexpr (D == 64) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(codes);
+    r.w[0] = v[0];
+    r.w[1] = v[1];
+    r.sc = *scales;
+  } else if constexpr (D == 128) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(codes);
+    r.w[0] = v[0];
+    r.w[1] = v[1];
+    r.w[2] = v[2];
+    r.w[3] = v[3];
+    r.sc = *reinterpret_cast<const uint16_t*>(scales);
+  } else {
+    const u32x4 v0 = *reinterpret_cast<const u32x4*>(codes);
+    const u32x4 v1 = *reinterpret_cast<const u32x4*>(codes + 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r.w[i] = v0[i];
+      r.w[4 + i] = v1[i];
+    }
+    r.sc = *reinterpret_cast<const uint32_t*>(scales);
+  }
+}
+
+// Eight fp16 code values of K-step kk of a raw slice; the sign of the page's global
+// scale is folded into the exact fp16 group scale (ReLU(g x) = |g| ReLU(sign(g) x)).
+template <int D>
+__device__ __forceinline__ half8v decode_step(const Raw<D>& r, int kk, float sgn) {
+  const _Float16 sh = (_Float16)(e4m3_to_f32((r.sc >> (8 * (kk >> 1))) & 0xffu) * sgn);
+  const half2v s2 = {sh, sh};
+  return decode8_f16(r.w[kk], s2);
+}
+
+// Work tile of a workgroup over (key chunk, row unit): with enough chunks per row,
+// chunks are grouped by XCD (units sharing pages hit one L2); otherwise units are
+// spread round-robin over the XCDs, highest (longest causal) rows first.
+__device__ __forceinline__ XcdTile score_tile(const ScoreArgs& a, int units) {
+  if (a.swizzle) return xcd_tile(blockIdx.x, units);
+  XcdTile t;
+  t.chunk = (int)blockIdx.x / units;
+  t.row = units - 1 - ((int)blockIdx.x % units);
+  return t;
+}
+
+// A operands (per-head power-of-two prescaled fp16 q) and accumulator-row weights
+// of query t, straight from global memory.  Lane (col, quarter) holds, for M-tile
+// mt and K-step kk, q[16 mt + col][quarter * D/4 + 8 kk .. + 8]; the head's max over
+// its D dims spans the four quarter lanes.  Row i of accumulator quarter q of tile
+// mt is head 16 mt + 4 q + i.  Queries past T get zeros.
+template <int MT, int D>
+__device__ __forceinline__ void load_query(const ScoreArgs& a, int t, int lane, half8v (&A)[MT][D / 32],
+                                           float (&wr)[MT][4]) {
+  constexpr int KW = D / 32;
+  const int col = lane & 15, quarter = lane >> 4;
+  const bool has = t < a.T;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int h = mt * 16 + col;
+    const bool hv = has && h < a.H;
+    const int64_t base = ((int64_t)t * a.H + h) * D + quarter * (D / 4);
+    float v[KW][8];
+    float mx = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KW; ++kk) {
+      if (a.q_bf16) {
+        u32x4 u = {0u, 0u, 0u, 0u};
+        if (hv) u = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) + base + kk * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[kk][2 * e] = __uint_as_float(u[e] << 16);
+          v[kk][2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+        }
+      } else {
+        float4v f0 = {0.f, 0.f, 0.f, 0.f}, f1 = {0.f, 0.f, 0.f, 0.f};
+        if (hv) {
+          const float* src = reinterpret_cast<const float*>(a.q) + base + kk * 8;
+          f0 = *reinterpret_cast<const float4v*>(src);
+          f1 = *reinterpret_cast<const float4v*>(src + 4);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[kk][e] = f0[e];
+          v[kk][4 + e] = f1[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[kk][e]));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const int j = prescale_exp(mx);  // exponent of head 16 mt + col
+#pragma unroll
+    for (int kk = 0; kk < KW; ++kk) {
+      half8v hv8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv8[e] = (_Float16)ldexpf(v[kk][e], j);
+      A[mt][kk] = hv8;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hr = mt * 16 + quarter * 4 + i;
+      const int jr = __shfl(j, quarter * 4 + i);
+      wr[mt][i] = (has && hr < a.H) ? ldexpf(a.w[(int64_t)t * a.H + hr], -jr) : 0.0f;
+    }
+  }
+}
+
+template <int MT>
+__device__ __forceinline__ void zero_acc(float4v (&acc)[MT]) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = float4v{0.f, 0.f, 0.f, 0.f};
+}
+
+// Head reduction of one 16-key step: in-lane over 4*MT heads, then across the four
+// lane quarters; lanes 0..15 store the step's 16 scores (keys below s_vend only).
+template <int MT>
+__device__ __forceinline__ void epilogue(const float4v (&acc)[MT], const float (&wr)[MT][4], float gabs, int s0,
+                                         int s_vend, float* out_row, int lane) {
+  float part = 0.0f;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part = fmaf(wr[mt][i], relu_bits(acc[mt][i]), part);
+  part += __shfl_xor(part, 16);
+  part += __shfl_xor(part, 32);
+  const int s = s0 + (lane & 15);
+  if (lane < 16 && s < s_vend) out_row[s] = gabs * part;
+}
+
+// One wave streams the 16-key steps first, first + stride, ... of [s_begin, s_vend)
+// for one query, decoding each lane's key slice straight into the B operand.  Loads
+// run three steps ahead (ring of four raw buffers); the epilogue of step i-1 is issued
+// beside the MFMAs of step i (two accumulator sets).  pid/pgs hold the page ids and
+// global scales of the logical blocks from lb0 on.
+template <int MT, int D, bool UPAGE>
+__device__ __forceinline__ void wave_stream(const ScoreArgs& a, const half8v (&A)[MT][D / 32],
+                                            const float (&wr)[MT][4], const int* pid, const float* pgs, int lb0,
+                                            int s_begin, int s_vend, int first, int stride, float* out_row,
+                                            int lane) {
+  constexpr int KW = D / 32;
+  const int n_vg = (s_vend - s_begin + 15) >> 4;
+  if (first >= n_vg) return;
+  const int col = lane & 15, quarter = lane >> 4;
+  const uint32_t lane_codes = (uint32_t)(quarter * (D / 8));
+  const uint32_t lane_scales = (uint32_t)(quarter * (D / 64));
+
+  auto load_step = [&](int gi, Raw<D>& r, float& g) {
+    const int gc = min(gi, n_vg - 1);  // past the end: re-read valid memory, result unused
+    const int s0 = s_begin + gc * 16;
+    const int s = min(s0 + col, s_vend - 1);
+    if constexpr (UPAGE) {
+      const uint32_t lb = div_epb((uint32_t)s0, a.epb_magic);
+      const int li = (int)lb - lb0;
+      const int p = __builtin_amdgcn_readfirstlane(pid[li]);
+      g = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(pgs[li])));
+      const uint32_t slot = (uint32_t)s - lb * (uint32_t)a.epb;
+      const uint8_t* kb = a.keys + (int64_t)p * a.epb * (D / 2);
+      const uint8_t* sb = a.kscale + (int64_t)p * a.epb * (D / 16);
+      load_raw<D>(r, kb + (slot * (D / 2) + lane_codes), sb + (slot * (D / 16) + lane_scales));
+    } else {
+      const uint32_t lb = div_epb((uint32_t)s, a.epb_magic);
+      const int li = (int)lb - lb0;
+      const int p = pid[li];
+      g = pgs[li];
+      const int64_t e = (int64_t)p * a.epb + (int64_t)((uint32_t)s - lb * (uint32_t)a.epb);
+      load_raw<D>(r, a.keys + e * (D / 2) + lane_codes, a.kscale + e * (D / 16) + lane_scales);
+    }
+  };
+  auto compute = [&](const Raw<D>& r, float g, float4v (&acc)[MT]) {
+    const float sgn = g < 0.0f ? -1.0f : 1.0f;
+#pragma unroll
+    for (int kk = 0; kk < KW; ++kk) {
+      const half8v B = decode_step<D>(r, kk, sgn);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][kk], B, kk == 0 ? float4v{0.f, 0.f, 0.f, 0.f} : acc[mt],
+                                                         0, 0, 0);
+    }
+  };
+
+  Raw<D> R0, R1, R2, R3;
+  float G0, G1, G2, G3;
+  float4v AC0[MT], AC1[MT];
+  zero_acc<MT>(AC1);
+  int gi = first;
+  load_step(gi, R0, G0);
+  load_step(gi + stride, R1, G1);
+  load_step(gi + 2 * stride, R2, G2);
+  int s_prev = 0x3fffffff;  // nothing pending: its stores are masked off
+  float g_prev = 0.0f;
+  bool last_ac1 = false;
+  for (;;) {
+    if (gi >= n_vg) { last_ac1 = true; break; }
+    load_step(gi + 3 * stride, R3, G3);
+    compute(R0, G0, AC0);
+    epilogue<MT>(AC1, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
+    s_prev = s_begin + gi * 16; g_prev = G0; gi += stride;
+
+    if (gi >= n_vg) { last_ac1 = false; break; }
+    load_step(gi + 3 * stride, R0, G0);
+    compute(R1, G1, AC1);
+    epilogue<MT>(AC0, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
+    s_prev = s_begin + gi * 16; g_prev = G1; gi += stride;
+
+    if (gi >= n_vg) { last_ac1 = true; break; }
+    load_step(gi + 3 * stride, R1, G1);
+    compute(R2, G2, AC0);
+    epilogue<MT>(AC1, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
+    s_prev = s_begin + gi * 16; g_prev = G2; gi += stride;
+
+    if (gi >= n_vg) { last_ac1 = false; break; }
+    load_step(gi + 3 * stride, R2, G2);
+    compute(R3, G3, AC1);
+    epilogue<MT>(AC0, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
+    s_prev = s_begin + gi * 16; g_prev = G3; gi += stride;
+  }
+  if (last_ac1) epilogue<MT>(AC1, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
+  else epilogue<MT>(AC0, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
+}
+
+// Loads the page ids and global scales of logical blocks lb0 .. lb0 + n - 1 of row t.
+__device__ __forceinline__ void load_pages(const ScoreArgs& a, int t, int lb0, int n, int* pid, float* pgs, int i0,
+                                           int step) {
+  const int32_t* bt_row = a.bt + (int64_t)t * a.bt_stride;
+  for (int i = i0; i < n; i += step) {
+    const int p = bt_row[lb0 + i];
+    pid[i] = p;
+    pgs[i] = a.gscale[p];
+  }
+}
+
+// Split scorer: one query per workgroup, the chunk's 16-key steps dealt round-robin
+// to the four waves.  Used when there are fewer than four query rows.
+template <int MT, int D, bool UPAGE>
+__global__ __launch_bounds__(256) void score_mfma_split_kernel(ScoreArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int* pid = reinterpret_cast<int*>(smem);
+  float* pgs = reinterpret_cast<float*>(pid + a.pid_cap);
+
+  const XcdTile tile = score_tile(a, a.T);
   if (tile.chunk >= a.n_chunks) return;
   const int t = tile.row;
   const int valid = a.valid_lens[t];
@@ -112,137 +313,158 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreArgs a) {
   if (s_begin >= s_lim) return;
   const int s_end = min(s_begin + a.chunk, s_lim);
   const int s_vend = min(s_end, valid);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float* out_row = a.scores + (int64_t)t * a.score_stride;
+  for (int s = max(s_vend, s_begin) + tid; s < s_end; s += 256) out_row[s] = -INFINITY;
+  if (s_vend <= s_begin) return;
 
-  // -- pages of this chunk
-  int lb0 = div_epb((uint32_t)s_begin, a.epb_magic);
-  int npages = 0;
-  if (s_vend > s_begin) npages = (int)div_epb((uint32_t)(s_vend - 1), a.epb_magic) - lb0 + 1;
-  const int32_t* bt_row = a.bt + (int64_t)t * a.bt_stride;
-  for (int i = tid; i < npages; i += 256) {
-    int p = bt_row[lb0 + i];
-    pid[i] = p;
-    pgs[i] = a.gscale[p];
-  }
+  const int lb0 = (int)div_epb((uint32_t)s_begin, a.epb_magic);
+  const int npages = (int)div_epb((uint32_t)(s_vend - 1), a.epb_magic) - lb0 + 1;
+  load_pages(a, t, lb0, npages, pid, pgs, tid, 256);
+  half8v A[MT][D / 32];
+  float wr[MT][4];
+  load_query<MT, D>(a, t, lane, A, wr);
+  __syncthreads();
+  wave_stream<MT, D, UPAGE>(a, A, wr, pid, pgs, lb0, s_begin, s_vend, wave, 4, out_row, lane);
+}
 
-  // -- q[t] -> LDS as per-head prescaled fp16, and the matching head weights
-  const int64_t qbase = (int64_t)t * a.H * D;
-  for (int h = wave; h < HP; h += 4) {
-    constexpr int PER = D / 64;
-    float v[PER];
-    float mx = 0.0f;
+// Group scorer: four consecutive query rows per workgroup (wave w scores row 4u + w)
+// over one chunk of keys.  When the four rows resolve the chunk to the same pages
+// (one sequence; checked at run time) each 64-key tile is decoded ONCE into LDS as
+// fp16 MFMA B operands and read by all four waves -- a quarter of the decode work
+// and of the key traffic per query.  Otherwise every wave streams its own row.
+template <int MT, int D, bool UPAGE>
+__global__ __launch_bounds__(256) void score_mfma_group_kernel(ScoreArgs a) {
+  constexpr int KW = D / 32;
+  constexpr int BLD = D + 8;  // LDS row of one decoded key (halves), padded against bank conflicts
+  constexpr int TILE = 64;
+  extern __shared__ __align__(16) unsigned char smem[];
+  _Float16* bbuf = reinterpret_cast<_Float16*>(smem);                          // [2][TILE][BLD]
+  float* gbuf = reinterpret_cast<float*>(smem + 2 * TILE * BLD * 2);           // [2][TILE]
+  int* pid = reinterpret_cast<int*>(gbuf + 2 * TILE);                          // [4][pid_cap]
+  float* pgs = reinterpret_cast<float*>(pid + 4 * a.pid_cap);                  // [4][pid_cap]
+  __shared__ int s_vend_w[4];
+  __shared__ int s_mismatch;
+
+  const int units = (a.T + 3) >> 2;
+  const XcdTile tile = score_tile(a, units);
+  if (tile.chunk >= a.n_chunks) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = tile.row * 4 + wave;
+  const bool has = t < a.T;
+  const int valid = has ? a.valid_lens[t] : 0;
+  const int s_begin = tile.chunk * a.chunk;
+  const int s_lim = a.write_tail ? a.n_cols : valid;
+  const int s_end = has ? min(s_begin + a.chunk, s_lim) : s_begin;
+  const int s_vend = max(s_begin, min(s_end, valid));
+  float* out_row = a.scores + (int64_t)(has ? t : 0) * a.score_stride;
+  for (int s = s_vend + lane; s < s_end; s += 64) out_row[s] = -INFINITY;
+
+  // pages of each row; the row reaching furthest leads
+  const int lb0 = (int)div_epb((uint32_t)s_begin, a.epb_magic);
+  const int np = s_vend > s_begin ? (int)div_epb((uint32_t)(s_vend - 1), a.epb_magic) - lb0 + 1 : 0;
+  int* mypid = pid + wave * a.pid_cap;
+  float* mypgs = pgs + wave * a.pid_cap;
+  if (has) load_pages(a, t, lb0, np, mypid, mypgs, lane, 64);
+  if (lane == 0) s_vend_w[wave] = s_vend;
+  if (tid == 0) s_mismatch = 0;
+  half8v A[MT][KW];
+  float wr[MT][4];
+  load_query<MT, D>(a, t, lane, A, wr);
+  __syncthreads();
+  int lead = 0, vmax = s_vend_w[0];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      v[i] = (h < a.H) ? load_q(a.q, a.q_bf16, qbase + (int64_t)h * D + lane * PER + i) : 0.0f;
-      mx = fmaxf(mx, fabsf(v[i]));
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    const int j = prescale_exp(mx);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) qh[h * QLD + lane * PER + i] = (_Float16)ldexpf(v[i], j);
-    if (lane == 0) wsc[h] = (h < a.H) ? ldexpf(a.w[(int64_t)t * a.H + h], -j) : 0.0f;
+  for (int w = 1; w < 4; ++w)
+    if (s_vend_w[w] > vmax) { vmax = s_vend_w[w]; lead = w; }
+  if (vmax <= s_begin) return;  // no key of this chunk is valid for any of the rows
+  {
+    const int* lp = pid + lead * a.pid_cap;
+    bool diff = false;
+    for (int i = lane; i < np; i += 64) diff |= mypid[i] != lp[i];
+    if (__ballot(diff) != 0ull && lane == 0) s_mismatch = 1;
   }
   __syncthreads();
 
-  // -- A operands (q) and the accumulator-row weights, per wave
-  const int quarter = lane >> 4;  // which D/4 slice of a key / q row this lane holds
-  const int col = lane & 15;
-  half8v A[MT][KW];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int kk = 0; kk < KW; ++kk)
-      A[mt][kk] = *reinterpret_cast<const half8v*>(qh + (mt * 16 + col) * QLD + quarter * (D / 4) + kk * 8);
-  float wr[MT][4];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wr[mt][i] = wsc[mt * 16 + quarter * 4 + i];
+  if (s_mismatch) {  // rows of different sequences: each wave streams its own row
+    wave_stream<MT, D, UPAGE>(a, A, wr, mypid, mypgs, lb0, s_begin, s_vend, 0, 1, out_row, lane);
+    return;
+  }
 
-  // -- stream the chunk, 16 keys per wave step
-  const int n_groups = (s_end - s_begin + 15) >> 4;
-  KeySlice<D> cur, nxt;
-  float g_cur = 0.0f, g_nxt = 0.0f;
-  bool in_cur = false, in_nxt = false;
-
-  auto fetch = [&](int gi, KeySlice<D>& ks, float& g, bool& in) {
-    const int s = s_begin + gi * 16 + col;
-    in = s < s_vend;
-    if (in) {
-      const uint32_t lb = div_epb((uint32_t)s, a.epb_magic);
-      const int li = (int)lb - lb0;
-      const int p = pid[li];
-      g = pgs[li];
-      const int64_t e = (int64_t)p * a.epb + (s - (int)lb * a.epb);
-      load_slice<D>(ks, a.keys, a.kscale, e, quarter);
-    } else {
+  // ---- shared pages: decode each 64-key tile once into LDS
+  const int* lpid = pid + lead * a.pid_cap;
+  const float* lpgs = pgs + lead * a.pid_cap;
+  const int n_tiles = (vmax - s_begin + TILE - 1) / TILE;
+  const int kt = tid >> 2, qs = tid & 3;  // staging: key of the tile, D/4 slice of it
+  Raw<D> raw;
+  float graw;
+  auto load_tile = [&](int j) {
+    const int s = min(s_begin + j * TILE + kt, vmax - 1);
+    const uint32_t lb = div_epb((uint32_t)s, a.epb_magic);
+    const int li = (int)lb - lb0;
+    const int p = lpid[li];
+    graw = lpgs[li];
+    const int64_t e = (int64_t)p * a.epb + (int64_t)((uint32_t)s - lb * (uint32_t)a.epb);
+    load_raw<D>(raw, a.keys + e * (D / 2) + qs * (D / 8), a.kscale + e * (D / 16) + qs * (D / 64));
+  };
+  auto decode_tile = [&](int buf) {
+    const float sgn = graw < 0.0f ? -1.0f : 1.0f;
+    _Float16* dst = bbuf + (buf * TILE + kt) * BLD + qs * (D / 4);
 #pragma unroll
-      for (int i = 0; i < KW; ++i) ks.w[i] = 0u;
-      ks.sc = 0u;
-      g = 0.0f;
+    for (int kk = 0; kk < KW; ++kk) *reinterpret_cast<half8v*>(dst + kk * 8) = decode_step<D>(raw, kk, sgn);
+    if (qs == 0) gbuf[buf * TILE + kt] = fabsf(graw);
+  };
+
+  const int col = lane & 15, quarter = lane >> 4;
+  float4v AC0[MT], AC1[MT];
+  zero_acc<MT>(AC1);
+  int s_prev = 0x3fffffff;  // pending epilogue (accumulators AC1) of the previous tile
+  float g_prev = 0.0f;
+  auto mfma_step = [&](int buf, int k, float4v (&acc)[MT]) {
+    const _Float16* src = bbuf + (buf * TILE + k * 16 + col) * BLD + quarter * (D / 4);
+#pragma unroll
+    for (int kk = 0; kk < KW; ++kk) {
+      const half8v B = *reinterpret_cast<const half8v*>(src + kk * 8);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][kk], B, kk == 0 ? float4v{0.f, 0.f, 0.f, 0.f} : acc[mt],
+                                                         0, 0, 0);
     }
   };
 
-  int gi = wave;
-  if (gi < n_groups) fetch(gi, cur, g_cur, in_cur);
-  for (; gi < n_groups; gi += 4) {
-    const int s0 = s_begin + gi * 16;
-    const bool has_next = gi + 4 < n_groups;
-    if (has_next) fetch(gi + 4, nxt, g_nxt, in_nxt);
-
-    if (s0 < s_vend) {
-      float4v acc[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int kk = 0; kk < KW; ++kk) {
-        const half2v s2 = splat_scale_f16((cur.sc >> (8 * (kk >> 1))) & 0xffu);
-        const half8v B = decode8_f16(cur.w[kk], s2);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][kk], B, acc[mt], 0, 0, 0);
-      }
-      // ReLU(g * dot) = |g| * ReLU(sign(g) * dot): the page scale leaves the ReLU.
-      float part = 0.0f;
-      float gabs = g_cur;
-      if (__ballot(g_cur < 0.0f) == 0ull) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) part = fmaf(wr[mt][i], fmaxf(acc[mt][i], 0.0f), part);
-      } else {
-        const float sg = g_cur < 0.0f ? -1.0f : 1.0f;
-        gabs = fabsf(g_cur);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) part = fmaf(wr[mt][i], fmaxf(acc[mt][i] * sg, 0.0f), part);
-      }
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
-      const int s = s0 + col;
-      if (lane < 16 && s < s_end) out_row[s] = in_cur ? gabs * part : -INFINITY;
-    } else {
-      const int s = s0 + col;
-      if (lane < 16 && s < s_end) out_row[s] = -INFINITY;
+  load_tile(0);
+  decode_tile(0);
+  if (n_tiles > 1) load_tile(1);
+  for (int j = 0; j < n_tiles; ++j) {
+    __syncthreads();  // tile j decoded; the other buffer is free again
+    const int buf = j & 1;
+    if (j + 1 < n_tiles) {
+      decode_tile(buf ^ 1);
+      if (j + 2 < n_tiles) load_tile(j + 2);
     }
-    if (has_next) {
-      cur = nxt;
-      g_cur = g_nxt;
-      in_cur = in_nxt;
+    const int t0 = s_begin + j * TILE;
+    if (t0 < s_vend) {
+      const float* gb = gbuf + buf * TILE + col;
+      mfma_step(buf, 0, AC0);
+      epilogue<MT>(AC1, wr, g_prev, s_prev, s_vend, out_row, lane);
+      const float g0 = gb[0], g1 = gb[16], g2 = gb[32], g3 = gb[48];
+      mfma_step(buf, 1, AC1);
+      epilogue<MT>(AC0, wr, g0, t0, s_vend, out_row, lane);
+      mfma_step(buf, 2, AC0);
+      epilogue<MT>(AC1, wr, g1, t0 + 16, s_vend, out_row, lane);
+      mfma_step(buf, 3, AC1);
+      epilogue<MT>(AC0, wr, g2, t0 + 32, s_vend, out_row, lane);
+      s_prev = t0 + 48;
+      g_prev = g3;
     }
   }
+  epilogue<MT>(AC1, wr, g_prev, s_prev, s_vend, out_row, lane);
 }
 
 // ------------------------------------------------------------------ FP32 scorer
 
 template <int D, int HM, int QBF16>
 __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs a) {
-  const XcdTile tile = xcd_tile(blockIdx.x, a.T);
+  const XcdTile tile = score_tile(a, a.T);
   if (tile.chunk >= a.n_chunks) return;
   const int t = tile.row;
   const int valid = a.valid_lens[t];
@@ -330,21 +552,31 @@ __global__ __launch_bounds__(256) void debug_dequant_kernel(const uint8_t* keys,
 // ------------------------------------------------------------------ launchers
 
 template <int MT, int D>
-static hipError_t launch_mfma_t(const ScoreArgs& a, int blocks, hipStream_t st) {
-  constexpr int HP = MT * 16;
-  const size_t lds = (size_t)HP * (D + 8) * 2 + HP * 4 + (size_t)a.pid_cap * 8;
-  hipLaunchKernelGGL((score_mfma_kernel<MT, D>), dim3(blocks), dim3(256), lds, st, a);
+static hipError_t launch_mfma_t(const ScoreArgs& a, int blocks, bool group, hipStream_t st) {
+  if (group) {
+    const size_t lds = (size_t)2 * 64 * (D + 8) * 2 + 2 * 64 * 4 + (size_t)4 * a.pid_cap * 8;
+    if (a.epb % 16 == 0)
+      hipLaunchKernelGGL((score_mfma_group_kernel<MT, D, true>), dim3(blocks), dim3(256), lds, st, a);
+    else
+      hipLaunchKernelGGL((score_mfma_group_kernel<MT, D, false>), dim3(blocks), dim3(256), lds, st, a);
+  } else {
+    const size_t lds = (size_t)a.pid_cap * 8;
+    if (a.epb % 16 == 0)
+      hipLaunchKernelGGL((score_mfma_split_kernel<MT, D, true>), dim3(blocks), dim3(256), lds, st, a);
+    else
+      hipLaunchKernelGGL((score_mfma_split_kernel<MT, D, false>), dim3(blocks), dim3(256), lds, st, a);
+  }
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_mfma_d(const ScoreArgs& a, int blocks, hipStream_t st) {
+static hipError_t launch_mfma_d(const ScoreArgs& a, int blocks, bool group, hipStream_t st) {
   const int mt = (a.H + 15) / 16;
   switch (mt) {
-    case 1: return launch_mfma_t<1, D>(a, blocks, st);
-    case 2: return launch_mfma_t<2, D>(a, blocks, st);
-    case 3: return launch_mfma_t<3, D>(a, blocks, st);
-    default: return launch_mfma_t<4, D>(a, blocks, st);
+    case 1: return launch_mfma_t<1, D>(a, blocks, group, st);
+    case 2: return launch_mfma_t<2, D>(a, blocks, group, st);
+    case 3: return launch_mfma_t<3, D>(a, blocks, group, st);
+    default: return launch_mfma_t<4, D>(a, blocks, group, st);
   }
 }
 
@@ -367,34 +599,42 @@ static hipError_t launch_f32_d(const ScoreArgs& a, int blocks, hipStream_t st) {
   return a.q_bf16 ? launch_f32_q<D, 1>(a, blocks, st) : launch_f32_q<D, 0>(a, blocks, st);
 }
 
-// Keys per workgroup for the MFMA scorer: about a thousand workgroups of work,
-// at least 512 keys (so the per-workgroup q staging stays small) and at most 4096.
-static int mfma_chunk(int T, int n_cols) {
-  const int64_t work = (int64_t)T * n_cols;
-  int64_t c = (work / 1024 + 63) / 64 * 64;
-  if (c < 512) c = 512;
+// Keys per workgroup: enough workgroups to fill the chip a few times over
+// (`target`), multiples of 64, between 256 and 4096, and few enough block-table
+// entries per chunk (<= 500) for the LDS page lists.
+static int chunk_keys(int units, int n_cols, int epb, int target) {
+  int64_t n_chunks = (target + units - 1) / units;
+  if (n_chunks < 1) n_chunks = 1;
+  int64_t c = ((int64_t)n_cols + n_chunks - 1) / n_chunks;
+  c = (c + 63) / 64 * 64;
+  if (c < 256) c = 256;
   if (c > 4096) c = 4096;
+  const int64_t cap = (int64_t)500 * epb / 64 * 64;
+  if (c > cap) c = cap < 64 ? 64 : cap;
   return (int)c;
 }
 
 hipError_t launch_score_rows(ScoreArgs a, int precision, hipStream_t st) {
+  const bool group = precision == 1 && a.T >= 4;
+  const int units = group ? (a.T + 3) / 4 : a.T;
   if (precision == 1) {
-    a.chunk = mfma_chunk(a.T, a.n_cols);
+    a.chunk = chunk_keys(units, a.n_cols, a.epb, group ? 768 : 1024);
     a.pid_cap = a.chunk / a.epb + 2;
   } else {
     a.chunk = 256;
     a.pid_cap = 0;
   }
   a.n_chunks = (a.n_cols + a.chunk - 1) / a.chunk;
-  const int64_t padded = (int64_t)((a.n_chunks + kXcds - 1) / kXcds) * kXcds;
-  const int64_t blocks = padded * a.T;
+  a.swizzle = a.n_chunks >= kXcds;
+  const int64_t per_unit = a.swizzle ? (int64_t)((a.n_chunks + kXcds - 1) / kXcds) * kXcds : a.n_chunks;
+  const int64_t blocks = per_unit * units;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (precision == 1) {
     switch (a.D) {
-      case 64: return launch_mfma_d<64>(a, (int)blocks, st);
-      case 128: return launch_mfma_d<128>(a, (int)blocks, st);
-      default: return launch_mfma_d<256>(a, (int)blocks, st);
+      case 64: return launch_mfma_d<64>(a, (int)blocks, group, st);
+      case 128: return launch_mfma_d<128>(a, (int)blocks, group, st);
+      default: return launch_mfma_d<256>(a, (int)blocks, group, st);
     }
   }
   switch (a.D) {
