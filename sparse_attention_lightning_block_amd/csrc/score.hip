@@ -28,6 +28,14 @@
 #include "internal.hpp"
 #include "nvfp4.hpp"
 
+// Workgroups to aim for when cutting rows into key chunks (build-time tunables).
+#ifndef SALB_GROUP_WGS
+#define SALB_GROUP_WGS 512
+#endif
+#ifndef SALB_SPLIT_WGS
+#define SALB_SPLIT_WGS 1024
+#endif
+
 namespace salb {
 
 // ------------------------------------------------------------------ helpers
@@ -179,10 +187,9 @@ __device__ __forceinline__ void zero_acc(float4v (&acc)[MT]) {
 }
 
 // Head reduction of one 16-key step: in-lane over 4*MT heads, then across the four
-// lane quarters; lanes 0..15 store the step's 16 scores (keys below s_vend only).
+// lane quarters; every lane ends with the total of its key column (lane & 15).
 template <int MT>
-__device__ __forceinline__ void epilogue(const float4v (&acc)[MT], const float (&wr)[MT][4], float gabs, int s0,
-                                         int s_vend, float* out_row, int lane) {
+__device__ __forceinline__ float head_sum(const float4v (&acc)[MT], const float (&wr)[MT][4]) {
   float part = 0.0f;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -190,6 +197,15 @@ __device__ __forceinline__ void epilogue(const float4v (&acc)[MT], const float (
     for (int i = 0; i < 4; ++i) part = fmaf(wr[mt][i], relu_bits(acc[mt][i]), part);
   part += __shfl_xor(part, 16);
   part += __shfl_xor(part, 32);
+  return part;
+}
+
+// Head reduction and store of one step: lanes 0..15 store its 16 scores (keys below
+// s_vend only).
+template <int MT>
+__device__ __forceinline__ void epilogue(const float4v (&acc)[MT], const float (&wr)[MT][4], float gabs, int s0,
+                                         int s_vend, float* out_row, int lane) {
+  const float part = head_sum<MT>(acc, wr);
   const int s = s0 + (lane & 15);
   if (lane < 16 && s < s_vend) out_row[s] = gabs * part;
 }
@@ -328,11 +344,14 @@ __global__ __launch_bounds__(256) void score_mfma_split_kernel(ScoreArgs a) {
   wave_stream<MT, D, UPAGE>(a, A, wr, pid, pgs, lb0, s_begin, s_vend, wave, 4, out_row, lane);
 }
 
-// Group scorer: four consecutive query rows per workgroup (wave w scores row 4u + w)
-// over one chunk of keys.  When the four rows resolve the chunk to the same pages
-// (one sequence; checked at run time) each 64-key tile is decoded ONCE into LDS as
-// fp16 MFMA B operands and read by all four waves -- a quarter of the decode work
-// and of the key traffic per query.  Otherwise every wave streams its own row.
+// Group scorer: a workgroup scores four query rows (one per wave) over one chunk of
+// keys.  For up to 256 rows, the rows are grouped by decreasing valid length, so the
+// four rows of a workgroup end at about the same key.  When the four rows resolve the
+// chunk to the same pages (one sequence; checked at run time) each 64-key tile is
+// decoded ONCE into LDS as fp16 MFMA B operands and read by all four waves -- a
+// quarter of the decode work and of the key traffic per row -- and the decode of tile
+// j+1 is spread between the MFMA steps of tile j.  Otherwise every wave streams its
+// own row.
 template <int MT, int D, bool UPAGE>
 __global__ __launch_bounds__(256) void score_mfma_group_kernel(ScoreArgs a) {
   constexpr int KW = D / 32;
@@ -344,13 +363,35 @@ __global__ __launch_bounds__(256) void score_mfma_group_kernel(ScoreArgs a) {
   int* pid = reinterpret_cast<int*>(gbuf + 2 * TILE);                          // [4][pid_cap]
   float* pgs = reinterpret_cast<float*>(pid + 4 * a.pid_cap);                  // [4][pid_cap]
   __shared__ int s_vend_w[4];
+  __shared__ int s_rows[4];
   __shared__ int s_mismatch;
+  __shared__ int s_valid[256];
 
   const int units = (a.T + 3) >> 2;
   const XcdTile tile = score_tile(a, units);
   if (tile.chunk >= a.n_chunks) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t = tile.row * 4 + wave;
+
+  // ---- the unit's rows
+  int t;
+  if (a.T <= 256) {
+    for (int i = tid; i < a.T; i += 256) s_valid[i] = a.valid_lens[i];
+    if (tid < 4) s_rows[tid] = a.T;  // slot past the last row: no row
+    __syncthreads();
+    if (tid < a.T) {
+      const int v = s_valid[tid];
+      int rank = 0;
+      for (int i = 0; i < a.T; ++i) {
+        const int vi = s_valid[i];
+        rank += (vi > v) || (vi == v && i < tid);
+      }
+      if ((rank >> 2) == tile.row) s_rows[rank & 3] = tid;
+    }
+    __syncthreads();
+    t = s_rows[wave];
+  } else {
+    t = tile.row * 4 + wave;
+  }
   const bool has = t < a.T;
   const int valid = has ? a.valid_lens[t] : 0;
   const int s_begin = tile.chunk * a.chunk;
@@ -360,17 +401,20 @@ __global__ __launch_bounds__(256) void score_mfma_group_kernel(ScoreArgs a) {
   float* out_row = a.scores + (int64_t)(has ? t : 0) * a.score_stride;
   for (int s = s_vend + lane; s < s_end; s += 64) out_row[s] = -INFINITY;
 
-  // pages of each row; the row reaching furthest leads
+  // pages of each row (loads issued before the query's); the row reaching furthest leads
   const int lb0 = (int)div_epb((uint32_t)s_begin, a.epb_magic);
   const int np = s_vend > s_begin ? (int)div_epb((uint32_t)(s_vend - 1), a.epb_magic) - lb0 + 1 : 0;
   int* mypid = pid + wave * a.pid_cap;
   float* mypgs = pgs + wave * a.pid_cap;
-  if (has) load_pages(a, t, lb0, np, mypid, mypgs, lane, 64);
-  if (lane == 0) s_vend_w[wave] = s_vend;
-  if (tid == 0) s_mismatch = 0;
+  const int32_t* bt_row = a.bt + (int64_t)t * a.bt_stride;
+  const int p_first = lane < np ? bt_row[lb0 + lane] : 0;
   half8v A[MT][KW];
   float wr[MT][4];
   load_query<MT, D>(a, t, lane, A, wr);
+  if (lane < np) mypid[lane] = p_first;
+  for (int i = lane + 64; i < np; i += 64) mypid[i] = bt_row[lb0 + i];
+  if (lane == 0) s_vend_w[wave] = s_vend;
+  if (tid == 0) s_mismatch = 0;
   __syncthreads();
   int lead = 0, vmax = s_vend_w[0];
 #pragma unroll
@@ -386,39 +430,46 @@ __global__ __launch_bounds__(256) void score_mfma_group_kernel(ScoreArgs a) {
   __syncthreads();
 
   if (s_mismatch) {  // rows of different sequences: each wave streams its own row
+    for (int i = lane; i < np; i += 64) mypgs[i] = a.gscale[mypid[i]];
     wave_stream<MT, D, UPAGE>(a, A, wr, mypid, mypgs, lb0, s_begin, s_vend, 0, 1, out_row, lane);
     return;
   }
 
   // ---- shared pages: decode each 64-key tile once into LDS
   const int* lpid = pid + lead * a.pid_cap;
-  const float* lpgs = pgs + lead * a.pid_cap;
   const int n_tiles = (vmax - s_begin + TILE - 1) / TILE;
   const int kt = tid >> 2, qs = tid & 3;  // staging: key of the tile, D/4 slice of it
-  Raw<D> raw;
-  float graw;
-  auto load_tile = [&](int j) {
+  // Raw tiles in flight: tile i lives in ring slot i % 2 from its load (issued two
+  // tiles ahead) until its decode, one tile before it is used.  Loads and decodes
+  // past the last tile touch valid memory and a free buffer; their results are unused.
+  Raw<D> R0, R1;
+  float G0 = 0.0f, G1 = 0.0f;
+  auto load_tile = [&](int j, Raw<D>& raw, float& graw) {
     const int s = min(s_begin + j * TILE + kt, vmax - 1);
     const uint32_t lb = div_epb((uint32_t)s, a.epb_magic);
-    const int li = (int)lb - lb0;
-    const int p = lpid[li];
-    graw = lpgs[li];
+    const int p = lpid[(int)lb - lb0];
+    graw = a.gscale[p];
     const int64_t e = (int64_t)p * a.epb + (int64_t)((uint32_t)s - lb * (uint32_t)a.epb);
     load_raw<D>(raw, a.keys + e * (D / 2) + qs * (D / 8), a.kscale + e * (D / 16) + qs * (D / 64));
   };
-  auto decode_tile = [&](int buf) {
+  // K-steps [k0, k1) of this thread's slice of a raw tile into LDS buffer buf.
+  auto decode_part = [&](int buf, const Raw<D>& raw, float graw, int k0, int k1) {
     const float sgn = graw < 0.0f ? -1.0f : 1.0f;
     _Float16* dst = bbuf + (buf * TILE + kt) * BLD + qs * (D / 4);
 #pragma unroll
-    for (int kk = 0; kk < KW; ++kk) *reinterpret_cast<half8v*>(dst + kk * 8) = decode_step<D>(raw, kk, sgn);
-    if (qs == 0) gbuf[buf * TILE + kt] = fabsf(graw);
+    for (int kk = k0; kk < k1; ++kk) *reinterpret_cast<half8v*>(dst + kk * 8) = decode_step<D>(raw, kk, sgn);
+    if (k1 == KW && qs == 0) gbuf[buf * TILE + kt] = fabsf(graw);
   };
 
   const int col = lane & 15, quarter = lane >> 4;
   float4v AC0[MT], AC1[MT];
   zero_acc<MT>(AC1);
-  int s_prev = 0x3fffffff;  // pending epilogue (accumulators AC1) of the previous tile
-  float g_prev = 0.0f;
+  // The scores of a tile are gathered so that lane l ends with key l of the tile
+  // (step = lane quarter, key column = lane & 15) and leave in one 256-byte store.
+  // Step 3 of a tile is reduced at the start of the next one, beside its MFMAs.
+  int t_prev = 0x3fffffff;  // previous tile (none yet: its store is masked off)
+  float g_prev = 0.0f;      // |global scale| of key t_prev + lane
+  float keep = 0.0f;
   auto mfma_step = [&](int buf, int k, float4v (&acc)[MT]) {
     const _Float16* src = bbuf + (buf * TILE + k * 16 + col) * BLD + quarter * (D / 4);
 #pragma unroll
@@ -430,34 +481,53 @@ __global__ __launch_bounds__(256) void score_mfma_group_kernel(ScoreArgs a) {
                                                          0, 0, 0);
     }
   };
-
-  load_tile(0);
-  decode_tile(0);
-  if (n_tiles > 1) load_tile(1);
-  for (int j = 0; j < n_tiles; ++j) {
+  auto flush_prev = [&]() {
+    const float v = head_sum<MT>(AC1, wr);
+    const float sc = quarter == 3 ? v : keep;
+    if (t_prev + lane < s_vend) out_row[t_prev + lane] = g_prev * sc;
+  };
+  // One tile: score tile j from LDS while decoding tile j+1 from its ring slot (`nx`)
+  // into the other buffer and reloading this tile's slot (`mine`) two tiles ahead.
+  auto run_tile = [&](int j, Raw<D>& mine, float& gmine, const Raw<D>& nx, float gnx) {
     __syncthreads();  // tile j decoded; the other buffer is free again
     const int buf = j & 1;
-    if (j + 1 < n_tiles) {
-      decode_tile(buf ^ 1);
-      if (j + 2 < n_tiles) load_tile(j + 2);
-    }
     const int t0 = s_begin + j * TILE;
     if (t0 < s_vend) {
-      const float* gb = gbuf + buf * TILE + col;
+      const float g_lane = gbuf[buf * TILE + lane];
       mfma_step(buf, 0, AC0);
-      epilogue<MT>(AC1, wr, g_prev, s_prev, s_vend, out_row, lane);
-      const float g0 = gb[0], g1 = gb[16], g2 = gb[32], g3 = gb[48];
+      flush_prev();
+      decode_part(buf ^ 1, nx, gnx, 0, KW / 2);
       mfma_step(buf, 1, AC1);
-      epilogue<MT>(AC0, wr, g0, t0, s_vend, out_row, lane);
+      keep = head_sum<MT>(AC0, wr);
+      decode_part(buf ^ 1, nx, gnx, KW / 2, KW);
       mfma_step(buf, 2, AC0);
-      epilogue<MT>(AC1, wr, g1, t0 + 16, s_vend, out_row, lane);
+      {
+        const float v = head_sum<MT>(AC1, wr);
+        keep = quarter == 1 ? v : keep;
+      }
+      load_tile(j + 2, mine, gmine);
       mfma_step(buf, 3, AC1);
-      epilogue<MT>(AC0, wr, g2, t0 + 32, s_vend, out_row, lane);
-      s_prev = t0 + 48;
-      g_prev = g3;
+      {
+        const float v = head_sum<MT>(AC0, wr);
+        keep = quarter == 2 ? v : keep;
+      }
+      t_prev = t0;
+      g_prev = g_lane;
+    } else {  // this row is done; the tile work is shared
+      decode_part(buf ^ 1, nx, gnx, 0, KW);
+      load_tile(j + 2, mine, gmine);
     }
+  };
+
+  load_tile(0, R0, G0);
+  load_tile(1, R1, G1);
+  decode_part(0, R0, G0, 0, KW);
+  for (int j = 0; j < n_tiles; j += 2) {
+    run_tile(j, R0, G0, R1, G1);
+    if (j + 1 >= n_tiles) break;
+    run_tile(j + 1, R1, G1, R0, G0);
   }
-  epilogue<MT>(AC1, wr, g_prev, s_prev, s_vend, out_row, lane);
+  flush_prev();
 }
 
 // ------------------------------------------------------------------ FP32 scorer
@@ -618,7 +688,7 @@ hipError_t launch_score_rows(ScoreArgs a, int precision, hipStream_t st) {
   const bool group = precision == 1 && a.T >= 4;
   const int units = group ? (a.T + 3) / 4 : a.T;
   if (precision == 1) {
-    a.chunk = chunk_keys(units, a.n_cols, a.epb, group ? 768 : 1024);
+    a.chunk = chunk_keys(units, a.n_cols, a.epb, group ? SALB_GROUP_WGS : SALB_SPLIT_WGS);
     a.pid_cap = a.chunk / a.epb + 2;
   } else {
     a.chunk = 256;
