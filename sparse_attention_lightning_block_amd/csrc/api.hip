@@ -125,7 +125,8 @@ size_t indexer_topk_workspace_size(int rows, int n_cols, int top_k) {
 static int check_select(int rows, int n_cols, int top_k, int64_t score_stride, int ratio) {
   if (rows < 0) return fail(IDX_ERR_SHAPE, "rows %d must be >= 0", rows);
   if (n_cols < 0 || n_cols >= kMaxCols) return fail(IDX_ERR_SHAPE, "n_cols %d out of range [0, 2^24)", n_cols);
-  if (top_k < 1 || top_k > 16384) return fail(IDX_ERR_UNSUPPORTED, "top_k %d (supported: 1..16384)", top_k);
+  if (top_k < 1 || top_k > salb::kMaxTopK)
+    return fail(IDX_ERR_UNSUPPORTED, "top_k %d (supported: 1..%d)", top_k, salb::kMaxTopK);
   if (score_stride < n_cols) return fail(IDX_ERR_SHAPE, "score_stride < n_cols");
   if (ratio < 0) return fail(IDX_ERR_SHAPE, "ratio %d must be >= 0", ratio);
   return IDX_OK;
@@ -141,7 +142,7 @@ int indexer_topk_select(const float* scores, int64_t score_stride, const int32_t
   if (!scores && n_cols > 0) return fail(IDX_ERR_NULL, "scores is required");
   salb::SelectPlan p;
   if (!salb::plan_select(rows, n_cols > 0 ? n_cols : 1, top_k, &p))
-    return fail(IDX_ERR_UNSUPPORTED, "top_k %d does not fit the device's LDS for rows of %d entries", top_k, n_cols);
+    return fail(IDX_ERR_UNSUPPORTED, "top_k %d is not supported", top_k);
   if (p.bytes > 0 && (!workspace || workspace_bytes < p.bytes))
     return fail(IDX_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", p.bytes, workspace_bytes);
   if (workspace && !aligned(workspace, 256)) return fail(IDX_ERR_SHAPE, "workspace must be 256-byte aligned");
@@ -179,7 +180,7 @@ int indexer_score_topk(const void* q, int q_dtype, const float* w, const uint8_t
   if (T == 0) return ok();
   salb::SelectPlan p;
   if (!salb::plan_select(T, n_cols, top_k, &p))
-    return fail(IDX_ERR_UNSUPPORTED, "top_k %d does not fit the device's LDS for rows of %d entries", top_k, n_cols);
+    return fail(IDX_ERR_UNSUPPORTED, "top_k %d is not supported", top_k);
   const size_t stride = round_up((size_t)n_cols, 64);
   const size_t score_bytes = round_up((size_t)T * stride * 4, 256);
   const size_t need = score_bytes + p.bytes;

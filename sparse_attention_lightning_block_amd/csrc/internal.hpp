@@ -36,23 +36,22 @@ hipError_t launch_debug_dequant(const uint8_t* keys, const uint8_t* kscale, cons
                                 hipStream_t st);
 
 // Per-row top-k (topk.hip).
+constexpr int kMaxTopK = 8192;
+
 struct SelectPlan {
   int rows, n_cols, top_k;
-  int seg;          // entries per first-level workgroup (score mode)
-  int nseg;         // first-level segments per row
-  int kseg;         // candidates kept per segment: min(top_k, seg)
-  int cap;          // candidate capacity of a merging workgroup
-  int levels;       // merge levels after the first (the last one writes the final result)
-  size_t bytes;     // workspace bytes
-  size_t lds_score; // dynamic LDS of a score-mode workgroup
-  size_t lds_cand;  // dynamic LDS of a candidate-mode workgroup
+  int two_pass;   // 0: one workgroup per row; 1: histogram + filter grid over (chunk, row)
+  int per;        // entries per thread (a row, or a chunk of the two-pass grid)
+  int chunks;     // chunks per row (two-pass)
+  int cand_lds;   // candidates the finishing workgroup holds in LDS (two-pass)
+  size_t lds;     // dynamic LDS of a workgroup that finishes a row
+  size_t bytes;   // workspace bytes
 };
 
 bool plan_select(int rows, int n_cols, int top_k, SelectPlan* p);
 hipError_t launch_select(const SelectPlan& p, const float* scores, int64_t score_stride,
                          const int32_t* valid_lens, int64_t first_pos, int ratio, int32_t* out_idx,
                          float* out_scores, void* ws, hipStream_t st);
-int max_lds_bytes();
 size_t select_workspace_bytes(int rows, int n_cols, int top_k);  // 0 if unsupported
 
 // QSA (qsa.hip).

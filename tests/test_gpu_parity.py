@@ -191,3 +191,26 @@ def test_topk_select_causal_rule():
         v = min(nb, (first + r + 1) // ratio)
         o_idx, _ = indexer.topk(s[r, :v].astype(np.float64), 10)
         assert gi[r].tolist() == o_idx.tolist()
+
+
+@pytest.mark.parametrize("n_cols,k", [(5000, 2048), (100000, 2048), (8192, 8192), (20000, 1)])
+def test_topk_select_degenerate(n_cols, k):
+    """Rows whose winners crowd one score value (sorting-network fallback), rows of
+    one repeated value (every entry a candidate), rows of exactly k entries."""
+    rng = np.random.default_rng(n_cols + k)
+    rows = 4
+    s = (rng.standard_normal((rows, n_cols)) * 0.01).astype(np.float32)
+    s[0, :] = 0.5                                     # one value everywhere
+    big = rng.choice(n_cols, 100, replace=False)
+    s[1, rng.choice(n_cols, min(3000, n_cols), replace=False)] = 1.0
+    s[1, big] = 1e6                                   # winners: 100 large + many equal ones
+    s[3, ::3] = -np.inf
+    valid = np.array([n_cols, n_cols, min(k, n_cols), n_cols], dtype=np.int32)
+    idx, val = salb.indexer_topk_select(torch.from_numpy(s).cuda(), k, valid_lens=torch.from_numpy(valid).cuda(),
+                                        with_scores=True)
+    gi, gv = _row(idx), _row(val)
+    for r in range(rows):
+        o_idx, o_val = indexer.topk(s[r, : valid[r]].astype(np.float64), k)
+        assert gi[r].tolist() == o_idx.tolist(), r
+        kk = min(k, int(valid[r]))
+        assert np.array_equal(gv[r][:kk], o_val[:kk].astype(np.float32)), r
