@@ -99,7 +99,7 @@ def main():
     scores = torch.empty((w.T, n_cols), dtype=torch.float32, device=dev)
     idx = torch.empty((w.T, w.top_k), dtype=torch.int32, device=dev)
     val = torch.empty((w.T, w.top_k), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(1, salb.indexer_topk_workspace_size(w.T, n_cols, w.top_k)), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(1, salb.indexer_topk_workspace_size(w.T, n_cols, w.top_k)), dtype=torch.uint8, device=dev)
     sc_view = scores
 
     def step(ev=None):

@@ -110,8 +110,13 @@ int indexer_score_rows(const void* q, int q_dtype, const float* w,
  *  scores      [rows, n_cols] fp32, row stride score_stride >= n_cols
  *  topk_idx    [rows, top_k] int32 output (logical indices s)
  *  topk_scores [rows, top_k] fp32 output or NULL
- *  workspace   device scratch of indexer_topk_workspace_size(...) bytes
- * Supported: 1 <= top_k <= 16384, n_cols < 2^24.
+ *  workspace   device scratch of indexer_topk_workspace_size(...) bytes, 256-byte
+ *              aligned, owned by the caller.  It must be zero-filled before its
+ *              first use; every call that returns IDX_OK leaves it ready for the
+ *              next call (its counters back at zero), so it is filled once, not per
+ *              call.  After an error return, zero-fill it again.  Calls sharing a
+ *              workspace must be ordered (same stream, or synchronised).
+ * Supported: 1 <= top_k <= 8192, n_cols < 2^24.
  */
 size_t indexer_topk_workspace_size(int rows, int n_cols, int top_k);
 int indexer_topk_select(const float* scores, int64_t score_stride, const int32_t* valid_lens,
@@ -127,7 +132,8 @@ int indexer_topk_select(const float* scores, int64_t score_stride, const int32_t
  * indexer_topk_select; the scores live only in the workspace.
  *  topk_idx    [T, top_k] int32 output: logical entry indices s, -1 padded
  *  topk_scores [T, top_k] fp32 output or NULL
- *  workspace   device scratch of indexer_score_topk_workspace_size(...) bytes
+ *  workspace   device scratch of indexer_score_topk_workspace_size(...) bytes; the
+ *              same zero-fill-once rule as indexer_topk_select's workspace.
  */
 size_t indexer_score_topk_workspace_size(int T, int max_lb, int epb, int top_k);
 int indexer_score_topk(const void* q, int q_dtype, const float* w,

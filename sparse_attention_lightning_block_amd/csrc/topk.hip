@@ -17,12 +17,12 @@
 //   * longer rows run as a pipeline of launches (kernel boundaries order them; no
 //     grid-wide fences, which write back the whole L2 on this chip): every
 //     workgroup of a (chunk, row) grid adds its chunk's LDS histogram of the top 12
-//     order-key bits into one of eight global copies (one per XCD, so contended
-//     atomics stay in one L2); one workgroup per row sums the copies and finds the
+//     order-key bits (the bins that can hold the row's K-th entry) into one of
+//     eight global copies (one per XCD, so contended atomics stay in one L2); one workgroup per row sums the copies and finds the
 //     bin holding the K-th entry; the (chunk, row) grid then writes every entry at
-//     or above that bin to the chunk's own candidate slots; one workgroup per row
-//     gathers those candidates (about K plus one bin's worth) into LDS, selects
-//     the K winners exactly and sorts them.
+//     or above that bin to the chunk's own candidate slots; one 1024-thread
+//     workgroup per row loads those candidates (about K plus one bin's worth)
+//     into registers, selects the K winners exactly and sorts them.
 //   * the sort buckets the winners on the 12 highest bits where they differ and
 //     ranks each against its bucket (a sorting network if a bucket is crowded).
 #include <hip/hip_runtime.h>
@@ -32,15 +32,17 @@
 
 namespace salb {
 
-constexpr int kSelThreads = 256;
-constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kDigit = 12;
-constexpr int kBins = 1 << kDigit;                   // 4096 histogram bins
-constexpr int kBinsPerThread = kBins / kSelThreads;  // 16
-constexpr int kTopShift = 64 - kDigit;               // first digit: the score's top 12 order bits
-constexpr int kRowMax = 32 * kSelThreads;            // 8192: one-workgroup rows
-constexpr int kBucketMax = 48;                       // crowded bucket: sorting network instead
-constexpr int kHistCopies = 8;                       // one global histogram per XCD
+constexpr int kBins = 1 << kDigit;       // 4096 histogram bins
+constexpr int kTopShift = 64 - kDigit;   // first digit: the score's top 12 order bits
+constexpr int kRowThreads = 256;         // one-workgroup rows
+constexpr int kChunkThreads = 256;       // histogram and filter chunks of long rows
+constexpr int kFinalThreads = 1024;      // the finishing workgroup of a long row
+constexpr int kFinalPer = 12;            // candidates per finishing thread held in registers
+constexpr int kRowMax = 32 * kRowThreads;  // 8192: one-workgroup rows
+constexpr int kBucketMax = 48;           // crowded bucket: sorting network instead
+constexpr int kHistCopies = kXcds;       // one global histogram per XCD
+constexpr int kMaxWaves = kFinalThreads / kWave;
 
 struct RowInfo {
   uint32_t bin;    // bin of the K-th entry (0 when every entry wins)
@@ -62,11 +64,10 @@ struct SelArgs {
   // long-row pipeline
   int chunk;         // entries per chunk workgroup
   int chunks;        // chunks per row
-  int cand_lds;      // candidates the final workgroup can hold in LDS
-  uint32_t* ghist;   // [rows][kHistCopies][kBins]
+  uint32_t* ghist;   // [rows][kHistCopies][kBins], zero between calls
   RowInfo* info;     // [rows]
-  uint32_t* ccnt;    // [rows][chunks] candidates per chunk
-  uint64_t* cand;    // [rows][chunks * chunk] candidate slots, chunk by chunk
+  uint32_t* ccount;  // [rows][chunks] candidates per chunk
+  uint64_t* cand;    // [rows][chunks][chunk] candidate slots
 };
 
 __device__ __forceinline__ int row_valid(const SelArgs& a, int row) {
@@ -84,14 +85,14 @@ __device__ __forceinline__ int row_valid(const SelArgs& a, int row) {
 }
 
 struct SelShared {
-  uint32_t wsum[kSelWaves];
-  uint64_t wred[2 * kSelWaves];
-  uint32_t digit, gt, cnt;
-  uint32_t fill;  // append counter of the candidate gather
+  uint32_t wsum[kMaxWaves];
+  uint64_t wred[2 * kMaxWaves];
+  uint32_t digit, gt, cnt, fill;
 };
 
 // Sum of v over the threads with a larger index.  Two calls must be separated by a
 // barrier after the first call's result is used.
+template <int NT>
 __device__ __forceinline__ uint32_t block_suffix(uint32_t v, SelShared& sh) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -105,11 +106,12 @@ __device__ __forceinline__ uint32_t block_suffix(uint32_t v, SelShared& sh) {
   __syncthreads();
   uint32_t above = 0;
 #pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) above += w > wave ? sh.wsum[w] : 0u;
+  for (int w = 0; w < NT / kWave; ++w) above += w > wave ? sh.wsum[w] : 0u;
   return above + x - v;
 }
 
 // Block-wide maximum and minimum (same barrier rule as block_suffix).
+template <int NT>
 __device__ __forceinline__ void block_minmax(uint64_t& mx, uint64_t& mn, SelShared& sh) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -120,21 +122,24 @@ __device__ __forceinline__ void block_minmax(uint64_t& mx, uint64_t& mn, SelShar
   }
   if ((threadIdx.x & 63) == 0) {
     sh.wred[threadIdx.x >> 6] = mx;
-    sh.wred[kSelWaves + (threadIdx.x >> 6)] = mn;
+    sh.wred[kMaxWaves + (threadIdx.x >> 6)] = mn;
   }
   __syncthreads();
 #pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const uint64_t a = sh.wred[w], b = sh.wred[kSelWaves + w];
+  for (int w = 0; w < NT / kWave; ++w) {
+    const uint64_t a = sh.wred[w], b = sh.wred[kMaxWaves + w];
     mx = a > mx ? a : mx;
     mn = b < mn ? b : mn;
   }
 }
 
-__device__ __forceinline__ void load_bins(const uint32_t* hist, uint32_t (&h)[kBinsPerThread]) {
-  const uint4* p = reinterpret_cast<const uint4*>(hist + threadIdx.x * kBinsPerThread);
+// Thread t owns bins [t * BPT, (t + 1) * BPT).
+template <int NT>
+__device__ __forceinline__ void load_bins(const uint32_t* hist, uint32_t (&h)[kBins / NT]) {
+  constexpr int BPT = kBins / NT;
+  const uint4* p = reinterpret_cast<const uint4*>(hist + threadIdx.x * BPT);
 #pragma unroll
-  for (int j = 0; j < kBinsPerThread / 4; ++j) {
+  for (int j = 0; j < BPT / 4; ++j) {
     const uint4 v = p[j];
     h[4 * j] = v.x;
     h[4 * j + 1] = v.y;
@@ -143,23 +148,27 @@ __device__ __forceinline__ void load_bins(const uint32_t* hist, uint32_t (&h)[kB
   }
 }
 
+template <int NT>
 __device__ __forceinline__ void clear_bins(uint32_t* hist) {
   uint4* p = reinterpret_cast<uint4*>(hist);
-  for (int j = threadIdx.x; j < kBins / 4; j += kSelThreads) p[j] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int j = threadIdx.x; j < kBins / 4; j += NT) p[j] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Digit search over a 4096-bin histogram (bins are owned 16 per thread, in
-// order): the bin holding the rem-th largest counted entry, the count above it and
-// its own count land in sh.digit / sh.gt / sh.cnt.  Requires 1 <= rem <= total.
-__device__ __forceinline__ void find_digit(const uint32_t (&h)[kBinsPerThread], uint32_t rem, SelShared& sh) {
+// Digit search over a 4096-bin histogram held as in load_bins: the bin holding
+// the rem-th largest counted entry, the count above it and its own count land in
+// sh.digit / sh.gt / sh.cnt.  Requires 1 <= rem <= total.
+template <int NT>
+__device__ __forceinline__ void find_digit(const uint32_t (&h)[kBins / NT], uint32_t rem, SelShared& sh) {
+  constexpr int BPT = kBins / NT;
   uint32_t own = 0;
 #pragma unroll
-  for (int q = 0; q < kBinsPerThread; ++q) own += h[q];
-  uint32_t ge = block_suffix(own, sh);
+  for (int q = 0; q < BPT; ++q) own += h[q];
+  uint32_t ge = block_suffix<NT>(own, sh);
 #pragma unroll
-  for (int q = kBinsPerThread - 1; q >= 0; --q) {
+  for (int q = BPT - 1; q >= 0; --q) {
     if (ge < rem && ge + h[q] >= rem) {
-      sh.digit = threadIdx.x * kBinsPerThread + q;
+      sh.digit = threadIdx.x * BPT + q;
       sh.gt = ge;
       sh.cnt = h[q];
     }
@@ -172,22 +181,22 @@ __device__ __forceinline__ void find_digit(const uint32_t (&h)[kBinsPerThread], 
 // agree with `prefix` on the bits of `mask` are >= thr (those above the prefix are
 // already counted out by the caller).  `each(f)` calls f(c) on every composite
 // this thread owns.  Digits are 12 bits wide, from bit `top` down.
-template <typename Each>
+template <int NT, typename Each>
 __device__ uint64_t radix_select(Each each, uint64_t prefix, uint64_t mask, uint32_t rem, int top,
                                  uint32_t* hist, SelShared& sh) {
   for (;;) {
     const int width = top + 1 < kDigit ? top + 1 : kDigit;
     const int shift = top + 1 - width;
     const uint32_t dmask = (1u << width) - 1u;
-    clear_bins(hist);
+    clear_bins<NT>(hist);
     __syncthreads();
     each([&](uint64_t c) {
       if ((c & mask) == prefix) atomicAdd(&hist[(uint32_t)(c >> shift) & dmask], 1u);
     });
     __syncthreads();
-    uint32_t h[kBinsPerThread];
-    load_bins(hist, h);
-    find_digit(h, rem, sh);
+    uint32_t h[kBins / NT];
+    load_bins<NT>(hist, h);
+    find_digit<NT>(h, rem, sh);
     const uint32_t digit = sh.digit, gt = sh.gt, cnt = sh.cnt;
     prefix |= (uint64_t)digit << shift;
     mask |= (uint64_t)dmask << shift;
@@ -198,11 +207,12 @@ __device__ uint64_t radix_select(Each each, uint64_t prefix, uint64_t mask, uint
 }
 
 // Descending bitonic sort of buf[0, n2) (n2 a power of two) by the whole block.
+template <int NT>
 __device__ void bitonic_desc(uint64_t* buf, int n2) {
   const int tid = threadIdx.x;
   for (int size = 2; size <= n2; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < (n2 >> 1); i += kSelThreads) {
+      for (int i = tid; i < (n2 >> 1); i += NT) {
         const int lo = 2 * i - (i & (stride - 1));
         const int hi = lo + stride;
         const uint64_t x = buf[lo], y = buf[hi];
@@ -226,10 +236,12 @@ __device__ __forceinline__ int pow2_at_least(int x) {
 // Sorts the K winners in sortbuf[0, K) (capacity pow2_at_least(K)) and writes the
 // row's output: K indices (and scores) in selection order, then -1 (and -inf) up
 // to top_k.  grp holds K entries; hist holds kBins + 4 counters.
+template <int NT>
 __device__ void finish_row(uint64_t* sortbuf, uint64_t* grp, uint32_t* hist, int K, int top_k, int32_t* oi,
                            float* os, SelShared& sh) {
+  constexpr int BPT = kBins / NT;
   const int tid = threadIdx.x;
-  for (int i = K + tid; i < top_k; i += kSelThreads) {
+  for (int i = K + tid; i < top_k; i += NT) {
     oi[i] = -1;
     if (os) os[i] = -INFINITY;
   }
@@ -242,35 +254,35 @@ __device__ void finish_row(uint64_t* sortbuf, uint64_t* grp, uint32_t* hist, int
     return;
   }
   uint64_t mx = 0ull, mn = ~0ull;
-  for (int i = tid; i < K; i += kSelThreads) {
+  for (int i = tid; i < K; i += NT) {
     const uint64_t c = sortbuf[i];
     mx = c > mx ? c : mx;
     mn = c < mn ? c : mn;
   }
-  block_minmax(mx, mn, sh);
+  block_minmax<NT>(mx, mn, sh);
   const int hb = 63 - __clzll(mx ^ mn);  // composites are distinct: mx != mn
   const int bsh = hb >= kDigit - 1 ? hb - (kDigit - 1) : 0;
   const uint64_t base = mn >> bsh;
-  clear_bins(hist);
+  clear_bins<NT>(hist);
   if (tid == 0) {
     hist[kBins] = 0u;  // start of the bucket above the top one
     sh.digit = 0u;
   }
   __syncthreads();
-  for (int i = tid; i < K; i += kSelThreads) atomicAdd(&hist[(uint32_t)((sortbuf[i] >> bsh) - base)], 1u);
+  for (int i = tid; i < K; i += NT) atomicAdd(&hist[(uint32_t)((sortbuf[i] >> bsh) - base)], 1u);
   __syncthreads();
-  uint32_t h[kBinsPerThread];
-  load_bins(hist, h);
+  uint32_t h[BPT];
+  load_bins<NT>(hist, h);
   uint32_t own = 0, bmax = 0;
 #pragma unroll
-  for (int q = 0; q < kBinsPerThread; ++q) {
+  for (int q = 0; q < BPT; ++q) {
     own += h[q];
     bmax = h[q] > bmax ? h[q] : bmax;
   }
-  uint32_t start = block_suffix(own, sh);  // larger buckets come first
+  uint32_t start = block_suffix<NT>(own, sh);  // larger buckets come first
 #pragma unroll
-  for (int q = kBinsPerThread - 1; q >= 0; --q) {
-    hist[tid * kBinsPerThread + q] = start;
+  for (int q = BPT - 1; q >= 0; --q) {
+    hist[tid * BPT + q] = start;
     start += h[q];
   }
 #pragma unroll
@@ -279,29 +291,33 @@ __device__ void finish_row(uint64_t* sortbuf, uint64_t* grp, uint32_t* hist, int
   __syncthreads();
   if (sh.digit > (uint32_t)kBucketMax) {
     const int n2 = pow2_at_least(K);
-    for (int i = K + tid; i < n2; i += kSelThreads) sortbuf[i] = 0ull;  // composites are never 0
+    for (int i = K + tid; i < n2; i += NT) sortbuf[i] = 0ull;  // composites are never 0
     __syncthreads();
-    bitonic_desc(sortbuf, n2);
+    bitonic_desc<NT>(sortbuf, n2);
   } else {
     // scatter into buckets; afterwards hist[b] is the end of bucket b and
     // hist[b + 1] its start
-    for (int i = tid; i < K; i += kSelThreads) {
+    for (int i = tid; i < K; i += NT) {
       const uint64_t c = sortbuf[i];
       grp[atomicAdd(&hist[(uint32_t)((c >> bsh) - base)], 1u)] = c;
     }
     __syncthreads();
-    for (int i = tid; i < K; i += kSelThreads) {
+    for (int i = tid; i < K; i += NT) {
       const uint64_t c = grp[i];
       const uint32_t b = (uint32_t)((c >> bsh) - base);
       const uint32_t e = hist[b];
       const uint32_t s = hist[b + 1];
-      uint32_t r = s;
-      for (uint32_t j = s; j < e; ++j) r += grp[j] > c;
+      uint32_t r = s, j = s;
+      for (; j + 4 <= e; j += 4) {
+        const uint64_t g0 = grp[j], g1 = grp[j + 1], g2 = grp[j + 2], g3 = grp[j + 3];
+        r += (g0 > c) + (g1 > c) + (g2 > c) + (g3 > c);
+      }
+      for (; j < e; ++j) r += grp[j] > c;
       sortbuf[r] = c;
     }
     __syncthreads();
   }
-  for (int i = tid; i < K; i += kSelThreads) {
+  for (int i = tid; i < K; i += NT) {
     const uint64_t c = sortbuf[i];
     oi[i] = (int32_t)(~(uint32_t)c);
     if (os) os[i] = ord_to_float((uint32_t)(c >> 32));
@@ -335,7 +351,8 @@ __device__ __forceinline__ FinishLds carve(unsigned char* smem, int top_k) {
 // One workgroup per row; entry e of the row sits in register i of thread t with
 // e = i * 256 + t (coalesced loads).
 template <int PER>
-__global__ __launch_bounds__(kSelThreads) void select_rows_kernel(SelArgs a) {
+__global__ __launch_bounds__(kRowThreads) void select_rows_kernel(SelArgs a) {
+  constexpr int NT = kRowThreads;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ SelShared sh;
   const int row = gridDim.x - 1 - blockIdx.x;  // causal rows grow with the index: longest first
@@ -348,29 +365,29 @@ __global__ __launch_bounds__(kSelThreads) void select_rows_kernel(SelArgs a) {
   uint32_t key[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int e = i * kSelThreads + tid;
+    const int e = i * NT + tid;
     key[i] = e < n ? ord_key(src[e]) : 0u;
   }
   auto each = [&](auto&& fn) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int e = i * kSelThreads + tid;
+      const int e = i * NT + tid;
       if (e < n) fn(composite(key[i], (uint32_t)e));
     }
   };
   uint64_t thr = 0ull;
-  if (K < n) thr = radix_select(each, 0ull, 0ull, (uint32_t)K, 63, f.hist, sh);
+  if (K < n) thr = radix_select<NT>(each, 0ull, 0ull, (uint32_t)K, 63, f.hist, sh);
   // gather the winners
   uint32_t mine = 0;
   each([&](uint64_t c) { mine += c >= thr; });
-  uint32_t off = block_suffix(mine, sh);
+  uint32_t off = block_suffix<NT>(mine, sh);
   each([&](uint64_t c) {
     if (c >= thr) f.sortbuf[off++] = c;
   });
   __syncthreads();
   int32_t* oi = a.out_idx + (int64_t)row * a.top_k;
   float* os = a.out_scores ? a.out_scores + (int64_t)row * a.top_k : nullptr;
-  finish_row(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, sh);
+  finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, sh);
 }
 
 // ------------------------------------------------------------------ long rows
@@ -379,50 +396,67 @@ __global__ __launch_bounds__(kSelThreads) void select_rows_kernel(SelArgs a) {
 // global copy of the XCD the workgroup runs on (workgroups are dealt to the eight
 // XCDs round robin by linear index).
 template <int PER>
-__global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelArgs a) {
+__global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelArgs a) {
+  constexpr int NT = kChunkThreads;
   __shared__ __align__(16) uint32_t hist[kBins];
+  __shared__ SelShared sh;
   const int row = blockIdx.y;
   const int tid = threadIdx.x;
   const int n = row_valid(a, row);
-  const int lo = blockIdx.x * (PER * kSelThreads);
+  const int lo = blockIdx.x * (PER * NT);
   if (lo >= n) return;
   const float* src = a.scores + (int64_t)row * a.score_stride;
-  clear_bins(hist);
+  float x[PER];  // every load in flight before the first LDS atomic
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lo + i * NT + tid;
+    x[i] = e < n ? src[e] : 0.0f;
+  }
+  clear_bins<NT>(hist);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int e = lo + i * kSelThreads + tid;
-    if (e < n) atomicAdd(&hist[ord_key(src[e]) >> (32 - kDigit)], 1u);
+    const int e = lo + i * NT + tid;
+    if (e < n) atomicAdd(&hist[ord_key(x[i]) >> (32 - kDigit)], 1u);
   }
   __syncthreads();
+  // The row's K-th entry is at least the chunk's K-th entry, so bins below the
+  // latter's never hold it and are not needed above it: they are not flushed.
+  const int K = n < a.top_k ? n : a.top_k;
+  const int m = n - lo < PER * NT ? n - lo : PER * NT;
+  uint32_t low = 0;
+  if (m > K) {
+    uint32_t h[kBins / NT];
+    load_bins<NT>(hist, h);
+    find_digit<NT>(h, (uint32_t)K, sh);
+    low = sh.digit;
+  }
   const int copy = (blockIdx.y * gridDim.x + blockIdx.x) % kHistCopies;
   uint32_t* gh = a.ghist + ((int64_t)row * kHistCopies + copy) * kBins;
 #pragma unroll
-  for (int q = 0; q < kBinsPerThread; ++q) {
-    const int b = q * kSelThreads + tid;
+  for (int q = 0; q < kBins / NT; ++q) {
+    const int b = q * NT + tid;
     const uint32_t v = hist[b];
-    if (v) atomicAdd(&gh[b], v);
+    if (v && (uint32_t)b >= low) atomicAdd(&gh[b], v);
   }
 }
 
 // Stage 2 (one workgroup per row): sum the copies, find the bin of the K-th entry.
-__global__ __launch_bounds__(kSelThreads) void select_thresh_kernel(SelArgs a) {
+__global__ __launch_bounds__(kChunkThreads) void select_thresh_kernel(SelArgs a) {
+  constexpr int NT = kChunkThreads;
+  constexpr int BPT = kBins / NT;
   __shared__ SelShared sh;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int n = row_valid(a, row);
   const int K = n < a.top_k ? n : a.top_k;
-  if (K == n) {  // every entry wins (also n == 0)
-    if (tid == 0) a.info[row] = RowInfo{0u, 0u, (uint32_t)n, 0u};
-    return;
-  }
-  uint32_t h[kBinsPerThread] = {};
-  const uint32_t* gh = a.ghist + (int64_t)row * kHistCopies * kBins + tid * kBinsPerThread;
+  uint32_t h[BPT] = {};
+  const uint32_t* gh = a.ghist + (int64_t)row * kHistCopies * kBins + tid * BPT;
 #pragma unroll
   for (int c = 0; c < kHistCopies; ++c) {
     const uint4* p = reinterpret_cast<const uint4*>(gh + c * kBins);
 #pragma unroll
-    for (int j = 0; j < kBinsPerThread / 4; ++j) {
+    for (int j = 0; j < BPT / 4; ++j) {
       const uint4 v = p[j];
       h[4 * j] += v.x;
       h[4 * j + 1] += v.y;
@@ -430,150 +464,167 @@ __global__ __launch_bounds__(kSelThreads) void select_thresh_kernel(SelArgs a) {
       h[4 * j + 3] += v.w;
     }
   }
-  find_digit(h, (uint32_t)K, sh);
+  if (K == n) {  // every entry wins (also n == 0)
+    if (tid == 0) a.info[row] = RowInfo{0u, 0u, (uint32_t)n, 0u};
+    return;
+  }
+  find_digit<NT>(h, (uint32_t)K, sh);
   if (tid == 0) a.info[row] = RowInfo{sh.digit, sh.gt, sh.cnt, 0u};
 }
 
 // Stage 3: every entry of the chunk in the K-th entry's bin or above goes to the
-// chunk's candidate slots (their order there does not matter: the composites are
-// ordered later).
+// chunk's own candidate slots (their order does not matter: the composites are
+// ordered later), and the chunk's count to ccount.  The histogram copies have been
+// read by now: each workgroup zeroes its share of its row's, for the next call.
 template <int PER>
-__global__ __launch_bounds__(kSelThreads) void select_filter_kernel(SelArgs a) {
+__global__ __launch_bounds__(kChunkThreads) void select_filter_kernel(SelArgs a) {
+  constexpr int NT = kChunkThreads;
   __shared__ SelShared sh;
   const int row = blockIdx.y;
   const int tid = threadIdx.x;
   const int n = row_valid(a, row);
-  const int lo = blockIdx.x * (PER * kSelThreads);
-  const int64_t slot = (int64_t)row * a.chunks + blockIdx.x;
+  const int lo = blockIdx.x * (PER * NT);
+  const int64_t slot = (int64_t)row * gridDim.x + blockIdx.x;
+  {
+    constexpr int kWords4 = kHistCopies * kBins / 4;
+    uint4* gh = reinterpret_cast<uint4*>(a.ghist + (int64_t)row * kHistCopies * kBins);
+    const int w0 = (int)(((int64_t)blockIdx.x * kWords4) / gridDim.x);
+    const int w1 = (int)(((int64_t)(blockIdx.x + 1) * kWords4) / gridDim.x);
+    for (int w = w0 + tid; w < w1; w += NT) gh[w] = make_uint4(0u, 0u, 0u, 0u);
+  }
   if (lo >= n) {
-    if (tid == 0) a.ccnt[slot] = 0u;
+    if (tid == 0) a.ccount[slot] = 0u;
     return;
   }
   const float* src = a.scores + (int64_t)row * a.score_stride;
   const uint32_t bin = a.info[row].bin;
-  // entry lo + t * PER + i of the chunk sits in register i of thread t
   uint32_t key[PER];
   uint32_t mine = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int e = lo + i * kSelThreads + tid;
+    const int e = lo + i * NT + tid;
     key[i] = e < n ? ord_key(src[e]) : 0u;
     mine += (e < n && (key[i] >> (32 - kDigit)) >= bin);
   }
-  uint32_t pos = block_suffix(mine, sh);
-  if (tid == 0) a.ccnt[slot] = pos + mine;
-  uint64_t* cd = a.cand + slot * a.chunk;
+  uint32_t pos = block_suffix<NT>(mine, sh);
+  if (tid == 0) a.ccount[slot] = pos + mine;
+  uint64_t* cd = a.cand + slot * (PER * NT);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int e = lo + i * kSelThreads + tid;
+    const int e = lo + i * NT + tid;
     if (e < n && (key[i] >> (32 - kDigit)) >= bin) cd[pos++] = composite(key[i], (uint32_t)e);
   }
 }
 
 // Stage 4 (one workgroup per row): exact selection among the candidates, sort,
-// output.  The candidates are read through a flat index over the chunks' slots.
-__global__ __launch_bounds__(kSelThreads) void select_final_kernel(SelArgs a) {
+// output.  Up to kFinalPer candidates per thread are held in registers, fetched
+// through an LDS map from list position to chunk; longer lists (rows crowded with
+// equal scores) are read chunk by chunk at every pass.
+__global__ __launch_bounds__(kFinalThreads) void select_final_kernel(SelArgs a) {
+  constexpr int NT = kFinalThreads;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ SelShared sh;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int n = row_valid(a, row);
   const int K = n < a.top_k ? n : a.top_k;
   const RowInfo info = a.info[row];
-  int C = K == n ? n : (int)(info.above + info.cnt);
+  const int nch = a.chunks;
   FinishLds f = carve(smem, a.top_k);
-  // LDS after the finishing buffers: chunk offsets [chunks + 1], then candidates
-  uint32_t* off = f.hist + kBins + 4;
-  uint64_t* lc = reinterpret_cast<uint64_t*>(off + ((a.chunks + 4) & ~3));
-  const uint32_t* cnt = a.ccnt + (int64_t)row * a.chunks;
-  const uint64_t* cd = a.cand + (int64_t)row * a.chunks * a.chunk;
-  if (tid == 0) sh.fill = 0u;
-  // exclusive prefix of the chunk counts (sequential per 256-chunk block)
-  {
-    uint32_t carry = 0;
-    for (int c0 = 0; c0 < a.chunks; c0 += kSelThreads) {
-      const int c = c0 + tid;
-      const uint32_t v = c < a.chunks ? cnt[c] : 0u;
-      // inclusive prefix within the block of 256 through the suffix helper
-      const uint32_t above = block_suffix(v, sh);
-      __syncthreads();
-      const uint32_t total = sh.wsum[0] + sh.wsum[1] + sh.wsum[2] + sh.wsum[3];
-      if (c < a.chunks) off[c] = carry + (total - above - v);
-      carry += total;
-      __syncthreads();
-    }
-    if (tid == 0) off[a.chunks] = carry;
+  uint32_t* off = f.hist + kBins + 4;                                   // [nch + 1]
+  uint16_t* owner = reinterpret_cast<uint16_t*>(off + ((nch + 4) & ~3));  // [NT * kFinalPer]
+  const uint32_t* cnt = a.ccount + (int64_t)row * nch;
+  const uint64_t* cd = a.cand + (int64_t)row * nch * a.chunk;
+  // exclusive prefix of the chunk counts, 1024 chunks at a time
+  uint32_t carry = 0;
+  for (int c0 = 0; c0 < nch; c0 += NT) {
+    const int c = c0 + tid;
+    const uint32_t v = c < nch ? cnt[c] : 0u;
+    const uint32_t above = block_suffix<NT>(v, sh);
+    uint32_t total = 0;
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) total += sh.wsum[w];
+    if (c < nch) off[c] = carry + (total - above - v);
+    carry += total;
     __syncthreads();
-    if ((uint32_t)C > carry) C = (int)carry;  // the chunk counts sum to C; never read past them
   }
-  // flat candidate i: chunk = last c with off[c] <= i
-  auto fetch = [&](int i) -> uint64_t {
-    int lo = 0, hi = a.chunks;  // off[lo] <= i < off[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (off[mid] <= (uint32_t)i) lo = mid; else hi = mid;
+  if (tid == 0) off[nch] = carry;
+  int C = K == n ? n : (int)(info.above + info.cnt);
+  if ((uint32_t)C > carry) C = (int)carry;  // the two agree; never read past the slots
+  const bool in_regs = C <= NT * kFinalPer;
+  uint64_t v[kFinalPer];
+  if (in_regs) {
+    __syncthreads();
+    for (int c = tid >> 6; c < nch; c += NT / kWave) {
+      const uint32_t o = off[c], e = min(off[c + 1], (uint32_t)C);
+      for (uint32_t i = o + (tid & 63); i < e; i += kWave) owner[i] = (uint16_t)c;
     }
-    return cd[(int64_t)lo * a.chunk + (i - (int)off[lo])];
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kFinalPer; ++r) {
+      const int i = r * NT + tid;
+      uint64_t x = 0ull;
+      if (i < C) {
+        const int c = owner[i];
+        x = cd[(int64_t)c * a.chunk + (i - (int)off[c])];
+      }
+      v[r] = x;
+    }
+  } else {
+    __syncthreads();
+  }
+  auto each = [&](auto&& fn) {
+    if (in_regs) {
+#pragma unroll
+      for (int r = 0; r < kFinalPer; ++r)
+        if (r * NT + tid < C) fn(v[r]);
+    } else {
+      for (int c = 0; c < nch; ++c) {
+        const int m = (int)(off[c + 1] - off[c]);
+        for (int i = tid; i < m; i += NT) fn(cd[(int64_t)c * a.chunk + i]);
+      }
+    }
   };
-  const bool in_lds = C <= a.cand_lds;
-  if (in_lds) {
-    for (int i = tid; i < C; i += kSelThreads) lc[i] = fetch(i);
-    __syncthreads();
-  }
-  auto get = [&](int i) -> uint64_t { return in_lds ? lc[i] : fetch(i); };
   uint64_t thr = 0ull;
   if (K < C) {
-    auto each = [&](auto&& fn) {
-      for (int i = tid; i < C; i += kSelThreads) fn(get(i));
-    };
     const uint64_t mask = (uint64_t)(kBins - 1) << kTopShift;
-    thr = radix_select(each, (uint64_t)info.bin << kTopShift, mask, (uint32_t)K - info.above, kTopShift - 1,
-                       f.hist, sh);
+    thr = radix_select<NT>(each, (uint64_t)info.bin << kTopShift, mask, (uint32_t)K - info.above, kTopShift - 1,
+                           f.hist, sh);
   }
-  for (int i0 = 0; i0 < C; i0 += kSelThreads) {
-    const int i = i0 + tid;
-    const uint64_t c = i < C ? get(i) : 0ull;
-    const bool sel = i < C && c >= thr;
-    const uint64_t m = __ballot(sel);
-    uint32_t wb = 0;
-    if (lane == 0 && m) wb = atomicAdd(&sh.fill, (uint32_t)__popcll(m));
-    wb = __shfl(wb, 0);
-    const uint32_t at = wb + __popcll(m & ((1ull << lane) - 1ull));
-    if (sel && at < (uint32_t)K) f.sortbuf[at] = c;  // exactly K are selected
-  }
+  uint32_t mine = 0;
+  each([&](uint64_t c) { mine += c >= thr; });
+  uint32_t pos = block_suffix<NT>(mine, sh);
+  each([&](uint64_t c) {
+    if (c >= thr && pos < (uint32_t)K) f.sortbuf[pos++] = c;  // exactly K are selected
+  });
   __syncthreads();
   int32_t* oi = a.out_idx + (int64_t)row * a.top_k;
   float* os = a.out_scores ? a.out_scores + (int64_t)row * a.top_k : nullptr;
-  finish_row(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, sh);
-}
-
-__global__ __launch_bounds__(256) void fill_zero_kernel(uint4* p, int64_t n16) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
-    p[i] = make_uint4(0u, 0u, 0u, 0u);
+  finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, sh);
 }
 
 // ------------------------------------------------------------------ host planning
 
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace of the long-row pipeline: histogram copies | row info | chunk counts |
-// candidate slots.
+// Workspace of the long-row pipeline: histogram copies (zero between calls: the
+// caller zero-fills the workspace once, every call leaves them zero) | row info |
+// chunk counts | candidate slots.
 struct WsLayout {
-  size_t hist, info, ccnt, cand, total;
+  size_t hist, info, ccount, cand, total;
 };
 
 static WsLayout ws_layout(int rows, int chunks, int chunk) {
   WsLayout l;
   l.hist = 0;
   l.info = round256((size_t)rows * kHistCopies * kBins * 4);
-  l.ccnt = round256(l.info + (size_t)rows * sizeof(RowInfo));
-  l.cand = round256(l.ccnt + (size_t)rows * chunks * 4);
+  l.ccount = round256(l.info + (size_t)rows * sizeof(RowInfo));
+  l.cand = round256(l.ccount + (size_t)rows * chunks * 4);
   l.total = round256(l.cand + (size_t)rows * chunks * chunk * 8);
   return l;
 }
 
-constexpr size_t kFinalLdsBudget = 160 * 1024;
+constexpr size_t kLdsMax = 160 * 1024;
 
 bool plan_select(int rows, int n_cols, int top_k, SelectPlan* p) {
   if (top_k < 1 || top_k > kMaxTopK) return false;
@@ -581,7 +632,6 @@ bool plan_select(int rows, int n_cols, int top_k, SelectPlan* p) {
   p->n_cols = n_cols;
   p->top_k = top_k;
   p->lds = finish_lds_bytes(top_k);
-  p->cand_lds = 0;
   if (n_cols <= kRowMax) {
     p->two_pass = 0;
     p->per = n_cols <= 1024 ? 4 : n_cols <= 2048 ? 8 : n_cols <= 4096 ? 16 : 32;
@@ -589,17 +639,13 @@ bool plan_select(int rows, int n_cols, int top_k, SelectPlan* p) {
     p->bytes = 0;
   } else {
     p->two_pass = 1;
-    const int64_t big = (int64_t)rows * ((n_cols + 4095) / 4096);
-    p->per = big >= 1024 ? 16 : 8;
-    const int chunk = p->per * kSelThreads;
+    p->per = (int64_t)rows * ((n_cols + 4095) / 4096) >= 1024 ? 16 : 8;
+    const int chunk = p->per * kChunkThreads;
     p->chunks = (n_cols + chunk - 1) / chunk;
     p->bytes = ws_layout(rows, p->chunks, chunk).total;
-    const size_t fixed = p->lds + (size_t)4 * ((p->chunks + 4) & ~3);
-    if (fixed > kFinalLdsBudget) return false;
-    size_t c = (kFinalLdsBudget - fixed) / 8;
-    if (c > 12288) c = 12288;
-    p->cand_lds = (int)c;
-    p->lds = fixed + (size_t)8 * p->cand_lds;
+    // the finishing workgroup also holds the chunk offsets and the position map
+    p->lds += (size_t)4 * ((p->chunks + 4) & ~3) + (size_t)2 * kFinalThreads * kFinalPer;
+    if (p->lds > kLdsMax) return false;
   }
   return true;
 }
@@ -622,28 +668,22 @@ template <int PER>
 static hipError_t launch_rows(const SelArgs& a, const SelectPlan& p, hipStream_t st) {
   hipError_t e = set_lds(select_rows_kernel<PER>, p.lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_rows_kernel<PER>, dim3(p.rows), dim3(kSelThreads), p.lds, st, a);
+  hipLaunchKernelGGL(select_rows_kernel<PER>, dim3(p.rows), dim3(kRowThreads), p.lds, st, a);
   return hipGetLastError();
 }
 
 template <int PER>
-static hipError_t launch_pipeline(const SelArgs& a, const SelectPlan& p, void* ws, size_t hist_bytes,
-                                  hipStream_t st) {
+static hipError_t launch_pipeline(const SelArgs& a, const SelectPlan& p, hipStream_t st) {
   hipError_t e = set_lds(select_final_kernel, p.lds);
   if (e != hipSuccess) return e;
-  const int64_t n16 = (int64_t)(hist_bytes / 16);
-  int blocks = (int)((n16 + 255) / 256);
-  if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, st, reinterpret_cast<uint4*>(ws), n16);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   const dim3 grid(p.chunks, p.rows);
-  hipLaunchKernelGGL(select_hist_kernel<PER>, grid, dim3(kSelThreads), 0, st, a);
+  hipLaunchKernelGGL(select_hist_kernel<PER>, grid, dim3(kChunkThreads), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(select_thresh_kernel, dim3(p.rows), dim3(kSelThreads), 0, st, a);
+  hipLaunchKernelGGL(select_thresh_kernel, dim3(p.rows), dim3(kChunkThreads), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(select_filter_kernel<PER>, grid, dim3(kSelThreads), 0, st, a);
+  hipLaunchKernelGGL(select_filter_kernel<PER>, grid, dim3(kChunkThreads), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(select_final_kernel, dim3(p.rows), dim3(kSelThreads), p.lds, st, a);
+  hipLaunchKernelGGL(select_final_kernel, dim3(p.rows), dim3(kFinalThreads), p.lds, st, a);
   return hipGetLastError();
 }
 
@@ -669,16 +709,15 @@ hipError_t launch_select(const SelectPlan& p, const float* scores, int64_t score
       default: return launch_rows<32>(a, p, st);
     }
   }
-  a.chunk = p.per * kSelThreads;
+  a.chunk = p.per * kChunkThreads;
   a.chunks = p.chunks;
-  a.cand_lds = p.cand_lds;
   const WsLayout l = ws_layout(p.rows, p.chunks, a.chunk);
   unsigned char* w = static_cast<unsigned char*>(ws);
   a.ghist = reinterpret_cast<uint32_t*>(w + l.hist);
   a.info = reinterpret_cast<RowInfo*>(w + l.info);
-  a.ccnt = reinterpret_cast<uint32_t*>(w + l.ccnt);
+  a.ccount = reinterpret_cast<uint32_t*>(w + l.ccount);
   a.cand = reinterpret_cast<uint64_t*>(w + l.cand);
-  return p.per == 16 ? launch_pipeline<16>(a, p, w, l.info, st) : launch_pipeline<8>(a, p, w, l.info, st);
+  return p.per == 16 ? launch_pipeline<16>(a, p, st) : launch_pipeline<8>(a, p, st);
 }
 
 }  // namespace salb

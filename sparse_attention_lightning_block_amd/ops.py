@@ -67,7 +67,10 @@ def indexer_topk_workspace_size(rows: int, n_cols: int, top_k: int) -> int:
 def indexer_topk_select(scores, top_k: int, *, valid_lens: Optional[torch.Tensor] = None, first_pos: int = 0,
                         ratio: int = 0, with_scores: bool = False, workspace: Optional[torch.Tensor] = None,
                         out_idx: Optional[torch.Tensor] = None, out_scores: Optional[torch.Tensor] = None):
-    """(idx [rows, top_k] int32, scores [rows, top_k] fp32 or None)."""
+    """(idx [rows, top_k] int32, scores [rows, top_k] fp32 or None).
+
+    A caller-provided workspace must be zero-filled before its first use; every
+    successful call leaves it ready for the next (re-zero it after an error)."""
     _dev(scores, "scores", torch.float32, 2)
     rows, n_cols = scores.shape
     dev = scores.device
@@ -79,7 +82,7 @@ def indexer_topk_select(scores, top_k: int, *, valid_lens: Optional[torch.Tensor
         out_scores = torch.empty((rows, top_k), dtype=torch.float32, device=dev)
     if workspace is None:
         nbytes = indexer_topk_workspace_size(rows, n_cols, top_k)
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)
     check(_lib.load().indexer_topk_select(
         _ptr(scores), scores.stride(0), _ptr(valid_lens), first_pos, ratio, rows, n_cols, top_k, _ptr(out_idx),
         _ptr(out_scores), _ptr(workspace), workspace.numel(), _stream()))
@@ -94,7 +97,10 @@ def indexer_score_topk(q, w, keys_fp4, key_scale, key_gscale, block_table, valid
                        precision: str = "mfma", with_scores: bool = False,
                        workspace: Optional[torch.Tensor] = None, out_idx: Optional[torch.Tensor] = None,
                        out_scores: Optional[torch.Tensor] = None):
-    """(idx [T, top_k] int32, scores [T, top_k] fp32 or None) = TopK of the indexer scores."""
+    """(idx [T, top_k] int32, scores [T, top_k] fp32 or None) = TopK of the indexer scores.
+
+    A caller-provided workspace must be zero-filled before its first use (see
+    indexer_topk_select)."""
     _dev(q, "q", (torch.float32, torch.bfloat16), 3)
     _dev(w, "w", torch.float32, 2)
     _dev(keys_fp4, "keys_fp4", torch.uint8, 3)
@@ -111,7 +117,7 @@ def indexer_score_topk(q, w, keys_fp4, key_scale, key_gscale, block_table, valid
     if with_scores and out_scores is None:
         out_scores = torch.empty((T, top_k), dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = torch.empty(max(indexer_score_topk_workspace_size(T, max_lb, epb, top_k), 1), dtype=torch.uint8,
+        workspace = torch.zeros(max(indexer_score_topk_workspace_size(T, max_lb, epb, top_k), 1), dtype=torch.uint8,
                                 device=dev)
     check(_lib.load().indexer_score_topk(
         _ptr(q), _q_dtype(q), _ptr(w), _ptr(keys_fp4), _ptr(key_scale), _ptr(key_gscale), _ptr(block_table),

@@ -214,3 +214,22 @@ def test_topk_select_degenerate(n_cols, k):
         assert gi[r].tolist() == o_idx.tolist(), r
         kk = min(k, int(valid[r]))
         assert np.array_equal(gv[r][:kk], o_val[:kk].astype(np.float32)), r
+
+
+def test_topk_select_workspace_reuse():
+    """One zero-filled workspace serves consecutive calls: each call leaves it ready."""
+    rows, n_cols, k = 5, 90000, 2048
+    ws = torch.zeros(salb.indexer_topk_workspace_size(rows, n_cols, k), dtype=torch.uint8, device="cuda")
+    for it in range(3):
+        rng = np.random.default_rng(500 + it)
+        s = rng.standard_normal((rows, n_cols)).astype(np.float32)
+        if it == 1:
+            s[:, ::5] = 2.0                  # ties at the threshold
+        valid = rng.integers(0, n_cols + 1, rows).astype(np.int32)
+        valid[0] = n_cols
+        idx, val = salb.indexer_topk_select(torch.from_numpy(s).cuda(), k, valid_lens=torch.from_numpy(valid).cuda(),
+                                            with_scores=True, workspace=ws)
+        gi = _row(idx)
+        for r in range(rows):
+            o_idx, _ = indexer.topk(s[r, : valid[r]].astype(np.float64), k)
+            assert gi[r].tolist() == o_idx.tolist(), (it, r)
