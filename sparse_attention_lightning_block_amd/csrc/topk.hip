@@ -14,12 +14,13 @@
 //     row in registers, finds the K-th composite with 12-bit-digit LDS histogram
 //     passes (stopping once the digit bin of the K-th entry is taken whole),
 //     gathers the winners and sorts them;
-//   * longer rows run as a pipeline of launches (kernel boundaries order them; no
-//     grid-wide fences, which write back the whole L2 on this chip): every
-//     workgroup of a (chunk, row) grid adds its chunk's LDS histogram of the top 12
-//     order-key bits (the bins that can hold the row's K-th entry) into one of
-//     eight global copies (one per XCD, so contended atomics stay in one L2); one workgroup per row sums the copies and finds the
-//     bin holding the K-th entry; the (chunk, row) grid then writes every entry at
+//   * longer rows run as a pipeline of three launches (kernel boundaries order
+//     them; no grid-wide fences, which write back the whole L2 on this chip):
+//     every workgroup of a (chunk, row) grid adds its chunk's LDS histogram of the
+//     top 12 order-key bits (the bins that can hold the row's K-th entry) into one
+//     of eight global copies (one per XCD, so contended atomics stay in one L2);
+//     the (chunk, row) grid then finds the bin holding the K-th entry from the
+//     copies (scanning down from the row's highest bin) and writes every entry at
 //     or above that bin to the chunk's own candidate slots; one 1024-thread
 //     workgroup per row loads those candidates (about K plus one bin's worth)
 //     into registers, selects the K winners exactly and sorts them.
@@ -65,6 +66,7 @@ struct SelArgs {
   int chunk;         // entries per chunk workgroup
   int chunks;        // chunks per row
   uint32_t* ghist;   // [rows][kHistCopies][kBins], zero between calls
+  uint32_t* gmax;    // [rows][kHistCopies] highest bin seen, zero between calls
   RowInfo* info;     // [rows]
   uint32_t* ccount;  // [rows][chunks] candidates per chunk
   uint64_t* cand;    // [rows][chunks][chunk] candidate slots
@@ -165,14 +167,21 @@ __device__ __forceinline__ void find_digit(const uint32_t (&h)[kBins / NT], uint
 #pragma unroll
   for (int q = 0; q < BPT; ++q) own += h[q];
   uint32_t ge = block_suffix<NT>(own, sh);
+  // exactly one thread holds the bin where the count from the top reaches rem
+  int hit = -1;
+  uint32_t hit_gt = 0, hit_cnt = 0;
 #pragma unroll
   for (int q = BPT - 1; q >= 0; --q) {
-    if (ge < rem && ge + h[q] >= rem) {
-      sh.digit = threadIdx.x * BPT + q;
-      sh.gt = ge;
-      sh.cnt = h[q];
-    }
+    const bool here = ge < rem && ge + h[q] >= rem;
+    hit = here ? q : hit;
+    hit_gt = here ? ge : hit_gt;
+    hit_cnt = here ? h[q] : hit_cnt;
     ge += h[q];
+  }
+  if (hit >= 0) {
+    sh.digit = threadIdx.x * BPT + hit;
+    sh.gt = hit_gt;
+    sh.cnt = hit_cnt;
   }
   __syncthreads();
 }
@@ -349,10 +358,9 @@ __device__ __forceinline__ FinishLds carve(unsigned char* smem, int top_k) {
 // ------------------------------------------------------------------ short rows
 
 // One workgroup per row; entry e of the row sits in register i of thread t with
-// e = i * 256 + t (coalesced loads).
-template <int PER>
-__global__ __launch_bounds__(kRowThreads) void select_rows_kernel(SelArgs a) {
-  constexpr int NT = kRowThreads;
+// e = i * NT + t (coalesced loads).
+template <int NT, int PER>
+__global__ __launch_bounds__(NT) void select_rows_kernel(SelArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ SelShared sh;
   const int row = gridDim.x - 1 - blockIdx.x;  // causal rows grow with the index: longest first
@@ -394,12 +402,14 @@ __global__ __launch_bounds__(kRowThreads) void select_rows_kernel(SelArgs a) {
 
 // Stage 1: the chunk's histogram of the top 12 order-key bits, added into the
 // global copy of the XCD the workgroup runs on (workgroups are dealt to the eight
-// XCDs round robin by linear index).
+// XCDs round robin by linear index), and the chunk's highest bin into that copy's
+// row maximum.
 template <int PER>
 __global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelArgs a) {
   constexpr int NT = kChunkThreads;
   __shared__ __align__(16) uint32_t hist[kBins];
   __shared__ SelShared sh;
+  __shared__ uint32_t top_bin;
   const int row = blockIdx.y;
   const int tid = threadIdx.x;
   const int n = row_valid(a, row);
@@ -413,12 +423,21 @@ __global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelArgs a) {
     x[i] = e < n ? src[e] : 0.0f;
   }
   clear_bins<NT>(hist);
+  if (tid == 0) top_bin = 0u;
   __syncthreads();
+  uint32_t mk = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lo + i * NT + tid;
-    if (e < n) atomicAdd(&hist[ord_key(x[i]) >> (32 - kDigit)], 1u);
+    if (e < n) {
+      const uint32_t b = ord_key(x[i]) >> (32 - kDigit);
+      atomicAdd(&hist[b], 1u);
+      mk = b > mk ? b : mk;
+    }
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mk = max(mk, (uint32_t)__shfl_xor((int)mk, off));
+  if ((tid & 63) == 0) atomicMax(&top_bin, mk);
   __syncthreads();
   // The row's K-th entry is at least the chunk's K-th entry, so bins below the
   // latter's never hold it and are not needed above it: they are not flushed.
@@ -439,43 +458,15 @@ __global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelArgs a) {
     const uint32_t v = hist[b];
     if (v && (uint32_t)b >= low) atomicAdd(&gh[b], v);
   }
+  if (tid == 0) atomicMax(&a.gmax[(int64_t)row * kHistCopies + copy], top_bin);
 }
 
-// Stage 2 (one workgroup per row): sum the copies, find the bin of the K-th entry.
-__global__ __launch_bounds__(kChunkThreads) void select_thresh_kernel(SelArgs a) {
-  constexpr int NT = kChunkThreads;
-  constexpr int BPT = kBins / NT;
-  __shared__ SelShared sh;
-  const int row = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int n = row_valid(a, row);
-  const int K = n < a.top_k ? n : a.top_k;
-  uint32_t h[BPT] = {};
-  const uint32_t* gh = a.ghist + (int64_t)row * kHistCopies * kBins + tid * BPT;
-#pragma unroll
-  for (int c = 0; c < kHistCopies; ++c) {
-    const uint4* p = reinterpret_cast<const uint4*>(gh + c * kBins);
-#pragma unroll
-    for (int j = 0; j < BPT / 4; ++j) {
-      const uint4 v = p[j];
-      h[4 * j] += v.x;
-      h[4 * j + 1] += v.y;
-      h[4 * j + 2] += v.z;
-      h[4 * j + 3] += v.w;
-    }
-  }
-  if (K == n) {  // every entry wins (also n == 0)
-    if (tid == 0) a.info[row] = RowInfo{0u, 0u, (uint32_t)n, 0u};
-    return;
-  }
-  find_digit<NT>(h, (uint32_t)K, sh);
-  if (tid == 0) a.info[row] = RowInfo{sh.digit, sh.gt, sh.cnt, 0u};
-}
-
-// Stage 3: every entry of the chunk in the K-th entry's bin or above goes to the
-// chunk's own candidate slots (their order does not matter: the composites are
-// ordered later), and the chunk's count to ccount.  The histogram copies have been
-// read by now: each workgroup zeroes its share of its row's, for the next call.
+// Stage 2: each workgroup finds the bin of its row's K-th entry from the copies,
+// scanning down from the row's highest bin (the bins above it are empty), then
+// writes every entry of its chunk in that bin or above to the chunk's own
+// candidate slots (their order does not matter: the composites are ordered later)
+// and the chunk's count to ccount.  The first chunk of the row also records the
+// bin for the last stage.
 template <int PER>
 __global__ __launch_bounds__(kChunkThreads) void select_filter_kernel(SelArgs a) {
   constexpr int NT = kChunkThreads;
@@ -485,19 +476,50 @@ __global__ __launch_bounds__(kChunkThreads) void select_filter_kernel(SelArgs a)
   const int n = row_valid(a, row);
   const int lo = blockIdx.x * (PER * NT);
   const int64_t slot = (int64_t)row * gridDim.x + blockIdx.x;
-  {
-    constexpr int kWords4 = kHistCopies * kBins / 4;
-    uint4* gh = reinterpret_cast<uint4*>(a.ghist + (int64_t)row * kHistCopies * kBins);
-    const int w0 = (int)(((int64_t)blockIdx.x * kWords4) / gridDim.x);
-    const int w1 = (int)(((int64_t)(blockIdx.x + 1) * kWords4) / gridDim.x);
-    for (int w = w0 + tid; w < w1; w += NT) gh[w] = make_uint4(0u, 0u, 0u, 0u);
+  if (lo >= n && blockIdx.x != 0) {
+    if (tid == 0) a.ccount[slot] = 0u;
+    return;
   }
+  const int K = n < a.top_k ? n : a.top_k;
+  RowInfo info{0u, 0u, (uint32_t)n, 0u};  // K == n: every entry is a candidate
+  if (K < n) {
+    const uint32_t* gm = a.gmax + (int64_t)row * kHistCopies;
+    uint32_t mb = 0;
+#pragma unroll
+    for (int c = 0; c < kHistCopies; ++c) mb = max(mb, gm[c]);
+    const uint32_t* gh = a.ghist + (int64_t)row * kHistCopies * kBins;
+    uint32_t carry = 0;
+    if (tid == 0) sh.digit = ~0u;
+    for (int base = 0; base <= (int)mb; base += NT) {
+      const int b = (int)mb - base - tid;  // thread t: the t-th bin down from the top
+      uint32_t v = 0;
+      if (b >= 0) {
+#pragma unroll
+        for (int c = 0; c < kHistCopies; ++c) v += gh[c * kBins + b];
+      }
+      const uint32_t below_me = block_suffix<NT>(v, sh);  // bins under this one, in this block
+      uint32_t total = 0;
+#pragma unroll
+      for (int w = 0; w < NT / kWave; ++w) total += sh.wsum[w];
+      const uint32_t above = carry + (total - below_me - v);
+      if (above < (uint32_t)K && above + v >= (uint32_t)K) {
+        sh.digit = (uint32_t)b;
+        sh.gt = above;
+        sh.cnt = v;
+      }
+      carry += total;
+      __syncthreads();
+      if (sh.digit != ~0u) break;
+    }
+    info = RowInfo{sh.digit, sh.gt, sh.cnt, 0u};
+  }
+  if (blockIdx.x == 0 && tid == 0) a.info[row] = info;
   if (lo >= n) {
     if (tid == 0) a.ccount[slot] = 0u;
     return;
   }
   const float* src = a.scores + (int64_t)row * a.score_stride;
-  const uint32_t bin = a.info[row].bin;
+  const uint32_t bin = info.bin;
   uint32_t key[PER];
   uint32_t mine = 0;
 #pragma unroll
@@ -516,7 +538,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_filter_kernel(SelArgs a)
   }
 }
 
-// Stage 4 (one workgroup per row): exact selection among the candidates, sort,
+// Stage 3 (one workgroup per row): exact selection among the candidates, sort,
 // output.  Up to kFinalPer candidates per thread are held in registers, fetched
 // through an LDS map from list position to chunk; longer lists (rows crowded with
 // equal scores) are read chunk by chunk at every pass.
@@ -535,6 +557,12 @@ __global__ __launch_bounds__(kFinalThreads) void select_final_kernel(SelArgs a) 
   uint16_t* owner = reinterpret_cast<uint16_t*>(off + ((nch + 4) & ~3));  // [NT * kFinalPer]
   const uint32_t* cnt = a.ccount + (int64_t)row * nch;
   const uint64_t* cd = a.cand + (int64_t)row * nch * a.chunk;
+  {
+    // the histogram copies and maxima have been read: leave them zero for the next call
+    uint4* gh = reinterpret_cast<uint4*>(a.ghist + (int64_t)row * kHistCopies * kBins);
+    for (int w = tid; w < kHistCopies * kBins / 4; w += NT) gh[w] = make_uint4(0u, 0u, 0u, 0u);
+    if (tid < kHistCopies) a.gmax[(int64_t)row * kHistCopies + tid] = 0u;
+  }
   // exclusive prefix of the chunk counts, 1024 chunks at a time
   uint32_t carry = 0;
   for (int c0 = 0; c0 < nch; c0 += NT) {
@@ -607,17 +635,18 @@ __global__ __launch_bounds__(kFinalThreads) void select_final_kernel(SelArgs a) 
 
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace of the long-row pipeline: histogram copies (zero between calls: the
-// caller zero-fills the workspace once, every call leaves them zero) | row info |
-// chunk counts | candidate slots.
+// Workspace of the long-row pipeline: histogram copies and row maxima (zero
+// between calls: the caller zero-fills the workspace once, every call leaves them
+// zero) | row info | chunk counts | candidate slots.
 struct WsLayout {
-  size_t hist, info, ccount, cand, total;
+  size_t hist, gmax, info, ccount, cand, total;
 };
 
 static WsLayout ws_layout(int rows, int chunks, int chunk) {
   WsLayout l;
   l.hist = 0;
-  l.info = round256((size_t)rows * kHistCopies * kBins * 4);
+  l.gmax = (size_t)rows * kHistCopies * kBins * 4;
+  l.info = round256(l.gmax + (size_t)rows * kHistCopies * 4);
   l.ccount = round256(l.info + (size_t)rows * sizeof(RowInfo));
   l.cand = round256(l.ccount + (size_t)rows * chunks * 4);
   l.total = round256(l.cand + (size_t)rows * chunks * chunk * 8);
@@ -664,11 +693,11 @@ static hipError_t set_lds(K kernel, size_t bytes) {
                              (int)bytes);
 }
 
-template <int PER>
+template <int NT, int PER>
 static hipError_t launch_rows(const SelArgs& a, const SelectPlan& p, hipStream_t st) {
-  hipError_t e = set_lds(select_rows_kernel<PER>, p.lds);
+  hipError_t e = set_lds(select_rows_kernel<NT, PER>, p.lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_rows_kernel<PER>, dim3(p.rows), dim3(kRowThreads), p.lds, st, a);
+  hipLaunchKernelGGL((select_rows_kernel<NT, PER>), dim3(p.rows), dim3(NT), p.lds, st, a);
   return hipGetLastError();
 }
 
@@ -678,8 +707,6 @@ static hipError_t launch_pipeline(const SelArgs& a, const SelectPlan& p, hipStre
   if (e != hipSuccess) return e;
   const dim3 grid(p.chunks, p.rows);
   hipLaunchKernelGGL(select_hist_kernel<PER>, grid, dim3(kChunkThreads), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(select_thresh_kernel, dim3(p.rows), dim3(kChunkThreads), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(select_filter_kernel<PER>, grid, dim3(kChunkThreads), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -703,10 +730,10 @@ hipError_t launch_select(const SelectPlan& p, const float* scores, int64_t score
   a.out_scores = out_scores;
   if (!p.two_pass) {
     switch (p.per) {
-      case 4: return launch_rows<4>(a, p, st);
-      case 8: return launch_rows<8>(a, p, st);
-      case 16: return launch_rows<16>(a, p, st);
-      default: return launch_rows<32>(a, p, st);
+      case 4: return launch_rows<kRowThreads, 4>(a, p, st);
+      case 8: return launch_rows<kRowThreads, 8>(a, p, st);
+      case 16: return launch_rows<kRowThreads, 16>(a, p, st);
+      default: return launch_rows<kRowThreads, 32>(a, p, st);
     }
   }
   a.chunk = p.per * kChunkThreads;
@@ -714,6 +741,7 @@ hipError_t launch_select(const SelectPlan& p, const float* scores, int64_t score
   const WsLayout l = ws_layout(p.rows, p.chunks, a.chunk);
   unsigned char* w = static_cast<unsigned char*>(ws);
   a.ghist = reinterpret_cast<uint32_t*>(w + l.hist);
+  a.gmax = reinterpret_cast<uint32_t*>(w + l.gmax);
   a.info = reinterpret_cast<RowInfo*>(w + l.info);
   a.ccount = reinterpret_cast<uint32_t*>(w + l.ccount);
   a.cand = reinterpret_cast<uint64_t*>(w + l.cand);
