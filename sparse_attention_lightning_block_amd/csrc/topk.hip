@@ -92,47 +92,82 @@ struct SelShared {
   uint32_t digit, gt, cnt, fill;
 };
 
+// Wave scans and reductions through DPP: shifts within 16-lane rows, then the row
+// broadcasts that carry the last lane of a row into the rows after it.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Inclusive prefix sum over the lanes of the wave.
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t x) {
+  x += dpp_or_zero<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_or_zero<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_or_zero<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_or_zero<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_or_zero<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_or_zero<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+// Maximum over the lanes of the wave (wave-uniform result).
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = max(x, dpp_or_zero<0x111, 0xf>(x));
+  x = max(x, dpp_or_zero<0x112, 0xf>(x));
+  x = max(x, dpp_or_zero<0x114, 0xf>(x));
+  x = max(x, dpp_or_zero<0x118, 0xf>(x));
+  x = max(x, dpp_or_zero<0x142, 0xa>(x));
+  x = max(x, dpp_or_zero<0x143, 0xc>(x));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+__device__ __forceinline__ uint64_t wave_max64(uint64_t x) {
+  const uint32_t hi = (uint32_t)(x >> 32);
+  const uint32_t mhi = wave_max(hi);
+  const uint32_t mlo = wave_max(hi == mhi ? (uint32_t)x : 0u);
+  return ((uint64_t)mhi << 32) | mlo;
+}
+
 // Sum of v over the threads with a larger index.  Two calls must be separated by a
 // barrier after the first call's result is used.
 template <int NT>
 __device__ __forceinline__ uint32_t block_suffix(uint32_t v, SelShared& sh) {
-  const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_down(x, off);
-    if (lane + off < 64) x += y;
-  }
-  if (lane == 0) sh.wsum[wave] = x;
+  const uint32_t incl = wave_prefix_sum(v);
+  const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  if ((threadIdx.x & 63) == 0) sh.wsum[wave] = tot;
   __syncthreads();
   uint32_t above = 0;
 #pragma unroll
   for (int w = 0; w < NT / kWave; ++w) above += w > wave ? sh.wsum[w] : 0u;
-  return above + x - v;
+  return above + tot - incl;
 }
 
-// Block-wide maximum and minimum (same barrier rule as block_suffix).
+// block_suffix, and the block-wide maximum and minimum of mx and mn (same barrier).
 template <int NT>
-__device__ __forceinline__ void block_minmax(uint64_t& mx, uint64_t& mn, SelShared& sh) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t a = __shfl_xor(mx, off);
-    const uint64_t b = __shfl_xor(mn, off);
-    mx = a > mx ? a : mx;
-    mn = b < mn ? b : mn;
-  }
+__device__ __forceinline__ uint32_t block_suffix_minmax(uint32_t v, uint64_t& mx, uint64_t& mn, SelShared& sh) {
+  const int wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_prefix_sum(v);
+  const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  const uint64_t wmx = wave_max64(mx);
+  const uint64_t wmn = ~wave_max64(~mn);
   if ((threadIdx.x & 63) == 0) {
-    sh.wred[threadIdx.x >> 6] = mx;
-    sh.wred[kMaxWaves + (threadIdx.x >> 6)] = mn;
+    sh.wsum[wave] = tot;
+    sh.wred[wave] = wmx;
+    sh.wred[kMaxWaves + wave] = wmn;
   }
   __syncthreads();
+  uint32_t above = 0;
+  mx = 0ull;
+  mn = ~0ull;
 #pragma unroll
   for (int w = 0; w < NT / kWave; ++w) {
+    above += w > wave ? sh.wsum[w] : 0u;
     const uint64_t a = sh.wred[w], b = sh.wred[kMaxWaves + w];
     mx = a > mx ? a : mx;
     mn = b < mn ? b : mn;
   }
+  return above + tot - incl;
 }
 
 // Thread t owns bins [t * BPT, (t + 1) * BPT).
@@ -244,10 +279,11 @@ __device__ __forceinline__ int pow2_at_least(int x) {
 
 // Sorts the K winners in sortbuf[0, K) (capacity pow2_at_least(K)) and writes the
 // row's output: K indices (and scores) in selection order, then -1 (and -inf) up
-// to top_k.  grp holds K entries; hist holds kBins + 4 counters.
+// to top_k.  mx and mn are the largest and smallest winner; grp holds K entries;
+// hist holds kBins + 4 counters.
 template <int NT>
 __device__ void finish_row(uint64_t* sortbuf, uint64_t* grp, uint32_t* hist, int K, int top_k, int32_t* oi,
-                           float* os, SelShared& sh) {
+                           float* os, uint64_t mx, uint64_t mn, SelShared& sh) {
   constexpr int BPT = kBins / NT;
   const int tid = threadIdx.x;
   for (int i = K + tid; i < top_k; i += NT) {
@@ -262,13 +298,6 @@ __device__ void finish_row(uint64_t* sortbuf, uint64_t* grp, uint32_t* hist, int
     }
     return;
   }
-  uint64_t mx = 0ull, mn = ~0ull;
-  for (int i = tid; i < K; i += NT) {
-    const uint64_t c = sortbuf[i];
-    mx = c > mx ? c : mx;
-    mn = c < mn ? c : mn;
-  }
-  block_minmax<NT>(mx, mn, sh);
   const int hb = 63 - __clzll(mx ^ mn);  // composites are distinct: mx != mn
   const int bsh = hb >= kDigit - 1 ? hb - (kDigit - 1) : 0;
   const uint64_t base = mn >> bsh;
@@ -294,8 +323,7 @@ __device__ void finish_row(uint64_t* sortbuf, uint64_t* grp, uint32_t* hist, int
     hist[tid * BPT + q] = start;
     start += h[q];
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) bmax = max(bmax, (uint32_t)__shfl_xor((int)bmax, off));
+  bmax = wave_max(bmax);
   if ((tid & 63) == 0) atomicMax(&sh.digit, bmax);
   __syncthreads();
   if (sh.digit > (uint32_t)kBucketMax) {
@@ -387,15 +415,22 @@ __global__ __launch_bounds__(NT) void select_rows_kernel(SelArgs a) {
   if (K < n) thr = radix_select<NT>(each, 0ull, 0ull, (uint32_t)K, 63, f.hist, sh);
   // gather the winners
   uint32_t mine = 0;
-  each([&](uint64_t c) { mine += c >= thr; });
-  uint32_t off = block_suffix<NT>(mine, sh);
+  uint64_t mx = 0ull, mn = ~0ull;
   each([&](uint64_t c) {
-    if (c >= thr) f.sortbuf[off++] = c;
+    if (c >= thr) {
+      ++mine;
+      mx = c > mx ? c : mx;
+      mn = c < mn ? c : mn;
+    }
+  });
+  uint32_t off = block_suffix_minmax<NT>(mine, mx, mn, sh);
+  each([&](uint64_t c) {
+    if (c >= thr && off < (uint32_t)K) f.sortbuf[off++] = c;  // exactly K are selected
   });
   __syncthreads();
   int32_t* oi = a.out_idx + (int64_t)row * a.top_k;
   float* os = a.out_scores ? a.out_scores + (int64_t)row * a.top_k : nullptr;
-  finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, sh);
+  finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, mx, mn, sh);
 }
 
 // ------------------------------------------------------------------ long rows
@@ -435,8 +470,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelArgs a) {
       mk = b > mk ? b : mk;
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mk = max(mk, (uint32_t)__shfl_xor((int)mk, off));
+  mk = wave_max(mk);
   if ((tid & 63) == 0) atomicMax(&top_bin, mk);
   __syncthreads();
   // The row's K-th entry is at least the chunk's K-th entry, so bins below the
@@ -534,7 +568,8 @@ __global__ __launch_bounds__(kChunkThreads) void select_filter_kernel(SelArgs a)
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lo + i * NT + tid;
-    if (e < n && (key[i] >> (32 - kDigit)) >= bin) cd[pos++] = composite(key[i], (uint32_t)e);
+    if (e < n && (key[i] >> (32 - kDigit)) >= bin && pos < (uint32_t)(PER * NT))
+      cd[pos++] = composite(key[i], (uint32_t)e);
   }
 }
 
@@ -557,6 +592,7 @@ __global__ __launch_bounds__(kFinalThreads) void select_final_kernel(SelArgs a) 
   uint16_t* owner = reinterpret_cast<uint16_t*>(off + ((nch + 4) & ~3));  // [NT * kFinalPer]
   const uint32_t* cnt = a.ccount + (int64_t)row * nch;
   const uint64_t* cd = a.cand + (int64_t)row * nch * a.chunk;
+  const uint32_t first = tid < nch ? cnt[tid] : 0u;  // in flight during the zeroing
   {
     // the histogram copies and maxima have been read: leave them zero for the next call
     uint4* gh = reinterpret_cast<uint4*>(a.ghist + (int64_t)row * kHistCopies * kBins);
@@ -567,7 +603,7 @@ __global__ __launch_bounds__(kFinalThreads) void select_final_kernel(SelArgs a) 
   uint32_t carry = 0;
   for (int c0 = 0; c0 < nch; c0 += NT) {
     const int c = c0 + tid;
-    const uint32_t v = c < nch ? cnt[c] : 0u;
+    const uint32_t v = c0 == 0 ? first : c < nch ? cnt[c] : 0u;
     const uint32_t above = block_suffix<NT>(v, sh);
     uint32_t total = 0;
 #pragma unroll
@@ -594,7 +630,8 @@ __global__ __launch_bounds__(kFinalThreads) void select_final_kernel(SelArgs a) 
       uint64_t x = 0ull;
       if (i < C) {
         const int c = owner[i];
-        x = cd[(int64_t)c * a.chunk + (i - (int)off[c])];
+        const int j = i - (int)off[c];  // in [0, count of chunk c)
+        x = (j >= 0 && j < a.chunk) ? cd[(int64_t)c * a.chunk + j] : 0ull;
       }
       v[r] = x;
     }
@@ -620,15 +657,22 @@ __global__ __launch_bounds__(kFinalThreads) void select_final_kernel(SelArgs a) 
                            f.hist, sh);
   }
   uint32_t mine = 0;
-  each([&](uint64_t c) { mine += c >= thr; });
-  uint32_t pos = block_suffix<NT>(mine, sh);
+  uint64_t mx = 0ull, mn = ~0ull;
+  each([&](uint64_t c) {
+    if (c >= thr) {
+      ++mine;
+      mx = c > mx ? c : mx;
+      mn = c < mn ? c : mn;
+    }
+  });
+  uint32_t pos = block_suffix_minmax<NT>(mine, mx, mn, sh);
   each([&](uint64_t c) {
     if (c >= thr && pos < (uint32_t)K) f.sortbuf[pos++] = c;  // exactly K are selected
   });
   __syncthreads();
   int32_t* oi = a.out_idx + (int64_t)row * a.top_k;
   float* os = a.out_scores ? a.out_scores + (int64_t)row * a.top_k : nullptr;
-  finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, sh);
+  finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, mx, mn, sh);
 }
 
 // ------------------------------------------------------------------ host planning
