@@ -62,10 +62,11 @@ def check_scores(got_row, ref, amag, precision, what=""):
     return float(err.max()) if n else 0.0
 
 
-def check_topk(gpu_idx, gpu_val, ref, amag, k, precision, what=""):
+def check_topk(gpu_idx, gpu_val, ref, amag, k, precision, what="", tol=None):
     """Set rules: K_t winners in [0, valid), distinct, -1 padded; any disagreement with the
     oracle's set lies within the score tolerance (both sides may err: 2 tau) of the
-    oracle's K-th score; the GPU order is its own scores descending, ties by index."""
+    oracle's K-th score; the GPU order is its own scores descending, ties by index.
+    ``tol`` (per entry) replaces the precision's score tolerance when given."""
     gpu_idx = np.asarray(gpu_idx)
     n = ref.shape[0]
     K = min(k, n)
@@ -77,7 +78,8 @@ def check_topk(gpu_idx, gpu_val, ref, amag, k, precision, what=""):
         return 0
     o_idx, o_val = indexer.topk(ref, k)
     vk = o_val[K - 1]
-    tol = score_tol(ref, amag, precision)
+    if tol is None:
+        tol = score_tol(ref, amag, precision)
     diff = set(g.tolist()) ^ set(o_idx[:K].tolist())
     tol_k = tol[o_idx[K - 1]]
     for s in diff:

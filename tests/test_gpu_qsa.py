@@ -1,0 +1,137 @@
+"""GPU parity of the QSA variant (block pooling, query prep, row scores, causal top-k)
+through the C ABI against the float64 oracle.  Needs an MI355X."""
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_lightning_block_amd as salb
+from oracle import indexer, qsa
+from tests.parity import MFMA_ROWMAX, check_topk
+from workloads import make
+
+pytestmark = pytest.mark.gpu
+
+# Pooled keys and prepared queries: each element within VEC_REL of the vector's
+# largest magnitude.  The GPU forms a 16-term mean, a sum of squares, one rsqrt and a
+# rotation in fp32 (angles in fp64, cos/sin rounded to fp32): each element carries a
+# few fp32 roundings (~1e-7 relative to the vector's scale); 1e-5 leaves a wide margin.
+VEC_REL = 1e-5
+# Row scores on the FP32 path from the same fp32 inputs: |dS| <= 1e-5 |S| + 1e-6 A,
+# A = sum_h sum_d |q_hd k_d| / sqrt(hd) (the FP32 tolerance of the CSA scores).
+# End to end from the bf16 inputs, the fp32 roundings of the pooled keys and the
+# prepared queries enter every product: the A term grows to 1e-5.
+S_REL, S_ABS_A, CHAIN_ABS_A = 1e-5, 1e-6, 1e-5
+
+
+def _bf16(bits):
+    return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
+
+
+def _pool_all(w, dev="cuda"):
+    raw = _bf16(w.raw_keys).to(dev)
+    kw = torch.from_numpy(w.k_norm_w).to(dev)
+    keys = torch.full((w.n_blocks, w.hd), float("nan"), dtype=torch.float32, device=dev)
+    salb.qsa_block_pool(raw, kw, keys, first_block=0, n_new=w.n_blocks, ratio=w.ratio, rot=w.rot, theta=w.theta,
+                        eps=w.eps)
+    return keys
+
+
+def _qprep(w, dev="cuda"):
+    qk = _bf16(w.qk).to(dev)
+    qw = torch.from_numpy(w.q_norm_w).to(dev)
+    return salb.qsa_qprep_rows(qk, qw, n_heads=w.n_heads, hd=w.hd, first_pos=w.first_pos, rot=w.rot, theta=w.theta,
+                               eps=w.eps)
+
+
+def _check_vectors(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    scale = np.max(np.abs(ref), axis=-1, keepdims=True)
+    err = np.abs(got - ref)
+    bad = np.argwhere(err > VEC_REL * scale)
+    assert bad.size == 0, f"{what}: {len(bad)} elements out of tolerance, first {bad[:3].tolist()}"
+
+
+def _abs_sum(q, keys, valid):
+    """A[r, b] = sum_h sum_d |q[r,h,d] k[b,d]| / sqrt(hd), for b < valid[r]."""
+    hd = q.shape[2]
+    return [np.abs(q[r]).sum(axis=0) @ np.abs(keys[: int(valid[r])]).T / np.sqrt(hd) for r in range(q.shape[0])]
+
+
+def test_block_pool_reduced():
+    w = make(5, reduced=1)
+    keys = _pool_all(w).cpu().numpy()
+    ref = qsa.block_pool(indexer.upcast(w.raw_keys, "bf16"), w.k_norm_w, 0, w.n_blocks, w.ratio, w.rot, w.theta,
+                         w.eps)
+    _check_vectors(keys, ref, "block pool")
+
+
+def test_block_pool_partial_range_and_empty():
+    """Only rows first_block .. first_block + n_new - 1 are written; n_new == 0 writes nothing."""
+    w = make(5, reduced=1)
+    raw = _bf16(w.raw_keys).cuda()
+    kw = torch.from_numpy(w.k_norm_w).cuda()
+    keys = torch.full((w.n_blocks, w.hd), 7.0, dtype=torch.float32, device="cuda")
+    salb.qsa_block_pool(raw, kw, keys, first_block=100, n_new=37, ratio=w.ratio, rot=w.rot, theta=w.theta, eps=w.eps)
+    salb.qsa_block_pool(raw, kw, keys, first_block=5, n_new=0, ratio=w.ratio, rot=w.rot, theta=w.theta, eps=w.eps)
+    got = keys.cpu().numpy()
+    assert np.all(got[:100] == 7.0) and np.all(got[137:] == 7.0)
+    ref = qsa.block_pool(indexer.upcast(w.raw_keys, "bf16"), w.k_norm_w, 100, 37, w.ratio, w.rot, w.theta, w.eps)
+    _check_vectors(got[100:137], ref, "block pool range")
+
+
+def test_qprep_rows_reduced():
+    w = make(5, reduced=1)
+    q = _qprep(w).cpu().numpy()
+    ref = qsa.qprep_rows(indexer.upcast(w.qk, "bf16"), w.q_norm_w, w.rows, w.first_pos, w.n_heads * w.hd, w.n_heads,
+                         w.hd, w.rot, w.theta, w.eps)
+    _check_vectors(q, ref, "qprep")
+
+
+@pytest.mark.parametrize("precision", ["fp32", "mfma"])
+def test_score_rows_and_topk_reduced(precision):
+    """Scores from the GPU's own pooled keys and prepared queries (the same fp32 inputs on
+    both sides), then the causal top-k on those scores."""
+    w = make(5, reduced=1)
+    keys_d = _pool_all(w)
+    q_d = _qprep(w)
+    sc = salb.qsa_score_rows(q_d, keys_d, first_pos=w.first_pos, ratio=w.ratio, precision=precision)
+    idx, val = salb.indexer_topk_select(sc, w.top_k, first_pos=w.first_pos, ratio=w.ratio, with_scores=True)
+    torch.cuda.synchronize()
+    q, keys = q_d.cpu().numpy().astype(np.float64), keys_d.cpu().numpy().astype(np.float64)
+    ref, valid = qsa.score_rows(q, keys, w.first_pos, w.ratio)
+    A = _abs_sum(q, keys, valid)
+    got, gi, gv = sc.cpu().numpy(), idx.cpu().numpy(), val.cpu().numpy()
+    for r in range(w.rows):
+        v = int(valid[r])
+        assert np.all(np.isneginf(got[r, v:])), f"row {r}: blocks past the complete count must be -inf"
+        if precision == "fp32":
+            tol = S_REL * np.abs(ref[r, :v]) + S_ABS_A * A[r]
+        else:
+            tol = np.full(v, MFMA_ROWMAX * np.max(np.abs(ref[r, :v])))
+        err = np.abs(got[r, :v].astype(np.float64) - ref[r, :v])
+        assert np.all(err <= tol), f"row {r}: max err {err.max()}"
+        check_topk(gi[r], gv[r], ref[r, :v], None, w.top_k, precision, f"qsa row {r}", tol=tol)
+
+
+def test_chain_end_to_end_reduced():
+    """bf16 raw keys and projections -> pooled keys, prepared q, scores, top-k; against the
+    oracle chain in float64."""
+    w = make(5, reduced=1)
+    keys_d = _pool_all(w)
+    q_d = _qprep(w)
+    sc = salb.qsa_score_rows(q_d, keys_d, first_pos=w.first_pos, ratio=w.ratio, precision="fp32")
+    idx, val = salb.indexer_topk_select(sc, w.top_k, first_pos=w.first_pos, ratio=w.ratio, with_scores=True)
+    keys = qsa.block_pool(indexer.upcast(w.raw_keys, "bf16"), w.k_norm_w, 0, w.n_blocks, w.ratio, w.rot, w.theta,
+                          w.eps)
+    q = qsa.qprep_rows(indexer.upcast(w.qk, "bf16"), w.q_norm_w, w.rows, w.first_pos, w.n_heads * w.hd, w.n_heads,
+                       w.hd, w.rot, w.theta, w.eps)
+    ref, valid = qsa.score_rows(q, keys, w.first_pos, w.ratio)
+    A = _abs_sum(q, keys, valid)
+    got, gi, gv = sc.cpu().numpy(), idx.cpu().numpy(), val.cpu().numpy()
+    for r in range(w.rows):
+        v = int(valid[r])
+        tol = S_REL * np.abs(ref[r, :v]) + CHAIN_ABS_A * A[r]
+        err = np.abs(got[r, :v].astype(np.float64) - ref[r, :v])
+        assert np.all(err <= tol), f"row {r}: max err {err.max()}"
+        check_topk(gi[r], gv[r], ref[r, :v], None, w.top_k, "fp32", f"qsa chain row {r}", tol=tol)
