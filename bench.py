@@ -12,6 +12,7 @@ JSON line.  The default workload is the decode configuration
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +34,36 @@ WORKLOADS = {
     "long_decode_T32_S262144": 3,
     "prefill_T4096": 4,
 }
+
+
+# HBM traffic of one scorer launch, from two rocprofv3 --pmc passes (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for a plain
+# 256 MiB copy (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0); the summaries are under
+# profiles/.  Valid only for the scorer sources they were taken with: a different
+# source hash reports null.
+SCORER_SOURCES = ["score.hip", "nvfp4.hpp", "common.hpp", "internal.hpp"]
+TRAFFIC_COPY_FACTOR = {"FETCH_SIZE": 1.9998, "WRITE_SIZE": 1.0}
+SCORER_TRAFFIC_KIB = {   # workload: (FETCH_SIZE, WRITE_SIZE) KiB per dispatch
+    "decode_T8_S65536": (3552.2, 2048.0),
+    "long_decode_T32_S262144": (13693.5, 32768.8),
+    "prefill_T4096": (35574.6, 65657.1),
+}
+SCORER_TRAFFIC_SHA = "bc82987ca976d653"
+
+
+def scorer_source_sha():
+    h = hashlib.sha256()
+    for f in SCORER_SOURCES:
+        with open(os.path.join(ROOT, "sparse_attention_lightning_block_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def scorer_traffic(workload):
+    kib = SCORER_TRAFFIC_KIB.get(workload)
+    if kib is None or scorer_source_sha() != SCORER_TRAFFIC_SHA:
+        return None
+    return int((kib[0] * TRAFFIC_COPY_FACTOR["FETCH_SIZE"] + kib[1] * TRAFFIC_COPY_FACTOR["WRITE_SIZE"]) * 1024)
 
 
 def key_bytes_per_entry(D, epb):
@@ -148,8 +179,8 @@ def main():
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
-        "traffic": None,
-        "kernel": "score_mfma_kernel" if mfma else "score_f32_kernel",
+        "traffic": scorer_traffic(w.name) if mfma else None,
+        "kernel": ("score_mfma_group_kernel" if w.T >= 4 else "score_mfma_split_kernel") if mfma else "score_f32_kernel",
         "kernel_avg_us": round(score_avg_s * 1e6, 2),
         "bytes_per_launch": int(bytes_alg),
         "compute": {

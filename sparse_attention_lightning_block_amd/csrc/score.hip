@@ -5,21 +5,27 @@
 // and the scoring loop of its main kernel), with the NVFP4 keys of a paged pool
 // resolved through a per-query block table (same page, main kernel).
 //
-// Two scorers share the work decomposition -- a workgroup owns one query row and a
-// contiguous chunk of that row's logical keys; chunks are spread over the XCDs so
-// that all rows of one chunk run on the same XCD (shared pages hit one L2):
+// The scorers share the work decomposition -- a workgroup owns one query row (or a
+// group of four) and a contiguous chunk of its logical keys; chunks are spread over
+// the XCDs so that all rows of one chunk run on the same XCD (shared pages hit one
+// L2):
 //
-//  * score_mfma_kernel (IDX_PREC_MFMA): the head x key contraction on the fp16
+//  * the MFMA scorers (IDX_PREC_MFMA) run the head x key contraction on the fp16
 //    matrix cores.  A 16x16x32 MFMA takes 16 heads (M) x 32 dims (K) of q from
-//    registers and 32 dims x 16 keys (N) of decoded NVFP4 keys; each lane decodes
-//    its own 16-byte slice of one key straight into the B operand (no LDS trip).
-//    The K order inside an instruction is a fixed permutation of the head dims
-//    applied to both operands, chosen so that every lane's slice is contiguous.
-//    The epilogue applies ReLU, the head weights and the per-page global scale to
-//    the fp32 accumulators, reduces the 64 heads (in-lane, then two lane swaps)
-//    and writes one score per key.  q is prescaled per head by a power of two so
-//    that its fp16 rounding is relative (11 bits); the inverse power is folded
-//    into the head weight, which keeps the result identical up to that rounding.
+//    registers and 32 dims x 16 keys (N) of decoded NVFP4 keys.  The K order inside
+//    an instruction is a fixed permutation of the head dims applied to both
+//    operands, chosen so that every lane's key slice is contiguous.  The epilogue
+//    applies ReLU, the head weights and the per-page global scale to the fp32
+//    accumulators, reduces the heads (in-lane, then two lane swaps) and writes one
+//    score per key.  q is prescaled per head by a power of two so that its fp16
+//    rounding is relative (11 bits); the inverse power is folded into the head
+//    weight, which keeps the result identical up to that rounding.
+//      - score_mfma_split_kernel (fewer than four rows): every wave streams its own
+//        keys of the row; each lane decodes its 16-byte slice of one key straight
+//        into the B operand (no LDS trip).
+//      - score_mfma_group_kernel (four rows or more): four rows per workgroup, one
+//        per wave; when the four rows resolve the chunk to the same pages, each
+//        64-key tile is decoded once into LDS and read by all four waves.
 //  * score_f32_kernel (IDX_PREC_FP32): one key per lane, fp32 FMAs with q read
 //    through the scalar cache, for results within ~1e-5 relative.
 #include <hip/hip_runtime.h>
