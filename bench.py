@@ -33,6 +33,7 @@ WORKLOADS = {
     "decode_T8_S65536": 2,
     "long_decode_T32_S262144": 3,
     "prefill_T4096": 4,
+    "qsa_prefill": 5,
 }
 
 
@@ -102,6 +103,139 @@ def cpu_baseline(w, budget_s=20.0):
     }
 
 
+def cpu_baseline_qsa(w, budget_s=20.0):
+    """Time the CPU oracle (as it stands) on the QSA chain for a bounded sample of rows."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import indexer, qsa
+
+    t0 = time.perf_counter()
+    keys = qsa.block_pool(indexer.upcast(w.raw_keys, "bf16"), w.k_norm_w, 0, w.n_blocks, w.ratio, w.rot, w.theta,
+                          w.eps)
+    t_pool = time.perf_counter() - t0
+    pairs = 0
+    rows = 0
+    t1 = time.perf_counter()
+    for r0 in range(0, w.rows, 8):
+        n = min(8, w.rows - r0)
+        q = qsa.qprep_rows(indexer.upcast(w.qk[r0:r0 + n], "bf16"), w.q_norm_w, n, w.first_pos + r0,
+                           w.n_heads * w.hd, w.n_heads, w.hd, w.rot, w.theta, w.eps)
+        sc, valid = qsa.score_rows(q, keys, w.first_pos + r0, w.ratio)
+        for i in range(n):
+            indexer.topk(sc[i, : int(valid[i])], w.top_k)
+        pairs += int(valid.sum())
+        rows += n
+        if time.perf_counter() - t1 > budget_s:
+            break
+    dt = time.perf_counter() - t1
+    # the pooling is shared by all rows: charge it pro rata to the sampled rows
+    dt_all = dt + t_pool * rows / w.rows
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {
+        "value": pairs / dt_all,
+        "unit": "scores/s",
+        "cores": int(min(threads, len(os.sched_getaffinity(0)))),
+        "kind": "oracle",
+        "sample": f"{rows} of {w.rows} rows ({pairs} row-block pairs): query prep, float64 scores, full sort top-k "
+                  f"({dt:.2f} s), plus {rows}/{w.rows} of the float64 block pooling ({t_pool:.2f} s in all)",
+    }
+
+
+def run_qsa(args, w):
+    import torch
+
+    import sparse_attention_lightning_block_amd as salb
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    raw = torch.from_numpy(w.raw_keys.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    kw = torch.from_numpy(w.k_norm_w).to(dev)
+    qk = torch.from_numpy(w.qk.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    qw = torch.from_numpy(w.q_norm_w).to(dev)
+    keys = torch.empty((w.n_blocks, w.hd), dtype=torch.float32, device=dev)
+    q = torch.empty((w.rows, w.n_heads, w.hd), dtype=torch.float32, device=dev)
+    scores = torch.empty((w.rows, w.n_blocks), dtype=torch.float32, device=dev)
+    idx = torch.empty((w.rows, w.top_k), dtype=torch.int32, device=dev)
+    ws = torch.zeros(max(1, salb.indexer_topk_workspace_size(w.rows, w.n_blocks, w.top_k)), dtype=torch.uint8,
+                     device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        salb.qsa_block_pool(raw, kw, keys, first_block=0, n_new=w.n_blocks, ratio=w.ratio, rot=w.rot, theta=w.theta,
+                            eps=w.eps)
+        salb.qsa_qprep_rows(qk, qw, n_heads=w.n_heads, hd=w.hd, first_pos=w.first_pos, rot=w.rot, theta=w.theta,
+                            eps=w.eps, out=q)
+        if ev is not None:
+            ev[1].record()
+        salb.qsa_score_rows(q, keys, first_pos=w.first_pos, ratio=w.ratio, precision=args.precision, out=scores)
+        if ev is not None:
+            ev[2].record()
+        salb.indexer_topk_select(scores, w.top_k, first_pos=w.first_pos, ratio=w.ratio, workspace=ws, out_idx=idx)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    prep_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    score_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    select_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    pos = w.first_pos + np.arange(w.rows, dtype=np.int64)
+    pairs = int(np.minimum((pos + 1) // w.ratio, w.n_blocks).sum())
+    flops = 2.0 * pairs * w.n_heads * w.hd
+    score_s = float(score_ms.mean()) / 1e3
+    tf = flops / score_s / 1e12
+    # the library's QSA scorer takes the matrix cores for hd 64/128 with 16, 32 or 64 heads
+    mfma = args.precision == "mfma" and w.hd in (64, 128) and w.n_heads in (16, 32, 64)
+    peak = MFMA_F16_PEAK_TFLOPS if mfma else VALU_F32_PEAK_TFLOPS
+    pool_bytes = w.n_blocks * w.ratio * w.hd * 2 + w.n_blocks * w.hd * 4
+    out = {
+        "metric": METRIC,
+        "value": pairs / (ms_per_step / 1e3),
+        "unit": "scores/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if mfma else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "rows": w.rows, "heads": w.n_heads, "hd": w.hd, "raw_keys": w.n_blocks * w.ratio,
+                   "ratio": w.ratio, "blocks": w.n_blocks, "top_k": w.top_k, "pairs": pairs,
+                   "precision": args.precision},
+        "step_ms": {"p50": float(np.median(prep_ms + score_ms + select_ms))},
+        "stage_ms": {"pool_and_qprep": float(np.median(prep_ms)), "score": float(np.median(score_ms)),
+                     "select": float(np.median(select_ms))},
+        "roofline": {
+            "bound": "mfma" if mfma else "alu",
+            "achieved": round(tf, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(tf / peak, 4),
+            "traffic": None,
+            "kernel": "qsa_score_mfma_kernel" if mfma else "qsa_score_f32_kernel",
+            "kernel_avg_us": round(score_s * 1e6, 2),
+            "flops_per_launch": int(flops),
+            "pool": {"bytes_per_launch": pool_bytes, "stage_ms_with_qprep": float(np.median(prep_ms))},
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_qsa(w),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +257,9 @@ def main():
     from workloads import make
 
     w = make(WORKLOADS[args.workload])
+    if w.kind == "qsa":
+        run_qsa(args, w)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     d = to_dev(w, dev)

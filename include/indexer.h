@@ -183,6 +183,9 @@ int qsa_qprep_rows(const uint16_t* qk, const float* q_norm_w, float* q_out,
  *  block_keys [n_blocks_max, hd] fp32
  *  scores     [rows, n_blocks_max] fp32 output, row stride score_stride >= n_blocks_max
  * Supported: hd in {64, 128, 256}, 1 <= n_heads <= 64; precision IDX_PREC_FP32 or IDX_PREC_MFMA.
+ * IDX_PREC_MFMA runs on the fp16 matrix cores (q and keys rounded to fp16, fp32
+ * accumulation; within 2e-3 of the row's largest score) when hd is 64 or 128 and
+ * n_heads is 16, 32 or 64, and on the fp32 path (~1e-5 relative) otherwise.
  */
 int qsa_score_rows(const float* q, const float* block_keys, float* scores,
                    uint32_t rows, uint32_t n_blocks_max, uint32_t first_pos, uint32_t score_stride,
