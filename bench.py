@@ -49,7 +49,7 @@ SCORER_TRAFFIC_KIB = {   # workload: (FETCH_SIZE, WRITE_SIZE) KiB per dispatch
     "long_decode_T32_S262144": (13693.5, 32768.8),
     "prefill_T4096": (35574.6, 65657.1),
 }
-SCORER_TRAFFIC_SHA = "bc82987ca976d653"
+SCORER_TRAFFIC_SHA = "a082dab864165972"
 
 
 def scorer_source_sha():

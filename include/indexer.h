@@ -155,6 +155,7 @@ int indexer_score_topk(const void* q, int q_dtype, const float* w,
  *  raw_keys   [>= ratio*(first_block+n_new), hd] bf16 (uint16 bit patterns)
  *  k_norm_w   [hd] fp32
  *  block_keys [>= first_block+n_new, hd] fp32 output (only the n_new rows are written)
+ * raw_keys and block_keys 16-byte aligned.
  * Supported: hd in {64, 128, 256}, rot even and <= hd, ratio >= 1.
  */
 int qsa_block_pool(const uint16_t* raw_keys, const float* k_norm_w, float* block_keys,
@@ -166,9 +167,12 @@ int qsa_block_pool(const uint16_t* raw_keys, const float* k_norm_w, float* block
  *
  * For row r and head h: x = qk[r, h*hd .. h*hd+hd-1];
  *     q_out[r, h, :] = RoPE(x / sqrt(mean(x^2) + eps) * (1 + q_norm_w), first_pos + r)
- *  qk       [rows, qkw] bf16 (uint16 bit patterns), qkw >= n_heads*hd
+ *  qk       [rows, qkw] bf16 (uint16 bit patterns), qkw >= n_heads*hd, qkw a multiple
+ *           of 8, 16-byte aligned
  *  q_norm_w [hd] fp32
- *  q_out    [rows, n_heads, hd] fp32 output
+ *  q_out    [rows, n_heads, hd] fp32 output, 16-byte aligned
+ * RoPE as in qsa_block_pool.
+ * Supported: hd in {64, 128, 256}, rot even and <= hd, n_heads * hd <= 32768.
  */
 int qsa_qprep_rows(const uint16_t* qk, const float* q_norm_w, float* q_out,
                    uint32_t rows, uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t hd,

@@ -210,8 +210,8 @@ int qsa_block_pool(const uint16_t* raw_keys, const float* k_norm_w, float* block
   if (rot > hd || (rot & 1)) return fail(IDX_ERR_SHAPE, "rot %u must be even and <= hd", rot);
   if (ratio < 1) return fail(IDX_ERR_SHAPE, "ratio must be >= 1");
   if ((uint64_t)first_block + n_new > 0x7fffffffull) return fail(IDX_ERR_SHAPE, "block range too large");
-  if (!aligned(raw_keys, 16) || !aligned(block_keys, 4) || !aligned(k_norm_w, 4))
-    return fail(IDX_ERR_SHAPE, "raw_keys must be 16-byte aligned");
+  if (!aligned(raw_keys, 16) || !aligned(block_keys, 16) || !aligned(k_norm_w, 4))
+    return fail(IDX_ERR_SHAPE, "raw_keys and block_keys must be 16-byte aligned");
   if (n_new == 0) return ok();
   hipError_t e = salb::launch_block_pool(raw_keys, k_norm_w, block_keys, first_block, n_new, ratio, hd, rot, theta,
                                          eps, stream);
@@ -227,6 +227,10 @@ int qsa_qprep_rows(const uint16_t* qk, const float* q_norm_w, float* q_out, uint
   if (rot > hd || (rot & 1)) return fail(IDX_ERR_SHAPE, "rot %u must be even and <= hd", rot);
   if (n_heads < 1 || n_heads > 65535) return fail(IDX_ERR_SHAPE, "n_heads %u out of range", n_heads);
   if ((uint64_t)n_heads * hd > qkw) return fail(IDX_ERR_SHAPE, "qkw %u < n_heads * hd", qkw);
+  if ((uint64_t)n_heads * hd > 32768)
+    return fail(IDX_ERR_UNSUPPORTED, "n_heads * hd = %llu (supported: <= 32768)", (unsigned long long)n_heads * hd);
+  if (qkw % 8 != 0 || !aligned(qk, 16) || !aligned(q_out, 16) || !aligned(q_norm_w, 4))
+    return fail(IDX_ERR_SHAPE, "qk and q_out must be 16-byte aligned and qkw a multiple of 8");
   if (rows == 0) return ok();
   hipError_t e = salb::launch_qprep_rows(qk, q_norm_w, q_out, rows, first_pos, qkw, n_heads, hd, rot, theta, eps,
                                          stream);

@@ -39,6 +39,11 @@ __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
   return ((uint64_t)key << 32) | (uint32_t)(~idx);
 }
 
+// ReLU through the integer max: a negative float (sign bit set) is a negative int32,
+// so max(bits, 0) gives +0.0 for it and leaves non-negative values unchanged.  One
+// VALU op, with no NaN canonicalisation.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Exact floor(s / epb) for s < 2^24 and epb <= 2^16: m = ceil(2^40 / epb).
 __device__ __forceinline__ uint32_t div_epb(uint32_t s, uint64_t magic) {
   return (uint32_t)(((uint64_t)s * magic) >> 40);

@@ -43,6 +43,7 @@ struct SelectPlan {
   int two_pass;   // 0: one workgroup per row; 1: histogram + filter grid over (chunk, row)
   int per;        // entries per thread (a row, or a chunk of the two-pass grid)
   int chunks;     // chunks per row (two-pass)
+  int final_nt;   // threads of the finishing workgroup (two-pass)
   size_t lds;     // dynamic LDS of a workgroup that finishes a row
   size_t bytes;   // workspace bytes
 };

@@ -11,7 +11,7 @@
 // pos * theta^(-2i/rot).  The page gives rot and theta but no pairing; the half
 // split is this library's convention.  At the positions of long prefills
 // (~5e5) an fp32 angle would be off by ~0.03 rad, so the angle, its sine and
-// cosine and the rotation are evaluated in fp64.
+// cosine and the rotation are evaluated in fp64 (once per position and pair).
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -21,94 +21,176 @@ namespace salb {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Sum over the block (blockDim.x <= 256, a multiple of 64).
-__device__ __forceinline__ float block_sum(float v, float* red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  float s = 0.0f;
-  const int nw = blockDim.x >> 6;
-  for (int w = 0; w < nw; ++w) s += red[w];
-  __syncthreads();
-  return s;
-}
-
-// Rotate the pairs (i, i + rot/2) of x (in LDS, fp32) at position pos; thread d < rot/2
-// writes both members of its pair into `out`.
-__device__ __forceinline__ void rope_pair(const float* x, float* out_row, int d, int hd, int rot, double pos,
-                                          double theta) {
-  const int half = rot >> 1;
-  if (d < half) {
-    const double inv_freq = pow(theta, -2.0 * (double)d / (double)rot);
-    double s, c;
-    sincos(pos * inv_freq, &s, &c);
-    const double a = x[d], b = x[d + half];
-    out_row[d] = (float)(a * c - b * s);
-    out_row[d + half] = (float)(a * s + b * c);
-  } else if (d >= rot && d < hd) {
-    out_row[d] = x[d];
-  }
-}
-
 // ------------------------------------------------------------------ block pool
 
+// Eight pooled blocks per 256-thread workgroup, 32 threads per block.  Thread j of a
+// block owns the 8-dim column group j % CG of the raw rows r = j / CG (mod 32 / CG):
+// every 16-byte load of the block is in flight at once.  The column sums meet
+// through lane swaps, the RMSNorm sum of squares through a reduction over the
+// column groups, and the rotation pairs through LDS.  The rotation angle and its
+// sine and cosine are evaluated in fp64 (at long-prefill positions an fp32 angle is
+// off by ~0.03 rad), once per (block, pair).
 template <int HD>
 __global__ __launch_bounds__(256) void block_pool_kernel(const uint16_t* __restrict__ raw,
                                                          const float* __restrict__ kw, float* __restrict__ out,
-                                                         uint32_t first_block, uint32_t ratio, int rot,
-                                                         float theta, float eps) {
-  constexpr int CG = HD / 8;        // 16-byte column groups per row
-  constexpr int RL = 256 / CG;      // rows handled in parallel
-  __shared__ float part[RL][HD];
-  __shared__ float xs[HD];
-  __shared__ float red[4];
-  const uint32_t b = first_block + blockIdx.x;
+                                                         uint32_t first_block, uint32_t n_new, uint32_t ratio,
+                                                         int rot, float theta, float eps) {
+  constexpr int TPB = 32;           // threads per block
+  constexpr int NBW = 256 / TPB;    // blocks per workgroup
+  constexpr int CG = HD / 8;        // 16-byte column groups per raw row
+  constexpr int RC = TPB / CG;      // raw-row classes (threads per column group)
+  static_assert(RC >= 1 && TPB % CG == 0, "head_dim");
+  __shared__ float xs[NBW][HD];
+  __shared__ double cs[NBW][HD / 2][2];
   const int tid = threadIdx.x;
-  const int cg = tid % CG, rl = tid / CG;
+  const int bi = tid / TPB, j = tid % TPB;
+  const int cg = j % CG, rc = j / CG;
+  const uint32_t nb_local = blockIdx.x * NBW + bi;
+  const bool live = nb_local < n_new;
+  const uint32_t b = first_block + nb_local;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const uint16_t* base = raw + (int64_t)b * ratio * HD;
-  for (uint32_t r = rl; r < ratio; r += RL) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(base + (int64_t)r * HD + cg * 8);
+  if (live) {
+    const uint16_t* base = raw + (int64_t)b * ratio * HD + cg * 8;
+    uint32_t r = rc;
+    for (; r + 3 * RC < ratio; r += 4 * RC) {
+      u32x4 v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += __uint_as_float(v[i] << 16);
-      acc[2 * i + 1] += __uint_as_float(v[i] & 0xffff0000u);
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const u32x4*>(base + (int64_t)(r + u * RC) * HD);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += __uint_as_float(v[u][i] << 16);
+          acc[2 * i + 1] += __uint_as_float(v[u][i] & 0xffff0000u);
+        }
+    }
+    for (; r < ratio; r += RC) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(base + (int64_t)r * HD);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += __uint_as_float(v[i] << 16);
+        acc[2 * i + 1] += __uint_as_float(v[i] & 0xffff0000u);
+      }
     }
   }
+  // sum the raw-row classes (lanes j ^ CG, j ^ 2 CG, ... of the same block)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) part[rl][cg * 8 + i] = acc[i];
-  __syncthreads();
-  float m = 0.0f;
-  if (tid < HD) {
-    for (int r = 0; r < RL; ++r) m += part[r][tid];
-    m = m / (float)ratio;
+  for (int off = CG; off < TPB; off <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], off);
+  float m[8], ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    m[i] = acc[i] / (float)ratio;
+    ss += m[i] * m[i];
   }
-  const float ss = block_sum(tid < HD ? m * m : 0.0f, red);
+  // sum of squares over the column groups (lanes j ^ 1 .. j ^ CG/2)
+#pragma unroll
+  for (int off = 1; off < CG; off <<= 1) ss += __shfl_xor(ss, off);
   const float inv = 1.0f / sqrtf(ss / (float)HD + eps);
-  if (tid < HD) xs[tid] = m * inv * (1.0f + kw[tid]);
+  if (rc == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xs[bi][cg * 8 + i] = m[i] * inv * (1.0f + kw[cg * 8 + i]);
+  }
+  const int half = rot >> 1;
+  for (int i = j; i < half; i += TPB) {
+    const double inv_freq = pow((double)theta, -2.0 * (double)i / (double)rot);
+    double sn, c;
+    sincos((double)b * (double)ratio * inv_freq, &sn, &c);
+    cs[bi][i][0] = c;
+    cs[bi][i][1] = sn;
+  }
   __syncthreads();
-  rope_pair(xs, out + (int64_t)b * HD, tid, HD, rot, (double)b * (double)ratio, (double)theta);
+  if (live && rc == 0) {
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int d = cg * 8 + i;
+      if (d < half) {
+        const double a = xs[bi][d], bb = xs[bi][d + half];
+        o[i] = (float)(a * cs[bi][d][0] - bb * cs[bi][d][1]);
+      } else if (d < rot) {
+        const double a = xs[bi][d - half], bb = xs[bi][d];
+        o[i] = (float)(a * cs[bi][d - half][1] + bb * cs[bi][d - half][0]);
+      } else {
+        o[i] = xs[bi][d];
+      }
+    }
+    float* dst = out + (int64_t)b * HD + cg * 8;
+    *reinterpret_cast<float4v*>(dst) = float4v{o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<float4v*>(dst + 4) = float4v{o[4], o[5], o[6], o[7]};
+  }
 }
 
 // ------------------------------------------------------------------ query prep
 
+// One 256-thread workgroup per row, all heads: the row's raw values go to LDS, a
+// wave computes each head's RMSNorm factor, the rotation angles (fp64) are formed
+// once per pair for the row and shared by its heads, then every thread writes 8
+// output dims at a time.
 template <int HD>
-__global__ __launch_bounds__(HD) void qprep_rows_kernel(const uint16_t* __restrict__ qk,
+__global__ __launch_bounds__(256) void qprep_rows_kernel(const uint16_t* __restrict__ qk,
                                                         const float* __restrict__ qw, float* __restrict__ out,
                                                         uint32_t first_pos, uint32_t qkw, uint32_t n_heads,
                                                         int rot, float theta, float eps) {
-  __shared__ float xs[HD];
-  __shared__ float red[4];
-  const uint32_t r = blockIdx.x, h = blockIdx.y;
-  const int d = threadIdx.x;
-  const float x = bf16_to_f32(qk[(int64_t)r * qkw + (int64_t)h * HD + d]);
-  const float ss = block_sum(x * x, red);
-  const float inv = 1.0f / sqrtf(ss / (float)HD + eps);
-  xs[d] = x * inv * (1.0f + qw[d]);
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* xr = reinterpret_cast<float*>(smem);                          // [n_heads * HD] raw values
+  float* hinv = xr + n_heads * HD;                                     // [n_heads]
+  double* cs = reinterpret_cast<double*>(hinv + ((n_heads + 3) & ~3));  // [HD / 2][2]
+  const uint32_t r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int groups = (int)n_heads * HD / 8;
+  const uint16_t* src = qk + (int64_t)r * qkw;
+  for (int g = tid; g < groups; g += 256) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + 8 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xr[8 * g + 2 * i] = __uint_as_float(v[i] << 16);
+      xr[8 * g + 2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+  }
+  const int half = rot >> 1;
+  const double pos = (double)first_pos + (double)r;
+  for (int i = tid; i < half; i += 256) {
+    const double inv_freq = pow((double)theta, -2.0 * (double)i / (double)rot);
+    double sn, c;
+    sincos(pos * inv_freq, &sn, &c);
+    cs[2 * i] = c;
+    cs[2 * i + 1] = sn;
+  }
   __syncthreads();
-  rope_pair(xs, out + ((int64_t)r * n_heads + h) * HD, d, HD, rot, (double)first_pos + (double)r, (double)theta);
+  for (uint32_t h = wave; h < n_heads; h += 4) {
+    float ss = 0.0f;
+    for (int d = lane; d < HD; d += 64) {
+      const float x = xr[h * HD + d];
+      ss += x * x;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    if (lane == 0) hinv[h] = 1.0f / sqrtf(ss / (float)HD + eps);
+  }
+  __syncthreads();
+  auto norm = [&](int h, int d) -> float { return xr[h * HD + d] * hinv[h] * (1.0f + qw[d]); };
+  for (int g = tid; g < groups; g += 256) {
+    const int h = (8 * g) / HD, d0 = (8 * g) % HD;
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int d = d0 + i;
+      if (d < half) {
+        const double a = norm(h, d), bb = norm(h, d + half);
+        o[i] = (float)(a * cs[2 * d] - bb * cs[2 * d + 1]);
+      } else if (d < rot) {
+        const double a = norm(h, d - half), bb = norm(h, d);
+        o[i] = (float)(a * cs[2 * (d - half) + 1] + bb * cs[2 * (d - half)]);
+      } else {
+        o[i] = norm(h, d);
+      }
+    }
+    float* dst = out + ((int64_t)r * n_heads + h) * HD + d0;
+    *reinterpret_cast<float4v*>(dst) = float4v{o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<float4v*>(dst + 4) = float4v{o[4], o[5], o[6], o[7]};
+  }
 }
 
 // ------------------------------------------------------------------ row scores (fp32)
@@ -154,28 +236,36 @@ __global__ __launch_bounds__(256) void qsa_score_f32_kernel(const float* __restr
 
 // Q[rows*heads, hd] x K[blocks, hd]^T on the fp16 matrix cores (16x16x32), then
 // ReLU, the head sum and 1/sqrt(hd).  A wave holds 64 consecutive (row, head) pairs
-// of q as A operands (RPW = 64 / NH rows); a workgroup (4 waves, RPG rows) streams
-// its key chunk in 64-key tiles converted to fp16 in LDS (two buffers: the next
-// tile's loads are in flight while the current one is multiplied).  The chunks are
+// of q as A operands (RPW = 64 / NH rows); a workgroup of 8 waves (RPG rows) streams
+// its key chunk in 64-key tiles converted to fp16 in LDS.  Every key tile is read
+// by the workgroup once for all its rows, so the key traffic per score is 1/RPG of
+// a key; the loads of tile j+2 are in flight (in registers) while tile j is
+// multiplied and tile j+1 waits in registers for its LDS buffer.  The chunks are
 // dealt so that all workgroups of one chunk run on one XCD: the chunk's keys (2 MB
 // at 32768 blocks) stay in that XCD's L2.  q and the keys come out of RMSNorm, so
 // their fp16 roundings are relative (2^-11) and the products stay far inside the
 // fp16 range; the accumulation is fp32.
+constexpr int kQsaThreads = 512;
+
 template <int HD, int NH>
-__global__ __launch_bounds__(256) void qsa_score_mfma_kernel(const float* __restrict__ q,
-                                                             const float* __restrict__ keys,
-                                                             float* __restrict__ scores, uint32_t rows,
-                                                             uint32_t nb, uint32_t first_pos, uint32_t stride,
-                                                             uint32_t ratio, uint32_t chunk, uint32_t n_groups,
-                                                             float out_scale) {
+__global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const float* __restrict__ q,
+                                                                     const float* __restrict__ keys,
+                                                                     float* __restrict__ scores, uint32_t rows,
+                                                                     uint32_t nb, uint32_t first_pos,
+                                                                     uint32_t stride, uint32_t ratio,
+                                                                     uint32_t chunk, uint32_t n_groups,
+                                                                     float out_scale) {
+  constexpr int NT = kQsaThreads;
+  constexpr int NW = NT / 64;     // waves
   constexpr int KW = HD / 32;     // K steps of 32 dims
   constexpr int RPW = 64 / NH;    // rows per wave
-  constexpr int RPG = 4 * RPW;    // rows per workgroup
+  constexpr int RPG = NW * RPW;   // rows per workgroup
   constexpr int MTR = NH / 16;    // M tiles per row
   constexpr int TILE = 64;
   constexpr int BLD = HD + 8;     // halves per LDS key row (padding against bank conflicts)
-  constexpr int LPK = 4;          // loader threads per key
+  constexpr int LPK = NT / TILE;  // loader threads per key
   constexpr int FPL = HD / LPK;   // floats each loader thread converts per tile
+  static_assert(FPL % 8 == 0, "loader slice");
   __shared__ __align__(16) _Float16 kb[2][TILE * BLD];
 
   const XcdTile xt = xcd_tile((int)blockIdx.x, (int)n_groups);
@@ -194,11 +284,13 @@ __global__ __launch_bounds__(256) void qsa_score_mfma_kernel(const float* __rest
   const int64_t vmax = valid_of(r_last);
   const int64_t kend = c1 < vmax ? c1 : vmax;  // keys [c0, kend) are multiplied
   // keys of the chunk past every row's valid count: -inf
-  for (int rr = 0; rr < RPG; ++rr) {
-    const int r = r0 + rr;
-    if (r >= (int)rows) break;
+  {
     const int64_t from = kend > c0 ? kend : c0;
-    for (int64_t s = from + tid; s < c1; s += 256) scores[(int64_t)r * stride + s] = -INFINITY;
+    for (int rr = 0; rr < RPG; ++rr) {
+      const int r = r0 + rr;
+      if (r >= (int)rows) break;
+      for (int64_t s = from + tid; s < c1; s += NT) scores[(int64_t)r * stride + s] = -INFINITY;
+    }
   }
   if (kend <= c0) return;
 
@@ -228,65 +320,62 @@ __global__ __launch_bounds__(256) void qsa_score_mfma_kernel(const float* __rest
       A[mt][kk] = a;
     }
   }
-  int64_t vrow[RPW];
+  // per row of the wave: its output row (a row past the last one writes nothing) and
+  // the end of its valid keys relative to the chunk start, key offsets are 32-bit
+  float* orow[RPW];
+  int vrel[RPW];
 #pragma unroll
   for (int rr = 0; rr < RPW; ++rr) {
     const int r = r0 + wave * RPW + rr;
-    vrow[rr] = r < (int)rows ? valid_of(r) : 0;
+    orow[rr] = r < (int)rows ? scores + (int64_t)r * stride + c0 : nullptr;
+    vrel[rr] = r < (int)rows ? (int)(valid_of(r) - c0) : 0;
   }
+  const int crel = (int)(c1 - c0);
 
   // tile loader: thread t converts FPL floats of key t / LPK
   const int lk = tid / LPK, lpart = tid % LPK;
-  float4v stage[FPL / 4];
-  auto load_tile = [&](int64_t k0) {
-    const int64_t kk = k0 + lk;
-    if (kk < kend) {
-      const float* src = keys + kk * HD + lpart * FPL;
+  // keys past kend are clamped onto the last one (their scores are masked at the store)
+  const float* kbase = keys + lpart * FPL;
+  auto load_tile = [&](int64_t k0, float4v (&st)[FPL / 4]) {
+    const int64_t kk = min(k0 + lk, kend - 1);
+    const float* src = kbase + kk * HD;
 #pragma unroll
-      for (int j = 0; j < FPL / 4; ++j) stage[j] = *reinterpret_cast<const float4v*>(src + 4 * j);
-    } else {
-#pragma unroll
-      for (int j = 0; j < FPL / 4; ++j) stage[j] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-    }
+    for (int j = 0; j < FPL / 4; ++j) st[j] = *reinterpret_cast<const float4v*>(src + 4 * j);
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, const float4v (&st)[FPL / 4]) {
     _Float16* dst = &kb[buf][lk * BLD + lpart * FPL];
 #pragma unroll
     for (int j = 0; j < FPL / 8; ++j) {
       half8v h;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        h[e] = (_Float16)stage[2 * j][e];
-        h[4 + e] = (_Float16)stage[2 * j + 1][e];
+        h[e] = (_Float16)st[2 * j][e];
+        h[4 + e] = (_Float16)st[2 * j + 1][e];
       }
       *reinterpret_cast<half8v*>(dst + 8 * j) = h;
     }
   };
-
-  load_tile(c0);
-  store_tile(0);
-  __syncthreads();
-  int buf = 0;
-  for (int64_t k0 = c0; k0 < kend; k0 += TILE) {
-    const bool more = k0 + TILE < kend;
-    if (more) load_tile(k0 + TILE);
+  // multiply one LDS tile, reduce the heads, write the scores
+  auto do_tile = [&](int buf, int64_t k0) {
     float4v acc[4][4];
+    // every B operand of the tile is read from LDS up front (one wait), then the
+    // MFMAs run back to back; the scheduler may not move the reads between them
+    half8v B[KW][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int kk = 0; kk < KW; ++kk) {
-      half8v B[4];
+    for (int kk = 0; kk < KW; ++kk)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
-        B[nt] = *reinterpret_cast<const half8v*>(&kb[buf][(16 * nt + col) * BLD + 32 * kk + 8 * quarter]);
+        B[kk][nt] = *reinterpret_cast<const half8v*>(&kb[buf][(16 * nt + col) * BLD + 32 * kk + 8 * quarter]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < KW; ++kk)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][kk], B[nt], acc[mt][nt], 0, 0, 0);
-    }
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              A[mt][kk], B[kk][nt], kk == 0 ? float4v{0.0f, 0.0f, 0.0f, 0.0f} : acc[mt][nt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
     // ReLU and head sum: lane (quarter, col) holds heads 4*quarter + i of each M tile
     // for key 16 * nt + col; the four quarters are then summed across lanes.
     float s[4][RPW];
@@ -298,7 +387,7 @@ __global__ __launch_bounds__(256) void qsa_score_mfma_kernel(const float* __rest
 #pragma unroll
         for (int j = 0; j < MTR; ++j) {
           const float4v a = acc[rr * MTR + j][nt];
-          x += fmaxf(a[0], 0.0f) + fmaxf(a[1], 0.0f) + fmaxf(a[2], 0.0f) + fmaxf(a[3], 0.0f);
+          x += relu_bits(a[0]) + relu_bits(a[1]) + relu_bits(a[2]) + relu_bits(a[3]);
         }
         x += __shfl_xor(x, 16);
         x += __shfl_xor(x, 32);
@@ -306,18 +395,36 @@ __global__ __launch_bounds__(256) void qsa_score_mfma_kernel(const float* __rest
       }
     }
     // lane (quarter, col) writes key 16 * quarter + col of the tile for each row
-    const int64_t key = k0 + 16 * quarter + col;
+    const int key = (int)(k0 - c0) + 16 * quarter + col;
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
-      const int r = r0 + wave * RPW + rr;
       float v = s[0][rr];
 #pragma unroll
       for (int nt = 1; nt < 4; ++nt) v = quarter == nt ? s[nt][rr] : v;
-      if (r < (int)rows && key < c1) scores[(int64_t)r * stride + key] = key < vrow[rr] ? v * out_scale : -INFINITY;
+      if (orow[rr] != nullptr && key < crel) orow[rr][key] = key < vrel[rr] ? v * out_scale : -INFINITY;
     }
-    if (more) store_tile(buf ^ 1);
+  };
+
+  // two register stages: tile j + 2 loads while tile j multiplies and tile j + 1
+  // waits for its LDS buffer
+  float4v sa[FPL / 4], sb[FPL / 4];
+  load_tile(c0, sa);
+  load_tile(c0 + TILE, sb);
+  store_tile(0, sa);
+  __syncthreads();
+  for (int64_t k0 = c0; k0 < kend; k0 += 2 * TILE) {
+    // tile k0 is in buffer 0, tile k0 + TILE in sb
+    if (k0 + 2 * TILE < kend) load_tile(k0 + 2 * TILE, sa);
+    do_tile(0, k0);
+    if (k0 + TILE >= kend) break;
+    store_tile(1, sb);
     __syncthreads();
-    buf ^= 1;
+    // tile k0 + TILE is in buffer 1, tile k0 + 2 TILE in sa
+    if (k0 + 3 * TILE < kend) load_tile(k0 + 3 * TILE, sb);
+    do_tile(1, k0 + TILE);
+    if (k0 + 2 * TILE >= kend) break;
+    store_tile(0, sa);
+    __syncthreads();
   }
 }
 
@@ -326,38 +433,54 @@ __global__ __launch_bounds__(256) void qsa_score_mfma_kernel(const float* __rest
 hipError_t launch_block_pool(const uint16_t* raw, const float* kw, float* out, uint32_t first_block,
                              uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot, float theta,
                              float eps, hipStream_t st) {
+  const dim3 grid((n_new + 7) / 8);
   switch (hd) {
     case 64:
-      hipLaunchKernelGGL(block_pool_kernel<64>, dim3(n_new), dim3(256), 0, st, raw, kw, out, first_block, ratio,
+      hipLaunchKernelGGL(block_pool_kernel<64>, grid, dim3(256), 0, st, raw, kw, out, first_block, n_new, ratio,
                          (int)rot, theta, eps);
       break;
     case 128:
-      hipLaunchKernelGGL(block_pool_kernel<128>, dim3(n_new), dim3(256), 0, st, raw, kw, out, first_block, ratio,
+      hipLaunchKernelGGL(block_pool_kernel<128>, grid, dim3(256), 0, st, raw, kw, out, first_block, n_new, ratio,
                          (int)rot, theta, eps);
       break;
     default:
-      hipLaunchKernelGGL(block_pool_kernel<256>, dim3(n_new), dim3(256), 0, st, raw, kw, out, first_block, ratio,
+      hipLaunchKernelGGL(block_pool_kernel<256>, grid, dim3(256), 0, st, raw, kw, out, first_block, n_new, ratio,
                          (int)rot, theta, eps);
       break;
   }
   return hipGetLastError();
 }
 
+size_t qprep_lds_bytes(uint32_t n_heads, uint32_t hd) {
+  return (size_t)4 * n_heads * hd + (size_t)4 * ((n_heads + 3) & ~3u) + (size_t)8 * hd;
+}
+
 hipError_t launch_qprep_rows(const uint16_t* qk, const float* qw, float* out, uint32_t rows,
                              uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t hd, uint32_t rot,
                              float theta, float eps, hipStream_t st) {
+  const size_t lds = qprep_lds_bytes(n_heads, hd);
+  hipError_t e;
   switch (hd) {
     case 64:
-      hipLaunchKernelGGL(qprep_rows_kernel<64>, dim3(rows, n_heads), dim3(64), 0, st, qk, qw, out, first_pos, qkw,
-                         n_heads, (int)rot, theta, eps);
+      if (lds > 65536 && (e = hipFuncSetAttribute(reinterpret_cast<const void*>(qprep_rows_kernel<64>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+        return e;
+      hipLaunchKernelGGL(qprep_rows_kernel<64>, dim3(rows), dim3(256), lds, st, qk, qw, out, first_pos, qkw, n_heads,
+                         (int)rot, theta, eps);
       break;
     case 128:
-      hipLaunchKernelGGL(qprep_rows_kernel<128>, dim3(rows, n_heads), dim3(128), 0, st, qk, qw, out, first_pos,
-                         qkw, n_heads, (int)rot, theta, eps);
+      if (lds > 65536 && (e = hipFuncSetAttribute(reinterpret_cast<const void*>(qprep_rows_kernel<128>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+        return e;
+      hipLaunchKernelGGL(qprep_rows_kernel<128>, dim3(rows), dim3(256), lds, st, qk, qw, out, first_pos, qkw, n_heads,
+                         (int)rot, theta, eps);
       break;
     default:
-      hipLaunchKernelGGL(qprep_rows_kernel<256>, dim3(rows, n_heads), dim3(256), 0, st, qk, qw, out, first_pos,
-                         qkw, n_heads, (int)rot, theta, eps);
+      if (lds > 65536 && (e = hipFuncSetAttribute(reinterpret_cast<const void*>(qprep_rows_kernel<256>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+        return e;
+      hipLaunchKernelGGL(qprep_rows_kernel<256>, dim3(rows), dim3(256), lds, st, qk, qw, out, first_pos, qkw, n_heads,
+                         (int)rot, theta, eps);
       break;
   }
   return hipGetLastError();
@@ -366,14 +489,14 @@ hipError_t launch_qprep_rows(const uint16_t* qk, const float* qw, float* out, ui
 template <int HD, int NH>
 static hipError_t launch_qsa_mfma(const float* q, const float* keys, float* scores, uint32_t rows, uint32_t nb,
                                   uint32_t first_pos, uint32_t stride, uint32_t ratio, hipStream_t st) {
-  constexpr uint32_t kRowsPerGroup = 4 * (64 / NH);
+  constexpr uint32_t kRowsPerGroup = (kQsaThreads / 64) * (64 / NH);
   const uint32_t n_groups = (rows + kRowsPerGroup - 1) / kRowsPerGroup;
   // one key chunk per XCD (a multiple of the 64-key tile)
   uint32_t chunk = (nb + kXcds - 1) / kXcds;
   chunk = (chunk + 63) / 64 * 64;
   const dim3 grid(n_groups * kXcds);
-  hipLaunchKernelGGL((qsa_score_mfma_kernel<HD, NH>), grid, dim3(256), 0, st, q, keys, scores, rows, nb, first_pos,
-                     stride, ratio, chunk, n_groups, 1.0f / sqrtf((float)HD));
+  hipLaunchKernelGGL((qsa_score_mfma_kernel<HD, NH>), grid, dim3(kQsaThreads), 0, st, q, keys, scores, rows, nb,
+                     first_pos, stride, ratio, chunk, n_groups, 1.0f / sqrtf((float)HD));
   return hipGetLastError();
 }
 

@@ -65,11 +65,6 @@ __device__ __forceinline__ int prescale_exp(float mx) {
 
 // ------------------------------------------------------------------ MFMA scorer
 
-// ReLU through the integer max: a negative float (sign bit set) is a negative int32,
-// so max(bits, 0) gives +0.0 for it and leaves non-negative values unchanged.  One
-// VALU op, with no NaN canonicalisation.
-__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
-
 // Raw bytes of one lane's slice of one key: D/8 code bytes and D/64 scale bytes.
 template <int D>
 struct Raw {

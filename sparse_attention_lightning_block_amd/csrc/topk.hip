@@ -21,9 +21,10 @@
 //     of eight global copies (one per XCD, so contended atomics stay in one L2);
 //     the (chunk, row) grid then finds the bin holding the K-th entry from the
 //     copies (scanning down from the row's highest bin) and writes every entry at
-//     or above that bin to the chunk's own candidate slots; one 1024-thread
-//     workgroup per row loads those candidates (about K plus one bin's worth)
-//     into registers, selects the K winners exactly and sorts them.
+//     or above that bin to the chunk's own candidate slots; one workgroup per row
+//     (1024 threads when rows are few, 256 when they are many) loads those
+//     candidates (about K plus one bin's worth) into registers, selects the K
+//     winners exactly and sorts them.
 //   * the sort buckets the winners on the 12 highest bits where they differ and
 //     ranks each against its bucket (a sorting network if a bucket is crowded).
 #include <hip/hip_runtime.h>
@@ -38,8 +39,11 @@ constexpr int kBins = 1 << kDigit;       // 4096 histogram bins
 constexpr int kTopShift = 64 - kDigit;   // first digit: the score's top 12 order bits
 constexpr int kRowThreads = 256;         // one-workgroup rows
 constexpr int kChunkThreads = 256;       // histogram and filter chunks of long rows
-constexpr int kFinalThreads = 1024;      // the finishing workgroup of a long row
+constexpr int kFinalThreads = 1024;      // the finishing workgroup of a long row when rows are few
 constexpr int kFinalPer = 12;            // candidates per finishing thread held in registers
+constexpr int kFinalThreadsMany = 256;   // ... and when rows are many (more rows in flight per CU)
+constexpr int kFinalPerMany = 16;
+constexpr int kFewRows = 256;
 constexpr int kRowMax = 32 * kRowThreads;  // 8192: one-workgroup rows
 constexpr int kBucketMax = 48;           // crowded bucket: sorting network instead
 constexpr int kHistCopies = kXcds;       // one global histogram per XCD
@@ -577,8 +581,8 @@ __global__ __launch_bounds__(kChunkThreads) void select_filter_kernel(SelArgs a)
 // output.  Up to kFinalPer candidates per thread are held in registers, fetched
 // through an LDS map from list position to chunk; longer lists (rows crowded with
 // equal scores) are read chunk by chunk at every pass.
-__global__ __launch_bounds__(kFinalThreads) void select_final_kernel(SelArgs a) {
-  constexpr int NT = kFinalThreads;
+template <int NT, int PER>
+__global__ __launch_bounds__(NT) void select_final_kernel(SelArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ SelShared sh;
   const int row = blockIdx.x;
@@ -589,7 +593,7 @@ __global__ __launch_bounds__(kFinalThreads) void select_final_kernel(SelArgs a) 
   const int nch = a.chunks;
   FinishLds f = carve(smem, a.top_k);
   uint32_t* off = f.hist + kBins + 4;                                   // [nch + 1]
-  uint16_t* owner = reinterpret_cast<uint16_t*>(off + ((nch + 4) & ~3));  // [NT * kFinalPer]
+  uint16_t* owner = reinterpret_cast<uint16_t*>(off + ((nch + 4) & ~3));  // [NT * PER]
   const uint32_t* cnt = a.ccount + (int64_t)row * nch;
   const uint64_t* cd = a.cand + (int64_t)row * nch * a.chunk;
   const uint32_t first = tid < nch ? cnt[tid] : 0u;  // in flight during the zeroing
@@ -615,8 +619,8 @@ __global__ __launch_bounds__(kFinalThreads) void select_final_kernel(SelArgs a) 
   if (tid == 0) off[nch] = carry;
   int C = K == n ? n : (int)(info.above + info.cnt);
   if ((uint32_t)C > carry) C = (int)carry;  // the two agree; never read past the slots
-  const bool in_regs = C <= NT * kFinalPer;
-  uint64_t v[kFinalPer];
+  const bool in_regs = C <= NT * PER;
+  uint64_t v[PER];
   if (in_regs) {
     __syncthreads();
     for (int c = tid >> 6; c < nch; c += NT / kWave) {
@@ -625,7 +629,7 @@ __global__ __launch_bounds__(kFinalThreads) void select_final_kernel(SelArgs a) 
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < kFinalPer; ++r) {
+    for (int r = 0; r < PER; ++r) {
       const int i = r * NT + tid;
       uint64_t x = 0ull;
       if (i < C) {
@@ -641,7 +645,7 @@ __global__ __launch_bounds__(kFinalThreads) void select_final_kernel(SelArgs a) 
   auto each = [&](auto&& fn) {
     if (in_regs) {
 #pragma unroll
-      for (int r = 0; r < kFinalPer; ++r)
+      for (int r = 0; r < PER; ++r)
         if (r * NT + tid < C) fn(v[r]);
     } else {
       for (int c = 0; c < nch; ++c) {
@@ -717,7 +721,9 @@ bool plan_select(int rows, int n_cols, int top_k, SelectPlan* p) {
     p->chunks = (n_cols + chunk - 1) / chunk;
     p->bytes = ws_layout(rows, p->chunks, chunk).total;
     // the finishing workgroup also holds the chunk offsets and the position map
-    p->lds += (size_t)4 * ((p->chunks + 4) & ~3) + (size_t)2 * kFinalThreads * kFinalPer;
+    p->final_nt = rows > kFewRows ? kFinalThreadsMany : kFinalThreads;
+    const int per = rows > kFewRows ? kFinalPerMany : kFinalPer;
+    p->lds += (size_t)4 * ((p->chunks + 4) & ~3) + (size_t)2 * p->final_nt * per;
     if (p->lds > kLdsMax) return false;
   }
   return true;
@@ -747,14 +753,20 @@ static hipError_t launch_rows(const SelArgs& a, const SelectPlan& p, hipStream_t
 
 template <int PER>
 static hipError_t launch_pipeline(const SelArgs& a, const SelectPlan& p, hipStream_t st) {
-  hipError_t e = set_lds(select_final_kernel, p.lds);
+  hipError_t e = p.final_nt == kFinalThreads ? set_lds(select_final_kernel<kFinalThreads, kFinalPer>, p.lds)
+                                              : set_lds(select_final_kernel<kFinalThreadsMany, kFinalPerMany>, p.lds);
   if (e != hipSuccess) return e;
   const dim3 grid(p.chunks, p.rows);
   hipLaunchKernelGGL(select_hist_kernel<PER>, grid, dim3(kChunkThreads), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(select_filter_kernel<PER>, grid, dim3(kChunkThreads), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(select_final_kernel, dim3(p.rows), dim3(kFinalThreads), p.lds, st, a);
+  if (p.final_nt == kFinalThreads)
+    hipLaunchKernelGGL((select_final_kernel<kFinalThreads, kFinalPer>), dim3(p.rows), dim3(kFinalThreads), p.lds, st,
+                       a);
+  else
+    hipLaunchKernelGGL((select_final_kernel<kFinalThreadsMany, kFinalPerMany>), dim3(p.rows),
+                       dim3(kFinalThreadsMany), p.lds, st, a);
   return hipGetLastError();
 }
 
