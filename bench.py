@@ -42,29 +42,29 @@ WORKLOADS = {
 # 256 MiB copy (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0); the summaries are under
 # profiles/.  Valid only for the scorer sources they were taken with: a different
 # source hash reports null.
-SCORER_SOURCES = ["score.hip", "nvfp4.hpp", "common.hpp", "internal.hpp"]
 TRAFFIC_COPY_FACTOR = {"FETCH_SIZE": 1.9998, "WRITE_SIZE": 1.0}
-SCORER_TRAFFIC_KIB = {   # workload: (FETCH_SIZE, WRITE_SIZE) KiB per dispatch
-    "decode_T8_S65536": (3552.2, 2048.0),
-    "long_decode_T32_S262144": (13693.5, 32768.8),
-    "prefill_T4096": (35574.6, 65657.1),
+SCORER_SOURCES = {"csa": ['score.hip', 'nvfp4.hpp', 'common.hpp', 'internal.hpp'], "qsa": ['qsa.hip', 'common.hpp', 'internal.hpp']}
+SCORER_TRAFFIC = {   # workload: (sources, sha, FETCH_SIZE KiB, WRITE_SIZE KiB per dispatch)
+    "decode_T8_S65536": ("csa", "09557835d10d456f", 3504.3, 2048.1),
+    "long_decode_T32_S262144": ("csa", "09557835d10d456f", 13693.3, 32768.8),
+    "prefill_T4096": ("csa", "09557835d10d456f", 35573.2, 65656.8),
+    "qsa_prefill": ("qsa", "c65f848829a03f7f", 163908.5, 262424.0),
 }
-SCORER_TRAFFIC_SHA = "a082dab864165972"
 
 
-def scorer_source_sha():
+def source_sha(kind):
     h = hashlib.sha256()
-    for f in SCORER_SOURCES:
+    for f in SCORER_SOURCES[kind]:
         with open(os.path.join(ROOT, "sparse_attention_lightning_block_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def scorer_traffic(workload):
-    kib = SCORER_TRAFFIC_KIB.get(workload)
-    if kib is None or scorer_source_sha() != SCORER_TRAFFIC_SHA:
+    t = SCORER_TRAFFIC.get(workload)
+    if t is None or source_sha(t[0]) != t[1]:
         return None
-    return int((kib[0] * TRAFFIC_COPY_FACTOR["FETCH_SIZE"] + kib[1] * TRAFFIC_COPY_FACTOR["WRITE_SIZE"]) * 1024)
+    return int((t[2] * TRAFFIC_COPY_FACTOR["FETCH_SIZE"] + t[3] * TRAFFIC_COPY_FACTOR["WRITE_SIZE"]) * 1024)
 
 
 def key_bytes_per_entry(D, epb):
@@ -225,7 +225,7 @@ def run_qsa(args, w):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(tf / peak, 4),
-            "traffic": None,
+            "traffic": scorer_traffic(w.name) if mfma else None,
             "kernel": "qsa_score_mfma_kernel" if mfma else "qsa_score_f32_kernel",
             "kernel_avg_us": round(score_s * 1e6, 2),
             "flops_per_launch": int(flops),

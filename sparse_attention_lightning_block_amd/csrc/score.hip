@@ -36,7 +36,7 @@
 
 // Workgroups to aim for when cutting rows into key chunks (build-time tunables).
 #ifndef SALB_GROUP_WGS
-#define SALB_GROUP_WGS 512
+#define SALB_GROUP_WGS 256
 #endif
 #ifndef SALB_SPLIT_WGS
 #define SALB_SPLIT_WGS 1024
