@@ -333,7 +333,10 @@ __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const float
   const int crel = (int)(c1 - c0);
 
   // tile loader: thread t converts FPL floats of key t / LPK
-  const int lk = tid / LPK, lpart = tid % LPK;
+  // each group of eight lanes converts the same part of eight different keys, whose
+  // LDS rows start on distinct bank groups: conflict-free tile writes
+  static_assert(LPK == 8 && NT % 64 == 0, "loader map");
+  const int lk = (tid & 7) | ((tid >> 6) << 3), lpart = (tid >> 3) & 7;
   // keys past kend are clamped onto the last one (their scores are masked at the store)
   const float* kbase = keys + lpart * FPL;
   auto load_tile = [&](int64_t k0, float4v (&st)[FPL / 4]) {

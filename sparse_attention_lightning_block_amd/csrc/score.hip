@@ -439,12 +439,16 @@ __global__ __launch_bounds__(256) void score_mfma_group_kernel(ScoreArgs a) {
   // ---- shared pages: decode each 64-key tile once into LDS
   const int* lpid = pid + lead * a.pid_cap;
   const int n_tiles = (vmax - s_begin + TILE - 1) / TILE;
-  const int kt = tid >> 2, qs = tid & 3;  // staging: key of the tile, D/4 slice of it
-  // Raw tiles in flight: tile i lives in ring slot i % 2 from its load (issued two
-  // tiles ahead) until its decode, one tile before it is used.  Loads and decodes
-  // past the last tile touch valid memory and a free buffer; their results are unused.
-  Raw<D> R0, R1;
-  float G0 = 0.0f, G1 = 0.0f;
+  // staging: key kt of the tile, D/4 slice qs of it.  Each group of eight lanes writes
+  // eight different keys (same slice), whose LDS rows start on distinct bank groups
+  // (the row pitch is an odd number of 16-byte granules): conflict-free writes.
+  const int kt = (tid & 7) | ((tid >> 5) << 3), qs = (tid >> 3) & 3;
+  // Raw tiles in flight: tile i lives in ring slot i % 4 from its load (issued four
+  // tiles ahead, so that about 18 KB per workgroup are in flight) until its decode,
+  // one tile before it is used.  Loads and decodes past the last tile touch valid
+  // memory and a free buffer; their results are unused.
+  Raw<D> R0, R1, R2, R3;
+  float G0 = 0.0f, G1 = 0.0f, G2 = 0.0f, G3 = 0.0f;
   auto load_tile = [&](int j, Raw<D>& raw, float& graw) {
     const int s = min(s_begin + j * TILE + kt, vmax - 1);
     const uint32_t lb = div_epb((uint32_t)s, a.epb_magic);
@@ -488,7 +492,7 @@ __global__ __launch_bounds__(256) void score_mfma_group_kernel(ScoreArgs a) {
     if (t_prev + lane < s_vend) out_row[t_prev + lane] = g_prev * sc;
   };
   // One tile: score tile j from LDS while decoding tile j+1 from its ring slot (`nx`)
-  // into the other buffer and reloading this tile's slot (`mine`) two tiles ahead.
+  // into the other buffer and reloading this tile's slot (`mine`) four tiles ahead.
   auto run_tile = [&](int j, Raw<D>& mine, float& gmine, const Raw<D>& nx, float gnx) {
     __syncthreads();  // tile j decoded; the other buffer is free again
     const int buf = j & 1;
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(256) void score_mfma_group_kernel(ScoreArgs a) {
         const float v = head_sum<MT>(AC1, wr);
         keep = quarter == 1 ? v : keep;
       }
-      load_tile(j + 2, mine, gmine);
+      load_tile(j + 4, mine, gmine);
       mfma_step(buf, 3, AC1);
       {
         const float v = head_sum<MT>(AC0, wr);
@@ -516,17 +520,23 @@ __global__ __launch_bounds__(256) void score_mfma_group_kernel(ScoreArgs a) {
       g_prev = g_lane;
     } else {  // this row is done; the tile work is shared
       decode_part(buf ^ 1, nx, gnx, 0, KW);
-      load_tile(j + 2, mine, gmine);
+      load_tile(j + 4, mine, gmine);
     }
   };
 
   load_tile(0, R0, G0);
   load_tile(1, R1, G1);
+  load_tile(2, R2, G2);
+  load_tile(3, R3, G3);
   decode_part(0, R0, G0, 0, KW);
-  for (int j = 0; j < n_tiles; j += 2) {
+  for (int j = 0; j < n_tiles; j += 4) {
     run_tile(j, R0, G0, R1, G1);
     if (j + 1 >= n_tiles) break;
-    run_tile(j + 1, R1, G1, R0, G0);
+    run_tile(j + 1, R1, G1, R2, G2);
+    if (j + 2 >= n_tiles) break;
+    run_tile(j + 2, R2, G2, R3, G3);
+    if (j + 3 >= n_tiles) break;
+    run_tile(j + 3, R3, G3, R0, G0);
   }
   flush_prev();
 }
