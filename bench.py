@@ -4,9 +4,12 @@ One step = one pass of the whole path over one batch of synthetic input resident
 HBM: the NVFP4 paged scorer (indexer_score_rows) and the per-row top-k
 (indexer_topk_select) -- the same two stages indexer_score_topk runs.  Prints ONE
 JSON line.  The default workload is the decode configuration
-(T=8 queries, H=64, D=128, 64 keys per page, S=65536, top_k=2048).
+(T=8 queries, H=64, D=128, 64 keys per page, S=65536, top_k=2048).  The stages are
+launched eagerly (--graph replays each from a captured HIP graph instead); HIP events
+between the stages time each one.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--precision mfma|fp32]
+                    [--graph] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -103,6 +106,50 @@ def cpu_baseline(w, budget_s=20.0):
     }
 
 
+def make_step(torch, stages, graph):
+    """step(ev): run the stages in order, with ev[i] recorded before stage i and ev[-1]
+    after the last.  With graph=True every stage is captured once into a HIP graph and
+    replayed (the library allocates nothing and issues no memset, so its launches
+    capture as plain kernel nodes); the events stay outside the graphs, on the same
+    stream."""
+    if graph:
+        graphs = []
+        for f in stages:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                f()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        runs = [g.replay for g in graphs]
+    else:
+        runs = list(stages)
+
+    def step(ev):
+        for i, r in enumerate(runs):
+            ev[i].record()
+            r()
+        ev[len(runs)].record()
+
+    return step
+
+
+def timed_steps(torch, step, n_stages, steps):
+    """ms per step over `steps` back-to-back steps, and each stage's per-step times (ms)."""
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_stages + 1)] for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    step(evs[0])  # one untimed pass through the replay path
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / steps
+    stage = [np.array([e[j].elapsed_time(e[j + 1]) for e in evs]) for j in range(n_stages)]
+    return ms_per_step, stage
+
+
 def cpu_baseline_qsa(w, budget_s=20.0):
     """Time the CPU oracle (as it stands) on the QSA chain for a bounded sample of rows."""
     from threadpoolctl import threadpool_info
@@ -159,38 +206,26 @@ def run_qsa(args, w):
     ws = torch.zeros(max(1, salb.indexer_topk_workspace_size(w.rows, w.n_blocks, w.top_k)), dtype=torch.uint8,
                      device=dev)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
+    def prep():
         salb.qsa_block_pool(raw, kw, keys, first_block=0, n_new=w.n_blocks, ratio=w.ratio, rot=w.rot, theta=w.theta,
                             eps=w.eps)
         salb.qsa_qprep_rows(qk, qw, n_heads=w.n_heads, hd=w.hd, first_pos=w.first_pos, rot=w.rot, theta=w.theta,
                             eps=w.eps, out=q)
-        if ev is not None:
-            ev[1].record()
-        salb.qsa_score_rows(q, keys, first_pos=w.first_pos, ratio=w.ratio, precision=args.precision, out=scores)
-        if ev is not None:
-            ev[2].record()
-        salb.indexer_topk_select(scores, w.top_k, first_pos=w.first_pos, ratio=w.ratio, workspace=ws, out_idx=idx)
-        if ev is not None:
-            ev[3].record()
 
+    def score():
+        salb.qsa_score_rows(q, keys, first_pos=w.first_pos, ratio=w.ratio, precision=args.precision, out=scores)
+
+    def select():
+        salb.indexer_topk_select(scores, w.top_k, first_pos=w.first_pos, ratio=w.ratio, workspace=ws, out_idx=idx)
+
+    stages = [prep, score, select]
     for _ in range(args.warmup):
-        step()
+        for f in stages:
+            f()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        step(evs[i])
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    prep_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    score_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    select_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    step = make_step(torch, stages, args.graph)
+    ms_per_step, stage = timed_steps(torch, step, len(stages), args.steps)
+    prep_ms, score_ms, select_ms = stage
     pos = w.first_pos + np.arange(w.rows, dtype=np.int64)
     pairs = int(np.minimum((pos + 1) // w.ratio, w.n_blocks).sum())
     flops = 2.0 * pairs * w.n_heads * w.hd
@@ -215,7 +250,7 @@ def run_qsa(args, w):
         "data": "synthetic",
         "config": {"workload": w.name, "rows": w.rows, "heads": w.n_heads, "hd": w.hd, "raw_keys": w.n_blocks * w.ratio,
                    "ratio": w.ratio, "blocks": w.n_blocks, "top_k": w.top_k, "pairs": pairs,
-                   "precision": args.precision},
+                   "precision": args.precision, "launch": "hip_graph" if args.graph else "eager"},
         "step_ms": {"p50": float(np.median(prep_ms + score_ms + select_ms))},
         "stage_ms": {"pool_and_qprep": float(np.median(prep_ms)), "score": float(np.median(score_ms)),
                      "select": float(np.median(select_ms))},
@@ -244,6 +279,9 @@ def main():
     ap.add_argument("--workload", default="decode_T8_S65536", choices=sorted(WORKLOADS))
     ap.add_argument("--precision", default="mfma", choices=["mfma", "fp32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each stage from a captured HIP graph (slower than eager launches on this "
+                         "ROCm stack: a graph launch costs more than the kernel launches it replaces)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the indexer path here is a "
@@ -270,34 +308,22 @@ def main():
     ws = torch.zeros(max(1, salb.indexer_topk_workspace_size(w.T, n_cols, w.top_k)), dtype=torch.uint8, device=dev)
     sc_view = scores
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
+    def score():
         salb.indexer_score_rows(**d, n_cols=n_cols, precision=args.precision, out=sc_view)
-        if ev is not None:
-            ev[1].record()
+
+    def select():
         salb.indexer_topk_select(sc_view, w.top_k, valid_lens=d["valid_lens"], workspace=ws, out_idx=idx,
                                  out_scores=val)
-        if ev is not None:
-            ev[2].record()
 
+    stages = [score, select]
     for _ in range(args.warmup):
-        step()
+        for f in stages:
+            f()
     torch.cuda.synchronize()
+    step = make_step(torch, stages, args.graph)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        step(evs[i])
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    score_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    select_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    ms_per_step, stage = timed_steps(torch, step, len(stages), args.steps)
+    score_ms, select_ms = stage[0], stage[1]
     step_ms = score_ms + select_ms
 
     pairs = w.pairs
@@ -344,7 +370,7 @@ def main():
         "config": {
             "workload": w.name,
             "T": w.T, "H": w.H, "D": w.D, "entries_per_block": w.epb, "S": n_cols, "top_k": w.top_k,
-            "pairs": pairs, "precision": args.precision,
+            "pairs": pairs, "precision": args.precision, "launch": "hip_graph" if args.graph else "eager",
         },
         "step_ms": {"p10": float(np.percentile(step_ms, 10)), "p50": float(np.median(step_ms)),
                     "p90": float(np.percentile(step_ms, 90))},

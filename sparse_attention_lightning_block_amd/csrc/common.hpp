@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <unordered_map>
+
 namespace salb {
 
 typedef _Float16 half2v __attribute__((__vector_size__(2 * sizeof(_Float16))));
@@ -69,6 +72,21 @@ __device__ __forceinline__ XcdTile xcd_tile(int b, int rows) {
   t.row = j % rows;
   t.chunk = (j / rows) * kXcds + xcd;
   return t;
+}
+
+// Raises a kernel's dynamic-LDS limit (needed above 64 KiB) once: later calls return
+// without touching the runtime, so launches made while a stream is captured into a
+// graph issue no attribute calls.
+inline hipError_t ensure_lds(const void* fn, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  static std::mutex mu;
+  static std::unordered_map<const void*, size_t> raised;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = raised.find(fn);
+  if (it != raised.end() && it->second >= bytes) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) raised[fn] = bytes;
+  return e;
 }
 
 }  // namespace salb

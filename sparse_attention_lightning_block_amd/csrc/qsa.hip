@@ -465,23 +465,17 @@ hipError_t launch_qprep_rows(const uint16_t* qk, const float* qw, float* out, ui
   hipError_t e;
   switch (hd) {
     case 64:
-      if (lds > 65536 && (e = hipFuncSetAttribute(reinterpret_cast<const void*>(qprep_rows_kernel<64>),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
-        return e;
+      if ((e = ensure_lds(reinterpret_cast<const void*>(qprep_rows_kernel<64>), lds)) != hipSuccess) return e;
       hipLaunchKernelGGL(qprep_rows_kernel<64>, dim3(rows), dim3(256), lds, st, qk, qw, out, first_pos, qkw, n_heads,
                          (int)rot, theta, eps);
       break;
     case 128:
-      if (lds > 65536 && (e = hipFuncSetAttribute(reinterpret_cast<const void*>(qprep_rows_kernel<128>),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
-        return e;
+      if ((e = ensure_lds(reinterpret_cast<const void*>(qprep_rows_kernel<128>), lds)) != hipSuccess) return e;
       hipLaunchKernelGGL(qprep_rows_kernel<128>, dim3(rows), dim3(256), lds, st, qk, qw, out, first_pos, qkw, n_heads,
                          (int)rot, theta, eps);
       break;
     default:
-      if (lds > 65536 && (e = hipFuncSetAttribute(reinterpret_cast<const void*>(qprep_rows_kernel<256>),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
-        return e;
+      if ((e = ensure_lds(reinterpret_cast<const void*>(qprep_rows_kernel<256>), lds)) != hipSuccess) return e;
       hipLaunchKernelGGL(qprep_rows_kernel<256>, dim3(rows), dim3(256), lds, st, qk, qw, out, first_pos, qkw, n_heads,
                          (int)rot, theta, eps);
       break;

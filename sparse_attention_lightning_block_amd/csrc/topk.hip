@@ -738,9 +738,7 @@ size_t select_workspace_bytes(int rows, int n_cols, int top_k) {
 
 template <typename K>
 static hipError_t set_lds(K kernel, size_t bytes) {
-  if (bytes <= 65536) return hipSuccess;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)bytes);
+  return ensure_lds(reinterpret_cast<const void*>(kernel), bytes);
 }
 
 template <int NT, int PER>

@@ -1,0 +1,90 @@
+"""The hot path captured into HIP graphs: every replay, with eager work and
+synchronisations between the replays, returns exactly what the eager calls return
+(the select workspace is left zeroed by each call, so nothing needs clearing between
+replays).  Needs an MI355X."""
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_lightning_block_amd as salb
+from tests.parity import to_dev
+from workloads import make
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("cfg,reduced", [(2, 0), (3, 1), (4, 1)])
+def test_graph_replays_match_eager(cfg, reduced):
+    w = make(cfg, reduced)
+    d = to_dev(w)
+    n_cols = w.max_lb * w.epb
+    scores = torch.empty((w.T, n_cols), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.T, w.top_k), dtype=torch.int32, device="cuda")
+    val = torch.empty((w.T, w.top_k), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(salb.indexer_topk_workspace_size(w.T, n_cols, w.top_k), dtype=torch.uint8, device="cuda")
+
+    def path():
+        salb.indexer_score_rows(**d, n_cols=n_cols, precision="mfma", out=scores)
+        salb.indexer_topk_select(scores, w.top_k, valid_lens=d["valid_lens"], workspace=ws, out_idx=idx,
+                                 out_scores=val)
+
+    path()
+    torch.cuda.synchronize()
+    ref_s, ref_i, ref_v = scores.clone(), idx.clone(), val.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        path()
+    other = make(2, 1)
+    od = to_dev(other)
+    for rep in range(4):
+        scores.fill_(7.0)
+        idx.fill_(-5)
+        val.fill_(3.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(scores.view(torch.int32), ref_s.view(torch.int32)), rep
+        assert torch.equal(idx, ref_i), rep
+        assert torch.equal(val.view(torch.int32), ref_v.view(torch.int32)), rep
+        # eager work between replays, on other buffers (its own workspace)
+        salb.indexer_score_topk(**od, top_k=other.top_k, precision="mfma")
+        torch.cuda.synchronize()
+
+
+def test_qsa_graph_replays_match_eager():
+    w = make(5, reduced=1)
+    raw = torch.from_numpy(w.raw_keys.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    kw = torch.from_numpy(w.k_norm_w).cuda()
+    qk = torch.from_numpy(w.qk.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    qw = torch.from_numpy(w.q_norm_w).cuda()
+    keys = torch.empty((w.n_blocks, w.hd), dtype=torch.float32, device="cuda")
+    q = torch.empty((w.rows, w.n_heads, w.hd), dtype=torch.float32, device="cuda")
+    sc = torch.empty((w.rows, w.n_blocks), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.rows, w.top_k), dtype=torch.int32, device="cuda")
+    ws = torch.zeros(salb.indexer_topk_workspace_size(w.rows, w.n_blocks, w.top_k), dtype=torch.uint8, device="cuda")
+
+    def path():
+        salb.qsa_block_pool(raw, kw, keys, first_block=0, n_new=w.n_blocks, ratio=w.ratio, rot=w.rot, theta=w.theta,
+                            eps=w.eps)
+        salb.qsa_qprep_rows(qk, qw, n_heads=w.n_heads, hd=w.hd, first_pos=w.first_pos, rot=w.rot, theta=w.theta,
+                            eps=w.eps, out=q)
+        salb.qsa_score_rows(q, keys, first_pos=w.first_pos, ratio=w.ratio, precision="mfma", out=sc)
+        salb.indexer_topk_select(sc, w.top_k, first_pos=w.first_pos, ratio=w.ratio, workspace=ws, out_idx=idx)
+
+    path()
+    torch.cuda.synchronize()
+    ref_k, ref_q, ref_s, ref_i = keys.clone(), q.clone(), sc.clone(), idx.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        path()
+    for rep in range(3):
+        for t in (keys, q, sc):
+            t.fill_(1.5)
+        idx.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(keys, ref_k) and torch.equal(q, ref_q), rep
+        assert torch.equal(sc.view(torch.int32), ref_s.view(torch.int32)), rep
+        assert torch.equal(idx, ref_i), rep
+        path()  # eager work between replays
+        torch.cuda.synchronize()
