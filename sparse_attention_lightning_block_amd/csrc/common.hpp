@@ -47,6 +47,19 @@ __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
 // VALU op, with no NaN canonicalisation.
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// Sum over the four 16-lane rows of a wave, for every lane position within a row
+// (the xor-16 and xor-32 butterflies).  gfx950's row-swap permutes exchange rows
+// between two registers on the VALU: swapping x with itself and adding the pair
+// gives the butterfly without an LDS round trip.
+__device__ __forceinline__ float row_sum4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Exact floor(s / epb) for s < 2^24 and epb <= 2^16: m = ceil(2^40 / epb).
 __device__ __forceinline__ uint32_t div_epb(uint32_t s, uint64_t magic) {
   return (uint32_t)(((uint64_t)s * magic) >> 40);

@@ -16,16 +16,17 @@
 //    an instruction is a fixed permutation of the head dims applied to both
 //    operands, chosen so that every lane's key slice is contiguous.  The epilogue
 //    applies ReLU, the head weights and the per-page global scale to the fp32
-//    accumulators, reduces the heads (in-lane, then two lane swaps) and writes one
-//    score per key.  q is prescaled per head by a power of two so that its fp16
+//    accumulators, reduces the heads (in-lane, then two row swaps on the VALU) and
+//    writes one score per key.  q is prescaled per head by a power of two so that its fp16
 //    rounding is relative (11 bits); the inverse power is folded into the head
 //    weight, which keeps the result identical up to that rounding.
 //      - score_mfma_split_kernel (fewer than four rows): every wave streams its own
 //        keys of the row; each lane decodes its 16-byte slice of one key straight
 //        into the B operand (no LDS trip).
-//      - score_mfma_group_kernel (four rows or more): four rows per workgroup, one
-//        per wave; when the four rows resolve the chunk to the same pages, each
-//        64-key tile is decoded once into LDS and read by all four waves.
+//      - score_mfma_group_kernel (four rows or more): four rows per workgroup (eight
+//        from sixteen rows on), one per wave; when the rows resolve the chunk to the
+//        same pages, each 64-key tile is decoded once into LDS (every thread decodes
+//        a 1/G slice of a key) and read by all the waves.
 //  * score_f32_kernel (IDX_PREC_FP32): one key per lane, fp32 FMAs with q read
 //    through the scalar cache, for results within ~1e-5 relative.
 #include <hip/hip_runtime.h>
@@ -40,6 +41,10 @@
 #endif
 #ifndef SALB_SPLIT_WGS
 #define SALB_SPLIT_WGS 1024
+#endif
+// Rows per workgroup of the group scorer once a call has sixteen rows or more (4 or 8).
+#ifndef SALB_GROUP_ROWS
+#define SALB_GROUP_ROWS 8
 #endif
 
 namespace salb {
@@ -65,21 +70,25 @@ __device__ __forceinline__ int prescale_exp(float mx) {
 
 // ------------------------------------------------------------------ MFMA scorer
 
-// Raw bytes of one lane's slice of one key: D/8 code bytes and D/64 scale bytes.
-template <int D>
-struct Raw {
-  uint32_t w[D / 32];
+// Raw bytes of a DIMS-dim slice of one key: DIMS/2 code bytes and its E4M3 scale
+// bytes (DIMS/16 of them; an 8-dim slice shares its 16-dim group's byte).
+template <int DIMS>
+struct Slice {
+  uint32_t w[DIMS / 8];
   uint32_t sc;
 };
 
-template <int D>
-__device__ __forceinline__ void load_raw(Raw<D>& r, const uint8_t* codes, const uint8_t* scales) {
-  if constexpr (D == 64) {
+template <int DIMS>
+__device__ __forceinline__ void load_slice(Slice<DIMS>& r, const uint8_t* codes, const uint8_t* scales) {
+  if constexpr (DIMS == 8) {
+    r.w[0] = *reinterpret_cast<const uint32_t*>(codes);
+    r.sc = *scales;
+  } else if constexpr (DIMS == 16) {
     const u32x2 v = *reinterpret_cast<const u32x2*>(codes);
     r.w[0] = v[0];
     r.w[1] = v[1];
     r.sc = *scales;
-  } else if constexpr (D == 128) {
+  } else if constexpr (DIMS == 32) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(codes);
     r.w[0] = v[0];
     r.w[1] = v[1];
@@ -87,6 +96,7 @@ __device__ __forceinline__ void load_raw(Raw<D>& r, const uint8_t* codes, const 
     r.w[3] = v[3];
     r.sc = *reinterpret_cast<const uint16_t*>(scales);
   } else {
+    static_assert(DIMS == 64, "slice width");
     const u32x4 v0 = *reinterpret_cast<const u32x4*>(codes);
     const u32x4 v1 = *reinterpret_cast<const u32x4*>(codes + 16);
 #pragma unroll
@@ -98,13 +108,28 @@ __device__ __forceinline__ void load_raw(Raw<D>& r, const uint8_t* codes, const 
   }
 }
 
-// Eight fp16 code values of K-step kk of a raw slice; the sign of the page's global
-// scale is folded into the exact fp16 group scale (ReLU(g x) = |g| ReLU(sign(g) x)).
-template <int D>
-__device__ __forceinline__ half8v decode_step(const Raw<D>& r, int kk, float sgn) {
+// Eight fp16 code values of step kk (dims 8 kk .. 8 kk + 7) of a raw slice; the sign
+// of the page's global scale is folded into the exact fp16 group scale
+// (ReLU(g x) = |g| ReLU(sign(g) x)).
+template <int DIMS>
+__device__ __forceinline__ half8v decode_slice(const Slice<DIMS>& r, int kk, float sgn) {
   const _Float16 sh = (_Float16)(e4m3_to_f32((r.sc >> (8 * (kk >> 1))) & 0xffu) * sgn);
   const half2v s2 = {sh, sh};
   return decode8_f16(r.w[kk], s2);
+}
+
+// A lane's quarter of a key in the streaming scorer.
+template <int D>
+using Raw = Slice<D / 4>;
+
+template <int D>
+__device__ __forceinline__ void load_raw(Raw<D>& r, const uint8_t* codes, const uint8_t* scales) {
+  load_slice<D / 4>(r, codes, scales);
+}
+
+template <int D>
+__device__ __forceinline__ half8v decode_step(const Raw<D>& r, int kk, float sgn) {
+  return decode_slice<D / 4>(r, kk, sgn);
 }
 
 // Work tile of a workgroup over (key chunk, row unit): with enough chunks per row,
@@ -196,9 +221,7 @@ __device__ __forceinline__ float head_sum(const float4v (&acc)[MT], const float 
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) part = fmaf(wr[mt][i], relu_bits(acc[mt][i]), part);
-  part += __shfl_xor(part, 16);
-  part += __shfl_xor(part, 32);
-  return part;
+  return row_sum4(part);
 }
 
 // Head reduction and store of one step: lanes 0..15 store its 16 scores (keys below
@@ -353,31 +376,37 @@ __global__ __launch_bounds__(256) void score_mfma_split_kernel(ScoreArgs a) {
 // quarter of the decode work and of the key traffic per row -- and the decode of tile
 // j+1 is spread between the MFMA steps of tile j.  Otherwise every wave streams its
 // own row.
-template <int MT, int D, bool UPAGE>
-__global__ __launch_bounds__(256) void score_mfma_group_kernel(ScoreArgs a) {
+template <int MT, int D, bool UPAGE, int G>
+__global__ __launch_bounds__(64 * G) void score_mfma_group_kernel(ScoreArgs a) {
+  constexpr int NT = 64 * G;  // one wave per row of the group
   constexpr int KW = D / 32;
+  constexpr int SD = D / G;   // dims of a key each staging thread loads and decodes
+  constexpr int SW = SD / 8;  // its eight-dim steps
+  constexpr int LG = G == 8 ? 3 : 2;
+  static_assert(G == 4 || G == 8, "group size");
   constexpr int BLD = D + 8;  // LDS row of one decoded key (halves), padded against bank conflicts
   constexpr int TILE = 64;
   extern __shared__ __align__(16) unsigned char smem[];
   _Float16* bbuf = reinterpret_cast<_Float16*>(smem);                          // [2][TILE][BLD]
   float* gbuf = reinterpret_cast<float*>(smem + 2 * TILE * BLD * 2);           // [2][TILE]
-  int* pid = reinterpret_cast<int*>(gbuf + 2 * TILE);                          // [4][pid_cap]
-  float* pgs = reinterpret_cast<float*>(pid + 4 * a.pid_cap);                  // [4][pid_cap]
-  __shared__ int s_vend_w[4];
-  __shared__ int s_rows[4];
+  int* pid = reinterpret_cast<int*>(gbuf + 2 * TILE);                          // [G][pid_cap]
+  float* pgs = reinterpret_cast<float*>(pid + G * a.pid_cap);                  // [G][pid_cap]
+  __shared__ int s_vend_w[G];
+  __shared__ int s_rows[G];
   __shared__ int s_mismatch;
   __shared__ int s_valid[256];
 
-  const int units = (a.T + 3) >> 2;
+  const int units = (a.T + G - 1) / G;
   const XcdTile tile = score_tile(a, units);
   if (tile.chunk >= a.n_chunks) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // ---- the unit's rows
+  // ---- the unit's rows: with several units, rows are ranked by valid length so that
+  // each unit holds rows of similar length (one unit takes the rows as they come)
   int t;
-  if (a.T <= 256) {
-    for (int i = tid; i < a.T; i += 256) s_valid[i] = a.valid_lens[i];
-    if (tid < 4) s_rows[tid] = a.T;  // slot past the last row: no row
+  if (a.T <= 256 && units > 1) {
+    for (int i = tid; i < a.T; i += NT) s_valid[i] = a.valid_lens[i];
+    if (tid < G) s_rows[tid] = a.T;  // slot past the last row: no row
     __syncthreads();
     if (tid < a.T) {
       const int v = s_valid[tid];
@@ -386,13 +415,16 @@ __global__ __launch_bounds__(256) void score_mfma_group_kernel(ScoreArgs a) {
         const int vi = s_valid[i];
         rank += (vi > v) || (vi == v && i < tid);
       }
-      if ((rank >> 2) == tile.row) s_rows[rank & 3] = tid;
+      if (rank / G == tile.row) s_rows[rank % G] = tid;
     }
     __syncthreads();
     t = s_rows[wave];
   } else {
-    t = tile.row * 4 + wave;
+    t = tile.row * G + wave;
   }
+  // one row per wave: keep the row and its bounds in scalar registers, so that every
+  // branch on them below is a scalar branch
+  t = __builtin_amdgcn_readfirstlane(t);
   const bool has = t < a.T;
   const int valid = has ? a.valid_lens[t] : 0;
   const int s_begin = tile.chunk * a.chunk;
@@ -412,14 +444,21 @@ __global__ __launch_bounds__(256) void score_mfma_group_kernel(ScoreArgs a) {
   half8v A[MT][KW];
   float wr[MT][4];
   load_query<MT, D>(a, t, lane, A, wr);
-  if (lane < np) mypid[lane] = p_first;
-  for (int i = lane + 64; i < np; i += 64) mypid[i] = bt_row[lb0 + i];
+  if (lane < np) {
+    mypid[lane] = p_first;
+    mypgs[lane] = a.gscale[p_first];
+  }
+  for (int i = lane + 64; i < np; i += 64) {
+    const int p = bt_row[lb0 + i];
+    mypid[i] = p;
+    mypgs[i] = a.gscale[p];
+  }
   if (lane == 0) s_vend_w[wave] = s_vend;
   if (tid == 0) s_mismatch = 0;
   __syncthreads();
   int lead = 0, vmax = s_vend_w[0];
 #pragma unroll
-  for (int w = 1; w < 4; ++w)
+  for (int w = 1; w < G; ++w)
     if (s_vend_w[w] > vmax) { vmax = s_vend_w[w]; lead = w; }
   if (vmax <= s_begin) return;  // no key of this chunk is valid for any of the rows
   {
@@ -431,39 +470,40 @@ __global__ __launch_bounds__(256) void score_mfma_group_kernel(ScoreArgs a) {
   __syncthreads();
 
   if (s_mismatch) {  // rows of different sequences: each wave streams its own row
-    for (int i = lane; i < np; i += 64) mypgs[i] = a.gscale[mypid[i]];
     wave_stream<MT, D, UPAGE>(a, A, wr, mypid, mypgs, lb0, s_begin, s_vend, 0, 1, out_row, lane);
     return;
   }
 
   // ---- shared pages: decode each 64-key tile once into LDS
   const int* lpid = pid + lead * a.pid_cap;
+  const float* lpgs = pgs + lead * a.pid_cap;
   const int n_tiles = (vmax - s_begin + TILE - 1) / TILE;
-  // staging: key kt of the tile, D/4 slice qs of it.  Each group of eight lanes writes
-  // eight different keys (same slice), whose LDS rows start on distinct bank groups
-  // (the row pitch is an odd number of 16-byte granules): conflict-free writes.
-  const int kt = (tid & 7) | ((tid >> 5) << 3), qs = (tid >> 3) & 3;
+  // staging: key kt of the tile, slice qs (dims qs*SD .. qs*SD + SD - 1) of it.  Each
+  // group of eight lanes writes eight different keys (same slice), whose LDS rows start
+  // on distinct bank groups (the row pitch is an odd number of 16-byte granules):
+  // conflict-free writes.
+  const int kt = (tid & 7) | ((tid >> (3 + LG)) << 3), qs = (tid >> 3) & (G - 1);
   // Raw tiles in flight: tile i lives in ring slot i % 4 from its load (issued four
   // tiles ahead, so that about 18 KB per workgroup are in flight) until its decode,
   // one tile before it is used.  Loads and decodes past the last tile touch valid
   // memory and a free buffer; their results are unused.
-  Raw<D> R0, R1, R2, R3;
+  Slice<SD> R0, R1, R2, R3;
   float G0 = 0.0f, G1 = 0.0f, G2 = 0.0f, G3 = 0.0f;
-  auto load_tile = [&](int j, Raw<D>& raw, float& graw) {
+  auto load_tile = [&](int j, Slice<SD>& raw, float& graw) {
     const int s = min(s_begin + j * TILE + kt, vmax - 1);
     const uint32_t lb = div_epb((uint32_t)s, a.epb_magic);
     const int p = lpid[(int)lb - lb0];
-    graw = a.gscale[p];
+    graw = lpgs[(int)lb - lb0];
     const int64_t e = (int64_t)p * a.epb + (int64_t)((uint32_t)s - lb * (uint32_t)a.epb);
-    load_raw<D>(raw, a.keys + e * (D / 2) + qs * (D / 8), a.kscale + e * (D / 16) + qs * (D / 64));
+    load_slice<SD>(raw, a.keys + e * (D / 2) + qs * (SD / 2), a.kscale + e * (D / 16) + (qs * SD) / 16);
   };
-  // K-steps [k0, k1) of this thread's slice of a raw tile into LDS buffer buf.
-  auto decode_part = [&](int buf, const Raw<D>& raw, float graw, int k0, int k1) {
+  // Steps [k0, k1) of this thread's slice of a raw tile into LDS buffer buf.
+  auto decode_part = [&](int buf, const Slice<SD>& raw, float graw, int k0, int k1) {
     const float sgn = graw < 0.0f ? -1.0f : 1.0f;
-    _Float16* dst = bbuf + (buf * TILE + kt) * BLD + qs * (D / 4);
+    _Float16* dst = bbuf + (buf * TILE + kt) * BLD + qs * SD;
 #pragma unroll
-    for (int kk = k0; kk < k1; ++kk) *reinterpret_cast<half8v*>(dst + kk * 8) = decode_step<D>(raw, kk, sgn);
-    if (k1 == KW && qs == 0) gbuf[buf * TILE + kt] = fabsf(graw);
+    for (int kk = k0; kk < k1; ++kk) *reinterpret_cast<half8v*>(dst + kk * 8) = decode_slice<SD>(raw, kk, sgn);
+    if (k1 == SW && qs == 0) gbuf[buf * TILE + kt] = fabsf(graw);
   };
 
   const int col = lane & 15, quarter = lane >> 4;
@@ -493,34 +533,38 @@ __global__ __launch_bounds__(256) void score_mfma_group_kernel(ScoreArgs a) {
   };
   // One tile: score tile j from LDS while decoding tile j+1 from its ring slot (`nx`)
   // into the other buffer and reloading this tile's slot (`mine`) four tiles ahead.
-  auto run_tile = [&](int j, Raw<D>& mine, float& gmine, const Raw<D>& nx, float gnx) {
+  auto run_tile = [&](int j, Slice<SD>& mine, float& gmine, const Slice<SD>& nx, float gnx) {
     __syncthreads();  // tile j decoded; the other buffer is free again
     const int buf = j & 1;
     const int t0 = s_begin + j * TILE;
-    if (t0 < s_vend) {
-      const float g_lane = gbuf[buf * TILE + lane];
+    // Rows done before the tile (a wave-uniform, scalar condition) skip its MFMAs but
+    // still share the decode and the loads, which run in one fixed order on every
+    // path: the outstanding loads are then the same wherever the waits are placed.
+    const bool act = t0 < s_vend;
+    float g_lane = 0.0f;
+    if (act) {
+      g_lane = gbuf[buf * TILE + lane];
       mfma_step(buf, 0, AC0);
       flush_prev();
-      decode_part(buf ^ 1, nx, gnx, 0, KW / 2);
+    }
+    decode_part(buf ^ 1, nx, gnx, 0, SW / 2);
+    if (act) {
       mfma_step(buf, 1, AC1);
       keep = head_sum<MT>(AC0, wr);
-      decode_part(buf ^ 1, nx, gnx, KW / 2, KW);
+    }
+    decode_part(buf ^ 1, nx, gnx, SW / 2, SW);
+    if (act) {
       mfma_step(buf, 2, AC0);
-      {
-        const float v = head_sum<MT>(AC1, wr);
-        keep = quarter == 1 ? v : keep;
-      }
-      load_tile(j + 4, mine, gmine);
+      const float v = head_sum<MT>(AC1, wr);
+      keep = quarter == 1 ? v : keep;
+    }
+    load_tile(j + 4, mine, gmine);
+    if (act) {
       mfma_step(buf, 3, AC1);
-      {
-        const float v = head_sum<MT>(AC0, wr);
-        keep = quarter == 2 ? v : keep;
-      }
+      const float v = head_sum<MT>(AC0, wr);
+      keep = quarter == 2 ? v : keep;
       t_prev = t0;
       g_prev = g_lane;
-    } else {  // this row is done; the tile work is shared
-      decode_part(buf ^ 1, nx, gnx, 0, KW);
-      load_tile(j + 4, mine, gmine);
     }
   };
 
@@ -528,7 +572,7 @@ __global__ __launch_bounds__(256) void score_mfma_group_kernel(ScoreArgs a) {
   load_tile(1, R1, G1);
   load_tile(2, R2, G2);
   load_tile(3, R3, G3);
-  decode_part(0, R0, G0, 0, KW);
+  decode_part(0, R0, G0, 0, SW);
   for (int j = 0; j < n_tiles; j += 4) {
     run_tile(j, R0, G0, R1, G1);
     if (j + 1 >= n_tiles) break;
@@ -632,14 +676,21 @@ __global__ __launch_bounds__(256) void debug_dequant_kernel(const uint8_t* keys,
 
 // ------------------------------------------------------------------ launchers
 
+template <int MT, int D, int G>
+static void launch_group(const ScoreArgs& a, int blocks, hipStream_t st) {
+  const size_t lds = (size_t)2 * 64 * (D + 8) * 2 + 2 * 64 * 4 + (size_t)G * a.pid_cap * 8;
+  if (a.epb % 16 == 0)
+    hipLaunchKernelGGL((score_mfma_group_kernel<MT, D, true, G>), dim3(blocks), dim3(64 * G), lds, st, a);
+  else
+    hipLaunchKernelGGL((score_mfma_group_kernel<MT, D, false, G>), dim3(blocks), dim3(64 * G), lds, st, a);
+}
+
 template <int MT, int D>
-static hipError_t launch_mfma_t(const ScoreArgs& a, int blocks, bool group, hipStream_t st) {
-  if (group) {
-    const size_t lds = (size_t)2 * 64 * (D + 8) * 2 + 2 * 64 * 4 + (size_t)4 * a.pid_cap * 8;
-    if (a.epb % 16 == 0)
-      hipLaunchKernelGGL((score_mfma_group_kernel<MT, D, true>), dim3(blocks), dim3(256), lds, st, a);
-    else
-      hipLaunchKernelGGL((score_mfma_group_kernel<MT, D, false>), dim3(blocks), dim3(256), lds, st, a);
+static hipError_t launch_mfma_t(const ScoreArgs& a, int blocks, int group, hipStream_t st) {
+  if (group == 8) {
+    launch_group<MT, D, 8>(a, blocks, st);
+  } else if (group == 4) {
+    launch_group<MT, D, 4>(a, blocks, st);
   } else {
     const size_t lds = (size_t)a.pid_cap * 8;
     if (a.epb % 16 == 0)
@@ -651,7 +702,7 @@ static hipError_t launch_mfma_t(const ScoreArgs& a, int blocks, bool group, hipS
 }
 
 template <int D>
-static hipError_t launch_mfma_d(const ScoreArgs& a, int blocks, bool group, hipStream_t st) {
+static hipError_t launch_mfma_d(const ScoreArgs& a, int blocks, int group, hipStream_t st) {
   const int mt = (a.H + 15) / 16;
   switch (mt) {
     case 1: return launch_mfma_t<1, D>(a, blocks, group, st);
@@ -696,8 +747,9 @@ static int chunk_keys(int units, int n_cols, int epb, int target) {
 }
 
 hipError_t launch_score_rows(ScoreArgs a, int precision, hipStream_t st) {
-  const bool group = precision == 1 && a.T >= 4;
-  const int units = group ? (a.T + 3) / 4 : a.T;
+  // rows per workgroup of the group scorer (0: the one-row split scorer)
+  const int group = precision != 1 ? 0 : a.T >= 16 ? SALB_GROUP_ROWS : a.T >= 4 ? 4 : 0;
+  const int units = group ? (a.T + group - 1) / group : a.T;
   if (precision == 1) {
     a.chunk = chunk_keys(units, a.n_cols, a.epb, group ? SALB_GROUP_WGS : SALB_SPLIT_WGS);
     a.pid_cap = a.chunk / a.epb + 2;

@@ -233,3 +233,38 @@ def test_topk_select_workspace_reuse():
         for r in range(rows):
             o_idx, _ = indexer.topk(s[r, : valid[r]].astype(np.float64), k)
             assert gi[r].tolist() == o_idx.tolist(), (it, r)
+
+
+GROUP_SHAPES = [
+    # T, H, D, epb, table
+    (5, 16, 64, 16, "shared"),      # four-row groups, one head tile
+    (11, 16, 64, 16, "shared"),     # eight-row groups (ragged), eight-dim staging slices
+    (13, 48, 128, 64, "shared"),    # three head tiles
+    (16, 64, 256, 32, "shared"),    # four head tiles, widest keys
+    (9, 32, 128, 7, "shared"),      # pages not a multiple of 16 keys
+    (12, 64, 128, 64, "per_row"),   # rows of different sequences in one group
+    (20, 64, 64, 16, "per_row"),
+]
+
+
+@pytest.mark.parametrize("T,H,D,epb,table", GROUP_SHAPES)
+def test_group_scorer_shapes(T, H, D, epb, table):
+    """Rows grouped four or eight to a workgroup, over every key width and head-tile count;
+    valid lengths spread so that rows of one group end in different tiles and chunks."""
+    max_lb = -(-3000 // epb)
+    P = max_lb + 8
+    w = csa(f"group_{T}_{D}_{epb}_{table}", [91, T, D], T=T, H=H, D=D, epb=epb, P=P, max_lb=max_lb, top_k=64,
+            valid_lens=lambda rng, n: rng.integers(0, max_lb * epb + 1, size=n), dist="gauss", w_scale=1 / H,
+            table=table)
+    d = to_dev(w)
+    n_cols = max_lb * epb
+    rows = salb.indexer_score_rows(**d, n_cols=n_cols, precision="mfma")
+    idx, val = salb.indexer_score_topk(**d, top_k=64, precision="mfma", with_scores=True)
+    torch.cuda.synchronize()
+    gr, gi, gv = _row(rows), _row(idx), _row(val)
+    ref, amag = oracle_rows(w)
+    for t in range(T):
+        v = int(w.valid_lens[t])
+        check_scores(gr[t], ref[t], amag[t], "mfma", f"group shape t{t}")
+        assert np.all(np.isneginf(gr[t, v:])), "tail must be -inf"
+        check_topk(gi[t], gv[t], ref[t], amag[t], 64, "mfma", f"group shape t{t}")
