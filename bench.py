@@ -9,7 +9,10 @@ launched eagerly (--graph replays each from a captured HIP graph instead); HIP e
 between the stages time each one.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--precision mfma|fp32]
-                    [--graph] [--no-cpu-baseline]
+                    [--graph] [--no-cpu-baseline] [--no-cold]
+
+The decode workloads are also timed cold (key pool rotated through copies, reported
+under "cold"; "value" stays the warm figure).
 """
 
 from __future__ import annotations
@@ -37,7 +40,14 @@ WORKLOADS = {
     "long_decode_T32_S262144": 3,
     "prefill_T4096": 4,
     "qsa_prefill": 5,
+    # diagnostic, not a configuration: the long-decode shape with every row on its own
+    # pages of a 604 MB pool, so that every key byte read comes from DRAM
+    "hbm_true_T32_S262144": "diag",
 }
+# Decode workloads also timed cold: the key pool rotates through enough copies that the
+# copies read between two uses of one copy exceed twice the 256 MB last-level cache.
+COLD_WORKLOADS = ("decode_T8_S65536", "long_decode_T32_S262144")
+COLD_SPAN_BYTES = 2 * 256 * 2**20
 
 
 # HBM traffic of one scorer launch, from two rocprofv3 --pmc passes (FETCH_SIZE, then
@@ -279,6 +289,7 @@ def main():
     ap.add_argument("--workload", default="decode_T8_S65536", choices=sorted(WORKLOADS))
     ap.add_argument("--precision", default="mfma", choices=["mfma", "fp32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold (rotated key pool) timing")
     ap.add_argument("--graph", action="store_true",
                     help="replay each stage from a captured HIP graph (slower than eager launches on this "
                          "ROCm stack: a graph launch costs more than the kernel launches it replaces)")
@@ -292,9 +303,9 @@ def main():
 
     import sparse_attention_lightning_block_amd as salb
     from tests.parity import to_dev
-    from workloads import make
+    from workloads import make, make_diag
 
-    w = make(WORKLOADS[args.workload])
+    w = make_diag(args.workload) if WORKLOADS[args.workload] == "diag" else make(WORKLOADS[args.workload])
     if w.kind == "qsa":
         run_qsa(args, w)
         return
@@ -328,6 +339,9 @@ def main():
 
     pairs = w.pairs
     value = pairs / (ms_per_step / 1e3)
+    cold = None
+    if args.workload in COLD_WORKLOADS and not args.no_cold and not args.graph:
+        cold = cold_timing(torch, salb, d, w, n_cols, args, sc_view, ws, idx, val)
     # dominant kernel: the scorer (one launch per step)
     bytes_alg = pairs * key_bytes_per_entry(w.D, w.epb) + w.T * w.H * w.D * (2 if w.q_dtype == "bf16" else 4) \
         + w.T * w.H * 4 + pairs * 4
@@ -376,9 +390,44 @@ def main():
                     "p90": float(np.percentile(step_ms, 90))},
         "stage_ms": {"score": float(np.median(score_ms)), "select": float(np.median(select_ms))},
         "roofline": roofline,
+        "cold": cold,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(w),
     }
     print(json.dumps(out), flush=True)
+
+
+def cold_timing(torch, salb, d, w, n_cols, args, scores, ws, idx, val):
+    """The same two stages with the key pool (codes, scales, global scales) rotated
+    through copies, so that a copy's keys have left the caches before it is used again."""
+    pool = [d["keys_fp4"], d["key_scale"], d["key_gscale"]]
+    pool_bytes = sum(t.numel() * t.element_size() for t in pool)
+    copies = max(2, -(-COLD_SPAN_BYTES // pool_bytes))
+    sets = [d] + [dict(d, keys_fp4=pool[0].clone(), key_scale=pool[1].clone(), key_gscale=pool[2].clone())
+                  for _ in range(copies - 1)]
+    turn = [0]
+
+    def score():
+        salb.indexer_score_rows(**sets[turn[0] % copies], n_cols=n_cols, precision=args.precision, out=scores)
+
+    def select():
+        salb.indexer_topk_select(scores, w.top_k, valid_lens=d["valid_lens"], workspace=ws, out_idx=idx,
+                                 out_scores=val)
+        turn[0] += 1
+
+    stages = [score, select]
+    for _ in range(min(args.warmup, copies)):
+        for f in stages:
+            f()
+    torch.cuda.synchronize()
+    ms_per_step, stage = timed_steps(torch, make_step(torch, stages, False), len(stages), args.steps)
+    del sets
+    return {
+        "copies": copies,
+        "pool_mb": round(pool_bytes / 2**20, 2),
+        "ms_per_step": ms_per_step,
+        "value": w.pairs / (ms_per_step / 1e3),
+        "stage_ms": {"score": float(np.median(stage[0])), "select": float(np.median(stage[1]))},
+    }
 
 
 if __name__ == "__main__":

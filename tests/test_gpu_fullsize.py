@@ -10,7 +10,7 @@ import torch
 import sparse_attention_lightning_block_amd as salb
 from oracle import indexer, qsa
 from tests.parity import MFMA_ROWMAX, check_scores, check_topk, oracle_rows, to_dev
-from workloads import make
+from workloads import make, make_diag
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +50,32 @@ def test_full_size_sampled_rows(cfg):
         K = min(w.top_k, int(w.valid_lens[t]))
         assert np.all(gi[t, K:] == -1) and len(set(gi[t, :K].tolist())) == K
         assert np.all((gi[t, :K] >= 0) & (gi[t, :K] < w.valid_lens[t]))
+
+
+def test_hbm_true_diagnostic_sampled_rows():
+    """The diagnostic pool where every row reads its own pages (no page shared between
+    the rows of a workgroup): sampled rows against the oracle, set rules on every row."""
+    w = make_diag("hbm_true_T32_S262144")
+    d = to_dev(w)
+    n_cols = w.max_lb * w.epb
+    scores = torch.empty((w.T, n_cols), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(1, salb.indexer_topk_workspace_size(w.T, n_cols, w.top_k)), dtype=torch.uint8,
+                     device="cuda")
+    salb.indexer_score_rows(**d, n_cols=n_cols, precision="mfma", out=scores)
+    idx, val = salb.indexer_topk_select(scores, w.top_k, valid_lens=d["valid_lens"], workspace=ws, with_scores=True)
+    torch.cuda.synchronize()
+    order = np.argsort(w.valid_lens)
+    rows = sorted({int(order[-1]), int(order[0])})
+    ref, amag = oracle_rows(w, rows)
+    for t in rows:
+        g = scores[t].cpu().numpy()
+        check_scores(g, ref[t], amag[t], "mfma", f"hbm_true t{t}")
+        assert np.all(np.isneginf(g[int(w.valid_lens[t]):]))
+        check_topk(idx[t].cpu().numpy(), val[t].cpu().numpy(), ref[t], amag[t], w.top_k, "mfma", f"hbm_true t{t}")
+    gi = idx.cpu().numpy()
+    for t in range(w.T):
+        K = min(w.top_k, int(w.valid_lens[t]))
+        assert np.all(gi[t, K:] == -1) and len(set(gi[t, :K].tolist())) == K
 
 
 def test_full_size_fused_matches_split():

@@ -7,4 +7,4 @@ pooling, normalisation or rotary embedding.  Both the CPU oracle's tests and the
 GPU path's tests and benchmark draw their inputs from here.
 """
 
-from .configs import CONFIGS, make, Workload  # noqa: F401
+from .configs import CONFIGS, make, make_diag, Workload  # noqa: F401

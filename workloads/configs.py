@@ -136,6 +136,9 @@ def csa(name, seed, T, H, D, epb, P, max_lb, top_k, valid_lens, dist, q_dtype="f
         bt = np.tile(row, (T, 1))
     elif table == "per_row":
         bt = np.stack([r_bt.permutation(P)[:max_lb] for _ in range(T)]).astype(np.int32)
+    elif table == "disjoint":   # every row its own pages: no page is shared between rows
+        assert P >= T * max_lb
+        bt = r_bt.permutation(P)[: T * max_lb].reshape(T, max_lb).astype(np.int32)
     else:
         raise ValueError(table)
     vl = valid_lens(r_v, T) if callable(valid_lens) else valid_lens
@@ -206,6 +209,21 @@ def make(i: int, reduced: int = 0) -> Workload:
             return qsa("qsa_reduced", seed, n_tok=16 * 700, hd=128, ratio=16, rows=40, n_heads=32, top_k=64)
         return qsa("qsa_prefill", seed, n_tok=524288, hd=128, ratio=16, rows=2048, n_heads=32, top_k=256)
     raise ValueError(i)
+
+
+def make_diag(name: str) -> Workload:
+    """Diagnostic workloads that are not configurations of their own.
+
+    ``hbm_true_T32_S262144``: the long-decode shape (32 rows, S=262144, H=64, D=128,
+    64 keys per page, top_k=2048, valid lengths U{131072..262144}) where every row
+    reads its own 4096 pages of a 131072-page pool (604 MB of NVFP4 keys, more than
+    the 256 MB last-level cache), so that every key byte a row reads comes from DRAM.
+    Keys use the uniform-code encoding (``dist="tiny"``) to keep generation fast.
+    """
+    if name == "hbm_true_T32_S262144":
+        return csa(name, [3, 100], T=32, H=64, D=128, epb=64, P=131072, max_lb=4096, top_k=2048,
+                   valid_lens=_uniform_valid(131072, 262144), dist="tiny", w_scale=1 / 64, table="disjoint")
+    raise ValueError(name)
 
 
 CONFIGS = {
