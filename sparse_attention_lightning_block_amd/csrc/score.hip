@@ -236,7 +236,7 @@ __device__ __forceinline__ void epilogue(const float4v (&acc)[MT], const float (
 
 // One wave streams the 16-key steps first, first + stride, ... of [s_begin, s_vend)
 // for one query, decoding each lane's key slice straight into the B operand.  Loads
-// run three steps ahead (ring of four raw buffers); the epilogue of step i-1 is issued
+// run seven steps ahead (ring of eight raw buffers); the epilogue of step i-1 is issued
 // beside the MFMAs of step i (two accumulator sets).  pid/pgs hold the page ids and
 // global scales of the logical blocks from lb0 on.
 template <int MT, int D, bool UPAGE>
@@ -285,41 +285,41 @@ __device__ __forceinline__ void wave_stream(const ScoreArgs& a, const half8v (&A
     }
   };
 
-  Raw<D> R0, R1, R2, R3;
-  float G0, G1, G2, G3;
+  // ring of raw steps: step i lives in slot i % kRing from its load, kRing - 1 steps
+  // ahead of its MFMAs, until its decode
+  constexpr int kRing = 8;
+  Raw<D> R[kRing];
+  float G[kRing];
   float4v AC0[MT], AC1[MT];
   zero_acc<MT>(AC1);
   int gi = first;
-  load_step(gi, R0, G0);
-  load_step(gi + stride, R1, G1);
-  load_step(gi + 2 * stride, R2, G2);
+#pragma unroll
+  for (int u = 0; u < kRing - 1; ++u) load_step(gi + u * stride, R[u], G[u]);
   int s_prev = 0x3fffffff;  // nothing pending: its stores are masked off
   float g_prev = 0.0f;
-  bool last_ac1 = false;
+  bool last_ac1 = false, done = false;
   for (;;) {
-    if (gi >= n_vg) { last_ac1 = true; break; }
-    load_step(gi + 3 * stride, R3, G3);
-    compute(R0, G0, AC0);
-    epilogue<MT>(AC1, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
-    s_prev = s_begin + gi * 16; g_prev = G0; gi += stride;
-
-    if (gi >= n_vg) { last_ac1 = false; break; }
-    load_step(gi + 3 * stride, R0, G0);
-    compute(R1, G1, AC1);
-    epilogue<MT>(AC0, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
-    s_prev = s_begin + gi * 16; g_prev = G1; gi += stride;
-
-    if (gi >= n_vg) { last_ac1 = true; break; }
-    load_step(gi + 3 * stride, R1, G1);
-    compute(R2, G2, AC0);
-    epilogue<MT>(AC1, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
-    s_prev = s_begin + gi * 16; g_prev = G2; gi += stride;
-
-    if (gi >= n_vg) { last_ac1 = false; break; }
-    load_step(gi + 3 * stride, R2, G2);
-    compute(R3, G3, AC1);
-    epilogue<MT>(AC0, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
-    s_prev = s_begin + gi * 16; g_prev = G3; gi += stride;
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      // the step before u left its scores in AC1 when u is even, in AC0 when odd
+      if (gi >= n_vg) {
+        last_ac1 = (u & 1) == 0;
+        done = true;
+        break;
+      }
+      load_step(gi + (kRing - 1) * stride, R[(u + kRing - 1) % kRing], G[(u + kRing - 1) % kRing]);
+      if (u & 1) {
+        compute(R[u], G[u], AC1);
+        epilogue<MT>(AC0, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
+      } else {
+        compute(R[u], G[u], AC0);
+        epilogue<MT>(AC1, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
+      }
+      s_prev = s_begin + gi * 16;
+      g_prev = G[u];
+      gi += stride;
+    }
+    if (done) break;
   }
   if (last_ac1) epilogue<MT>(AC1, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
   else epilogue<MT>(AC0, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
