@@ -60,6 +60,20 @@ __device__ __forceinline__ float row_sum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Four values per lane, x0..x3; lane i of row r (lanes 16 r .. 16 r + 15) returns the
+// sum of x_r over lane i of all four rows -- four butterflies' worth of sums, each
+// kept by one row, in three row swaps.  The 32-lane swap of (x0, x2) leaves the lower
+// half with x0 of both halves and the upper half with x2 of both; likewise (x1, x3);
+// the 16-lane swap of those two then pairs rows 0/1 and 2/3.
+__device__ __forceinline__ float row_transpose_sum4(float x0, float x1, float x2, float x3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x2), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x1), __float_as_uint(x3), false, false);
+  const float y02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const float y13 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(y02), __float_as_uint(y13), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // Exact floor(s / epb) for s < 2^24 and epb <= 2^16: m = ceil(2^40 / epb).
 __device__ __forceinline__ uint32_t div_epb(uint32_t s, uint64_t magic) {
   return (uint32_t)(((uint64_t)s * magic) >> 40);

@@ -380,30 +380,23 @@ __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const float
               A[mt][kk], B[kk][nt], kk == 0 ? float4v{0.0f, 0.0f, 0.0f, 0.0f} : acc[mt][nt], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
     // ReLU and head sum: lane (quarter, col) holds heads 4*quarter + i of each M tile
-    // for key 16 * nt + col; the four quarters are then summed across lanes.
-    float s[4][RPW];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-      for (int rr = 0; rr < RPW; ++rr) {
-        float x = 0.0f;
-#pragma unroll
-        for (int j = 0; j < MTR; ++j) {
-          const float4v a = acc[rr * MTR + j][nt];
-          x += relu_bits(a[0]) + relu_bits(a[1]) + relu_bits(a[2]) + relu_bits(a[3]);
-        }
-        x += __shfl_xor(x, 16);
-        x += __shfl_xor(x, 32);
-        s[nt][rr] = x;
-      }
-    }
-    // lane (quarter, col) writes key 16 * quarter + col of the tile for each row
+    // for key 16 * nt + col.  The in-lane sums of the four N tiles are then reduced over
+    // the quarters so that quarter q keeps N tile q: lane (quarter, col) ends with key
+    // 16 * quarter + col of the tile, for each row.
     const int key = (int)(k0 - c0) + 16 * quarter + col;
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
-      float v = s[0][rr];
+      float x[4];
 #pragma unroll
-      for (int nt = 1; nt < 4; ++nt) v = quarter == nt ? s[nt][rr] : v;
+      for (int nt = 0; nt < 4; ++nt) {
+        x[nt] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < MTR; ++j) {
+          const float4v a = acc[rr * MTR + j][nt];
+          x[nt] += relu_bits(a[0]) + relu_bits(a[1]) + relu_bits(a[2]) + relu_bits(a[3]);
+        }
+      }
+      const float v = row_transpose_sum4(x[0], x[1], x[2], x[3]);
       if (orow[rr] != nullptr && key < crel) orow[rr][key] = key < vrel[rr] ? v * out_scale : -INFINITY;
     }
   };

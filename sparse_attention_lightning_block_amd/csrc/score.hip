@@ -215,13 +215,18 @@ __device__ __forceinline__ void zero_acc(float4v (&acc)[MT]) {
 // Head reduction of one 16-key step: in-lane over 4*MT heads, then across the four
 // lane quarters; every lane ends with the total of its key column (lane & 15).
 template <int MT>
-__device__ __forceinline__ float head_sum(const float4v (&acc)[MT], const float (&wr)[MT][4]) {
+__device__ __forceinline__ float head_part(const float4v (&acc)[MT], const float (&wr)[MT][4]) {
   float part = 0.0f;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) part = fmaf(wr[mt][i], relu_bits(acc[mt][i]), part);
-  return row_sum4(part);
+  return part;
+}
+
+template <int MT>
+__device__ __forceinline__ float head_sum(const float4v (&acc)[MT], const float (&wr)[MT][4]) {
+  return row_sum4(head_part<MT>(acc, wr));
 }
 
 // Head reduction and store of one step: lanes 0..15 store its 16 scores (keys below
@@ -509,12 +514,14 @@ __global__ __launch_bounds__(64 * G) void score_mfma_group_kernel(ScoreArgs a) {
   const int col = lane & 15, quarter = lane >> 4;
   float4v AC0[MT], AC1[MT];
   zero_acc<MT>(AC1);
-  // The scores of a tile are gathered so that lane l ends with key l of the tile
-  // (step = lane quarter, key column = lane & 15) and leave in one 256-byte store.
-  // Step 3 of a tile is reduced at the start of the next one, beside its MFMAs.
+  // Each step leaves one in-lane head sum per lane (its quarter's heads, key column
+  // lane & 15); the four steps of a tile are reduced over the quarters together, so
+  // that lane l ends with key l of the tile (step = lane quarter) and the tile leaves
+  // in one 256-byte store.  Step 3 of a tile is reduced at the start of the next one,
+  // beside its MFMAs.
   int t_prev = 0x3fffffff;  // previous tile (none yet: its store is masked off)
   float g_prev = 0.0f;      // |global scale| of key t_prev + lane
-  float keep = 0.0f;
+  float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f;
   auto mfma_step = [&](int buf, int k, float4v (&acc)[MT]) {
     const _Float16* src = bbuf + (buf * TILE + k * 16 + col) * BLD + quarter * (D / 4);
 #pragma unroll
@@ -527,8 +534,7 @@ __global__ __launch_bounds__(64 * G) void score_mfma_group_kernel(ScoreArgs a) {
     }
   };
   auto flush_prev = [&]() {
-    const float v = head_sum<MT>(AC1, wr);
-    const float sc = quarter == 3 ? v : keep;
+    const float sc = row_transpose_sum4(p0, p1, p2, head_part<MT>(AC1, wr));
     if (t_prev + lane < s_vend) out_row[t_prev + lane] = g_prev * sc;
   };
   // One tile: score tile j from LDS while decoding tile j+1 from its ring slot (`nx`)
@@ -550,19 +556,17 @@ __global__ __launch_bounds__(64 * G) void score_mfma_group_kernel(ScoreArgs a) {
     decode_part(buf ^ 1, nx, gnx, 0, SW / 2);
     if (act) {
       mfma_step(buf, 1, AC1);
-      keep = head_sum<MT>(AC0, wr);
+      p0 = head_part<MT>(AC0, wr);
     }
     decode_part(buf ^ 1, nx, gnx, SW / 2, SW);
     if (act) {
       mfma_step(buf, 2, AC0);
-      const float v = head_sum<MT>(AC1, wr);
-      keep = quarter == 1 ? v : keep;
+      p1 = head_part<MT>(AC1, wr);
     }
     load_tile(j + 4, mine, gmine);
     if (act) {
       mfma_step(buf, 3, AC1);
-      const float v = head_sum<MT>(AC0, wr);
-      keep = quarter == 2 ? v : keep;
+      p2 = head_part<MT>(AC0, wr);
       t_prev = t0;
       g_prev = g_lane;
     }
