@@ -58,10 +58,11 @@ COLD_SPAN_BYTES = 2 * 256 * 2**20
 TRAFFIC_COPY_FACTOR = {"FETCH_SIZE": 1.9998, "WRITE_SIZE": 1.0}
 SCORER_SOURCES = {"csa": ['score.hip', 'nvfp4.hpp', 'common.hpp', 'internal.hpp'], "qsa": ['qsa.hip', 'common.hpp', 'internal.hpp']}
 SCORER_TRAFFIC = {   # workload: (sources, sha, FETCH_SIZE KiB, WRITE_SIZE KiB per dispatch)
-    "decode_T8_S65536": ("csa", "09557835d10d456f", 3504.3, 2048.1),
-    "long_decode_T32_S262144": ("csa", "09557835d10d456f", 13693.3, 32768.8),
-    "prefill_T4096": ("csa", "09557835d10d456f", 35573.2, 65656.8),
-    "qsa_prefill": ("qsa", "c65f848829a03f7f", 163908.5, 262424.0),
+    "decode_T8_S65536": ("csa", "28bc860158dc9676", 3536.7, 2048.1),
+    "long_decode_T32_S262144": ("csa", "28bc860158dc9676", 13712.8, 32768.8),
+    "prefill_T4096": ("csa", "28bc860158dc9676", 35433.1, 65671.1),
+    "qsa_prefill": ("qsa", "e113669cefd0ce62", 163883.1, 262424.0),
+    "hbm_true_T32_S262144": ("csa", "28bc860158dc9676", 228976.1, 32773.0),
 }
 
 

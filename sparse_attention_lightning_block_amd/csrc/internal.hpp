@@ -41,6 +41,8 @@ constexpr int kMaxTopK = 8192;
 struct SelectPlan {
   int rows, n_cols, top_k;
   int two_pass;   // 0: one workgroup per row; 1: histogram + filter grid over (chunk, row)
+  int row_nt;     // threads of the one-workgroup rows (two_pass == 0)
+  int cand_cap;   // LDS candidate slots of a one-workgroup row kept in LDS (per == 0)
   int per;        // entries per thread (a row, or a chunk of the two-pass grid)
   int chunks;     // chunks per row (two-pass)
   int final_nt;   // threads of the finishing workgroup (two-pass)

@@ -45,6 +45,12 @@ constexpr int kFinalThreadsMany = 256;   // ... and when rows are many (more row
 constexpr int kFinalPerMany = 16;
 constexpr int kFewRows = 256;
 constexpr int kRowMax = 32 * kRowThreads;  // 8192: one-workgroup rows
+// Wider one-workgroup rows (1024 threads: 16 entries each in registers, or up to
+// 32768 entries in LDS) once there are enough rows to fill the GPU with one workgroup
+// per row: the row is read once, with no global histogram or candidate pass.
+constexpr int kRowThreadsWide = 1024;
+constexpr int kRowMaxWide = 32 * kRowThreadsWide;  // 32768
+constexpr int kWideRowsMin = 256;
 constexpr int kBucketMax = 48;           // crowded bucket: sorting network instead
 constexpr int kHistCopies = kXcds;       // one global histogram per XCD
 constexpr int kMaxWaves = kFinalThreads / kWave;
@@ -66,6 +72,7 @@ struct SelArgs {
   int top_k;
   int32_t* out_idx;
   float* out_scores;
+  int cand_cap;      // LDS candidate slots of a one-workgroup row kept in LDS
   // long-row pipeline
   int chunk;         // entries per chunk workgroup
   int chunks;        // chunks per row
@@ -287,7 +294,7 @@ __device__ __forceinline__ int pow2_at_least(int x) {
 // hist holds kBins + 4 counters.
 template <int NT>
 __device__ void finish_row(uint64_t* sortbuf, uint64_t* grp, uint32_t* hist, int K, int top_k, int32_t* oi,
-                           float* os, uint64_t mx, uint64_t mn, SelShared& sh) {
+                           float* os, uint64_t mx, uint64_t mn, SelShared& sh, uint32_t kbase = 0u) {
   constexpr int BPT = kBins / NT;
   const int tid = threadIdx.x;
   for (int i = K + tid; i < top_k; i += NT) {
@@ -298,7 +305,7 @@ __device__ void finish_row(uint64_t* sortbuf, uint64_t* grp, uint32_t* hist, int
     if (K == 1 && tid == 0) {
       const uint64_t c = sortbuf[0];
       oi[0] = (int32_t)(~(uint32_t)c);
-      if (os) os[0] = ord_to_float((uint32_t)(c >> 32));
+      if (os) os[0] = ord_to_float((uint32_t)(c >> 32) + kbase);
     }
     return;
   }
@@ -361,7 +368,7 @@ __device__ void finish_row(uint64_t* sortbuf, uint64_t* grp, uint32_t* hist, int
   for (int i = tid; i < K; i += NT) {
     const uint64_t c = sortbuf[i];
     oi[i] = (int32_t)(~(uint32_t)c);
-    if (os) os[i] = ord_to_float((uint32_t)(c >> 32));
+    if (os) os[i] = ord_to_float((uint32_t)(c >> 32) + kbase);
   }
 }
 
@@ -377,6 +384,11 @@ struct FinishLds {
   uint64_t* grp;
   uint32_t* hist;
 };
+
+// LDS of a row's order keys held by a one-workgroup select (16-byte multiple).
+__host__ __device__ __forceinline__ size_t row_keys_lds_bytes(int n_cols) {
+  return ((size_t)n_cols * 4 + 15) & ~(size_t)15;
+}
 
 __device__ __forceinline__ FinishLds carve(unsigned char* smem, int top_k) {
   const int p = pow2_at_least(top_k);
@@ -408,15 +420,34 @@ __global__ __launch_bounds__(NT) void select_rows_kernel(SelArgs a) {
     const int e = i * NT + tid;
     key[i] = e < n ? ord_key(src[e]) : 0u;
   }
-  auto each = [&](auto&& fn) {
+  auto each_key = [&](auto&& fn) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = i * NT + tid;
-      if (e < n) fn(composite(key[i], (uint32_t)e));
+      if (e < n) fn(key[i], e);
     }
   };
+  // The row's keys are taken relative to its smallest one, and the radix starts at the
+  // highest bit in which any two differ: the first digit then splits the row's actual
+  // range (a row of close scores would otherwise crowd a few bins of the first digit,
+  // and its LDS atomics with them).
+  uint32_t kbase = 0u;
+  int top = 63;
+  if (K < n) {
+    uint64_t kmx = 0ull, kmn = ~0ull;
+    each_key([&](uint32_t k, int) {
+      kmx = k > kmx ? k : kmx;
+      kmn = k < kmn ? k : kmn;
+    });
+    block_suffix_minmax<NT>(0u, kmx, kmn, sh);
+    __syncthreads();  // sh is used again below
+    kbase = (uint32_t)kmn;
+    const uint32_t span = (uint32_t)kmx - kbase;
+    top = 32 + (span ? 31 - __clz(span) : 0);
+  }
+  auto each = [&](auto&& fn) { each_key([&](uint32_t k, int e) { fn(composite(k - kbase, (uint32_t)e)); }); };
   uint64_t thr = 0ull;
-  if (K < n) thr = radix_select<NT>(each, 0ull, 0ull, (uint32_t)K, 63, f.hist, sh);
+  if (K < n) thr = radix_select<NT>(each, 0ull, 0ull, (uint32_t)K, top, f.hist, sh);
   // gather the winners
   uint32_t mine = 0;
   uint64_t mx = 0ull, mn = ~0ull;
@@ -434,7 +465,148 @@ __global__ __launch_bounds__(NT) void select_rows_kernel(SelArgs a) {
   __syncthreads();
   int32_t* oi = a.out_idx + (int64_t)row * a.top_k;
   float* os = a.out_scores ? a.out_scores + (int64_t)row * a.top_k : nullptr;
-  finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, mx, mn, sh);
+  finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, mx, mn, sh, kbase);
+}
+
+// Rows too long for registers (up to 32768 entries), one workgroup each.  The row's
+// order keys go to LDS once, with their range.  One histogram pass over a 12-bit
+// digit of the key relative to the row's smallest (the digit spans the row's actual
+// range) finds the bin of the K-th entry; the entries from that bin up -- K plus the
+// rest of the bin -- are compacted into an LDS candidate list, where the radix select
+// finishes and the winners are gathered.  A bin crowded past the list's capacity falls
+// back to radix passes over the whole row.  Thread t owns the runs of four entries
+// 4 (t + m NT) .. + 3 of the LDS row, read as 16-byte words, eight in flight per pass.
+template <int NT>
+__global__ __launch_bounds__(NT) void select_rows_lds_kernel(SelArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ SelShared sh;
+  __shared__ uint32_t s_kmx[NT / kWave], s_kmn[NT / kWave];
+  const int row = gridDim.x - 1 - blockIdx.x;  // causal rows grow with the index: longest first
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int n = row_valid(a, row);
+  const int K = n < a.top_k ? n : a.top_k;
+  const float* src = a.scores + (int64_t)row * a.score_stride;
+  const size_t key_bytes = row_keys_lds_bytes(a.n_cols);
+  uint32_t* lkey = reinterpret_cast<uint32_t*>(smem);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(smem + key_bytes);
+  FinishLds f = carve(smem + key_bytes + (size_t)a.cand_cap * 8, a.top_k);
+
+  // the row's keys into LDS, eight loads in flight per thread, and their range
+  uint32_t kmx = 0u, kmn = ~0u;
+  {
+    int e = tid;
+    for (; e + 7 * NT < n; e += 8 * NT) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = src[e + i * NT];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t k = ord_key(x[i]);
+        lkey[e + i * NT] = k;
+        kmx = k > kmx ? k : kmx;
+        kmn = k < kmn ? k : kmn;
+      }
+    }
+    for (; e < n; e += NT) {
+      const uint32_t k = ord_key(src[e]);
+      lkey[e] = k;
+      kmx = k > kmx ? k : kmx;
+      kmn = k < kmn ? k : kmn;
+    }
+  }
+  kmx = wave_max(kmx);
+  kmn = ~wave_max(~kmn);
+  if (lane == 0) {
+    s_kmx[wave] = kmx;
+    s_kmn[wave] = kmn;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NT / kWave; ++w) {
+    kmx = s_kmx[w] > kmx ? s_kmx[w] : kmx;
+    kmn = s_kmn[w] < kmn ? s_kmn[w] : kmn;
+  }
+  auto each_key = [&](auto&& fn) {
+    const uint4* lk4 = reinterpret_cast<const uint4*>(lkey);
+    for (int m0 = 0; m0 * 4 * NT < n; m0 += 8) {
+      uint4 v[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int w = (m0 + m) * NT + tid;
+        v[m] = 4 * w < n ? lk4[w] : uint4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int e = 4 * ((m0 + m) * NT + tid);
+        if (e < n) fn(v[m].x, e);
+        if (e + 1 < n) fn(v[m].y, e + 1);
+        if (e + 2 < n) fn(v[m].z, e + 2);
+        if (e + 3 < n) fn(v[m].w, e + 3);
+      }
+    }
+  };
+  const uint32_t kbase = kmn;
+  auto each_row = [&](auto&& fn) { each_key([&](uint32_t k, int e) { fn(composite(k - kbase, (uint32_t)e)); }); };
+  int C = -1;  // candidates in the list (-1: the whole row is the candidate set)
+  auto each_cand = [&](auto&& fn) {
+    for (int i = tid; i < C; i += NT) fn(cand[i]);
+  };
+  uint64_t thr = 0ull;
+  if (K < n) {
+    const uint32_t span = kmx - kbase;
+    const int bits = span ? 32 - __clz(span) : 1;
+    const int shift = bits > kDigit ? bits - kDigit : 0;
+    clear_bins<NT>(f.hist);
+    if (tid == 0) sh.fill = 0u;
+    __syncthreads();
+    each_key([&](uint32_t k, int) { atomicAdd(&f.hist[(k - kbase) >> shift], 1u); });
+    __syncthreads();
+    uint32_t h[kBins / NT];
+    load_bins<NT>(f.hist, h);
+    find_digit<NT>(h, (uint32_t)K, sh);
+    const uint32_t b1 = sh.digit, gt = sh.gt, cnt = sh.cnt;
+    const uint64_t prefix = (uint64_t)b1 << (32 + shift);
+    if (gt + cnt <= (uint32_t)a.cand_cap) {
+      const uint32_t kthr = kbase + (b1 << shift);  // smallest key of bin b1
+      each_key([&](uint32_t k, int e) {
+        if (k >= kthr) cand[atomicAdd(&sh.fill, 1u)] = composite(k - kbase, (uint32_t)e);
+      });
+      __syncthreads();
+      C = (int)(gt + cnt);
+      if (gt + cnt == (uint32_t)K)
+        thr = prefix;  // the bin is taken whole
+      else
+        thr = radix_select<NT>(each_cand, prefix, (uint64_t)(kBins - 1) << (32 + shift), (uint32_t)K - gt,
+                               31 + shift, f.hist, sh);
+    } else {
+      thr = radix_select<NT>(each_row, prefix, (uint64_t)(kBins - 1) << (32 + shift), (uint32_t)K - gt, 31 + shift,
+                             f.hist, sh);
+    }
+  }
+  // gather the winners
+  auto each = [&](auto&& fn) {
+    if (C >= 0)
+      each_cand(fn);
+    else
+      each_row(fn);
+  };
+  uint32_t mine = 0;
+  uint64_t mx = 0ull, mn = ~0ull;
+  each([&](uint64_t c) {
+    if (c >= thr) {
+      ++mine;
+      mx = c > mx ? c : mx;
+      mn = c < mn ? c : mn;
+    }
+  });
+  uint32_t off = block_suffix_minmax<NT>(mine, mx, mn, sh);
+  each([&](uint64_t c) {
+    if (c >= thr && off < (uint32_t)K) f.sortbuf[off++] = c;  // exactly K are selected
+  });
+  __syncthreads();
+  int32_t* oi = a.out_idx + (int64_t)row * a.top_k;
+  float* os = a.out_scores ? a.out_scores + (int64_t)row * a.top_k : nullptr;
+  finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, mx, mn, sh, kbase);
 }
 
 // ------------------------------------------------------------------ long rows
@@ -702,6 +874,7 @@ static WsLayout ws_layout(int rows, int chunks, int chunk) {
 }
 
 constexpr size_t kLdsMax = 160 * 1024;
+constexpr size_t kStaticLdsReserve = 1024;  // static LDS of the one-workgroup row kernels
 
 bool plan_select(int rows, int n_cols, int top_k, SelectPlan* p) {
   if (top_k < 1 || top_k > kMaxTopK) return false;
@@ -709,9 +882,28 @@ bool plan_select(int rows, int n_cols, int top_k, SelectPlan* p) {
   p->n_cols = n_cols;
   p->top_k = top_k;
   p->lds = finish_lds_bytes(top_k);
+  p->cand_cap = 0;
   if (n_cols <= kRowMax) {
     p->two_pass = 0;
+    p->row_nt = kRowThreads;
     p->per = n_cols <= 1024 ? 4 : n_cols <= 2048 ? 8 : n_cols <= 4096 ? 16 : 32;
+    p->chunks = 1;
+    p->bytes = 0;
+  } else if (rows >= kWideRowsMin && n_cols <= 16 * kRowThreadsWide) {
+    p->two_pass = 0;  // 1024 threads x 16 registers
+    p->row_nt = kRowThreadsWide;
+    p->per = 16;
+    p->chunks = 1;
+    p->bytes = 0;
+  } else if (rows >= kWideRowsMin && n_cols <= kRowMaxWide &&
+             p->lds + row_keys_lds_bytes(n_cols) + kStaticLdsReserve <= kLdsMax) {
+    p->two_pass = 0;  // 1024 threads, the row's keys in LDS, then a candidate list
+    p->row_nt = kRowThreadsWide;
+    p->per = 0;
+    const size_t fixed = p->lds + row_keys_lds_bytes(n_cols);
+    const size_t cap = (kLdsMax - kStaticLdsReserve - fixed) / 8;
+    p->cand_cap = (int)(cap < (size_t)kRowMaxWide ? cap : (size_t)kRowMaxWide) & ~1;  // keeps 16-byte alignment
+    p->lds = fixed + (size_t)p->cand_cap * 8;
     p->chunks = 1;
     p->bytes = 0;
   } else {
@@ -749,6 +941,14 @@ static hipError_t launch_rows(const SelArgs& a, const SelectPlan& p, hipStream_t
   return hipGetLastError();
 }
 
+template <int NT>
+static hipError_t launch_rows_lds(const SelArgs& a, const SelectPlan& p, hipStream_t st) {
+  hipError_t e = set_lds(select_rows_lds_kernel<NT>, p.lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((select_rows_lds_kernel<NT>), dim3(p.rows), dim3(NT), p.lds, st, a);
+  return hipGetLastError();
+}
+
 template <int PER>
 static hipError_t launch_pipeline(const SelArgs& a, const SelectPlan& p, hipStream_t st) {
   hipError_t e = p.final_nt == kFinalThreads ? set_lds(select_final_kernel<kFinalThreads, kFinalPer>, p.lds)
@@ -782,7 +982,10 @@ hipError_t launch_select(const SelectPlan& p, const float* scores, int64_t score
   a.top_k = p.top_k;
   a.out_idx = out_idx;
   a.out_scores = out_scores;
+  a.cand_cap = p.cand_cap;
   if (!p.two_pass) {
+    if (p.row_nt == kRowThreadsWide)
+      return p.per == 16 ? launch_rows<kRowThreadsWide, 16>(a, p, st) : launch_rows_lds<kRowThreadsWide>(a, p, st);
     switch (p.per) {
       case 4: return launch_rows<kRowThreads, 4>(a, p, st);
       case 8: return launch_rows<kRowThreads, 8>(a, p, st);

@@ -181,6 +181,38 @@ def test_topk_select_exact(n_cols, k):
         assert np.array_equal(gv[r][:kk], o_val[:kk].astype(np.float32))
 
 
+@pytest.mark.parametrize("n_cols,k", [(12000, 256), (30000, 256), (32768, 2048), (20000, 1)])
+def test_topk_select_many_long_rows(n_cols, k):
+    """Many rows (one workgroup per row of 1024 threads: entries in registers up to 16384
+    columns, in LDS up to 32768): exact against the oracle on sampled rows, with ties,
+    empty rows, rows shorter than k and full rows; set rules on every row."""
+    rng = np.random.default_rng(n_cols + 7 * k)
+    rows = 300
+    s = rng.standard_normal((rows, n_cols)).astype(np.float32)
+    s[0, ::7] = 1.5                          # heavy ties
+    s[1] = np.round(s[1] * 4) / 4             # coarse values: ties at the threshold
+    s[2, :] = 0.25                            # one value everywhere
+    s[3, ::3] = -np.inf
+    valid = rng.integers(0, n_cols + 1, rows).astype(np.int32)
+    valid[:4] = n_cols
+    valid[4], valid[5], valid[6] = 0, max(0, k - 3), k
+    idx, val = salb.indexer_topk_select(torch.from_numpy(s).cuda(), k, valid_lens=torch.from_numpy(valid).cuda(),
+                                        with_scores=True)
+    gi, gv = _row(idx), _row(val)
+    for r in list(range(8)) + [rows // 2, rows - 1]:
+        o_idx, o_val = indexer.topk(s[r, : valid[r]].astype(np.float64), k)
+        assert gi[r].tolist() == o_idx.tolist(), r
+        kk = min(k, int(valid[r]))
+        assert np.array_equal(gv[r][:kk], o_val[:kk].astype(np.float32)), r
+    for r in range(rows):
+        kk = min(k, int(valid[r]))
+        assert np.all(gi[r, kk:] == -1) and len(set(gi[r, :kk].tolist())) == kk, r
+        if kk:   # the k-th value bounds every unselected entry
+            sel = np.zeros(int(valid[r]), bool)
+            sel[gi[r, :kk]] = True
+            assert np.all(s[r, : valid[r]][~sel] <= gv[r, kk - 1]), r
+
+
 def test_topk_select_causal_rule():
     rng = np.random.default_rng(9)
     rows, nb, ratio, first = 5, 64, 16, 900
