@@ -28,6 +28,7 @@ struct ScoreArgs {
   int n_chunks;
   int pid_cap;     // LDS slots for the chunk's block-table entries
   int swizzle;     // 1: chunk-major XCD grouping (see score_tile)
+  int balance;     // 1: group scorer work split evenly over the grid by weighted tiles
 };
 
 hipError_t launch_score_rows(ScoreArgs a, int precision, hipStream_t st);

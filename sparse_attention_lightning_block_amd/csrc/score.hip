@@ -31,6 +31,8 @@
 //    through the scalar cache, for results within ~1e-5 relative.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 #include "nvfp4.hpp"
@@ -42,6 +44,8 @@
 #ifndef SALB_SPLIT_WGS
 #define SALB_SPLIT_WGS 1024
 #endif
+// LDS for the block-table entries of a balanced group-scorer segment.
+constexpr int kBalancePidBytes = 48 * 1024;
 // Rows per workgroup of the group scorer once a call has sixteen rows or more (4 or 8).
 #ifndef SALB_GROUP_ROWS
 #define SALB_GROUP_ROWS 8
@@ -397,44 +401,22 @@ __global__ __launch_bounds__(64 * G) void score_mfma_group_kernel(ScoreArgs a) {
   int* pid = reinterpret_cast<int*>(gbuf + 2 * TILE);                          // [G][pid_cap]
   float* pgs = reinterpret_cast<float*>(pid + G * a.pid_cap);                  // [G][pid_cap]
   __shared__ int s_vend_w[G];
-  __shared__ int s_rows[G];
   __shared__ int s_mismatch;
   __shared__ int s_valid[256];
-
+  __shared__ int s_order[256];
   const int units = (a.T + G - 1) / G;
-  const XcdTile tile = score_tile(a, units);
-  if (tile.chunk >= a.n_chunks) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // ---- the unit's rows: with several units, rows are ranked by valid length so that
-  // each unit holds rows of similar length (one unit takes the rows as they come)
-  int t;
-  if (a.T <= 256 && units > 1) {
-    for (int i = tid; i < a.T; i += NT) s_valid[i] = a.valid_lens[i];
-    if (tid < G) s_rows[tid] = a.T;  // slot past the last row: no row
-    __syncthreads();
-    if (tid < a.T) {
-      const int v = s_valid[tid];
-      int rank = 0;
-      for (int i = 0; i < a.T; ++i) {
-        const int vi = s_valid[i];
-        rank += (vi > v) || (vi == v && i < tid);
-      }
-      if (rank / G == tile.row) s_rows[rank % G] = tid;
-    }
-    __syncthreads();
-    t = s_rows[wave];
-  } else {
-    t = tile.row * G + wave;
-  }
+  // Scores of this wave's row t over keys [s_begin, s_cap); with tail, the part of
+  // that range past the row's valid length gets -inf.  Every wave of the workgroup
+  // calls it with the same key range.
+  auto run_segment = [&](int t, const int s_begin, const int s_cap, const bool tail) {
   // one row per wave: keep the row and its bounds in scalar registers, so that every
   // branch on them below is a scalar branch
   t = __builtin_amdgcn_readfirstlane(t);
   const bool has = t < a.T;
   const int valid = has ? a.valid_lens[t] : 0;
-  const int s_begin = tile.chunk * a.chunk;
-  const int s_lim = a.write_tail ? a.n_cols : valid;
-  const int s_end = has ? min(s_begin + a.chunk, s_lim) : s_begin;
+  const int s_end = !has ? s_begin : tail ? min(s_cap, a.n_cols) : max(s_begin, min(s_cap, valid));
   const int s_vend = max(s_begin, min(s_end, valid));
   float* out_row = a.scores + (int64_t)(has ? t : 0) * a.score_stride;
   for (int s = s_vend + lane; s < s_end; s += 64) out_row[s] = -INFINITY;
@@ -587,6 +569,101 @@ __global__ __launch_bounds__(64 * G) void score_mfma_group_kernel(ScoreArgs a) {
     run_tile(j + 3, R3, G3, R0, G0);
   }
   flush_prev();
+  };
+
+  int64_t lo = 0, hi = 0;  // balanced: this workgroup's stretch of the total weight
+  auto unit_tiles = [&](int u, int& n, int& m) {
+    n = (s_valid[s_order[u * G]] + TILE - 1) / TILE;
+    m = (G > 4 && u * G + 4 < a.T) ? (s_valid[s_order[u * G + 4]] + TILE - 1) / TILE : 0;
+  };
+  if (a.balance) {
+    // Balanced split (at most 256 rows).  Rows are ranked by valid length (clamped to
+    // n_cols) and cut into units of G, so that each unit holds rows of similar length.
+    // A unit's 64-key tiles up to its longest row weigh 2, plus 1 while five rows or
+    // more are still active (those tiles keep two waves busy on some SIMD); the grid
+    // splits the total weight evenly, every workgroup one contiguous stretch of it,
+    // which may run over a few units.
+    for (int i = tid; i < a.T; i += NT) s_valid[i] = min(max(a.valid_lens[i], 0), a.n_cols);
+    __syncthreads();
+    if (tid < a.T) {
+      const int v = s_valid[tid];
+      int rank = 0;
+      for (int i = 0; i < a.T; ++i) {
+        const int vi = s_valid[i];
+        rank += (vi > v) || (vi == v && i < tid);
+      }
+      s_order[rank] = tid;
+    }
+    __syncthreads();
+    int64_t total = 0;
+    for (int u = 0; u < units; ++u) {
+      int n, m;
+      unit_tiles(u, n, m);
+      total += 2 * n + m;
+    }
+    lo = total * blockIdx.x / gridDim.x;
+    hi = total * (blockIdx.x + 1) / gridDim.x;
+  }
+  // first tile of a unit whose weight offset is at least y
+  auto tile_at = [](int64_t y, int n, int m) {
+    const int64_t j = y <= 3 * (int64_t)m ? (y + 2) / 3 : m + (y - 3 * (int64_t)m + 1) / 2;
+    return (int)(j < n ? j : n);
+  };
+  // Segments in turn, through one call site: the chunk of the chunked split (which
+  // also writes its rows' tails), or each unit's part of the balanced stretch.
+  int u_next = 0;
+  int64_t base = 0;
+  for (;;) {
+    int t, s_begin, s_cap;
+    bool tail;
+    if (!a.balance) {
+      if (u_next++ > 0) break;
+      const XcdTile tile = score_tile(a, units);
+      if (tile.chunk >= a.n_chunks) break;
+      t = tile.row * G + wave;
+      s_begin = tile.chunk * a.chunk;
+      s_cap = s_begin + a.chunk;
+      tail = a.write_tail != 0;
+    } else {
+      int j0 = 0, j1 = 0, u = u_next;
+      for (; u < units && base < hi; ++u) {
+        int n, m;
+        unit_tiles(u, n, m);
+        const int64_t w = 2 * n + m;
+        if (base + w > lo) {
+          j0 = tile_at(max(lo - base, (int64_t)0), n, m);
+          j1 = tile_at(min(hi - base, w), n, m);
+        }
+        base += w;
+        if (j1 > j0) break;
+      }
+      if (!(j1 > j0)) break;
+      u_next = u + 1;
+      t = u * G + wave < a.T ? s_order[u * G + wave] : a.T;
+      s_begin = j0 * TILE;
+      s_cap = min(j1 * TILE, s_valid[s_order[u * G]]);
+      tail = false;
+    }
+    run_segment(t, s_begin, s_cap, tail);
+    __syncthreads();  // the LDS of a segment is reused by the next one
+  }
+  if (!a.balance) return;
+  // the rows' -inf tails [valid, n_cols), split evenly over the grid
+  if (a.write_tail) {
+    int64_t tails = 0;
+    for (int r = 0; r < a.T; ++r) tails += a.n_cols - s_valid[r];
+    const int64_t t0 = tails * blockIdx.x / gridDim.x, t1 = tails * (blockIdx.x + 1) / gridDim.x;
+    int64_t c = 0;
+    for (int r = 0; r < a.T && c < t1; ++r) {
+      const int len = a.n_cols - s_valid[r];
+      const int64_t a0 = max(t0, c), a1 = min(t1, c + len);
+      if (a1 > a0) {
+        float* row = a.scores + (int64_t)r * a.score_stride + s_valid[r];
+        for (int64_t i = a0 - c + tid; i < a1 - c; i += NT) row[i] = -INFINITY;
+      }
+      c += len;
+    }
+  }
 }
 
 // ------------------------------------------------------------------ FP32 scorer
@@ -764,7 +841,24 @@ hipError_t launch_score_rows(ScoreArgs a, int precision, hipStream_t st) {
   a.n_chunks = (a.n_cols + a.chunk - 1) / a.chunk;
   a.swizzle = a.n_chunks >= kXcds;
   const int64_t per_unit = a.swizzle ? (int64_t)((a.n_chunks + kXcds - 1) / kXcds) * kXcds : a.n_chunks;
-  const int64_t blocks = per_unit * units;
+  int64_t blocks = per_unit * units;
+  a.balance = 0;
+  if (group && a.T >= 16 && a.T <= 256) {
+    // balanced split (from 16 rows on; fewer rows keep the chunked split, which has
+    // the shorter start-up): the grid shares the rows' weighted 64-key tiles evenly.  Tiles
+    // weigh 2 or 3, so a workgroup's stretch of one unit spans at most half its share
+    // of the weight plus two tiles; the grid grows until that fits the LDS page slots.
+    a.balance = 1;
+    const int64_t tiles = (int64_t)units * ((a.n_cols + 63) / 64);
+    const int64_t weight = tiles * (group == 8 ? 3 : 2);
+    const int64_t max_pid = (int64_t)kBalancePidBytes / (group * 8);
+    const int64_t max_tiles = std::max<int64_t>(3, (max_pid - 2) * a.epb / 64);
+    int64_t nw = std::max<int64_t>(1, std::min<int64_t>(SALB_GROUP_WGS, tiles));
+    auto seg_tiles = [&](int64_t n) { return (weight + n - 1) / n / 2 + 2; };
+    if (seg_tiles(nw) > max_tiles) nw = (weight + 2 * (max_tiles - 2) - 1) / (2 * (max_tiles - 2));
+    a.pid_cap = (int)(seg_tiles(nw) * 64 / a.epb + 2);
+    blocks = nw;
+  }
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (precision == 1) {

@@ -276,6 +276,9 @@ GROUP_SHAPES = [
     (9, 32, 128, 7, "shared"),      # pages not a multiple of 16 keys
     (12, 64, 128, 64, "per_row"),   # rows of different sequences in one group
     (20, 64, 64, 16, "per_row"),
+    (256, 16, 64, 16, "shared"),    # the most rows of the balanced split
+    (257, 16, 64, 16, "shared"),    # one more: the chunked split
+    (40, 32, 128, 1, "shared"),     # one key per page: short balanced segments
 ]
 
 
@@ -283,7 +286,7 @@ GROUP_SHAPES = [
 def test_group_scorer_shapes(T, H, D, epb, table):
     """Rows grouped four or eight to a workgroup, over every key width and head-tile count;
     valid lengths spread so that rows of one group end in different tiles and chunks."""
-    max_lb = -(-3000 // epb)
+    max_lb = -(-(3000 if T < 200 else 700) // epb)
     P = max_lb + 8
     w = csa(f"group_{T}_{D}_{epb}_{table}", [91, T, D], T=T, H=H, D=D, epb=epb, P=P, max_lb=max_lb, top_k=64,
             valid_lens=lambda rng, n: rng.integers(0, max_lb * epb + 1, size=n), dist="gauss", w_scale=1 / H,
