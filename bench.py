@@ -58,11 +58,11 @@ COLD_SPAN_BYTES = 2 * 256 * 2**20
 TRAFFIC_COPY_FACTOR = {"FETCH_SIZE": 1.9998, "WRITE_SIZE": 1.0}
 SCORER_SOURCES = {"csa": ['score.hip', 'nvfp4.hpp', 'common.hpp', 'internal.hpp'], "qsa": ['qsa.hip', 'common.hpp', 'internal.hpp']}
 SCORER_TRAFFIC = {   # workload: (sources, sha, FETCH_SIZE KiB, WRITE_SIZE KiB per dispatch)
-    "decode_T8_S65536": ("csa", "28bc860158dc9676", 3536.7, 2048.1),
-    "long_decode_T32_S262144": ("csa", "28bc860158dc9676", 13712.8, 32768.8),
-    "prefill_T4096": ("csa", "28bc860158dc9676", 35433.1, 65671.1),
-    "qsa_prefill": ("qsa", "e113669cefd0ce62", 163883.1, 262424.0),
-    "hbm_true_T32_S262144": ("csa", "28bc860158dc9676", 228976.1, 32773.0),
+    "decode_T8_S65536": ("csa", "955db9dea3e3b582", 3551.1, 2048.0),
+    "long_decode_T32_S262144": ("csa", "955db9dea3e3b582", 33782.4, 32776.0),
+    "prefill_T4096": ("csa", "955db9dea3e3b582", 35459.9, 65671.1),
+    "qsa_prefill": ("qsa", "11fb9a70e3ef0af4", 163863.7, 262424.0),
+    "hbm_true_T32_S262144": ("csa", "955db9dea3e3b582", 229543.2, 32783.1),
 }
 
 
