@@ -411,164 +411,164 @@ __global__ __launch_bounds__(64 * G) void score_mfma_group_kernel(ScoreArgs a) {
   // that range past the row's valid length gets -inf.  Every wave of the workgroup
   // calls it with the same key range.
   auto run_segment = [&](int t, const int s_begin, const int s_cap, const bool tail) {
-  // one row per wave: keep the row and its bounds in scalar registers, so that every
-  // branch on them below is a scalar branch
-  t = __builtin_amdgcn_readfirstlane(t);
-  const bool has = t < a.T;
-  const int valid = has ? a.valid_lens[t] : 0;
-  const int s_end = !has ? s_begin : tail ? min(s_cap, a.n_cols) : max(s_begin, min(s_cap, valid));
-  const int s_vend = max(s_begin, min(s_end, valid));
-  float* out_row = a.scores + (int64_t)(has ? t : 0) * a.score_stride;
-  for (int s = s_vend + lane; s < s_end; s += 64) out_row[s] = -INFINITY;
+    // one row per wave: keep the row and its bounds in scalar registers, so that every
+    // branch on them below is a scalar branch
+    t = __builtin_amdgcn_readfirstlane(t);
+    const bool has = t < a.T;
+    const int valid = has ? a.valid_lens[t] : 0;
+    const int s_end = !has ? s_begin : tail ? min(s_cap, a.n_cols) : max(s_begin, min(s_cap, valid));
+    const int s_vend = max(s_begin, min(s_end, valid));
+    float* out_row = a.scores + (int64_t)(has ? t : 0) * a.score_stride;
+    for (int s = s_vend + lane; s < s_end; s += 64) out_row[s] = -INFINITY;
 
-  // pages of each row (loads issued before the query's); the row reaching furthest leads
-  const int lb0 = (int)div_epb((uint32_t)s_begin, a.epb_magic);
-  const int np = s_vend > s_begin ? (int)div_epb((uint32_t)(s_vend - 1), a.epb_magic) - lb0 + 1 : 0;
-  int* mypid = pid + wave * a.pid_cap;
-  float* mypgs = pgs + wave * a.pid_cap;
-  const int32_t* bt_row = a.bt + (int64_t)t * a.bt_stride;
-  const int p_first = lane < np ? bt_row[lb0 + lane] : 0;
-  half8v A[MT][KW];
-  float wr[MT][4];
-  load_query<MT, D>(a, t, lane, A, wr);
-  if (lane < np) {
-    mypid[lane] = p_first;
-    mypgs[lane] = a.gscale[p_first];
-  }
-  for (int i = lane + 64; i < np; i += 64) {
-    const int p = bt_row[lb0 + i];
-    mypid[i] = p;
-    mypgs[i] = a.gscale[p];
-  }
-  if (lane == 0) s_vend_w[wave] = s_vend;
-  if (tid == 0) s_mismatch = 0;
-  __syncthreads();
-  int lead = 0, vmax = s_vend_w[0];
+    // pages of each row (loads issued before the query's); the row reaching furthest leads
+    const int lb0 = (int)div_epb((uint32_t)s_begin, a.epb_magic);
+    const int np = s_vend > s_begin ? (int)div_epb((uint32_t)(s_vend - 1), a.epb_magic) - lb0 + 1 : 0;
+    int* mypid = pid + wave * a.pid_cap;
+    float* mypgs = pgs + wave * a.pid_cap;
+    const int32_t* bt_row = a.bt + (int64_t)t * a.bt_stride;
+    const int p_first = lane < np ? bt_row[lb0 + lane] : 0;
+    half8v A[MT][KW];
+    float wr[MT][4];
+    load_query<MT, D>(a, t, lane, A, wr);
+    if (lane < np) {
+      mypid[lane] = p_first;
+      mypgs[lane] = a.gscale[p_first];
+    }
+    for (int i = lane + 64; i < np; i += 64) {
+      const int p = bt_row[lb0 + i];
+      mypid[i] = p;
+      mypgs[i] = a.gscale[p];
+    }
+    if (lane == 0) s_vend_w[wave] = s_vend;
+    if (tid == 0) s_mismatch = 0;
+    __syncthreads();
+    int lead = 0, vmax = s_vend_w[0];
 #pragma unroll
-  for (int w = 1; w < G; ++w)
-    if (s_vend_w[w] > vmax) { vmax = s_vend_w[w]; lead = w; }
-  if (vmax <= s_begin) return;  // no key of this chunk is valid for any of the rows
-  {
-    const int* lp = pid + lead * a.pid_cap;
-    bool diff = false;
-    for (int i = lane; i < np; i += 64) diff |= mypid[i] != lp[i];
-    if (__ballot(diff) != 0ull && lane == 0) s_mismatch = 1;
-  }
-  __syncthreads();
+    for (int w = 1; w < G; ++w)
+      if (s_vend_w[w] > vmax) { vmax = s_vend_w[w]; lead = w; }
+    if (vmax <= s_begin) return;  // no key of this chunk is valid for any of the rows
+    {
+      const int* lp = pid + lead * a.pid_cap;
+      bool diff = false;
+      for (int i = lane; i < np; i += 64) diff |= mypid[i] != lp[i];
+      if (__ballot(diff) != 0ull && lane == 0) s_mismatch = 1;
+    }
+    __syncthreads();
 
-  if (s_mismatch) {  // rows of different sequences: each wave streams its own row
-    wave_stream<MT, D, UPAGE>(a, A, wr, mypid, mypgs, lb0, s_begin, s_vend, 0, 1, out_row, lane);
-    return;
-  }
+    if (s_mismatch) {  // rows of different sequences: each wave streams its own row
+      wave_stream<MT, D, UPAGE>(a, A, wr, mypid, mypgs, lb0, s_begin, s_vend, 0, 1, out_row, lane);
+      return;
+    }
 
-  // ---- shared pages: decode each 64-key tile once into LDS
-  const int* lpid = pid + lead * a.pid_cap;
-  const float* lpgs = pgs + lead * a.pid_cap;
-  const int n_tiles = (vmax - s_begin + TILE - 1) / TILE;
-  // staging: key kt of the tile, slice qs (dims qs*SD .. qs*SD + SD - 1) of it.  Each
-  // group of eight lanes writes eight different keys (same slice), whose LDS rows start
-  // on distinct bank groups (the row pitch is an odd number of 16-byte granules):
-  // conflict-free writes.
-  const int kt = (tid & 7) | ((tid >> (3 + LG)) << 3), qs = (tid >> 3) & (G - 1);
-  // Raw tiles in flight: tile i lives in ring slot i % 4 from its load (issued four
-  // tiles ahead, so that about 18 KB per workgroup are in flight) until its decode,
-  // one tile before it is used.  Loads and decodes past the last tile touch valid
-  // memory and a free buffer; their results are unused.
-  Slice<SD> R0, R1, R2, R3;
-  float G0 = 0.0f, G1 = 0.0f, G2 = 0.0f, G3 = 0.0f;
-  auto load_tile = [&](int j, Slice<SD>& raw, float& graw) {
-    const int s = min(s_begin + j * TILE + kt, vmax - 1);
-    const uint32_t lb = div_epb((uint32_t)s, a.epb_magic);
-    const int p = lpid[(int)lb - lb0];
-    graw = lpgs[(int)lb - lb0];
-    const int64_t e = (int64_t)p * a.epb + (int64_t)((uint32_t)s - lb * (uint32_t)a.epb);
-    load_slice<SD>(raw, a.keys + e * (D / 2) + qs * (SD / 2), a.kscale + e * (D / 16) + (qs * SD) / 16);
-  };
-  // Steps [k0, k1) of this thread's slice of a raw tile into LDS buffer buf.
-  auto decode_part = [&](int buf, const Slice<SD>& raw, float graw, int k0, int k1) {
-    const float sgn = graw < 0.0f ? -1.0f : 1.0f;
-    _Float16* dst = bbuf + (buf * TILE + kt) * BLD + qs * SD;
+    // ---- shared pages: decode each 64-key tile once into LDS
+    const int* lpid = pid + lead * a.pid_cap;
+    const float* lpgs = pgs + lead * a.pid_cap;
+    const int n_tiles = (vmax - s_begin + TILE - 1) / TILE;
+    // staging: key kt of the tile, slice qs (dims qs*SD .. qs*SD + SD - 1) of it.  Each
+    // group of eight lanes writes eight different keys (same slice), whose LDS rows start
+    // on distinct bank groups (the row pitch is an odd number of 16-byte granules):
+    // conflict-free writes.
+    const int kt = (tid & 7) | ((tid >> (3 + LG)) << 3), qs = (tid >> 3) & (G - 1);
+    // Raw tiles in flight: tile i lives in ring slot i % 4 from its load (issued four
+    // tiles ahead, so that about 18 KB per workgroup are in flight) until its decode,
+    // one tile before it is used.  Loads and decodes past the last tile touch valid
+    // memory and a free buffer; their results are unused.
+    Slice<SD> R0, R1, R2, R3;
+    float G0 = 0.0f, G1 = 0.0f, G2 = 0.0f, G3 = 0.0f;
+    auto load_tile = [&](int j, Slice<SD>& raw, float& graw) {
+      const int s = min(s_begin + j * TILE + kt, vmax - 1);
+      const uint32_t lb = div_epb((uint32_t)s, a.epb_magic);
+      const int p = lpid[(int)lb - lb0];
+      graw = lpgs[(int)lb - lb0];
+      const int64_t e = (int64_t)p * a.epb + (int64_t)((uint32_t)s - lb * (uint32_t)a.epb);
+      load_slice<SD>(raw, a.keys + e * (D / 2) + qs * (SD / 2), a.kscale + e * (D / 16) + (qs * SD) / 16);
+    };
+    // Steps [k0, k1) of this thread's slice of a raw tile into LDS buffer buf.
+    auto decode_part = [&](int buf, const Slice<SD>& raw, float graw, int k0, int k1) {
+      const float sgn = graw < 0.0f ? -1.0f : 1.0f;
+      _Float16* dst = bbuf + (buf * TILE + kt) * BLD + qs * SD;
 #pragma unroll
-    for (int kk = k0; kk < k1; ++kk) *reinterpret_cast<half8v*>(dst + kk * 8) = decode_slice<SD>(raw, kk, sgn);
-    if (k1 == SW && qs == 0) gbuf[buf * TILE + kt] = fabsf(graw);
-  };
+      for (int kk = k0; kk < k1; ++kk) *reinterpret_cast<half8v*>(dst + kk * 8) = decode_slice<SD>(raw, kk, sgn);
+      if (k1 == SW && qs == 0) gbuf[buf * TILE + kt] = fabsf(graw);
+    };
 
-  const int col = lane & 15, quarter = lane >> 4;
-  float4v AC0[MT], AC1[MT];
-  zero_acc<MT>(AC1);
-  // Each step leaves one in-lane head sum per lane (its quarter's heads, key column
-  // lane & 15); the four steps of a tile are reduced over the quarters together, so
-  // that lane l ends with key l of the tile (step = lane quarter) and the tile leaves
-  // in one 256-byte store.  Step 3 of a tile is reduced at the start of the next one,
-  // beside its MFMAs.
-  int t_prev = 0x3fffffff;  // previous tile (none yet: its store is masked off)
-  float g_prev = 0.0f;      // |global scale| of key t_prev + lane
-  float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f;
-  auto mfma_step = [&](int buf, int k, float4v (&acc)[MT]) {
-    const _Float16* src = bbuf + (buf * TILE + k * 16 + col) * BLD + quarter * (D / 4);
+    const int col = lane & 15, quarter = lane >> 4;
+    float4v AC0[MT], AC1[MT];
+    zero_acc<MT>(AC1);
+    // Each step leaves one in-lane head sum per lane (its quarter's heads, key column
+    // lane & 15); the four steps of a tile are reduced over the quarters together, so
+    // that lane l ends with key l of the tile (step = lane quarter) and the tile leaves
+    // in one 256-byte store.  Step 3 of a tile is reduced at the start of the next one,
+    // beside its MFMAs.
+    int t_prev = 0x3fffffff;  // previous tile (none yet: its store is masked off)
+    float g_prev = 0.0f;      // |global scale| of key t_prev + lane
+    float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f;
+    auto mfma_step = [&](int buf, int k, float4v (&acc)[MT]) {
+      const _Float16* src = bbuf + (buf * TILE + k * 16 + col) * BLD + quarter * (D / 4);
 #pragma unroll
-    for (int kk = 0; kk < KW; ++kk) {
-      const half8v B = *reinterpret_cast<const half8v*>(src + kk * 8);
+      for (int kk = 0; kk < KW; ++kk) {
+        const half8v B = *reinterpret_cast<const half8v*>(src + kk * 8);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][kk], B, kk == 0 ? float4v{0.f, 0.f, 0.f, 0.f} : acc[mt],
-                                                         0, 0, 0);
-    }
-  };
-  auto flush_prev = [&]() {
-    const float sc = row_transpose_sum4(p0, p1, p2, head_part<MT>(AC1, wr));
-    if (t_prev + lane < s_vend) out_row[t_prev + lane] = g_prev * sc;
-  };
-  // One tile: score tile j from LDS while decoding tile j+1 from its ring slot (`nx`)
-  // into the other buffer and reloading this tile's slot (`mine`) four tiles ahead.
-  auto run_tile = [&](int j, Slice<SD>& mine, float& gmine, const Slice<SD>& nx, float gnx) {
-    __syncthreads();  // tile j decoded; the other buffer is free again
-    const int buf = j & 1;
-    const int t0 = s_begin + j * TILE;
-    // Rows done before the tile (a wave-uniform, scalar condition) skip its MFMAs but
-    // still share the decode and the loads, which run in one fixed order on every
-    // path: the outstanding loads are then the same wherever the waits are placed.
-    const bool act = t0 < s_vend;
-    float g_lane = 0.0f;
-    if (act) {
-      g_lane = gbuf[buf * TILE + lane];
-      mfma_step(buf, 0, AC0);
-      flush_prev();
-    }
-    decode_part(buf ^ 1, nx, gnx, 0, SW / 2);
-    if (act) {
-      mfma_step(buf, 1, AC1);
-      p0 = head_part<MT>(AC0, wr);
-    }
-    decode_part(buf ^ 1, nx, gnx, SW / 2, SW);
-    if (act) {
-      mfma_step(buf, 2, AC0);
-      p1 = head_part<MT>(AC1, wr);
-    }
-    load_tile(j + 4, mine, gmine);
-    if (act) {
-      mfma_step(buf, 3, AC1);
-      p2 = head_part<MT>(AC0, wr);
-      t_prev = t0;
-      g_prev = g_lane;
-    }
-  };
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              A[mt][kk], B, kk == 0 ? float4v{0.f, 0.f, 0.f, 0.f} : acc[mt], 0, 0, 0);
+      }
+    };
+    auto flush_prev = [&]() {
+      const float sc = row_transpose_sum4(p0, p1, p2, head_part<MT>(AC1, wr));
+      if (t_prev + lane < s_vend) out_row[t_prev + lane] = g_prev * sc;
+    };
+    // One tile: score tile j from LDS while decoding tile j+1 from its ring slot (`nx`)
+    // into the other buffer and reloading this tile's slot (`mine`) four tiles ahead.
+    auto run_tile = [&](int j, Slice<SD>& mine, float& gmine, const Slice<SD>& nx, float gnx) {
+      __syncthreads();  // tile j decoded; the other buffer is free again
+      const int buf = j & 1;
+      const int t0 = s_begin + j * TILE;
+      // Rows done before the tile (a wave-uniform, scalar condition) skip its MFMAs but
+      // still share the decode and the loads, which run in one fixed order on every
+      // path: the outstanding loads are then the same wherever the waits are placed.
+      const bool act = t0 < s_vend;
+      float g_lane = 0.0f;
+      if (act) {
+        g_lane = gbuf[buf * TILE + lane];
+        mfma_step(buf, 0, AC0);
+        flush_prev();
+      }
+      decode_part(buf ^ 1, nx, gnx, 0, SW / 2);
+      if (act) {
+        mfma_step(buf, 1, AC1);
+        p0 = head_part<MT>(AC0, wr);
+      }
+      decode_part(buf ^ 1, nx, gnx, SW / 2, SW);
+      if (act) {
+        mfma_step(buf, 2, AC0);
+        p1 = head_part<MT>(AC1, wr);
+      }
+      load_tile(j + 4, mine, gmine);
+      if (act) {
+        mfma_step(buf, 3, AC1);
+        p2 = head_part<MT>(AC0, wr);
+        t_prev = t0;
+        g_prev = g_lane;
+      }
+    };
 
-  load_tile(0, R0, G0);
-  load_tile(1, R1, G1);
-  load_tile(2, R2, G2);
-  load_tile(3, R3, G3);
-  decode_part(0, R0, G0, 0, SW);
-  for (int j = 0; j < n_tiles; j += 4) {
-    run_tile(j, R0, G0, R1, G1);
-    if (j + 1 >= n_tiles) break;
-    run_tile(j + 1, R1, G1, R2, G2);
-    if (j + 2 >= n_tiles) break;
-    run_tile(j + 2, R2, G2, R3, G3);
-    if (j + 3 >= n_tiles) break;
-    run_tile(j + 3, R3, G3, R0, G0);
-  }
-  flush_prev();
+    load_tile(0, R0, G0);
+    load_tile(1, R1, G1);
+    load_tile(2, R2, G2);
+    load_tile(3, R3, G3);
+    decode_part(0, R0, G0, 0, SW);
+    for (int j = 0; j < n_tiles; j += 4) {
+      run_tile(j, R0, G0, R1, G1);
+      if (j + 1 >= n_tiles) break;
+      run_tile(j + 1, R1, G1, R2, G2);
+      if (j + 2 >= n_tiles) break;
+      run_tile(j + 2, R2, G2, R3, G3);
+      if (j + 3 >= n_tiles) break;
+      run_tile(j + 3, R3, G3, R0, G0);
+    }
+    flush_prev();
   };
 
   int64_t lo = 0, hi = 0;  // balanced: this workgroup's stretch of the total weight
