@@ -303,3 +303,22 @@ def test_group_scorer_shapes(T, H, D, epb, table):
         check_scores(gr[t], ref[t], amag[t], "mfma", f"group shape t{t}")
         assert np.all(np.isneginf(gr[t, v:])), "tail must be -inf"
         check_topk(gi[t], gv[t], ref[t], amag[t], 64, "mfma", f"group shape t{t}")
+
+
+def test_fused_entry_balanced_split():
+    """The fused entry at 40 rows (the balanced split, no -inf tails written): equal to
+    indexer_score_rows + indexer_topk_select, and to the oracle within tolerance."""
+    T, epb = 40, 64
+    max_lb = 50
+    w = csa("fused_balanced", [92], T=T, H=64, D=128, epb=epb, P=max_lb + 8, max_lb=max_lb, top_k=256,
+            valid_lens=lambda rng, n: rng.integers(0, max_lb * epb + 1, size=n), dist="gauss", w_scale=1 / 64)
+    d = to_dev(w)
+    a_idx, a_val = salb.indexer_score_topk(**d, top_k=256, precision="mfma", with_scores=True)
+    rows = salb.indexer_score_rows(**d, n_cols=max_lb * epb, precision="mfma")
+    b_idx, b_val = salb.indexer_topk_select(rows, 256, valid_lens=d["valid_lens"], with_scores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a_idx, b_idx) and torch.equal(a_val.view(torch.int32), b_val.view(torch.int32))
+    ref, amag = oracle_rows(w)
+    gi, gv = _row(a_idx), _row(a_val)
+    for t in range(T):
+        check_topk(gi[t], gv[t], ref[t], amag[t], 256, "mfma", f"fused balanced t{t}")
