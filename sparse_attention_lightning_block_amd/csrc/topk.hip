@@ -51,6 +51,8 @@ constexpr int kRowMax = 32 * kRowThreads;  // 8192: one-workgroup rows
 constexpr int kRowThreadsWide = 1024;
 constexpr int kRowMaxWide = 32 * kRowThreadsWide;  // 32768
 constexpr int kWideRowsMin = 256;
+constexpr int kRowThreadsLds = 512;    // persistent rows kept in LDS: 64 entries per thread
+constexpr int kPersistentWgs = 256;    // one workgroup per CU (the row fills its LDS)
 constexpr int kBucketMax = 48;           // crowded bucket: sorting network instead
 constexpr int kHistCopies = kXcds;       // one global histogram per XCD
 constexpr int kMaxWaves = kFinalThreads / kWave;
@@ -468,8 +470,11 @@ __global__ __launch_bounds__(NT) void select_rows_kernel(SelArgs a) {
   finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, mx, mn, sh, kbase);
 }
 
-// Rows too long for registers (up to 32768 entries), one workgroup each.  The row's
-// order keys go to LDS once, with their range.  One histogram pass over a 12-bit
+// Rows too long for registers (up to 32768 entries), one at a time per workgroup
+// (a persistent grid, one workgroup per CU, each taking every grid-th row, longest
+// first).  While a row is selected, the loads of the workgroup's next row are in
+// flight into registers (64 entries per thread).  The row's order keys go to LDS once,
+// with their range.  One histogram pass over a 12-bit
 // digit of the key relative to the row's smallest (the digit spans the row's actual
 // range) finds the bin of the K-th entry; the entries from that bin up -- K plus the
 // rest of the bin -- are compacted into an LDS candidate list, where the radix select
@@ -477,136 +482,138 @@ __global__ __launch_bounds__(NT) void select_rows_kernel(SelArgs a) {
 // back to radix passes over the whole row.  Thread t owns the runs of four entries
 // 4 (t + m NT) .. + 3 of the LDS row, read as 16-byte words, eight in flight per pass.
 template <int NT>
-__global__ __launch_bounds__(NT) void select_rows_lds_kernel(SelArgs a) {
+__global__ __launch_bounds__(NT) void select_rows_lds_kernel(SelArgs a, int rows) {
+  constexpr int PF = kRowMaxWide / NT;  // a row's entries per thread
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ SelShared sh;
   __shared__ uint32_t s_kmx[NT / kWave], s_kmn[NT / kWave];
-  const int row = gridDim.x - 1 - blockIdx.x;  // causal rows grow with the index: longest first
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int n = row_valid(a, row);
-  const int K = n < a.top_k ? n : a.top_k;
-  const float* src = a.scores + (int64_t)row * a.score_stride;
-  const size_t key_bytes = row_keys_lds_bytes(a.n_cols);
+  const size_t key_bytes = row_keys_lds_bytes(kRowMaxWide);
   uint32_t* lkey = reinterpret_cast<uint32_t*>(smem);
   uint64_t* cand = reinterpret_cast<uint64_t*>(smem + key_bytes);
   FinishLds f = carve(smem + key_bytes + (size_t)a.cand_cap * 8, a.top_k);
 
-  // the row's keys into LDS, eight loads in flight per thread, and their range
-  uint32_t kmx = 0u, kmn = ~0u;
-  {
-    int e = tid;
-    for (; e + 7 * NT < n; e += 8 * NT) {
-      float x[8];
+  float x[PF];  // the next row, entry i * NT + tid in x[i]
+  auto fetch = [&](int r) {
+    const int nr = row_valid(a, r);
+    const float* src = a.scores + (int64_t)r * a.score_stride;
+    const int last = nr > 0 ? nr - 1 : 0;  // past the valid entries: re-read valid memory
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = src[e + i * NT];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t k = ord_key(x[i]);
-        lkey[e + i * NT] = k;
-        kmx = k > kmx ? k : kmx;
-        kmn = k < kmn ? k : kmn;
-      }
-    }
-    for (; e < n; e += NT) {
-      const uint32_t k = ord_key(src[e]);
-      lkey[e] = k;
-      kmx = k > kmx ? k : kmx;
-      kmn = k < kmn ? k : kmn;
-    }
-  }
-  kmx = wave_max(kmx);
-  kmn = ~wave_max(~kmn);
-  if (lane == 0) {
-    s_kmx[wave] = kmx;
-    s_kmn[wave] = kmn;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < NT / kWave; ++w) {
-    kmx = s_kmx[w] > kmx ? s_kmx[w] : kmx;
-    kmn = s_kmn[w] < kmn ? s_kmn[w] : kmn;
-  }
-  auto each_key = [&](auto&& fn) {
-    const uint4* lk4 = reinterpret_cast<const uint4*>(lkey);
-    for (int m0 = 0; m0 * 4 * NT < n; m0 += 8) {
-      uint4 v[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int w = (m0 + m) * NT + tid;
-        v[m] = 4 * w < n ? lk4[w] : uint4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int e = 4 * ((m0 + m) * NT + tid);
-        if (e < n) fn(v[m].x, e);
-        if (e + 1 < n) fn(v[m].y, e + 1);
-        if (e + 2 < n) fn(v[m].z, e + 2);
-        if (e + 3 < n) fn(v[m].w, e + 3);
-      }
-    }
+    for (int i = 0; i < PF; ++i) x[i] = src[min(i * NT + tid, last)];
   };
-  const uint32_t kbase = kmn;
-  auto each_row = [&](auto&& fn) { each_key([&](uint32_t k, int e) { fn(composite(k - kbase, (uint32_t)e)); }); };
-  int C = -1;  // candidates in the list (-1: the whole row is the candidate set)
-  auto each_cand = [&](auto&& fn) {
-    for (int i = tid; i < C; i += NT) fn(cand[i]);
-  };
-  uint64_t thr = 0ull;
-  if (K < n) {
-    const uint32_t span = kmx - kbase;
-    const int bits = span ? 32 - __clz(span) : 1;
-    const int shift = bits > kDigit ? bits - kDigit : 0;
-    clear_bins<NT>(f.hist);
-    if (tid == 0) sh.fill = 0u;
+  if ((int)blockIdx.x >= rows) return;
+  fetch(rows - 1 - (int)blockIdx.x);
+  for (int idx = blockIdx.x; idx < rows; idx += gridDim.x) {
+    const int row = rows - 1 - idx;  // causal rows grow with the index: longest first
+    const int n = row_valid(a, row);
+    const int K = n < a.top_k ? n : a.top_k;
+    __syncthreads();  // the previous row is done with the LDS
+
+    // the row's keys into LDS (slots past n hold values never read) and their range
+    uint32_t kmx = 0u, kmn = ~0u;
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const uint32_t k = ord_key(x[i]);
+      lkey[i * NT + tid] = k;
+      const bool v = i * NT + tid < n;
+      kmx = v && k > kmx ? k : kmx;
+      kmn = v && k < kmn ? k : kmn;
+    }
+    if (idx + (int)gridDim.x < rows) fetch(rows - 1 - (idx + (int)gridDim.x));
+    kmx = wave_max(kmx);
+    kmn = ~wave_max(~kmn);
+    if (lane == 0) {
+      s_kmx[wave] = kmx;
+      s_kmn[wave] = kmn;
+    }
     __syncthreads();
-    each_key([&](uint32_t k, int) { atomicAdd(&f.hist[(k - kbase) >> shift], 1u); });
-    __syncthreads();
-    uint32_t h[kBins / NT];
-    load_bins<NT>(f.hist, h);
-    find_digit<NT>(h, (uint32_t)K, sh);
-    const uint32_t b1 = sh.digit, gt = sh.gt, cnt = sh.cnt;
-    const uint64_t prefix = (uint64_t)b1 << (32 + shift);
-    if (gt + cnt <= (uint32_t)a.cand_cap) {
-      const uint32_t kthr = kbase + (b1 << shift);  // smallest key of bin b1
-      each_key([&](uint32_t k, int e) {
-        if (k >= kthr) cand[atomicAdd(&sh.fill, 1u)] = composite(k - kbase, (uint32_t)e);
-      });
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) {
+      kmx = s_kmx[w] > kmx ? s_kmx[w] : kmx;
+      kmn = s_kmn[w] < kmn ? s_kmn[w] : kmn;
+    }
+    auto each_key = [&](auto&& fn) {
+      const uint4* lk4 = reinterpret_cast<const uint4*>(lkey);
+      for (int m0 = 0; m0 * 4 * NT < n; m0 += 8) {
+        uint4 v[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int w = (m0 + m) * NT + tid;
+          v[m] = 4 * w < n ? lk4[w] : uint4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int e = 4 * ((m0 + m) * NT + tid);
+          if (e < n) fn(v[m].x, e);
+          if (e + 1 < n) fn(v[m].y, e + 1);
+          if (e + 2 < n) fn(v[m].z, e + 2);
+          if (e + 3 < n) fn(v[m].w, e + 3);
+        }
+      }
+    };
+    const uint32_t kbase = kmn;
+    auto each_row = [&](auto&& fn) { each_key([&](uint32_t k, int e) { fn(composite(k - kbase, (uint32_t)e)); }); };
+    int C = -1;  // candidates in the list (-1: the whole row is the candidate set)
+    auto each_cand = [&](auto&& fn) {
+      for (int i = tid; i < C; i += NT) fn(cand[i]);
+    };
+    uint64_t thr = 0ull;
+    if (K < n) {
+      const uint32_t span = kmx - kbase;
+      const int bits = span ? 32 - __clz(span) : 1;
+      const int shift = bits > kDigit ? bits - kDigit : 0;
+      clear_bins<NT>(f.hist);
+      if (tid == 0) sh.fill = 0u;
       __syncthreads();
-      C = (int)(gt + cnt);
-      if (gt + cnt == (uint32_t)K)
-        thr = prefix;  // the bin is taken whole
+      each_key([&](uint32_t k, int) { atomicAdd(&f.hist[(k - kbase) >> shift], 1u); });
+      __syncthreads();
+      uint32_t h[kBins / NT];
+      load_bins<NT>(f.hist, h);
+      find_digit<NT>(h, (uint32_t)K, sh);
+      const uint32_t b1 = sh.digit, gt = sh.gt, cnt = sh.cnt;
+      const uint64_t prefix = (uint64_t)b1 << (32 + shift);
+      if (gt + cnt <= (uint32_t)a.cand_cap) {
+        const uint32_t kthr = kbase + (b1 << shift);  // smallest key of bin b1
+        each_key([&](uint32_t k, int e) {
+          if (k >= kthr) cand[atomicAdd(&sh.fill, 1u)] = composite(k - kbase, (uint32_t)e);
+        });
+        __syncthreads();
+        C = (int)(gt + cnt);
+        if (gt + cnt == (uint32_t)K)
+          thr = prefix;  // the bin is taken whole
+        else
+          thr = radix_select<NT>(each_cand, prefix, (uint64_t)(kBins - 1) << (32 + shift), (uint32_t)K - gt,
+                                 31 + shift, f.hist, sh);
+      } else {
+        thr = radix_select<NT>(each_row, prefix, (uint64_t)(kBins - 1) << (32 + shift), (uint32_t)K - gt, 31 + shift,
+                               f.hist, sh);
+      }
+    }
+    // gather the winners
+    auto each = [&](auto&& fn) {
+      if (C >= 0)
+        each_cand(fn);
       else
-        thr = radix_select<NT>(each_cand, prefix, (uint64_t)(kBins - 1) << (32 + shift), (uint32_t)K - gt,
-                               31 + shift, f.hist, sh);
-    } else {
-      thr = radix_select<NT>(each_row, prefix, (uint64_t)(kBins - 1) << (32 + shift), (uint32_t)K - gt, 31 + shift,
-                             f.hist, sh);
-    }
+        each_row(fn);
+    };
+    uint32_t mine = 0;
+    uint64_t mx = 0ull, mn = ~0ull;
+    each([&](uint64_t c) {
+      if (c >= thr) {
+        ++mine;
+        mx = c > mx ? c : mx;
+        mn = c < mn ? c : mn;
+      }
+    });
+    uint32_t off = block_suffix_minmax<NT>(mine, mx, mn, sh);
+    each([&](uint64_t c) {
+      if (c >= thr && off < (uint32_t)K) f.sortbuf[off++] = c;  // exactly K are selected
+    });
+    __syncthreads();
+    int32_t* oi = a.out_idx + (int64_t)row * a.top_k;
+    float* os = a.out_scores ? a.out_scores + (int64_t)row * a.top_k : nullptr;
+    finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, mx, mn, sh, kbase);
   }
-  // gather the winners
-  auto each = [&](auto&& fn) {
-    if (C >= 0)
-      each_cand(fn);
-    else
-      each_row(fn);
-  };
-  uint32_t mine = 0;
-  uint64_t mx = 0ull, mn = ~0ull;
-  each([&](uint64_t c) {
-    if (c >= thr) {
-      ++mine;
-      mx = c > mx ? c : mx;
-      mn = c < mn ? c : mn;
-    }
-  });
-  uint32_t off = block_suffix_minmax<NT>(mine, mx, mn, sh);
-  each([&](uint64_t c) {
-    if (c >= thr && off < (uint32_t)K) f.sortbuf[off++] = c;  // exactly K are selected
-  });
-  __syncthreads();
-  int32_t* oi = a.out_idx + (int64_t)row * a.top_k;
-  float* os = a.out_scores ? a.out_scores + (int64_t)row * a.top_k : nullptr;
-  finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, mx, mn, sh, kbase);
 }
 
 // ------------------------------------------------------------------ long rows
@@ -896,11 +903,11 @@ bool plan_select(int rows, int n_cols, int top_k, SelectPlan* p) {
     p->chunks = 1;
     p->bytes = 0;
   } else if (rows >= kWideRowsMin && n_cols <= kRowMaxWide &&
-             p->lds + row_keys_lds_bytes(n_cols) + kStaticLdsReserve <= kLdsMax) {
-    p->two_pass = 0;  // 1024 threads, the row's keys in LDS, then a candidate list
-    p->row_nt = kRowThreadsWide;
+             p->lds + row_keys_lds_bytes(kRowMaxWide) + kStaticLdsReserve <= kLdsMax) {
+    p->two_pass = 0;  // persistent workgroups, the row's keys in LDS, then a candidate list
+    p->row_nt = kRowThreadsLds;
     p->per = 0;
-    const size_t fixed = p->lds + row_keys_lds_bytes(n_cols);
+    const size_t fixed = p->lds + row_keys_lds_bytes(kRowMaxWide);
     const size_t cap = (kLdsMax - kStaticLdsReserve - fixed) / 8;
     p->cand_cap = (int)(cap < (size_t)kRowMaxWide ? cap : (size_t)kRowMaxWide) & ~1;  // keeps 16-byte alignment
     p->lds = fixed + (size_t)p->cand_cap * 8;
@@ -945,7 +952,8 @@ template <int NT>
 static hipError_t launch_rows_lds(const SelArgs& a, const SelectPlan& p, hipStream_t st) {
   hipError_t e = set_lds(select_rows_lds_kernel<NT>, p.lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((select_rows_lds_kernel<NT>), dim3(p.rows), dim3(NT), p.lds, st, a);
+  const int grid = p.rows < kPersistentWgs ? p.rows : kPersistentWgs;
+  hipLaunchKernelGGL((select_rows_lds_kernel<NT>), dim3(grid), dim3(NT), p.lds, st, a, p.rows);
   return hipGetLastError();
 }
 
@@ -984,8 +992,8 @@ hipError_t launch_select(const SelectPlan& p, const float* scores, int64_t score
   a.out_scores = out_scores;
   a.cand_cap = p.cand_cap;
   if (!p.two_pass) {
-    if (p.row_nt == kRowThreadsWide)
-      return p.per == 16 ? launch_rows<kRowThreadsWide, 16>(a, p, st) : launch_rows_lds<kRowThreadsWide>(a, p, st);
+    if (p.row_nt == kRowThreadsLds) return launch_rows_lds<kRowThreadsLds>(a, p, st);
+    if (p.row_nt == kRowThreadsWide) return launch_rows<kRowThreadsWide, 16>(a, p, st);
     switch (p.per) {
       case 4: return launch_rows<kRowThreads, 4>(a, p, st);
       case 8: return launch_rows<kRowThreads, 8>(a, p, st);
