@@ -263,6 +263,45 @@ __device__ uint64_t radix_select(Each each, uint64_t prefix, uint64_t mask, uint
   }
 }
 
+// Radix select on 32-bit values: the digit walk for the rem-th largest value, which
+// stops at the first digit whose bin holds exactly the remaining count (every value in
+// that bin wins) or after the last bit.  On return `thr` has zero bits below the last
+// digit taken and `gt_all` counts the values above its bin.  With `whole` set the
+// winners are exactly the values >= thr; otherwise thr is the rem-th largest value
+// itself and more values equal it than win (ties the caller breaks by index).  Digits
+// are 12 bits wide, from bit `top` down.
+template <int NT, typename Each>
+__device__ void radix_select32(Each each, uint32_t rem, int top, uint32_t* hist, SelShared& sh, uint32_t& thr,
+                               uint32_t& gt_all, bool& whole) {
+  uint32_t prefix = 0u, mask = 0u;
+  gt_all = 0u;
+  for (;;) {
+    const int width = top + 1 < kDigit ? top + 1 : kDigit;
+    const int shift = top + 1 - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    clear_bins<NT>(hist);
+    __syncthreads();
+    each([&](uint32_t r) {
+      if ((r & mask) == prefix) atomicAdd(&hist[(r >> shift) & dmask], 1u);
+    });
+    __syncthreads();
+    uint32_t h[kBins / NT];
+    load_bins<NT>(hist, h);
+    find_digit<NT>(h, rem, sh);
+    const uint32_t digit = sh.digit, gt = sh.gt, cnt = sh.cnt;
+    prefix |= digit << shift;
+    mask |= dmask << shift;
+    rem -= gt;
+    gt_all += gt;
+    if (cnt == rem || shift == 0) {
+      thr = prefix;
+      whole = cnt == rem;
+      return;
+    }
+    top = shift - 1;
+  }
+}
+
 // Descending bitonic sort of buf[0, n2) (n2 a power of two) by the whole block.
 template <int NT>
 __device__ void bitonic_desc(uint64_t* buf, int n2) {
@@ -406,7 +445,7 @@ __device__ __forceinline__ FinishLds carve(unsigned char* smem, int top_k) {
 // One workgroup per row; entry e of the row sits in register i of thread t with
 // e = i * NT + t (coalesced loads).
 template <int NT, int PER>
-__global__ __launch_bounds__(NT) void select_rows_kernel(SelArgs a) {
+__global__ __launch_bounds__(NT, (NT == kRowThreads && PER <= 16) ? 5 : 1) void select_rows_kernel(SelArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ SelShared sh;
   const int row = gridDim.x - 1 - blockIdx.x;  // causal rows grow with the index: longest first
@@ -422,9 +461,12 @@ __global__ __launch_bounds__(NT) void select_rows_kernel(SelArgs a) {
     const int e = i * NT + tid;
     key[i] = e < n ? ord_key(src[e]) : 0u;
   }
+  // registers past the row's last entry are skipped on a wave-uniform branch: a short
+  // row costs passes over its own length, not over the workgroup's capacity
   auto each_key = [&](auto&& fn) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
+      if (i * NT >= n) break;
       const int e = i * NT + tid;
       if (e < n) fn(key[i], e);
     }
@@ -432,38 +474,69 @@ __global__ __launch_bounds__(NT) void select_rows_kernel(SelArgs a) {
   // The row's keys are taken relative to its smallest one, and the radix starts at the
   // highest bit in which any two differ: the first digit then splits the row's actual
   // range (a row of close scores would otherwise crowd a few bins of the first digit,
-  // and its LDS atomics with them).
-  uint32_t kbase = 0u;
-  int top = 63;
+  // and its LDS atomics with them).  The walk runs on the 32-bit keys; the entry index
+  // only enters when equal scores straddle the K-th position.
+  uint32_t kbase = 0u, thr32 = 0u, gt = 0u;
+  bool whole = true;  // the winners are exactly the keys >= kbase + thr32
   if (K < n) {
-    uint64_t kmx = 0ull, kmn = ~0ull;
+    uint32_t kmx32 = 0u, kmn32 = ~0u;
     each_key([&](uint32_t k, int) {
-      kmx = k > kmx ? k : kmx;
-      kmn = k < kmn ? k : kmn;
+      kmx32 = k > kmx32 ? k : kmx32;
+      kmn32 = k < kmn32 ? k : kmn32;
     });
+    uint64_t kmx = kmx32, kmn = kmn32;
     block_suffix_minmax<NT>(0u, kmx, kmn, sh);
     __syncthreads();  // sh is used again below
     kbase = (uint32_t)kmn;
     const uint32_t span = (uint32_t)kmx - kbase;
-    top = 32 + (span ? 31 - __clz(span) : 0);
+    const int top = span ? 31 - __clz(span) : 0;
+    radix_select32<NT>([&](auto&& fn) { each_key([&](uint32_t k, int) { fn(k - kbase); }); }, (uint32_t)K, top,
+                       f.hist, sh, thr32, gt, whole);
   }
   auto each = [&](auto&& fn) { each_key([&](uint32_t k, int e) { fn(composite(k - kbase, (uint32_t)e)); }); };
-  uint64_t thr = 0ull;
-  if (K < n) thr = radix_select<NT>(each, 0ull, 0ull, (uint32_t)K, top, f.hist, sh);
-  // gather the winners
-  uint32_t mine = 0;
-  uint64_t mx = 0ull, mn = ~0ull;
-  each([&](uint64_t c) {
-    if (c >= thr) {
-      ++mine;
-      mx = c > mx ? c : mx;
-      mn = c < mn ? c : mn;
+  uint32_t off;
+  uint64_t mx, mn;
+  if (whole) {
+    // gather the winners on the 32-bit keys; the bounds handed to the sort are widened
+    // over the index bits (every winner's composite lies between them)
+    uint32_t mine = 0, rmx = 0u, rmn = ~0u;
+    each_key([&](uint32_t k, int) {
+      const uint32_t r = k - kbase;
+      if (r >= thr32) {
+        ++mine;
+        rmx = r > rmx ? r : rmx;
+        rmn = r < rmn ? r : rmn;
+      }
+    });
+    mx = ((uint64_t)rmx << 32) | 0xffffffffull;
+    mn = (uint64_t)rmn << 32;
+    if (mine == 0) {  // neutral elements for the block reduction
+      mx = 0ull;
+      mn = ~0ull;
     }
-  });
-  uint32_t off = block_suffix_minmax<NT>(mine, mx, mn, sh);
-  each([&](uint64_t c) {
-    if (c >= thr && off < (uint32_t)K) f.sortbuf[off++] = c;  // exactly K are selected
-  });
+    off = block_suffix_minmax<NT>(mine, mx, mn, sh);
+    each_key([&](uint32_t k, int e) {
+      if (k - kbase >= thr32 && off < (uint32_t)K) f.sortbuf[off++] = composite(k - kbase, (uint32_t)e);
+    });
+  } else {
+    // equal keys at the K-th position: the lowest indices among them win
+    const uint64_t thr = radix_select<NT>(each, (uint64_t)thr32 << 32, 0xffffffff00000000ull, (uint32_t)K - gt,
+                                          31, f.hist, sh);
+    uint32_t mine = 0;
+    mx = 0ull;
+    mn = ~0ull;
+    each([&](uint64_t c) {
+      if (c >= thr) {
+        ++mine;
+        mx = c > mx ? c : mx;
+        mn = c < mn ? c : mn;
+      }
+    });
+    off = block_suffix_minmax<NT>(mine, mx, mn, sh);
+    each([&](uint64_t c) {
+      if (c >= thr && off < (uint32_t)K) f.sortbuf[off++] = c;  // exactly K are selected
+    });
+  }
   __syncthreads();
   int32_t* oi = a.out_idx + (int64_t)row * a.top_k;
   float* os = a.out_scores ? a.out_scores + (int64_t)row * a.top_k : nullptr;
@@ -824,8 +897,10 @@ __global__ __launch_bounds__(NT) void select_final_kernel(SelArgs a) {
   auto each = [&](auto&& fn) {
     if (in_regs) {
 #pragma unroll
-      for (int r = 0; r < PER; ++r)
+      for (int r = 0; r < PER; ++r) {
+        if (r * NT >= C) break;  // wave-uniform: only the registers that hold candidates
         if (r * NT + tid < C) fn(v[r]);
+      }
     } else {
       for (int c = 0; c < nch; ++c) {
         const int m = (int)(off[c + 1] - off[c]);
