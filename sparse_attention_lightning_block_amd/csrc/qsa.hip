@@ -361,15 +361,14 @@ __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const float
   // multiply one LDS tile, reduce the heads, write the scores
   auto do_tile = [&](int buf, int64_t k0) {
     float4v acc[4][4];
-    // every B operand of the tile is read from LDS up front (one wait), then the
-    // MFMAs run back to back; the scheduler may not move the reads between them
+    // every B operand of the tile is read from LDS up front; the compiler places the
+    // waits, so the later reads complete under the first MFMAs
     half8v B[KW][4];
 #pragma unroll
     for (int kk = 0; kk < KW; ++kk)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
         B[kk][nt] = *reinterpret_cast<const half8v*>(&kb[buf][(16 * nt + col) * BLD + 32 * kk + 8 * quarter]);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < KW; ++kk)
 #pragma unroll
@@ -378,7 +377,6 @@ __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const float
         for (int nt = 0; nt < 4; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
               A[mt][kk], B[kk][nt], kk == 0 ? float4v{0.0f, 0.0f, 0.0f, 0.0f} : acc[mt][nt], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
     // ReLU and head sum: lane (quarter, col) holds heads 4*quarter + i of each M tile
     // for key 16 * nt + col.  The in-lane sums of the four N tiles are then reduced over
     // the quarters so that quarter q keeps N tile q: lane (quarter, col) ends with key

@@ -504,16 +504,22 @@ __global__ __launch_bounds__(64 * G) void score_mfma_group_kernel(ScoreArgs a) {
     int t_prev = 0x3fffffff;  // previous tile (none yet: its store is masked off)
     float g_prev = 0.0f;      // |global scale| of key t_prev + lane
     float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f;
-    auto mfma_step = [&](int buf, int k, float4v (&acc)[MT]) {
+    // B operands of step k, read from LDS one step before their MFMAs: the reads of
+    // step k+1 are in flight while step k multiplies (only step 0 of a tile, which
+    // follows the barrier, waits for its own reads).
+    half8v BA[KW], BB[KW];
+    auto read_b = [&](int buf, int k, half8v (&B)[KW]) {
       const _Float16* src = bbuf + (buf * TILE + k * 16 + col) * BLD + quarter * (D / 4);
 #pragma unroll
-      for (int kk = 0; kk < KW; ++kk) {
-        const half8v B = *reinterpret_cast<const half8v*>(src + kk * 8);
+      for (int kk = 0; kk < KW; ++kk) B[kk] = *reinterpret_cast<const half8v*>(src + kk * 8);
+    };
+    auto mfma_step = [&](const half8v (&B)[KW], float4v (&acc)[MT]) {
+#pragma unroll
+      for (int kk = 0; kk < KW; ++kk)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              A[mt][kk], B, kk == 0 ? float4v{0.f, 0.f, 0.f, 0.f} : acc[mt], 0, 0, 0);
-      }
+              A[mt][kk], B[kk], kk == 0 ? float4v{0.f, 0.f, 0.f, 0.f} : acc[mt], 0, 0, 0);
     };
     auto flush_prev = [&]() {
       const float sc = row_transpose_sum4(p0, p1, p2, head_part<MT>(AC1, wr));
@@ -532,22 +538,26 @@ __global__ __launch_bounds__(64 * G) void score_mfma_group_kernel(ScoreArgs a) {
       float g_lane = 0.0f;
       if (act) {
         g_lane = gbuf[buf * TILE + lane];
-        mfma_step(buf, 0, AC0);
+        read_b(buf, 0, BA);
+        read_b(buf, 1, BB);
+        mfma_step(BA, AC0);
         flush_prev();
       }
       decode_part(buf ^ 1, nx, gnx, 0, SW / 2);
       if (act) {
-        mfma_step(buf, 1, AC1);
+        read_b(buf, 2, BA);
+        mfma_step(BB, AC1);
         p0 = head_part<MT>(AC0, wr);
       }
       decode_part(buf ^ 1, nx, gnx, SW / 2, SW);
       if (act) {
-        mfma_step(buf, 2, AC0);
+        read_b(buf, 3, BB);
+        mfma_step(BA, AC0);
         p1 = head_part<MT>(AC1, wr);
       }
       load_tile(j + 4, mine, gmine);
       if (act) {
-        mfma_step(buf, 3, AC1);
+        mfma_step(BB, AC1);
         p2 = head_part<MT>(AC0, wr);
         t_prev = t0;
         g_prev = g_lane;
