@@ -58,11 +58,12 @@ COLD_SPAN_BYTES = 2 * 256 * 2**20
 TRAFFIC_COPY_FACTOR = {"FETCH_SIZE": 1.9998, "WRITE_SIZE": 1.0}
 SCORER_SOURCES = {"csa": ['score.hip', 'nvfp4.hpp', 'common.hpp', 'internal.hpp'], "qsa": ['qsa.hip', 'common.hpp', 'internal.hpp']}
 SCORER_TRAFFIC = {   # workload: (sources, sha, FETCH_SIZE KiB, WRITE_SIZE KiB per dispatch)
-    "decode_T8_S65536": ("csa", "84dc3d5c434a511b", 3551.1, 2048.0),
-    "long_decode_T32_S262144": ("csa", "84dc3d5c434a511b", 33782.4, 32776.0),
-    "prefill_T4096": ("csa", "84dc3d5c434a511b", 35459.9, 65671.1),
-    "qsa_prefill": ("qsa", "11fb9a70e3ef0af4", 163863.7, 262424.0),
-    "hbm_true_T32_S262144": ("csa", "84dc3d5c434a511b", 229543.2, 32783.1),
+    "tiny_decode": ("csa", "9f239881bb026004", 77.9, 16.0),
+    "decode_T8_S65536": ("csa", "9f239881bb026004", 3558.6, 2048.0),
+    "long_decode_T32_S262144": ("csa", "9f239881bb026004", 33755.7, 32776.0),
+    "prefill_T4096": ("csa", "9f239881bb026004", 35454.5, 65671.2),
+    "qsa_prefill": ("qsa", "bfaf228ad589f054", 163863.6, 262424.0),
+    "hbm_true_T32_S262144": ("csa", "9f239881bb026004", 229554.7, 32785.6),
 }
 
 
