@@ -147,14 +147,19 @@ __device__ __forceinline__ XcdTile score_tile(const ScoreArgs& a, int units) {
   return t;
 }
 
-// A operands (per-head power-of-two prescaled fp16 q) and accumulator-row weights
-// of query t, straight from global memory.  Lane (col, quarter) holds, for M-tile
-// mt and K-step kk, q[16 mt + col][quarter * D/4 + 8 kk .. + 8]; the head's max over
-// its D dims spans the four quarter lanes.  Row i of accumulator quarter q of tile
-// mt is head 16 mt + 4 q + i.  Queries past T get zeros.
+// Raw query of row t as loaded: lane (col, quarter) holds, for M-tile mt and K-step kk,
+// q[16 mt + col][quarter * D/4 + 8 kk .. + 8] (eight bf16 in raw[mt][kk][0], or eight
+// fp32 in raw[mt][kk][0..1]), and the weights of accumulator rows 16 mt + 4 quarter + i.
+// Issuing these loads apart from the conversion lets the page loads of the segment go
+// out while they are in flight.  Queries past T get zeros.
 template <int MT, int D>
-__device__ __forceinline__ void load_query(const ScoreArgs& a, int t, int lane, half8v (&A)[MT][D / 32],
-                                           float (&wr)[MT][4]) {
+struct QueryRaw {
+  u32x4 q[MT][D / 32][2];
+  float w[MT][4];
+};
+
+template <int MT, int D>
+__device__ __forceinline__ void issue_query(const ScoreArgs& a, int t, int lane, QueryRaw<MT, D>& r) {
   constexpr int KW = D / 32;
   const int col = lane & 15, quarter = lane >> 4;
   const bool has = t < a.T;
@@ -163,29 +168,53 @@ __device__ __forceinline__ void load_query(const ScoreArgs& a, int t, int lane, 
     const int h = mt * 16 + col;
     const bool hv = has && h < a.H;
     const int64_t base = ((int64_t)t * a.H + h) * D + quarter * (D / 4);
+#pragma unroll
+    for (int kk = 0; kk < KW; ++kk) {
+      r.q[mt][kk][0] = u32x4{0u, 0u, 0u, 0u};
+      r.q[mt][kk][1] = u32x4{0u, 0u, 0u, 0u};
+      if (hv) {
+        if (a.q_bf16) {
+          r.q[mt][kk][0] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) + base + kk * 8);
+        } else {
+          const float* src = reinterpret_cast<const float*>(a.q) + base + kk * 8;
+          r.q[mt][kk][0] = *reinterpret_cast<const u32x4*>(src);
+          r.q[mt][kk][1] = *reinterpret_cast<const u32x4*>(src + 4);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hr = mt * 16 + quarter * 4 + i;
+      r.w[mt][i] = (has && hr < a.H) ? a.w[(int64_t)t * a.H + hr] : 0.0f;
+    }
+  }
+}
+
+// A operands (per-head power-of-two prescaled fp16 q) and accumulator-row weights from
+// the raw query.  Row i of accumulator quarter q of tile mt is head 16 mt + 4 q + i; the
+// head's max over its D dims spans the four quarter lanes.
+template <int MT, int D>
+__device__ __forceinline__ void convert_query(const ScoreArgs& a, const QueryRaw<MT, D>& r,
+                                              half8v (&A)[MT][D / 32], float (&wr)[MT][4], int lane) {
+  constexpr int KW = D / 32;
+  const int quarter = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
     float v[KW][8];
     float mx = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < KW; ++kk) {
       if (a.q_bf16) {
-        u32x4 u = {0u, 0u, 0u, 0u};
-        if (hv) u = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) + base + kk * 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          v[kk][2 * e] = __uint_as_float(u[e] << 16);
-          v[kk][2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+          v[kk][2 * e] = __uint_as_float(r.q[mt][kk][0][e] << 16);
+          v[kk][2 * e + 1] = __uint_as_float(r.q[mt][kk][0][e] & 0xffff0000u);
         }
       } else {
-        float4v f0 = {0.f, 0.f, 0.f, 0.f}, f1 = {0.f, 0.f, 0.f, 0.f};
-        if (hv) {
-          const float* src = reinterpret_cast<const float*>(a.q) + base + kk * 8;
-          f0 = *reinterpret_cast<const float4v*>(src);
-          f1 = *reinterpret_cast<const float4v*>(src + 4);
-        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          v[kk][e] = f0[e];
-          v[kk][4 + e] = f1[e];
+          v[kk][e] = __uint_as_float(r.q[mt][kk][0][e]);
+          v[kk][4 + e] = __uint_as_float(r.q[mt][kk][1][e]);
         }
       }
 #pragma unroll
@@ -203,11 +232,18 @@ __device__ __forceinline__ void load_query(const ScoreArgs& a, int t, int lane, 
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int hr = mt * 16 + quarter * 4 + i;
       const int jr = __shfl(j, quarter * 4 + i);
-      wr[mt][i] = (has && hr < a.H) ? ldexpf(a.w[(int64_t)t * a.H + hr], -jr) : 0.0f;
+      wr[mt][i] = ldexpf(r.w[mt][i], -jr);
     }
   }
+}
+
+template <int MT, int D>
+__device__ __forceinline__ void load_query(const ScoreArgs& a, int t, int lane, half8v (&A)[MT][D / 32],
+                                           float (&wr)[MT][4]) {
+  QueryRaw<MT, D> r;
+  issue_query<MT, D>(a, t, lane, r);
+  convert_query<MT, D>(a, r, A, wr, lane);
 }
 
 template <int MT>
@@ -415,6 +451,10 @@ __global__ __launch_bounds__(64 * G) void score_mfma_group_kernel(ScoreArgs a) {
     // branch on them below is a scalar branch
     t = __builtin_amdgcn_readfirstlane(t);
     const bool has = t < a.T;
+    // the query loads go out first: they need only the row, and the valid length, the
+    // block table and the global scales are fetched under them
+    QueryRaw<MT, D> qraw;
+    issue_query<MT, D>(a, t, lane, qraw);
     const int valid = has ? a.valid_lens[t] : 0;
     const int s_end = !has ? s_begin : tail ? min(s_cap, a.n_cols) : max(s_begin, min(s_cap, valid));
     const int s_vend = max(s_begin, min(s_end, valid));
@@ -428,12 +468,15 @@ __global__ __launch_bounds__(64 * G) void score_mfma_group_kernel(ScoreArgs a) {
     float* mypgs = pgs + wave * a.pid_cap;
     const int32_t* bt_row = a.bt + (int64_t)t * a.bt_stride;
     const int p_first = lane < np ? bt_row[lb0 + lane] : 0;
+    // global scales of the first 64 pages (entry 0 of the pool stands in for lanes past
+    // the row's pages), then the query conversion
+    const float g_first = a.gscale[lane < np ? p_first : 0];
     half8v A[MT][KW];
     float wr[MT][4];
-    load_query<MT, D>(a, t, lane, A, wr);
+    convert_query<MT, D>(a, qraw, A, wr, lane);
     if (lane < np) {
       mypid[lane] = p_first;
-      mypgs[lane] = a.gscale[p_first];
+      mypgs[lane] = g_first;
     }
     for (int i = lane + 64; i < np; i += 64) {
       const int p = bt_row[lb0 + i];
