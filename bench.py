@@ -120,10 +120,10 @@ def cpu_baseline(w, budget_s=20.0):
 
 def make_step(torch, stages, graph):
     """step(ev): run the stages in order, with ev[i] recorded before stage i and ev[-1]
-    after the last.  With graph=True every stage is captured once into a HIP graph and
-    replayed (the library allocates nothing and issues no memset, so its launches
-    capture as plain kernel nodes); the events stay outside the graphs, on the same
-    stream."""
+    after the last (ev=None: no events).  With graph=True every stage is captured once
+    into a HIP graph and replayed (the library allocates nothing and issues no memset,
+    so its launches capture as plain kernel nodes); the events stay outside the graphs,
+    on the same stream."""
     if graph:
         graphs = []
         for f in stages:
@@ -137,6 +137,10 @@ def make_step(torch, stages, graph):
         runs = list(stages)
 
     def step(ev):
+        if ev is None:
+            for r in runs:
+                r()
+            return
         for i, r in enumerate(runs):
             ev[i].record()
             r()
@@ -146,7 +150,11 @@ def make_step(torch, stages, graph):
 
 
 def timed_steps(torch, step, n_stages, steps):
-    """ms per step over `steps` back-to-back steps, and each stage's per-step times (ms)."""
+    """ms per step over `steps` back-to-back steps, and each stage's per-step times (ms).
+
+    The steps are timed with one event before the first and one after the last, so no
+    marker sits between the kernels of the timed region; the per-stage times come from a
+    second pass over the same number of steps with an event around every stage."""
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_stages + 1)] for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -154,10 +162,13 @@ def timed_steps(torch, step, n_stages, steps):
     torch.cuda.synchronize()
     t_start.record()
     for i in range(steps):
-        step(evs[i])
+        step(None)
     t_end.record()
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / steps
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     stage = [np.array([e[j].elapsed_time(e[j + 1]) for e in evs]) for j in range(n_stages)]
     return ms_per_step, stage
 
