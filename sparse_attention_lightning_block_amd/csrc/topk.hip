@@ -22,7 +22,7 @@
 //     the (chunk, row) grid then finds the bin holding the K-th entry from the
 //     copies (scanning down from the row's highest bin) and writes every entry at
 //     or above that bin to the chunk's own candidate slots; one workgroup per row
-//     (1024 threads when rows are few, 256 when they are many) loads those
+//     (512 threads when rows are few, 256 when they are many) loads those
 //     candidates (about K plus one bin's worth) into registers, selects the K
 //     winners exactly and sorts them.
 //   * the sort buckets the winners on the 12 highest bits where they differ and
@@ -39,8 +39,8 @@ constexpr int kBins = 1 << kDigit;       // 4096 histogram bins
 constexpr int kTopShift = 64 - kDigit;   // first digit: the score's top 12 order bits
 constexpr int kRowThreads = 256;         // one-workgroup rows
 constexpr int kChunkThreads = 256;       // histogram and filter chunks of long rows
-constexpr int kFinalThreads = 1024;      // the finishing workgroup of a long row when rows are few
-constexpr int kFinalPer = 12;            // candidates per finishing thread held in registers
+constexpr int kFinalThreads = 512;       // the finishing workgroup of a long row when rows are few
+constexpr int kFinalPer = 16;            // candidates per finishing thread held in registers
 constexpr int kFinalThreadsMany = 256;   // ... and when rows are many (more rows in flight per CU)
 constexpr int kFinalPerMany = 16;
 constexpr int kFewRows = 256;
@@ -55,7 +55,7 @@ constexpr int kRowThreadsLds = 512;    // persistent rows kept in LDS: 64 entrie
 constexpr int kPersistentWgs = 256;    // one workgroup per CU (the row fills its LDS)
 constexpr int kBucketMax = 48;           // crowded bucket: sorting network instead
 constexpr int kHistCopies = kXcds;       // one global histogram per XCD
-constexpr int kMaxWaves = kFinalThreads / kWave;
+constexpr int kMaxWaves = 1024 / kWave;  // widest workgroup of the select kernels
 
 struct RowInfo {
   uint32_t bin;    // bin of the K-th entry (0 when every entry wins)
