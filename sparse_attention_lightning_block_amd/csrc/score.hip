@@ -564,6 +564,16 @@ __global__ __launch_bounds__(64 * G) void score_mfma_group_kernel(ScoreArgs a) {
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
               A[mt][kk], B[kk], kk == 0 ? float4v{0.f, 0.f, 0.f, 0.f} : acc[mt], 0, 0, 0);
     };
+    // Interleave a step's MFMAs with the VALU work of its block: the B reads first, then
+    // one MFMA and two VALU instructions at a time.
+    auto interleave = [&]() {
+      __builtin_amdgcn_sched_group_barrier(0x100, KW, 0);
+#pragma unroll
+      for (int i = 0; i < KW * MT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+    };
     auto flush_prev = [&]() {
       const float sc = row_transpose_sum4(p0, p1, p2, head_part<MT>(AC1, wr));
       if (t_prev + lane < s_vend) out_row[t_prev + lane] = g_prev * sc;
@@ -585,23 +595,27 @@ __global__ __launch_bounds__(64 * G) void score_mfma_group_kernel(ScoreArgs a) {
         read_b(buf, 1, BB);
         mfma_step(BA, AC0);
         flush_prev();
+        interleave();
       }
       decode_part(buf ^ 1, nx, gnx, 0, SW / 2);
       if (act) {
         read_b(buf, 2, BA);
         mfma_step(BB, AC1);
         p0 = head_part<MT>(AC0, wr);
+        interleave();
       }
       decode_part(buf ^ 1, nx, gnx, SW / 2, SW);
       if (act) {
         read_b(buf, 3, BB);
         mfma_step(BA, AC0);
         p1 = head_part<MT>(AC1, wr);
+        interleave();
       }
       load_tile(j + 4, mine, gmine);
       if (act) {
         mfma_step(BB, AC1);
         p2 = head_part<MT>(AC0, wr);
+        interleave();
         t_prev = t0;
         g_prev = g_lane;
       }
