@@ -58,12 +58,12 @@ COLD_SPAN_BYTES = 2 * 256 * 2**20
 TRAFFIC_COPY_FACTOR = {"FETCH_SIZE": 1.9998, "WRITE_SIZE": 1.0}
 SCORER_SOURCES = {"csa": ['score.hip', 'nvfp4.hpp', 'common.hpp', 'internal.hpp'], "qsa": ['qsa.hip', 'common.hpp', 'internal.hpp']}
 SCORER_TRAFFIC = {   # workload: (sources, sha, FETCH_SIZE KiB, WRITE_SIZE KiB per dispatch)
-    "tiny_decode": ("csa", "d7c8c1b395bd1041", 77.6, 16.0),
-    "decode_T8_S65536": ("csa", "d7c8c1b395bd1041", 3550.1, 2048.0),
-    "long_decode_T32_S262144": ("csa", "d7c8c1b395bd1041", 33838.7, 32776.0),
-    "prefill_T4096": ("csa", "d7c8c1b395bd1041", 35441.9, 65691.5),
+    "tiny_decode": ("csa", "336ac98e4195ea72", 77.6, 16.0),
+    "decode_T8_S65536": ("csa", "336ac98e4195ea72", 3560.6, 2048.0),
+    "long_decode_T32_S262144": ("csa", "336ac98e4195ea72", 33870.7, 32776.0),
+    "prefill_T4096": ("csa", "336ac98e4195ea72", 35448.9, 65692.6),
     "qsa_prefill": ("qsa", "bfaf228ad589f054", 163863.2, 262424.0),
-    "hbm_true_T32_S262144": ("csa", "d7c8c1b395bd1041", 229542.6, 32783.5),
+    "hbm_true_T32_S262144": ("csa", "336ac98e4195ea72", 229545.1, 32783.4),
 }
 
 

@@ -564,13 +564,13 @@ __global__ __launch_bounds__(64 * G) void score_mfma_group_kernel(ScoreArgs a) {
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
               A[mt][kk], B[kk], kk == 0 ? float4v{0.f, 0.f, 0.f, 0.f} : acc[mt], 0, 0, 0);
     };
-    // Interleave a step's MFMAs with the VALU work of its block: the B reads first, then
-    // one MFMA and two VALU instructions at a time.
+    // Interleave a step's MFMAs with the other work of its block: one MFMA and two VALU
+    // instructions at a time, with the next step's B reads spread over the first MFMAs.
     auto interleave = [&]() {
-      __builtin_amdgcn_sched_group_barrier(0x100, KW, 0);
 #pragma unroll
       for (int i = 0; i < KW * MT; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < KW) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
       }
     };
