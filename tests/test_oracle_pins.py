@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from oracle import indexer, nvfp4, qsa
-from tests.heap_replay import heap_topk
+from tests.insertion_topk import insertion_topk
 from workloads import make
 from workloads.configs import csa
 
@@ -149,6 +149,24 @@ def test_duplicate_page_gives_equal_scores():
         assert pos[2 * w.epb + j] < pos[5 * w.epb + j]
 
 
+def test_dequant_f32_is_one_rounding_of_the_exact_product():
+    # Code 0b011 (1.5) with scale byte 0x3A (1.25) and global scale g = 1 + 2^-22 (an fp32
+    # value).  Worked by hand: c = 1.875 and c*g = 1.875 + 3.75 * 2^-23; the fp32 spacing
+    # on [1, 2) is 2^-23, so one rounding gives 1.875 + 4 * 2^-23.  The listing's code
+    # rounds e4m3*g first: 1.25 + 2.5 * 2^-23 is a tie that goes to the even 1.25 + 2 * 2^-23,
+    # and 1.5 times that is 1.875 + 3 * 2^-23 -- a different float.
+    keys = np.array([[0x03, 0, 0, 0, 0, 0, 0, 0]], dtype=np.uint8)
+    sc = np.array([[0x3A]], dtype=np.uint8)
+    c = nvfp4.code_values(keys, sc)
+    assert c[0, 0] == 1.875 and np.all(c[0, 1:] == 0.0)
+    g = np.array([np.float32(1.0 + 2.0 ** -22)], dtype=np.float32)
+    assert float(g[0]) == 1.0 + 2.0 ** -22
+    k = nvfp4.dequant_f32(c, g)
+    assert k.dtype == np.float32
+    assert float(k[0, 0]) == 1.875 + 4 * 2.0 ** -23
+    assert float(k[0, 0]) != 1.875 + 3 * 2.0 ** -23
+
+
 # ---------------------------------------------------------------- scores
 
 def _hand_case():
@@ -275,7 +293,7 @@ def test_topk_three_ways(k):
     for t in range(w.T):
         r = rows[t]
         idx, val = indexer.topk(r, k)
-        hb, hs = heap_topk(list(r), k)
+        hb, hs = insertion_topk(list(r), k)
         assert idx.tolist() == hb
         nl = heapq.nlargest(k, ((v, -s) for s, v in enumerate(r)))
         exp = [-s for _, s in nl] + [-1] * (k - len(nl))
@@ -365,7 +383,9 @@ def test_qsa_score_rows_brute_force_and_mask():
     q = rng.standard_normal((rows, H, hd))
     k = rng.standard_normal((nb, hd))
     s, valid = qsa.score_rows(q, k, first, ratio)
-    assert valid.tolist() == [min(nb, (first + r + 1) // ratio) for r in range(rows)]   # 7, 8, 8
+    # rows at positions 30, 31, 32 with 4 tokens per block: blocks 0..6 hold tokens 0..27
+    # (complete at 30), block 7 completes with token 31; the table holds 10 blocks
+    assert valid.tolist() == [7, 8, 8]
     for r in range(rows):
         for b in range(nb):
             if b >= valid[r]:
@@ -373,6 +393,54 @@ def test_qsa_score_rows_brute_force_and_mask():
             else:
                 exp = sum(max(0.0, math.fsum(q[r, h, d] * k[b, d] for d in range(hd))) for h in range(H)) / 4.0
                 assert s[r, b] == pytest.approx(exp, rel=1e-13)
+
+
+def _rot(a, b, ang):
+    return a * math.cos(ang) - b * math.sin(ang), a * math.sin(ang) + b * math.cos(ang)
+
+
+def test_qprep_rows_hand_worked():
+    # Two rows at positions 5 and 6 (first_pos 5), two heads of 4 dims read from rows of
+    # width qkw = 10 (the last two columns are not q), rot = 4 (pairs (0,2) and (1,3)),
+    # theta = 100: pair 0 turns by pos, pair 1 by pos * 100^(-1/2) = pos / 10.  eps = 0.
+    qk = np.array([[1, 1, 1, 1, 2, 0, 0, 0, 100, -100],
+                   [0, 3, 0, 4, -1, -1, 1, 1, 7, 7]], dtype=np.float64)
+    wq = np.array([0.0, 0.5, -0.5, 1.0])             # scale 1 + w = (1, 1.5, 0.5, 2)
+    got = qsa.qprep_rows(qk, wq, 2, 5, 10, 2, 4, 4, 100.0, 0.0)
+    assert got.shape == (2, 2, 4)
+    # normalised and scaled by hand: rms of (1,1,1,1) and (2,0,0,0) and (-1,-1,1,1) is 1,
+    # of (0,3,0,4) it is 2.5
+    normed = {(0, 0): (1.0, 1.5, 0.5, 2.0), (0, 1): (2.0, 0.0, 0.0, 0.0),
+              (1, 0): (0.0, 1.8, 0.0, 3.2), (1, 1): (-1.0, -1.5, 0.5, 2.0)}
+    for (r, h), (n0, n1, n2, n3) in normed.items():
+        pos = 5 + r
+        o0, o2 = _rot(n0, n2, pos * 1.0)
+        o1, o3 = _rot(n1, n3, pos / 10.0)
+        np.testing.assert_allclose(got[r, h], [o0, o1, o2, o3], rtol=1e-13, atol=1e-14)
+
+
+def test_block_pool_rotates_at_the_block_first_position():
+    # ratio 2: block b pools raw rows 2b, 2b+1 and sits at position 2b.  Blocks 3 and 4:
+    # means (1,1,1,1) and (2,0,0,0), both of rms 1; rot = 4, theta = 100 (pair 1 turns
+    # by pos / 10), eps = 0.  The other raw rows must not be read.
+    raw = np.full((10, 4), 50.0)
+    raw[6], raw[7] = [0, 2, 1, 1], [2, 0, 1, 1]
+    raw[8], raw[9] = [3, 0, 0, 0], [1, 0, 0, 0]
+    wk = np.array([0.0, 0.5, -0.5, 1.0])
+    got = qsa.block_pool(raw, wk, 3, 2, 2, 4, 100.0, 0.0)
+    assert got.shape == (2, 4)
+    for i, (pos, (n0, n1, n2, n3)) in enumerate([(6, (1.0, 1.5, 0.5, 2.0)), (8, (2.0, 0.0, 0.0, 0.0))]):
+        o0, o2 = _rot(n0, n2, pos * 1.0)
+        o1, o3 = _rot(n1, n3, pos / 10.0)
+        np.testing.assert_allclose(got[i], [o0, o1, o2, o3], rtol=1e-13, atol=1e-14)
+
+
+def test_complete_blocks_literal():
+    # positions 14..18 with 4 tokens per block: tokens 0..15 fill blocks 0..3 at position 15
+    assert qsa.complete_blocks(14, 5, 4, 100).tolist() == [3, 4, 4, 4, 4]
+    assert qsa.complete_blocks(14, 5, 4, 4).tolist() == [3, 4, 4, 4, 4]
+    assert qsa.complete_blocks(14, 5, 4, 3).tolist() == [3, 3, 3, 3, 3]      # capped by the table
+    assert qsa.complete_blocks(0, 3, 1, 10).tolist() == [1, 2, 3]             # ratio 1: every token
 
 
 def test_generator_is_deterministic():
