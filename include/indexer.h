@@ -26,7 +26,12 @@
  *    IDX_OK without launching anything ([qsa.rs] qsa_block_pool: no launch when
  *    there is no work).
  *  - Out-of-range data (a valid length beyond the table, a page id outside the
- *    pool) is undefined behaviour; callers must validate such data.
+ *    pool) is undefined behaviour unless the call is made with IDX_F_VALIDATE,
+ *    which checks it first and returns IDX_ERR_DATA (see the flags below).
+ *  - Workspaces are scratch: every call writes each part of its workspace before
+ *    reading it, so a workspace needs no initialisation and may serve calls of any
+ *    shape in turn (the size rule of each call still applies).  Calls that share a
+ *    workspace must be ordered (one stream, or synchronised).
  */
 #ifndef SALB_INDEXER_H
 #define SALB_INDEXER_H
@@ -46,6 +51,15 @@ extern "C" {
 #define IDX_ERR_WORKSPACE 3    /* workspace missing or smaller than the *_workspace_size() value */
 #define IDX_ERR_UNSUPPORTED 4  /* a size or mode this build does not implement */
 #define IDX_ERR_HIP 5          /* a HIP runtime call failed (message in indexer_last_error) */
+#define IDX_ERR_DATA 6         /* IDX_F_VALIDATE found a valid length or page id out of range */
+
+/* flags of the paged scorers */
+#define IDX_F_VALIDATE 1u      /* check valid_lens and the block-table entries they use before
+                                  any scoring: a one-workgroup check kernel, then a
+                                  synchronisation of `stream` (so the call blocks and must not
+                                  be captured into a graph); on bad data nothing else is
+                                  launched and IDX_ERR_DATA names the first bad row or entry.
+                                  Without it such data is undefined behaviour. */
 
 /* element type of q */
 #define IDX_DTYPE_F32 0
@@ -83,12 +97,14 @@ const char* indexer_last_error(void);
  *  scores      [T, n_cols] fp32 output with row stride score_stride >= n_cols
  * Supported: D in {64, 128, 256}; 1 <= H <= 64; 1 <= epb <= 65536; n_cols < 2^24.
  * precision: IDX_PREC_FP32 or IDX_PREC_MFMA.
+ * flags: 0 or IDX_F_VALIDATE (the check uses the first 16 bytes of `scores` as its
+ *        status word; scores must then be 8-byte aligned).
  */
 int indexer_score_rows(const void* q, int q_dtype, const float* w,
                        const uint8_t* keys_fp4, const uint8_t* key_scale, const float* key_gscale,
                        const int32_t* block_table, int64_t bt_stride, const int32_t* valid_lens,
                        int T, int H, int D, int epb, int max_lb, int n_pages,
-                       int precision, float* scores, int64_t score_stride, int n_cols,
+                       int precision, unsigned flags, float* scores, int64_t score_stride, int n_cols,
                        hipStream_t stream);
 
 /*
@@ -111,11 +127,9 @@ int indexer_score_rows(const void* q, int q_dtype, const float* w,
  *  topk_idx    [rows, top_k] int32 output (logical indices s)
  *  topk_scores [rows, top_k] fp32 output or NULL
  *  workspace   device scratch of indexer_topk_workspace_size(...) bytes, 256-byte
- *              aligned, owned by the caller.  It must be zero-filled before its
- *              first use; every call that returns IDX_OK leaves it ready for the
- *              next call (its counters back at zero), so it is filled once, not per
- *              call.  After an error return, zero-fill it again.  Calls sharing a
- *              workspace must be ordered (same stream, or synchronised).
+ *              aligned, owned by the caller; no initialisation needed (rows longer
+ *              than 8192 entries zero its histogram counters with one small launch
+ *              ahead of the select).  May be NULL when the size is 0.
  * Supported: 1 <= top_k <= 8192, n_cols < 2^24.
  */
 size_t indexer_topk_workspace_size(int rows, int n_cols, int top_k);
@@ -132,15 +146,18 @@ int indexer_topk_select(const float* scores, int64_t score_stride, const int32_t
  * indexer_topk_select; the scores live only in the workspace.
  *  topk_idx    [T, top_k] int32 output: logical entry indices s, -1 padded
  *  topk_scores [T, top_k] fp32 output or NULL
- *  workspace   device scratch of indexer_score_topk_workspace_size(...) bytes; the
- *              same zero-fill-once rule as indexer_topk_select's workspace.
+ *  flags       0 or IDX_F_VALIDATE
+ *  workspace   device scratch of indexer_score_topk_workspace_size(...) bytes, 256-byte
+ *              aligned, no initialisation needed: it holds the [T, max_lb*epb] score
+ *              matrix and the select's buffers; the scorer launch also zeroes the
+ *              select's histogram counters.
  */
 size_t indexer_score_topk_workspace_size(int T, int max_lb, int epb, int top_k);
 int indexer_score_topk(const void* q, int q_dtype, const float* w,
                        const uint8_t* keys_fp4, const uint8_t* key_scale, const float* key_gscale,
                        const int32_t* block_table, int64_t bt_stride, const int32_t* valid_lens,
                        int T, int H, int D, int epb, int max_lb, int n_pages, int top_k,
-                       int precision, int32_t* topk_idx, float* topk_scores,
+                       int precision, unsigned flags, int32_t* topk_idx, float* topk_scores,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*

@@ -13,4 +13,4 @@ from .ops import (  # noqa: F401
     qsa_qprep_rows,
     qsa_score_rows,
 )
-from ._lib import IndexerError, load  # noqa: F401
+from ._lib import IDX_ERR_DATA, IDX_F_VALIDATE, IndexerError, load  # noqa: F401

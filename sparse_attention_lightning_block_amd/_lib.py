@@ -18,6 +18,9 @@ IDX_ERR_SHAPE = 2
 IDX_ERR_WORKSPACE = 3
 IDX_ERR_UNSUPPORTED = 4
 IDX_ERR_HIP = 5
+IDX_ERR_DATA = 6
+
+IDX_F_VALIDATE = 1
 
 IDX_DTYPE_F32 = 0
 IDX_DTYPE_BF16 = 1
@@ -34,12 +37,13 @@ _SZ = ctypes.c_size_t
 # name -> (restype, argtypes), in header order
 SIGNATURES = {
     "indexer_last_error": (ctypes.c_char_p, []),
-    "indexer_score_rows": (_I, [_P, _I, _P, _P, _P, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I64, _I, _P]),
+    "indexer_score_rows": (_I, [_P, _I, _P, _P, _P, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _I, _U32, _P, _I64, _I,
+                                _P]),
     "indexer_topk_workspace_size": (_SZ, [_I, _I, _I]),
     "indexer_topk_select": (_I, [_P, _I64, _P, _I64, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "indexer_score_topk_workspace_size": (_SZ, [_I, _I, _I, _I]),
-    "indexer_score_topk": (_I, [_P, _I, _P, _P, _P, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P,
-                                _SZ, _P]),
+    "indexer_score_topk": (_I, [_P, _I, _P, _P, _P, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _I, _I, _U32, _P, _P,
+                                _P, _SZ, _P]),
     "qsa_block_pool": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _F, _F, _P]),
     "qsa_qprep_rows": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _F, _F, _P]),
     "qsa_score_rows": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _I, _P]),

@@ -16,7 +16,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsalb_indexer.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "score.hip", "topk.hip", "qsa.hip"]
+SOURCES = ["api.hip", "score.hip", "topk.hip", "qsa.hip", "validate.hip"]
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",

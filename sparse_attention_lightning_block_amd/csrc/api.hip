@@ -87,6 +87,27 @@ salb::ScoreArgs make_args(const void* q, int q_dtype, const float* w, const uint
   return a;
 }
 
+// IDX_F_VALIDATE: the metadata check, run to completion before anything else is
+// launched.  dev_status: 16 bytes of device memory the call may overwrite.
+int validate_if_asked(unsigned flags, const int32_t* bt, int64_t bt_stride, const int32_t* valid_lens, int T,
+                      int max_lb, int epb, int cap, int n_pages, void* dev_status, hipStream_t stream) {
+  if (!(flags & IDX_F_VALIDATE)) return IDX_OK;
+  int64_t st[2] = {-1, -1};
+  hipError_t e = salb::validate_pages(bt, bt_stride, valid_lens, T, max_lb, epb, cap, n_pages,
+                                      static_cast<int64_t*>(dev_status), st, stream);
+  if (e != hipSuccess) return hip_fail(e, "validation");
+  if (st[0] >= 0) return fail(IDX_ERR_DATA, "valid_lens[%lld] is outside [0, %d]", (long long)st[0], cap);
+  if (st[1] >= 0)
+    return fail(IDX_ERR_DATA, "block_table[%lld][%lld] names a page outside [0, %d)", (long long)(st[1] / max_lb),
+                (long long)(st[1] % max_lb), n_pages);
+  return IDX_OK;
+}
+
+int check_flags(unsigned flags) {
+  if (flags & ~(unsigned)IDX_F_VALIDATE) return fail(IDX_ERR_UNSUPPORTED, "flags 0x%x", flags);
+  return IDX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -96,16 +117,26 @@ const char* indexer_last_error(void) { return g_err.c_str(); }
 int indexer_score_rows(const void* q, int q_dtype, const float* w, const uint8_t* keys_fp4,
                        const uint8_t* key_scale, const float* key_gscale, const int32_t* block_table,
                        int64_t bt_stride, const int32_t* valid_lens, int T, int H, int D, int epb, int max_lb,
-                       int n_pages, int precision, float* scores, int64_t score_stride, int n_cols,
-                       hipStream_t stream) {
+                       int n_pages, int precision, unsigned flags, float* scores, int64_t score_stride,
+                       int n_cols, hipStream_t stream) {
   int rc = check_paged(q, q_dtype, w, keys_fp4, key_scale, key_gscale, block_table, bt_stride, valid_lens, T, H, D,
                        epb, max_lb, n_pages, precision);
   if (rc) return rc;
+  if ((rc = check_flags(flags))) return rc;
   if (!scores) return fail(IDX_ERR_NULL, "scores is required");
   if (n_cols < 0 || n_cols >= kMaxCols) return fail(IDX_ERR_SHAPE, "n_cols %d out of range [0, 2^24)", n_cols);
   if (score_stride < n_cols) return fail(IDX_ERR_SHAPE, "score_stride < n_cols");
   if (!aligned(scores, 4)) return fail(IDX_ERR_SHAPE, "scores must be 4-byte aligned");
   if (T == 0 || n_cols == 0) return ok();
+  if (flags & IDX_F_VALIDATE) {
+    if (!aligned(scores, 8)) return fail(IDX_ERR_SHAPE, "IDX_F_VALIDATE needs 8-byte aligned scores");
+    if ((int64_t)(T - 1) * score_stride + n_cols < 4)
+      return fail(IDX_ERR_SHAPE, "IDX_F_VALIDATE needs a scores buffer of at least 4 floats");
+    const int cap = (int64_t)max_lb * epb < n_cols ? max_lb * epb : n_cols;
+    if ((rc = validate_if_asked(flags, block_table, bt_stride, valid_lens, T, max_lb, epb, cap, n_pages, scores,
+                                stream)))
+      return rc;
+  }
   salb::ScoreArgs a = make_args(q, q_dtype, w, keys_fp4, key_scale, key_gscale, block_table, bt_stride, valid_lens,
                                 T, H, D, epb, max_lb);
   a.scores = scores;
@@ -151,7 +182,7 @@ int indexer_topk_select(const float* scores, int64_t score_stride, const int32_t
     p.n_cols = 0;
   }
   hipError_t e = salb::launch_select(p, scores, score_stride, valid_lens, first_pos, ratio, topk_idx, topk_scores,
-                                     workspace, stream);
+                                     workspace, false, stream);
   if (e != hipSuccess) return hip_fail(e, "select kernel launch");
   return ok();
 }
@@ -168,11 +199,12 @@ size_t indexer_score_topk_workspace_size(int T, int max_lb, int epb, int top_k) 
 int indexer_score_topk(const void* q, int q_dtype, const float* w, const uint8_t* keys_fp4,
                        const uint8_t* key_scale, const float* key_gscale, const int32_t* block_table,
                        int64_t bt_stride, const int32_t* valid_lens, int T, int H, int D, int epb, int max_lb,
-                       int n_pages, int top_k, int precision, int32_t* topk_idx, float* topk_scores,
-                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                       int n_pages, int top_k, int precision, unsigned flags, int32_t* topk_idx,
+                       float* topk_scores, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int rc = check_paged(q, q_dtype, w, keys_fp4, key_scale, key_gscale, block_table, bt_stride, valid_lens, T, H, D,
                        epb, max_lb, n_pages, precision);
   if (rc) return rc;
+  if ((rc = check_flags(flags))) return rc;
   const int n_cols = max_lb * epb;
   rc = check_select(T, n_cols, top_k, n_cols, 0);
   if (rc) return rc;
@@ -187,6 +219,9 @@ int indexer_score_topk(const void* q, int q_dtype, const float* w, const uint8_t
   if (!workspace || workspace_bytes < need)
     return fail(IDX_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace_bytes);
   if (!aligned(workspace, 256)) return fail(IDX_ERR_SHAPE, "workspace must be 256-byte aligned");
+  if ((rc = validate_if_asked(flags, block_table, bt_stride, valid_lens, T, max_lb, epb, n_cols, n_pages, workspace,
+                              stream)))
+    return rc;
   float* sc = static_cast<float*>(workspace);
   salb::ScoreArgs a = make_args(q, q_dtype, w, keys_fp4, key_scale, key_gscale, block_table, bt_stride, valid_lens,
                                 T, H, D, epb, max_lb);
@@ -194,10 +229,13 @@ int indexer_score_topk(const void* q, int q_dtype, const float* w, const uint8_t
   a.score_stride = (int64_t)stride;
   a.n_cols = n_cols;
   a.write_tail = 0;
+  // the scorer launch also zeroes the select's histogram counters (no clearing launch)
+  unsigned char* sel_ws = static_cast<unsigned char*>(workspace) + score_bytes;
+  a.zero_ptr = reinterpret_cast<uint4*>(sel_ws);
+  a.zero_n16 = (int64_t)(salb::select_counter_bytes(p) / 16);
   hipError_t e = salb::launch_score_rows(a, precision, stream);
   if (e != hipSuccess) return hip_fail(e, "score kernel launch");
-  e = salb::launch_select(p, sc, (int64_t)stride, valid_lens, 0, 0, topk_idx, topk_scores,
-                          static_cast<unsigned char*>(workspace) + score_bytes, stream);
+  e = salb::launch_select(p, sc, (int64_t)stride, valid_lens, 0, 0, topk_idx, topk_scores, sel_ws, true, stream);
   if (e != hipSuccess) return hip_fail(e, "select kernel launch");
   return ok();
 }

@@ -23,6 +23,10 @@ struct ScoreArgs {
   int64_t score_stride;
   int n_cols;
   int write_tail;  // 1: s in [valid, n_cols) gets -inf
+  // 16-byte words the launch zeroes besides its scores (the select counters of the
+  // fused path, so that the select needs no clearing launch of its own)
+  uint4* zero_ptr;
+  int64_t zero_n16;
   // filled by the launcher
   int chunk;       // keys per workgroup
   int n_chunks;
@@ -35,6 +39,11 @@ hipError_t launch_score_rows(ScoreArgs a, int precision, hipStream_t st);
 hipError_t launch_debug_dequant(const uint8_t* keys, const uint8_t* kscale, const float* gscale,
                                 const int32_t* bt_row, int n, int D, int epb, int mode, float* out,
                                 hipStream_t st);
+
+// Checks valid lengths and the block-table entries they use (validate.hip); waits for
+// the result.  host_status[0]: first bad row (-1 none), [1]: first bad row*max_lb+block.
+hipError_t validate_pages(const int32_t* bt, int64_t bt_stride, const int32_t* valid_lens, int T, int max_lb, int epb,
+                          int cap, int n_pages, int64_t* dev_status, int64_t host_status[2], hipStream_t st);
 
 // Per-row top-k (topk.hip).
 constexpr int kMaxTopK = 8192;
@@ -52,9 +61,12 @@ struct SelectPlan {
 };
 
 bool plan_select(int rows, int n_cols, int top_k, SelectPlan* p);
+// counters_zeroed: the first select_counter_bytes(p) bytes of ws were zeroed by an
+// earlier launch of this call on the same stream (else the select zeroes them itself).
 hipError_t launch_select(const SelectPlan& p, const float* scores, int64_t score_stride,
                          const int32_t* valid_lens, int64_t first_pos, int ratio, int32_t* out_idx,
-                         float* out_scores, void* ws, hipStream_t st);
+                         float* out_scores, void* ws, bool counters_zeroed, hipStream_t st);
+size_t select_counter_bytes(const SelectPlan& p);
 size_t select_workspace_bytes(int rows, int n_cols, int top_k);  // 0 if unsupported
 
 // QSA (qsa.hip).

@@ -63,6 +63,15 @@ __device__ __forceinline__ float load_q(const void* q, int bf16, int64_t i) {
   return reinterpret_cast<const float*>(q)[i];
 }
 
+// The words a launch zeroes besides its scores, spread over the whole grid (every
+// workgroup runs this before any early exit).
+__device__ __forceinline__ void zero_side_words(const ScoreArgs& a, int nt) {
+  if (a.zero_n16 == 0) return;
+  const int64_t step = (int64_t)gridDim.x * nt;
+  for (int64_t i = (int64_t)blockIdx.x * nt + threadIdx.x; i < a.zero_n16; i += step)
+    a.zero_ptr[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 // Power-of-two exponent j with max|x| * 2^j in [2^14, 2^15) (0 for zero/non-finite).
 __device__ __forceinline__ int prescale_exp(float mx) {
   if (!(mx > 0.0f) || !(mx < 3.0e38f)) return 0;
@@ -388,6 +397,7 @@ __global__ __launch_bounds__(256) void score_mfma_split_kernel(ScoreArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   int* pid = reinterpret_cast<int*>(smem);
   float* pgs = reinterpret_cast<float*>(pid + a.pid_cap);
+  zero_side_words(a, 256);
 
   const XcdTile tile = score_tile(a, a.T);
   if (tile.chunk >= a.n_chunks) return;
@@ -442,6 +452,7 @@ __global__ __launch_bounds__(64 * G) void score_mfma_group_kernel(ScoreArgs a) {
   __shared__ int s_order[256];
   const int units = (a.T + G - 1) / G;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  zero_side_words(a, NT);
 
   // Scores of this wave's row t over keys [s_begin, s_cap); with tail, the part of
   // that range past the row's valid length gets -inf.  Every wave of the workgroup
@@ -737,6 +748,7 @@ __global__ __launch_bounds__(64 * G) void score_mfma_group_kernel(ScoreArgs a) {
 
 template <int D, int HM, int QBF16>
 __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs a) {
+  zero_side_words(a, 256);
   const XcdTile tile = score_tile(a, a.T);
   if (tile.chunk >= a.n_chunks) return;
   const int t = tile.row;
@@ -926,7 +938,9 @@ hipError_t launch_score_rows(ScoreArgs a, int precision, hipStream_t st) {
     a.pid_cap = (int)(seg_tiles(nw) * 64 / a.epb + 2);
     blocks = nw;
   }
-  if (blocks == 0) return hipSuccess;
+  // T >= 1 and n_cols >= 1 here (the entry points return before), so blocks >= 1 and
+  // the launch also zeroes the side words it was given
+  if (blocks <= 0) return hipErrorInvalidConfiguration;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (precision == 1) {
     switch (a.D) {

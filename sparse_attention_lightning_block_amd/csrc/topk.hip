@@ -18,7 +18,9 @@
 //     them; no grid-wide fences, which write back the whole L2 on this chip):
 //     every workgroup of a (chunk, row) grid adds its chunk's LDS histogram of the
 //     top 12 order-key bits (the bins that can hold the row's K-th entry) into one
-//     of eight global copies (one per XCD, so contended atomics stay in one L2);
+//     of eight global copies (one per XCD, so contended atomics stay in one L2),
+//     which the call zeroes first (a clearing launch, or the scorer launch that
+//     precedes the select in the fused path);
 //     the (chunk, row) grid then finds the bin holding the K-th entry from the
 //     copies (scanning down from the row's highest bin) and writes every entry at
 //     or above that bin to the chunk's own candidate slots; one workgroup per row
@@ -28,6 +30,8 @@
 //   * the sort buckets the winners on the 12 highest bits where they differ and
 //     ranks each against its bucket (a sorting network if a bucket is crowded).
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -78,8 +82,8 @@ struct SelArgs {
   // long-row pipeline
   int chunk;         // entries per chunk workgroup
   int chunks;        // chunks per row
-  uint32_t* ghist;   // [rows][kHistCopies][kBins], zero between calls
-  uint32_t* gmax;    // [rows][kHistCopies] highest bin seen, zero between calls
+  uint32_t* ghist;   // [rows][kHistCopies][kBins], zeroed by the call before stage 1
+  uint32_t* gmax;    // [rows][kHistCopies] highest bin seen, zeroed with ghist
   RowInfo* info;     // [rows]
   uint32_t* ccount;  // [rows][chunks] candidates per chunk
   uint64_t* cand;    // [rows][chunks][chunk] candidate slots
@@ -777,6 +781,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_filter_kernel(SelArgs a)
     uint32_t mb = 0;
 #pragma unroll
     for (int c = 0; c < kHistCopies; ++c) mb = max(mb, gm[c]);
+    mb = min(mb, (uint32_t)(kBins - 1));  // a bin index; never scan past the histogram
     const uint32_t* gh = a.ghist + (int64_t)row * kHistCopies * kBins;
     uint32_t carry = 0;
     if (tid == 0) sh.digit = ~0u;
@@ -848,13 +853,7 @@ __global__ __launch_bounds__(NT) void select_final_kernel(SelArgs a) {
   uint16_t* owner = reinterpret_cast<uint16_t*>(off + ((nch + 4) & ~3));  // [NT * PER]
   const uint32_t* cnt = a.ccount + (int64_t)row * nch;
   const uint64_t* cd = a.cand + (int64_t)row * nch * a.chunk;
-  const uint32_t first = tid < nch ? cnt[tid] : 0u;  // in flight during the zeroing
-  {
-    // the histogram copies and maxima have been read: leave them zero for the next call
-    uint4* gh = reinterpret_cast<uint4*>(a.ghist + (int64_t)row * kHistCopies * kBins);
-    for (int w = tid; w < kHistCopies * kBins / 4; w += NT) gh[w] = make_uint4(0u, 0u, 0u, 0u);
-    if (tid < kHistCopies) a.gmax[(int64_t)row * kHistCopies + tid] = 0u;
-  }
+  const uint32_t first = tid < nch ? cnt[tid] : 0u;
   // exclusive prefix of the chunk counts, 1024 chunks at a time
   uint32_t carry = 0;
   for (int c0 = 0; c0 < nch; c0 += NT) {
@@ -933,13 +932,21 @@ __global__ __launch_bounds__(NT) void select_final_kernel(SelArgs a) {
   finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, mx, mn, sh);
 }
 
+// Zeroes n16 16-byte words (the histogram copies and row maxima of the long-row
+// pipeline) ahead of its first stage.
+__global__ __launch_bounds__(256) void select_clear_kernel(uint4* p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 // ------------------------------------------------------------------ host planning
 
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace of the long-row pipeline: histogram copies and row maxima (zero
-// between calls: the caller zero-fills the workspace once, every call leaves them
-// zero) | row info | chunk counts | candidate slots.
+// Workspace of the long-row pipeline: histogram copies and row maxima (zeroed by
+// each call before its first stage) | row info | chunk counts | candidate slots.
+// Every region is written by the call before it is read: the workspace carries
+// nothing from one call to the next.
 struct WsLayout {
   size_t hist, gmax, info, ccount, cand, total;
 };
@@ -1033,10 +1040,17 @@ static hipError_t launch_rows_lds(const SelArgs& a, const SelectPlan& p, hipStre
 }
 
 template <int PER>
-static hipError_t launch_pipeline(const SelArgs& a, const SelectPlan& p, hipStream_t st) {
+static hipError_t launch_pipeline(const SelArgs& a, const SelectPlan& p, bool counters_zeroed, hipStream_t st) {
   hipError_t e = p.final_nt == kFinalThreads ? set_lds(select_final_kernel<kFinalThreads, kFinalPer>, p.lds)
                                               : set_lds(select_final_kernel<kFinalThreadsMany, kFinalPerMany>, p.lds);
   if (e != hipSuccess) return e;
+  if (!counters_zeroed) {
+    const int64_t n16 = (int64_t)select_counter_bytes(p) / 16;
+    const int64_t blocks = std::min<int64_t>((n16 + 255) / 256, 2048);
+    hipLaunchKernelGGL(select_clear_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                       reinterpret_cast<uint4*>(a.ghist), n16);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const dim3 grid(p.chunks, p.rows);
   hipLaunchKernelGGL(select_hist_kernel<PER>, grid, dim3(kChunkThreads), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1051,9 +1065,16 @@ static hipError_t launch_pipeline(const SelArgs& a, const SelectPlan& p, hipStre
   return hipGetLastError();
 }
 
+// Bytes at the start of the workspace that the long-row pipeline needs zeroed before
+// its first stage (the histogram copies and row maxima); 0 for the one-workgroup rows.
+size_t select_counter_bytes(const SelectPlan& p) {
+  if (!p.two_pass) return 0;
+  return ws_layout(p.rows, p.chunks, p.per * kChunkThreads).info;
+}
+
 hipError_t launch_select(const SelectPlan& p, const float* scores, int64_t score_stride,
                          const int32_t* valid_lens, int64_t first_pos, int ratio, int32_t* out_idx,
-                         float* out_scores, void* ws, hipStream_t st) {
+                         float* out_scores, void* ws, bool counters_zeroed, hipStream_t st) {
   if (p.rows == 0) return hipSuccess;
   SelArgs a{};
   a.scores = scores;
@@ -1085,7 +1106,7 @@ hipError_t launch_select(const SelectPlan& p, const float* scores, int64_t score
   a.info = reinterpret_cast<RowInfo*>(w + l.info);
   a.ccount = reinterpret_cast<uint32_t*>(w + l.ccount);
   a.cand = reinterpret_cast<uint64_t*>(w + l.cand);
-  return p.per == 16 ? launch_pipeline<16>(a, p, st) : launch_pipeline<8>(a, p, st);
+  return p.per == 16 ? launch_pipeline<16>(a, p, counters_zeroed, st) : launch_pipeline<8>(a, p, counters_zeroed, st);
 }
 
 }  // namespace salb

@@ -9,7 +9,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import IDX_DTYPE_BF16, IDX_DTYPE_F32, IDX_PREC_FP32, IDX_PREC_MFMA, check
+from ._lib import IDX_DTYPE_BF16, IDX_DTYPE_F32, IDX_F_VALIDATE, IDX_PREC_FP32, IDX_PREC_MFMA, check
 
 PRECISION = {"fp32": IDX_PREC_FP32, "mfma": IDX_PREC_MFMA}
 
@@ -39,8 +39,13 @@ def _q_dtype(q: torch.Tensor) -> int:
 
 
 def indexer_score_rows(q, w, keys_fp4, key_scale, key_gscale, block_table, valid_lens, *, n_cols: int,
-                       precision: str = "mfma", out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """scores [T, n_cols] fp32: I[t, s] for s < valid_lens[t], -inf beyond."""
+                       precision: str = "mfma", validate: bool = False,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """scores [T, n_cols] fp32: I[t, s] for s < valid_lens[t], -inf beyond.
+
+    validate=True checks valid_lens and the block-table entries first (IDX_F_VALIDATE:
+    the call then waits for the check) and raises IndexerError (code IDX_ERR_DATA) on
+    out-of-range metadata."""
     _dev(q, "q", (torch.float32, torch.bfloat16), 3)
     _dev(w, "w", torch.float32, 2)
     _dev(keys_fp4, "keys_fp4", torch.uint8, 3)
@@ -56,7 +61,7 @@ def indexer_score_rows(q, w, keys_fp4, key_scale, key_gscale, block_table, valid
     check(_lib.load().indexer_score_rows(
         _ptr(q), _q_dtype(q), _ptr(w), _ptr(keys_fp4), _ptr(key_scale), _ptr(key_gscale), _ptr(block_table),
         block_table.stride(0), _ptr(valid_lens), T, H, D, epb, block_table.shape[1], P, PRECISION[precision],
-        _ptr(out), out.stride(0), n_cols, _stream()))
+        IDX_F_VALIDATE if validate else 0, _ptr(out), out.stride(0), n_cols, _stream()))
     return out
 
 
@@ -69,8 +74,8 @@ def indexer_topk_select(scores, top_k: int, *, valid_lens: Optional[torch.Tensor
                         out_idx: Optional[torch.Tensor] = None, out_scores: Optional[torch.Tensor] = None):
     """(idx [rows, top_k] int32, scores [rows, top_k] fp32 or None).
 
-    A caller-provided workspace must be zero-filled before its first use; every
-    successful call leaves it ready for the next (re-zero it after an error)."""
+    A caller-provided workspace is scratch of at least indexer_topk_workspace_size bytes
+    (no initialisation needed)."""
     _dev(scores, "scores", torch.float32, 2)
     rows, n_cols = scores.shape
     dev = scores.device
@@ -82,7 +87,7 @@ def indexer_topk_select(scores, top_k: int, *, valid_lens: Optional[torch.Tensor
         out_scores = torch.empty((rows, top_k), dtype=torch.float32, device=dev)
     if workspace is None:
         nbytes = indexer_topk_workspace_size(rows, n_cols, top_k)
-        workspace = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     check(_lib.load().indexer_topk_select(
         _ptr(scores), scores.stride(0), _ptr(valid_lens), first_pos, ratio, rows, n_cols, top_k, _ptr(out_idx),
         _ptr(out_scores), _ptr(workspace), workspace.numel(), _stream()))
@@ -94,13 +99,13 @@ def indexer_score_topk_workspace_size(T: int, max_lb: int, epb: int, top_k: int)
 
 
 def indexer_score_topk(q, w, keys_fp4, key_scale, key_gscale, block_table, valid_lens, *, top_k: int,
-                       precision: str = "mfma", with_scores: bool = False,
+                       precision: str = "mfma", with_scores: bool = False, validate: bool = False,
                        workspace: Optional[torch.Tensor] = None, out_idx: Optional[torch.Tensor] = None,
                        out_scores: Optional[torch.Tensor] = None):
     """(idx [T, top_k] int32, scores [T, top_k] fp32 or None) = TopK of the indexer scores.
 
-    A caller-provided workspace must be zero-filled before its first use (see
-    indexer_topk_select)."""
+    A caller-provided workspace is scratch of at least indexer_score_topk_workspace_size
+    bytes (no initialisation needed).  validate=True as for indexer_score_rows."""
     _dev(q, "q", (torch.float32, torch.bfloat16), 3)
     _dev(w, "w", torch.float32, 2)
     _dev(keys_fp4, "keys_fp4", torch.uint8, 3)
@@ -117,12 +122,13 @@ def indexer_score_topk(q, w, keys_fp4, key_scale, key_gscale, block_table, valid
     if with_scores and out_scores is None:
         out_scores = torch.empty((T, top_k), dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = torch.zeros(max(indexer_score_topk_workspace_size(T, max_lb, epb, top_k), 1), dtype=torch.uint8,
+        workspace = torch.empty(max(indexer_score_topk_workspace_size(T, max_lb, epb, top_k), 256), dtype=torch.uint8,
                                 device=dev)
     check(_lib.load().indexer_score_topk(
         _ptr(q), _q_dtype(q), _ptr(w), _ptr(keys_fp4), _ptr(key_scale), _ptr(key_gscale), _ptr(block_table),
-        block_table.stride(0), _ptr(valid_lens), T, H, D, epb, max_lb, P, top_k, PRECISION[precision], _ptr(out_idx),
-        _ptr(out_scores), _ptr(workspace), workspace.numel(), _stream()))
+        block_table.stride(0), _ptr(valid_lens), T, H, D, epb, max_lb, P, top_k, PRECISION[precision],
+        IDX_F_VALIDATE if validate else 0, _ptr(out_idx), _ptr(out_scores), _ptr(workspace), workspace.numel(),
+        _stream()))
     return out_idx, out_scores
 
 

@@ -34,12 +34,12 @@ def test_every_declared_symbol_is_exported():
 
 def _score_rows(lib, **over):
     args = dict(q=8, q_dtype=0, w=16, keys=256, scale=512, gscale=1024, bt=2048, bt_stride=4, valid=4096, T=1, H=4,
-                D=64, epb=16, max_lb=4, P=4, prec=1, scores=8192, stride=64, n_cols=64)
+                D=64, epb=16, max_lb=4, P=4, prec=1, flags=0, scores=8192, stride=64, n_cols=64)
     args.update(over)
     return lib.indexer_score_rows(args["q"], args["q_dtype"], args["w"], args["keys"], args["scale"], args["gscale"],
                                   args["bt"], args["bt_stride"], args["valid"], args["T"], args["H"], args["D"],
-                                  args["epb"], args["max_lb"], args["P"], args["prec"], args["scores"], args["stride"],
-                                  args["n_cols"], None)
+                                  args["epb"], args["max_lb"], args["P"], args["prec"], args["flags"], args["scores"],
+                                  args["stride"], args["n_cols"], None)
 
 
 def test_argument_checks_without_gpu():
@@ -53,6 +53,9 @@ def test_argument_checks_without_gpu():
     assert _score_rows(lib, prec=7) == _lib.IDX_ERR_UNSUPPORTED
     assert _score_rows(lib, keys=264) == _lib.IDX_ERR_SHAPE       # misaligned key pool
     assert _score_rows(lib, stride=10) == _lib.IDX_ERR_SHAPE
+    assert _score_rows(lib, flags=2) == _lib.IDX_ERR_UNSUPPORTED  # unknown flag bits
+    assert b"flags" in lib.indexer_last_error()
+    assert _score_rows(lib, T=0, flags=_lib.IDX_F_VALIDATE) == _lib.IDX_OK   # no work: no check, no launch
     assert _score_rows(lib, T=0) == _lib.IDX_OK                   # no work: no launch
     assert lib.indexer_last_error() == b""
     # select
@@ -61,9 +64,12 @@ def test_argument_checks_without_gpu():
     assert lib.indexer_topk_select(16, 60, None, 0, 0, 2, 64, 8, 32, None, None, 0, None) == _lib.IDX_ERR_SHAPE
     assert lib.indexer_topk_select(16, 64, None, 0, 0, 0, 64, 8, 32, None, None, 0, None) == _lib.IDX_OK
     # fused: workspace too small is reported before any launch
-    rc = lib.indexer_score_topk(8, 0, 16, 256, 512, 1024, 2048, 4, 4096, 1, 4, 64, 16, 4, 4, 8, 1, 8192, None, 256, 16,
-                                None)
+    rc = lib.indexer_score_topk(8, 0, 16, 256, 512, 1024, 2048, 4, 4096, 1, 4, 64, 16, 4, 4, 8, 1, 0, 8192, None, 256,
+                                16, None)
     assert rc == _lib.IDX_ERR_WORKSPACE
+    rc = lib.indexer_score_topk(8, 0, 16, 256, 512, 1024, 2048, 4, 4096, 1, 4, 64, 16, 4, 4, 8, 1, 4, 8192, None, 256,
+                                1 << 20, None)
+    assert rc == _lib.IDX_ERR_UNSUPPORTED
     # QSA
     assert lib.qsa_block_pool(None, 16, 32, 0, 1, 16, 128, 64, 1e4, 1e-6, None) == _lib.IDX_ERR_NULL
     assert lib.qsa_block_pool(16, 16, 32, 0, 1, 16, 100, 64, 1e4, 1e-6, None) == _lib.IDX_ERR_UNSUPPORTED

@@ -39,3 +39,29 @@ def test_traffic_entries_name_known_sources():
         assert w in bench.WORKLOADS
         assert kind in bench.SCORER_SOURCES
         assert len(sha) == 16 and fetch > 0 and write > 0
+
+
+def test_default_workload_is_the_long_context_decode():
+    assert bench.DEFAULT_WORKLOAD == "long_decode_T32_S262144"
+    assert bench.WORKLOADS[bench.DEFAULT_WORKLOAD] == 3
+
+
+def test_roofline_bound_follows_the_unique_byte_intensity():
+    from workloads.configs import csa
+
+    def wl(table):
+        return csa("rf", [5], T=8, H=64, D=128, epb=64, P=8 * 40, max_lb=40, top_k=64,
+                   valid_lens=[2560] * 8, dist="tiny", table=table)
+
+    shared = bench.csa_roofline(wl("shared"), 10e-6, "mfma")     # 8 rows share every page
+    own = bench.csa_roofline(wl("disjoint"), 10e-6, "mfma")       # every row on its own pages
+    assert shared["bound"] == "mfma" and shared["unit"] == "TFLOP/s"
+    assert own["bound"] == "hbm" and own["unit"] == "GB/s"
+    flops = 2.0 * 8 * 2560 * 64 * 128
+    assert shared["flops_per_launch"] == int(flops)
+    assert shared["achieved"] == pytest.approx(flops / 10e-6 / 1e12, rel=1e-3)
+    # per-stream bytes equal for both; the key bytes are 8x smaller when the pages are shared (q and
+    # the scores are the same in both)
+    assert shared["bytes_per_launch"] == own["bytes_per_launch"]
+    assert own["unique_bytes_per_launch"] > 3 * shared["unique_bytes_per_launch"]
+    assert bench.csa_roofline(wl("shared"), 10e-6, "fp32")["bound"] == "alu"

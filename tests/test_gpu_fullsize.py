@@ -9,25 +9,20 @@ import torch
 
 import sparse_attention_lightning_block_amd as salb
 from oracle import indexer, qsa
-from tests.parity import MFMA_ROWMAX, check_scores, check_topk, oracle_rows, to_dev
+from tests.parity import MFMA_ROWMAX, check_scores, check_topk, oracle_rows, oracle_rows_all, to_dev
 from workloads import make, make_diag
 
 pytestmark = pytest.mark.gpu
-
-# sampled rows: the longest and shortest valid rows, and a fixed middle one
-SAMPLE = {2: 3, 3: 1, 4: None}
 
 
 def _rows(w, cfg):
     if cfg == 4:
         return [w.T - 1, 2048, 513, 512, 511, 1, 0]     # causal rows across the k = 512 edge
-    order = np.argsort(w.valid_lens)
-    picks = [int(order[-1]), int(order[0]), w.T // 2]
-    return sorted(set(picks))[: SAMPLE[cfg]]
+    return list(range(w.T))                             # decode configs: every row
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_full_size_sampled_rows(cfg):
+def test_full_size_rows(cfg):
     w = make(cfg)
     d = to_dev(w)
     n_cols = w.max_lb * w.epb
@@ -38,7 +33,7 @@ def test_full_size_sampled_rows(cfg):
     idx, val = salb.indexer_topk_select(scores, w.top_k, valid_lens=d["valid_lens"], workspace=ws, with_scores=True)
     torch.cuda.synchronize()
     rows = _rows(w, cfg)
-    ref, amag = oracle_rows(w, rows)
+    ref, amag = oracle_rows_all(w, rows)
     for t in rows:
         g = scores[t].cpu().numpy()
         check_scores(g, ref[t], amag[t], "mfma", f"cfg{cfg} full t{t}")
@@ -78,9 +73,10 @@ def test_hbm_true_diagnostic_sampled_rows():
         assert np.all(gi[t, K:] == -1) and len(set(gi[t, :K].tolist())) == K
 
 
-def test_full_size_fused_matches_split():
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_full_size_fused_matches_split(cfg):
     """indexer_score_topk (the fused entry) returns what the two calls return."""
-    w = make(2)
+    w = make(cfg)
     d = to_dev(w)
     n_cols = w.max_lb * w.epb
     a_idx, a_val = salb.indexer_score_topk(**d, top_k=w.top_k, precision="mfma", with_scores=True)
@@ -116,14 +112,19 @@ def test_qsa_full_size_sampled():
         qr = qsa.qprep_rows(indexer.upcast(w.qk[r:r + 1], "bf16"), w.q_norm_w, 1, w.first_pos + r, w.n_heads * w.hd,
                             w.n_heads, w.hd, w.rot, w.theta, w.eps)[0]
         assert np.all(np.abs(q[r] - qr) <= 1e-5 * np.max(np.abs(qr), axis=-1, keepdims=True))
-    # scores and top-k of sampled rows, from the GPU's pooled keys and prepared queries
+    # scores and top-k of sampled rows against the oracle's own chain (pooled keys from the
+    # bf16 raw keys, prepared queries from the bf16 projections), not the GPU's intermediates
+    keys_o = qsa.block_pool(raw64, w.k_norm_w, 0, w.n_blocks, w.ratio, w.rot, w.theta, w.eps)
+    del raw64
     got = sc.cpu().numpy()
     gi, gv = idx.cpu().numpy(), val.cpu().numpy()
-    for r in (0, w.rows // 2, w.rows - 1):
-        ref, valid = qsa.score_rows(q[r:r + 1], keys, w.first_pos + r, w.ratio)
+    for r in (0, 1, w.rows // 3, w.rows // 2, w.rows - 2, w.rows - 1):
+        q_o = qsa.qprep_rows(indexer.upcast(w.qk[r:r + 1], "bf16"), w.q_norm_w, 1, w.first_pos + r,
+                             w.n_heads * w.hd, w.n_heads, w.hd, w.rot, w.theta, w.eps)
+        ref, valid = qsa.score_rows(q_o, keys_o, w.first_pos + r, w.ratio)
         v = int(valid[0])
         tol = np.full(v, MFMA_ROWMAX * np.max(np.abs(ref[0, :v])))
         err = np.abs(got[r, :v].astype(np.float64) - ref[0, :v])
-        assert np.all(err <= tol), f"qsa full row {r}: max err {err.max()}"
+        assert np.all(err <= tol), f"qsa full row {r}: max err {err.max()} tol {tol[0]}"
         assert np.all(np.isneginf(got[r, v:]))
         check_topk(gi[r], gv[r], ref[0, :v], None, w.top_k, "mfma", f"qsa full row {r}", tol=tol)

@@ -1,7 +1,7 @@
 """The hot path captured into HIP graphs: every replay, with eager work and
 synchronisations between the replays, returns exactly what the eager calls return
-(the select workspace is left zeroed by each call, so nothing needs clearing between
-replays).  Needs an MI355X."""
+(every call zeroes the workspace counters it needs inside its own launches, so nothing
+needs clearing between replays).  Needs an MI355X."""
 
 import numpy as np
 import pytest
@@ -22,7 +22,8 @@ def test_graph_replays_match_eager(cfg, reduced):
     scores = torch.empty((w.T, n_cols), dtype=torch.float32, device="cuda")
     idx = torch.empty((w.T, w.top_k), dtype=torch.int32, device="cuda")
     val = torch.empty((w.T, w.top_k), dtype=torch.float32, device="cuda")
-    ws = torch.zeros(salb.indexer_topk_workspace_size(w.T, n_cols, w.top_k), dtype=torch.uint8, device="cuda")
+    ws = torch.full((max(256, salb.indexer_topk_workspace_size(w.T, n_cols, w.top_k)),), 0xA5, dtype=torch.uint8,
+                    device="cuda")
 
     def path():
         salb.indexer_score_rows(**d, n_cols=n_cols, precision="mfma", out=scores)
@@ -87,4 +88,39 @@ def test_qsa_graph_replays_match_eager():
         assert torch.equal(sc.view(torch.int32), ref_s.view(torch.int32)), rep
         assert torch.equal(idx, ref_i), rep
         path()  # eager work between replays
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("cfg,reduced", [(2, 0), (3, 1)])
+def test_fused_entry_graph_replays_match_eager(cfg, reduced):
+    """indexer_score_topk captured whole (scorer, select stages; the scorer launch zeroes
+    the select counters): replays on a workspace left with another call's data between
+    replays equal the eager result."""
+    w = make(cfg, reduced)
+    d = to_dev(w)
+    nbytes = salb.indexer_score_topk_workspace_size(w.T, w.max_lb, w.epb, w.top_k)
+    ws = torch.full((nbytes,), 0x5A, dtype=torch.uint8, device="cuda")
+    idx = torch.empty((w.T, w.top_k), dtype=torch.int32, device="cuda")
+    val = torch.empty((w.T, w.top_k), dtype=torch.float32, device="cuda")
+
+    def path():
+        salb.indexer_score_topk(**d, top_k=w.top_k, precision="mfma", workspace=ws, out_idx=idx, out_scores=val)
+
+    path()
+    torch.cuda.synchronize()
+    ref_i, ref_v = idx.clone(), val.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        path()
+    other = make(2, 1)
+    od = to_dev(other)
+    for rep in range(3):
+        idx.fill_(-5)
+        val.fill_(3.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref_i), rep
+        assert torch.equal(val.view(torch.int32), ref_v.view(torch.int32)), rep
+        # eager work between replays, on the same workspace (another shape)
+        salb.indexer_score_topk(**od, top_k=other.top_k, precision="mfma", workspace=ws)
         torch.cuda.synchronize()

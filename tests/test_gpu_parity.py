@@ -249,9 +249,9 @@ def test_topk_select_degenerate(n_cols, k):
 
 
 def test_topk_select_workspace_reuse():
-    """One zero-filled workspace serves consecutive calls: each call leaves it ready."""
+    """One workspace, never cleared by the caller, serves consecutive calls of one shape."""
     rows, n_cols, k = 5, 90000, 2048
-    ws = torch.zeros(salb.indexer_topk_workspace_size(rows, n_cols, k), dtype=torch.uint8, device="cuda")
+    ws = torch.full((salb.indexer_topk_workspace_size(rows, n_cols, k),), 0x3C, dtype=torch.uint8, device="cuda")
     for it in range(3):
         rng = np.random.default_rng(500 + it)
         s = rng.standard_normal((rows, n_cols)).astype(np.float32)
@@ -322,3 +322,134 @@ def test_fused_entry_balanced_split():
     gi, gv = _row(a_idx), _row(a_val)
     for t in range(T):
         check_topk(gi[t], gv[t], ref[t], amag[t], 256, "mfma", f"fused balanced t{t}")
+
+
+# ------------------------------------------------------------------ signs of g and w
+
+SIGN_SHAPES = [
+    # T, table, epb: the kernel each one reaches on the MFMA path
+    (2, "shared", 64),     # fewer than four rows: the one-row split scorer (page-uniform steps)
+    (3, "per_row", 7),     # split scorer, steps crossing pages
+    (6, "shared", 64),     # four-row groups, each tile decoded once into LDS
+    (6, "per_row", 64),    # four-row groups whose rows read different pages: per-wave streams
+    (24, "shared", 64),    # eight-row groups, balanced split
+    (24, "per_row", 16),   # eight-row groups, per-wave streams
+    (260, "shared", 16),   # more than 256 rows: chunked eight-row groups
+]
+
+
+@pytest.mark.parametrize("precision", ["mfma", "fp32"])
+@pytest.mark.parametrize("T,table,epb", SIGN_SHAPES)
+def test_negative_gscale_and_weights(T, table, epb, precision):
+    """Global scales negative on every third page and head weights negative on some heads
+    (the header allows any sign): ReLU acts on g * dot, so the sign of g is folded into
+    the decoded code values and |g| applied after the ReLU on the MFMA path.  Every
+    kernel shape against the oracle, scores and top-k."""
+    if precision == "fp32" and T > 24:
+        pytest.skip("the fp32 scorer has one shape; covered by the smaller cases")
+    n_keys = 1500 if T < 200 else 400
+    max_lb = -(-n_keys // epb)
+    w = csa(f"signs_{T}_{table}", [93, T, epb], T=T, H=64, D=128, epb=epb, P=max_lb * 2 + 3, max_lb=max_lb,
+            top_k=48, valid_lens=lambda rng, n: rng.integers(1, max_lb * epb + 1, size=n), dist="gauss",
+            w_scale=1 / 64, table=table)
+    w.key_gscale = w.key_gscale.copy()
+    w.key_gscale[::3] *= -1.0
+    w.w = w.w.copy()
+    w.w[:, 1::5] *= -1.0
+    w.w[: T // 2, 0] = -0.5
+    d = to_dev(w)
+    n_cols = max_lb * epb
+    rows = salb.indexer_score_rows(**d, n_cols=n_cols, precision=precision)
+    idx, val = salb.indexer_score_topk(**d, top_k=48, precision=precision, with_scores=True)
+    torch.cuda.synchronize()
+    gr, gi, gv = _row(rows), _row(idx), _row(val)
+    ref, amag = oracle_rows(w)
+    assert any(np.any(r < 0) for r in ref.values()), "the case must produce negative scores"
+    for t in range(T):
+        check_scores(gr[t], ref[t], amag[t], precision, f"signs T{T} {table} t{t}")
+        assert np.all(np.isneginf(gr[t, int(w.valid_lens[t]):]))
+        check_topk(gi[t], gv[t], ref[t], amag[t], 48, precision, f"signs T{T} {table} t{t}")
+
+
+# ------------------------------------------------------------------ IDX_F_VALIDATE
+
+def test_validate_accepts_in_range_data():
+    w = make(2, reduced=1)
+    d = to_dev(w)
+    a_idx, a_val = salb.indexer_score_topk(**d, top_k=w.top_k, precision="mfma", with_scores=True, validate=True)
+    b_idx, b_val = salb.indexer_score_topk(**d, top_k=w.top_k, precision="mfma", with_scores=True)
+    assert torch.equal(a_idx, b_idx) and torch.equal(a_val.view(torch.int32), b_val.view(torch.int32))
+    n_cols = w.max_lb * w.epb
+    a = salb.indexer_score_rows(**d, n_cols=n_cols, precision="mfma", validate=True)
+    b = salb.indexer_score_rows(**d, n_cols=n_cols, precision="mfma")
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_validate_rejects_bad_metadata_before_scoring():
+    """A page id outside the pool inside a row's valid range, or a valid length past the
+    table: IDX_ERR_DATA names it and nothing else is launched (the outputs keep their
+    contents).  Only the check kernel runs on such data, and it reads valid_lens and the
+    block table alone."""
+    w = make(2, reduced=1)
+    d = to_dev(w)
+    bt = d["block_table"].clone()
+    bt[1, 5] = w.P            # row 1 reads logical block 5 (valid 2000 > 5 * 64)
+    idx = torch.full((w.T, w.top_k), -7, dtype=torch.int32, device="cuda")
+    with pytest.raises(salb.IndexerError) as e:
+        salb.indexer_score_topk(**dict(d, block_table=bt), top_k=w.top_k, precision="mfma", validate=True,
+                                out_idx=idx)
+    assert e.value.code == salb.IDX_ERR_DATA and "block_table[1][5]" in str(e.value)
+    assert torch.all(idx == -7)
+    vl = d["valid_lens"].clone()
+    vl[2] = w.max_lb * w.epb + 1
+    with pytest.raises(salb.IndexerError) as e:
+        salb.indexer_score_topk(**dict(d, valid_lens=vl), top_k=w.top_k, precision="mfma", validate=True,
+                                out_idx=idx)
+    assert e.value.code == salb.IDX_ERR_DATA and "valid_lens[2]" in str(e.value)
+    assert torch.all(idx == -7)
+    # the split entry: its scores buffer only carries the check's status word
+    n_cols = w.max_lb * w.epb
+    out = torch.full((w.T, n_cols), 2.5, dtype=torch.float32, device="cuda")
+    with pytest.raises(salb.IndexerError) as e:
+        salb.indexer_score_rows(**dict(d, block_table=bt), n_cols=n_cols, precision="mfma", validate=True, out=out)
+    assert e.value.code == salb.IDX_ERR_DATA
+    assert torch.all(out.view(-1)[4:] == 2.5)
+    # entries past a row's valid keys are never read, so -1 there is accepted
+    bt2 = d["block_table"].clone()
+    for t in range(w.T):
+        bt2[t, -(-int(w.valid_lens[t]) // w.epb):] = -1
+    a_idx, _ = salb.indexer_score_topk(**dict(d, block_table=bt2), top_k=w.top_k, precision="mfma", validate=True)
+    b_idx, _ = salb.indexer_score_topk(**d, top_k=w.top_k, precision="mfma")
+    assert torch.equal(a_idx, b_idx)
+
+
+# ------------------------------------------------------------------ workspace as scratch
+
+def test_one_workspace_serves_every_shape():
+    """One workspace, filled with garbage first, serves selects and fused calls of
+    different shapes in turn (each call initialises what it reads): every result equals
+    the oracle's (selects on fixed scores are exact) or a fresh-workspace call's."""
+    shapes = [(5, 90000, 2048), (3, 300000, 1024), (9, 20000, 512), (5, 90000, 2048), (40, 12000, 64)]
+    need = max(salb.indexer_topk_workspace_size(r, n, k) for r, n, k in shapes)
+    w2 = make(2, reduced=1)
+    w3 = make(3, reduced=1)
+    need = max(need, *(salb.indexer_score_topk_workspace_size(w.T, w.max_lb, w.epb, w.top_k) for w in (w2, w3)))
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    fused_ref = {}
+    for w in (w2, w3):
+        fused_ref[w.name] = salb.indexer_score_topk(**to_dev(w), top_k=w.top_k, precision="mfma")[0]
+    for it, (rows, n_cols, k) in enumerate(shapes):
+        rng = np.random.default_rng(700 + it)
+        s = rng.standard_normal((rows, n_cols)).astype(np.float32)
+        s[0, ::5] = 2.0                          # ties at the threshold
+        valid = rng.integers(0, n_cols + 1, rows).astype(np.int32)
+        valid[0] = n_cols
+        idx, _ = salb.indexer_topk_select(torch.from_numpy(s).cuda(), k, valid_lens=torch.from_numpy(valid).cuda(),
+                                          workspace=ws)
+        gi = _row(idx)
+        for r in range(rows):
+            o_idx, _ = indexer.topk(s[r, : valid[r]].astype(np.float64), k)
+            assert gi[r].tolist() == o_idx.tolist(), (it, r)
+        w = (w2, w3)[it % 2]
+        got = salb.indexer_score_topk(**to_dev(w), top_k=w.top_k, precision="mfma", workspace=ws)[0]
+        assert torch.equal(got, fused_ref[w.name]), (it, w.name)
