@@ -161,6 +161,29 @@ int indexer_score_topk(const void* q, int q_dtype, const float* w,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * indexer_score_topk_noalloc -- indexer_score_topk for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without the workspace, which lives instead in
+ * a scratch array of IDX_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends.  Results are those of indexer_score_topk.
+ *  - Calls whose indexer_score_topk_workspace_size(T, max_lb, epb, top_k) exceeds the
+ *    scratch return IDX_ERR_WORKSPACE before any HIP call.
+ *  - The scratch of the current device (hipGetDevice) is used; `stream` must belong to
+ *    that device.  Its address is looked up once per device; no call allocates or
+ *    frees anything.
+ *  - All calls on one GPU share its scratch: calls that overlap in time on one GPU
+ *    (different streams, or threads without ordering) race and give undefined results.
+ *    Each call initialises what it reads, so calls of any shapes may follow each other.
+ */
+#define IDX_NOALLOC_SCRATCH_BYTES (128ull << 20)
+int indexer_score_topk_noalloc(const void* q, int q_dtype, const float* w,
+                               const uint8_t* keys_fp4, const uint8_t* key_scale, const float* key_gscale,
+                               const int32_t* block_table, int64_t bt_stride, const int32_t* valid_lens,
+                               int T, int H, int D, int epb, int max_lb, int n_pages, int top_k,
+                               int precision, unsigned flags, int32_t* topk_idx, float* topk_scores,
+                               hipStream_t stream);
+
+/*
  * qsa_block_pool -- pooled QSA block keys ([qsa.rs] qsa_block_pool).
  *
  * For b in [first_block, first_block + n_new):

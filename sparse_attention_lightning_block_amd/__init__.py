@@ -6,6 +6,7 @@ from .ops import (  # noqa: F401
     indexer_debug_dequant,
     indexer_score_rows,
     indexer_score_topk,
+    indexer_score_topk_noalloc,
     indexer_score_topk_workspace_size,
     indexer_topk_select,
     indexer_topk_workspace_size,

@@ -21,6 +21,7 @@ IDX_ERR_HIP = 5
 IDX_ERR_DATA = 6
 
 IDX_F_VALIDATE = 1
+IDX_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 IDX_DTYPE_F32 = 0
 IDX_DTYPE_BF16 = 1
@@ -44,6 +45,8 @@ SIGNATURES = {
     "indexer_score_topk_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "indexer_score_topk": (_I, [_P, _I, _P, _P, _P, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _I, _I, _U32, _P, _P,
                                 _P, _SZ, _P]),
+    "indexer_score_topk_noalloc": (_I, [_P, _I, _P, _P, _P, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _I, _I, _U32,
+                                        _P, _P, _P]),
     "qsa_block_pool": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _F, _F, _P]),
     "qsa_qprep_rows": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _F, _F, _P]),
     "qsa_score_rows": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _I, _P]),

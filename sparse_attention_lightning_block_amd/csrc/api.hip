@@ -4,6 +4,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/indexer.h"
@@ -106,6 +107,40 @@ int validate_if_asked(unsigned flags, const int32_t* bt, int64_t bt_stride, cons
 int check_flags(unsigned flags) {
   if (flags & ~(unsigned)IDX_F_VALIDATE) return fail(IDX_ERR_UNSUPPORTED, "flags 0x%x", flags);
   return IDX_OK;
+}
+
+}  // namespace
+
+// Workspace of indexer_score_topk_noalloc: one copy per GPU, held from the library's
+// load until the process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory: only the address hipGetSymbolAddress returns for the current device
+// may be handed to kernels.
+static __device__ __align__(256) unsigned char scratch[IDX_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// The current device's address of `scratch`, looked up once per device (with that
+// device current) and kept; NULL with the HIP error in *err on failure.
+void* scratch_on_current_device(hipError_t* err) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
 }
 
 }  // namespace
@@ -238,6 +273,32 @@ int indexer_score_topk(const void* q, int q_dtype, const float* w, const uint8_t
   e = salb::launch_select(p, sc, (int64_t)stride, valid_lens, 0, 0, topk_idx, topk_scores, sel_ws, true, stream);
   if (e != hipSuccess) return hip_fail(e, "select kernel launch");
   return ok();
+}
+
+int indexer_score_topk_noalloc(const void* q, int q_dtype, const float* w, const uint8_t* keys_fp4,
+                               const uint8_t* key_scale, const float* key_gscale, const int32_t* block_table,
+                               int64_t bt_stride, const int32_t* valid_lens, int T, int H, int D, int epb,
+                               int max_lb, int n_pages, int top_k, int precision, unsigned flags,
+                               int32_t* topk_idx, float* topk_scores, hipStream_t stream) {
+  // the size rule first, on the host: no HIP call for a call that cannot fit
+  if (T > 0 && max_lb > 0 && epb > 0 && top_k > 0) {
+    const size_t need = indexer_score_topk_workspace_size(T, max_lb, epb, top_k);
+    if (need > (size_t)IDX_NOALLOC_SCRATCH_BYTES)
+      return fail(IDX_ERR_WORKSPACE, "the call needs %zu bytes of scratch; the no-alloc entry holds %llu", need,
+                  (unsigned long long)IDX_NOALLOC_SCRATCH_BYTES);
+  }
+  int rc = check_paged(q, q_dtype, w, keys_fp4, key_scale, key_gscale, block_table, bt_stride, valid_lens, T, H, D,
+                       epb, max_lb, n_pages, precision);
+  if (rc) return rc;
+  if (T == 0) return indexer_score_topk(q, q_dtype, w, keys_fp4, key_scale, key_gscale, block_table, bt_stride,
+                                        valid_lens, T, H, D, epb, max_lb, n_pages, top_k, precision, flags, topk_idx,
+                                        topk_scores, nullptr, 0, stream);
+  hipError_t e = hipSuccess;
+  void* ws = scratch_on_current_device(&e);
+  if (!ws) return hip_fail(e, "no-alloc scratch address");
+  return indexer_score_topk(q, q_dtype, w, keys_fp4, key_scale, key_gscale, block_table, bt_stride, valid_lens, T, H,
+                            D, epb, max_lb, n_pages, top_k, precision, flags, topk_idx, topk_scores, ws,
+                            (size_t)IDX_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int qsa_block_pool(const uint16_t* raw_keys, const float* k_norm_w, float* block_keys, uint32_t first_block,

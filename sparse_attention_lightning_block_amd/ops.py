@@ -132,6 +132,29 @@ def indexer_score_topk(q, w, keys_fp4, key_scale, key_gscale, block_table, valid
     return out_idx, out_scores
 
 
+def indexer_score_topk_noalloc(q, w, keys_fp4, key_scale, key_gscale, block_table, valid_lens, *, top_k: int,
+                               precision: str = "mfma", validate: bool = False, out_idx: Optional[torch.Tensor] = None,
+                               out_scores: Optional[torch.Tensor] = None, with_scores: bool = False):
+    """indexer_score_topk with the library's own per-GPU scratch instead of a workspace
+    (for callers that cannot allocate device memory; the outputs are still the caller's)."""
+    _dev(q, "q", (torch.float32, torch.bfloat16), 3)
+    for t, name, dt, nd in ((w, "w", torch.float32, 2), (keys_fp4, "keys_fp4", torch.uint8, 3),
+                            (key_scale, "key_scale", torch.uint8, 3), (key_gscale, "key_gscale", torch.float32, 1),
+                            (block_table, "block_table", torch.int32, 2), (valid_lens, "valid_lens", torch.int32, 1)):
+        _dev(t, name, dt, nd)
+    T, H, D = q.shape
+    P, epb, _ = keys_fp4.shape
+    if out_idx is None:
+        out_idx = torch.empty((T, top_k), dtype=torch.int32, device=q.device)
+    if with_scores and out_scores is None:
+        out_scores = torch.empty((T, top_k), dtype=torch.float32, device=q.device)
+    check(_lib.load().indexer_score_topk_noalloc(
+        _ptr(q), _q_dtype(q), _ptr(w), _ptr(keys_fp4), _ptr(key_scale), _ptr(key_gscale), _ptr(block_table),
+        block_table.stride(0), _ptr(valid_lens), T, H, D, epb, block_table.shape[1], P, top_k, PRECISION[precision],
+        IDX_F_VALIDATE if validate else 0, _ptr(out_idx), _ptr(out_scores), _stream()))
+    return out_idx, out_scores
+
+
 def qsa_block_pool(raw_keys, k_norm_w, block_keys, *, first_block: int, n_new: int, ratio: int, rot: int,
                    theta: float, eps: float) -> torch.Tensor:
     """Writes block_keys[first_block : first_block + n_new] (fp32) from bf16 raw keys."""
