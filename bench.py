@@ -43,6 +43,9 @@ WORKLOADS = {
     # diagnostic, not a configuration: the long-decode shape with every row on its own
     # pages of a 604 MB pool, so that every key byte read comes from DRAM
     "hbm_true_T32_S262144": "diag",
+    # the selected-entry gathers that consume the top-k (workloads/gather.py)
+    "gather_T32_k2048": "gather",
+    "qsa_gather_4096": "gather",
 }
 # Decode workloads also timed cold: the key pool rotates through enough copies that the
 # copies read between two uses of one copy exceed twice the 256 MB last-level cache.
@@ -297,6 +300,96 @@ def run_qsa(args, w):
     print(json.dumps(out), flush=True)
 
 
+def run_gather(args, name):
+    """The selected-entry gathers: one step is one gather call, timed back to back."""
+    import torch
+
+    import sparse_attention_lightning_block_amd as salb
+    from workloads.device import bf16_tensor
+    from workloads.gather import GATHER_WORKLOADS
+
+    w = GATHER_WORKLOADS[name]()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if name.startswith("qsa"):
+        k = bf16_tensor(w.k_cache).to(dev)
+        v = bf16_tensor(w.v_cache).to(dev)
+        bt = torch.from_numpy(w.block_table).to(dev)
+        sel = torch.from_numpy(w.sel).to(dev)
+        ko = torch.empty((w.n_sel, w.nkv, w.hd), dtype=torch.bfloat16, device=dev)
+        vo = torch.empty_like(ko)
+
+        def step():
+            salb.qsa_gather(k, v, bt, sel, k_out=ko, v_out=vo)
+
+        row = w.nkv * w.hd * 2
+        bytes_moved = w.n_sel * (2 * row * 2 + 4 + 4)      # K and V rows read and written, position, table entry
+        units, unit = w.n_sel, "positions"
+        kernel = "qsa_gather_kernel"
+        cfg = {"workload": name, "n_sel": w.n_sel, "block_size": w.block_size, "nkv": w.nkv, "hd": w.hd,
+               "cache_tokens": w.n_blocks * w.block_size}
+    else:
+        fp8 = torch.from_numpy(w.fp8).to(dev)
+        sc = torch.from_numpy(w.scale).to(dev)
+        rope = bf16_tensor(w.rope_bits).to(dev)
+        bt = torch.from_numpy(w.block_table).to(dev)
+        idx = torch.from_numpy(w.topk_idx).to(dev)
+        out = torch.empty((w.T, w.top_k, w.d_nope + w.d_rope), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            salb.indexer_gather_kv(fp8, sc, rope, bt, idx, group=w.group, out=out)
+
+        n = w.entries
+        per_entry = w.d_nope + 4 * (w.d_nope // w.group) + 2 * w.d_rope      # FP8 codes, scales, rope
+        bytes_moved = n * (per_entry + 4) + w.T * w.top_k * (4 + 2 * (w.d_nope + w.d_rope))
+        units, unit = n, "entries"
+        kernel = "gather_kv_kernel"
+        cfg = {"workload": name, "T": w.T, "top_k": w.top_k, "entries": n, "entries_per_block": w.epb,
+               "d_nope": w.d_nope, "d_rope": w.d_rope, "group": w.group}
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step, stage = timed_steps(torch, make_step(torch, [step], args.graph), 1, args.steps)
+    kern_ms = back_to_back_ms(torch, step, args.steps)
+    gbs = bytes_moved / (kern_ms / 1e3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": units / (ms_per_step / 1e3),
+        "unit": f"{unit}/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": dict(cfg, launch="hip_graph" if args.graph else "eager"),
+        "step_ms": {"p10": float(np.percentile(stage[0], 10)), "p50": float(np.median(stage[0])),
+                    "p90": float(np.percentile(stage[0], 90))},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kernel,
+                     "kernel_avg_us": round(kern_ms * 1e3, 2), "bytes_per_launch": int(bytes_moved)},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_gather(w, name, units, unit),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_gather(w, name, units, unit):
+    """The oracle gather on the whole workload (a few seconds), as it stands."""
+    from oracle import gather
+
+    t0 = time.perf_counter()
+    if name.startswith("qsa"):
+        gather.qsa_gather(w.k_cache, w.v_cache, w.block_table, w.sel, w.block_size)
+    else:
+        gather.gather_kv(w.fp8, w.scale, w.rope_bits, w.block_table, w.topk_idx, w.epb, w.group)
+    dt = time.perf_counter() - t0
+    return {"value": units / dt, "unit": f"{unit}/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole workload ({units} {unit}), numpy on one thread: {dt:.2f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,6 +414,9 @@ def main():
     from workloads.device import to_dev
     from workloads import make, make_diag
 
+    if WORKLOADS[args.workload] == "gather":
+        run_gather(args, args.workload)
+        return
     w = make_diag(args.workload) if WORKLOADS[args.workload] == "diag" else make(WORKLOADS[args.workload])
     if w.kind == "qsa":
         run_qsa(args, w)

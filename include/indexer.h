@@ -184,6 +184,46 @@ int indexer_score_topk_noalloc(const void* q, int q_dtype, const float* w,
                                hipStream_t stream);
 
 /*
+ * indexer_gather_kv -- the selected entries as a dense bf16 tile ([commits] c2f705a21a,
+ * gather_kv.cu: FP8 + BF16 split entries of a paged pool, resolved through the block
+ * table, dequantised to one dense [T, top_k, head_dim] bf16 tile).
+ *
+ * For t < T and i < top_k, with s = topk_idx[t, i]:
+ *   s in [0, max_lb*epb): p = block_table[t * bt_stride + s / epb], e = p * epb + s % epb,
+ *     out[t, i, d]          = bf16(E4M3(kv_fp8[e, d]) * kv_scale[e, d / group])  d < d_nope
+ *     out[t, i, d_nope + j] = kv_rope[e, j]                                      j < d_rope
+ *   otherwise (the -1 padding of a top-k): out[t, i, :] = 0.
+ * bf16(x) is one round-to-nearest-even of the exact product (for products in the normal
+ * fp32 range; the product is never rounded to fp32 first).
+ *  kv_fp8    [n_pages, epb, d_nope] uint8 OCP E4M3 codes, 16-byte aligned
+ *  kv_scale  [n_pages, epb, d_nope / group] fp32
+ *  kv_rope   [n_pages, epb, d_rope] bf16 (uint16 bit patterns), 16-byte aligned
+ *  out       [T, top_k, d_nope + d_rope] bf16 output, 16-byte aligned
+ * Page ids outside [0, n_pages) among the entries selected are undefined behaviour (the
+ * indices come from indexer_score_topk, which only returns entries below valid_lens).
+ * Supported: d_nope a multiple of 16, group a multiple of 16 dividing it, d_rope a
+ * multiple of 8, 1 <= epb <= 65536, max_lb * epb < 2^24.
+ */
+int indexer_gather_kv(const uint8_t* kv_fp8, const float* kv_scale, const uint16_t* kv_rope,
+                      const int32_t* block_table, int64_t bt_stride, const int32_t* topk_idx,
+                      int T, int top_k, int epb, int max_lb, int n_pages, int d_nope, int d_rope, int group,
+                      uint16_t* out, hipStream_t stream);
+
+/*
+ * qsa_gather -- selected tokens' K/V rows into contiguous scratch ([qsa.rs] qsa_gather):
+ *   k_out[i, :, :] = k_cache[block_table[sel[i] / block_size], sel[i] % block_size, :, :]
+ *   v_out[i, :, :] = v_cache[...same...]                                       i < n_sel
+ *  k_cache, v_cache [n_blocks, block_size, nkv, hd] 2-byte elements (bf16), 16-byte aligned
+ *  block_table      [>= max(sel) / block_size + 1] int32 (one sequence)
+ *  sel              [n_sel] int32 token positions; outside the table is undefined behaviour
+ *  k_out, v_out     [n_sel, nkv, hd] outputs, 16-byte aligned
+ * A bit copy.  Supported: nkv * hd a multiple of 8.
+ */
+int qsa_gather(const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* block_table, const int32_t* sel,
+               uint16_t* k_out, uint16_t* v_out, uint32_t n_sel, uint32_t block_size, uint32_t nkv, uint32_t hd,
+               hipStream_t stream);
+
+/*
  * qsa_block_pool -- pooled QSA block keys ([qsa.rs] qsa_block_pool).
  *
  * For b in [first_block, first_block + n_new):

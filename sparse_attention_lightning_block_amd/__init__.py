@@ -4,6 +4,7 @@ hand-written HIP kernels of libsalb_indexer.so."""
 
 from .ops import (  # noqa: F401
     indexer_debug_dequant,
+    indexer_gather_kv,
     indexer_score_rows,
     indexer_score_topk,
     indexer_score_topk_noalloc,
@@ -11,6 +12,7 @@ from .ops import (  # noqa: F401
     indexer_topk_select,
     indexer_topk_workspace_size,
     qsa_block_pool,
+    qsa_gather,
     qsa_qprep_rows,
     qsa_score_rows,
 )

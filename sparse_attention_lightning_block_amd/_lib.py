@@ -47,6 +47,8 @@ SIGNATURES = {
                                 _P, _SZ, _P]),
     "indexer_score_topk_noalloc": (_I, [_P, _I, _P, _P, _P, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _I, _I, _U32,
                                         _P, _P, _P]),
+    "indexer_gather_kv": (_I, [_P, _P, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "qsa_gather": (_I, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _P]),
     "qsa_block_pool": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _F, _F, _P]),
     "qsa_qprep_rows": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _F, _F, _P]),
     "qsa_score_rows": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _I, _P]),

@@ -301,6 +301,53 @@ int indexer_score_topk_noalloc(const void* q, int q_dtype, const float* w, const
                             (size_t)IDX_NOALLOC_SCRATCH_BYTES, stream);
 }
 
+int indexer_gather_kv(const uint8_t* kv_fp8, const float* kv_scale, const uint16_t* kv_rope,
+                      const int32_t* block_table, int64_t bt_stride, const int32_t* topk_idx, int T, int top_k,
+                      int epb, int max_lb, int n_pages, int d_nope, int d_rope, int group, uint16_t* out,
+                      hipStream_t stream) {
+  if (T < 0 || top_k < 1) return fail(IDX_ERR_SHAPE, "T = %d, top_k = %d: need T >= 0 and top_k >= 1", T, top_k);
+  if (!block_table || !topk_idx || !out || (d_nope > 0 && (!kv_fp8 || !kv_scale)) || (d_rope > 0 && !kv_rope))
+    return fail(IDX_ERR_NULL, "block_table, topk_idx, out and the pool arrays of nonzero width are required");
+  if (epb < 1 || epb > 65536) return fail(IDX_ERR_SHAPE, "entries_per_block %d (supported: 1..65536)", epb);
+  if (max_lb < 1 || n_pages < 1) return fail(IDX_ERR_SHAPE, "max_lb and n_pages must be >= 1");
+  if (bt_stride < max_lb) return fail(IDX_ERR_SHAPE, "bt_stride %lld < max_lb %d", (long long)bt_stride, max_lb);
+  if ((int64_t)max_lb * epb >= kMaxCols)
+    return fail(IDX_ERR_UNSUPPORTED, "max_lb * epb = %lld (supported: < 2^24)", (long long)max_lb * epb);
+  if (d_nope < 0 || d_nope % 16 || d_rope < 0 || d_rope % 8 || d_nope + d_rope < 8)
+    return fail(IDX_ERR_UNSUPPORTED, "d_nope %d must be a multiple of 16 and d_rope %d of 8 (sum >= 8)", d_nope,
+                d_rope);
+  if (d_nope > 0 && (group < 16 || group % 16 || d_nope % group))
+    return fail(IDX_ERR_UNSUPPORTED, "group %d must be a multiple of 16 dividing d_nope %d", group, d_nope);
+  if (!aligned(kv_fp8, 16) || !aligned(kv_rope, 16) || !aligned(out, 16) || !aligned(kv_scale, 4) ||
+      !aligned(block_table, 4) || !aligned(topk_idx, 4))
+    return fail(IDX_ERR_SHAPE, "kv_fp8, kv_rope and out must be 16-byte aligned");
+  if (T == 0) return ok();
+  hipError_t e = salb::launch_gather_kv(kv_fp8, kv_scale, kv_rope, block_table, bt_stride, topk_idx, T, top_k, epb,
+                                        max_lb, d_nope, d_rope, group, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return ok();
+}
+
+int qsa_gather(const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* block_table, const int32_t* sel,
+               uint16_t* k_out, uint16_t* v_out, uint32_t n_sel, uint32_t block_size, uint32_t nkv, uint32_t hd,
+               hipStream_t stream) {
+  if (!k_cache || !v_cache || !block_table || !sel || !k_out || !v_out)
+    return fail(IDX_ERR_NULL, "k_cache, v_cache, block_table, sel, k_out and v_out are required");
+  if (block_size < 1) return fail(IDX_ERR_SHAPE, "block_size must be >= 1");
+  if (nkv < 1 || hd < 1 || ((uint64_t)nkv * hd) % 8 || (uint64_t)nkv * hd > (1u << 20))
+    return fail(IDX_ERR_UNSUPPORTED, "nkv * hd = %llu must be a multiple of 8 (at most 2^20)",
+                (unsigned long long)nkv * hd);
+  if (n_sel > 0x7fffffffu) return fail(IDX_ERR_SHAPE, "n_sel too large");
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) ||
+      !aligned(block_table, 4) || !aligned(sel, 4))
+    return fail(IDX_ERR_SHAPE, "caches and outputs must be 16-byte aligned");
+  if (n_sel == 0) return ok();
+  hipError_t e = salb::launch_qsa_gather(k_cache, v_cache, block_table, sel, k_out, v_out, (int)n_sel,
+                                         (int)block_size, (int)nkv, (int)hd, stream);
+  if (e != hipSuccess) return hip_fail(e, "QSA gather launch");
+  return ok();
+}
+
 int qsa_block_pool(const uint16_t* raw_keys, const float* k_norm_w, float* block_keys, uint32_t first_block,
                    uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot, float theta, float eps,
                    hipStream_t stream) {

@@ -69,6 +69,14 @@ hipError_t launch_select(const SelectPlan& p, const float* scores, int64_t score
 size_t select_counter_bytes(const SelectPlan& p);
 size_t select_workspace_bytes(int rows, int n_cols, int top_k);  // 0 if unsupported
 
+// Selected-entry gathers (gather.hip).
+hipError_t launch_gather_kv(const uint8_t* fp8, const float* scale, const uint16_t* rope, const int32_t* bt,
+                            int64_t bt_stride, const int32_t* idx, int T, int top_k, int epb, int max_lb,
+                            int d_nope, int d_rope, int group, uint16_t* out, hipStream_t st);
+hipError_t launch_qsa_gather(const uint16_t* k, const uint16_t* v, const int32_t* bt, const int32_t* sel,
+                             uint16_t* k_out, uint16_t* v_out, int n_sel, int block_size, int nkv, int hd,
+                             hipStream_t st);
+
 // QSA (qsa.hip).
 hipError_t launch_block_pool(const uint16_t* raw, const float* kw, float* out, uint32_t first_block,
                              uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot, float theta,

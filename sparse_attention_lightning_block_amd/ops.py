@@ -34,6 +34,11 @@ def _dev(t: torch.Tensor, name: str, dtype=None, dims=None) -> torch.Tensor:
     return t
 
 
+def _row_stride(t: torch.Tensor) -> int:
+    """Elements between rows of a 2-D tensor (a single row's stride is its width)."""
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
 def _q_dtype(q: torch.Tensor) -> int:
     return IDX_DTYPE_BF16 if q.dtype == torch.bfloat16 else IDX_DTYPE_F32
 
@@ -60,8 +65,8 @@ def indexer_score_rows(q, w, keys_fp4, key_scale, key_gscale, block_table, valid
     _dev(out, "out", torch.float32, 2)
     check(_lib.load().indexer_score_rows(
         _ptr(q), _q_dtype(q), _ptr(w), _ptr(keys_fp4), _ptr(key_scale), _ptr(key_gscale), _ptr(block_table),
-        block_table.stride(0), _ptr(valid_lens), T, H, D, epb, block_table.shape[1], P, PRECISION[precision],
-        IDX_F_VALIDATE if validate else 0, _ptr(out), out.stride(0), n_cols, _stream()))
+        _row_stride(block_table), _ptr(valid_lens), T, H, D, epb, block_table.shape[1], P, PRECISION[precision],
+        IDX_F_VALIDATE if validate else 0, _ptr(out), _row_stride(out), n_cols, _stream()))
     return out
 
 
@@ -89,7 +94,7 @@ def indexer_topk_select(scores, top_k: int, *, valid_lens: Optional[torch.Tensor
         nbytes = indexer_topk_workspace_size(rows, n_cols, top_k)
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     check(_lib.load().indexer_topk_select(
-        _ptr(scores), scores.stride(0), _ptr(valid_lens), first_pos, ratio, rows, n_cols, top_k, _ptr(out_idx),
+        _ptr(scores), _row_stride(scores), _ptr(valid_lens), first_pos, ratio, rows, n_cols, top_k, _ptr(out_idx),
         _ptr(out_scores), _ptr(workspace), workspace.numel(), _stream()))
     return out_idx, out_scores
 
@@ -126,7 +131,7 @@ def indexer_score_topk(q, w, keys_fp4, key_scale, key_gscale, block_table, valid
                                 device=dev)
     check(_lib.load().indexer_score_topk(
         _ptr(q), _q_dtype(q), _ptr(w), _ptr(keys_fp4), _ptr(key_scale), _ptr(key_gscale), _ptr(block_table),
-        block_table.stride(0), _ptr(valid_lens), T, H, D, epb, max_lb, P, top_k, PRECISION[precision],
+        _row_stride(block_table), _ptr(valid_lens), T, H, D, epb, max_lb, P, top_k, PRECISION[precision],
         IDX_F_VALIDATE if validate else 0, _ptr(out_idx), _ptr(out_scores), _ptr(workspace), workspace.numel(),
         _stream()))
     return out_idx, out_scores
@@ -150,9 +155,47 @@ def indexer_score_topk_noalloc(q, w, keys_fp4, key_scale, key_gscale, block_tabl
         out_scores = torch.empty((T, top_k), dtype=torch.float32, device=q.device)
     check(_lib.load().indexer_score_topk_noalloc(
         _ptr(q), _q_dtype(q), _ptr(w), _ptr(keys_fp4), _ptr(key_scale), _ptr(key_gscale), _ptr(block_table),
-        block_table.stride(0), _ptr(valid_lens), T, H, D, epb, block_table.shape[1], P, top_k, PRECISION[precision],
+        _row_stride(block_table), _ptr(valid_lens), T, H, D, epb, block_table.shape[1], P, top_k, PRECISION[precision],
         IDX_F_VALIDATE if validate else 0, _ptr(out_idx), _ptr(out_scores), _stream()))
     return out_idx, out_scores
+
+
+def indexer_gather_kv(kv_fp8, kv_scale, kv_rope, block_table, topk_idx, *, group: int = 128,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dense bf16 tiles [T, top_k, d_nope + d_rope] of the selected entries (-1: zeros)."""
+    _dev(kv_fp8, "kv_fp8", torch.uint8, 3)
+    _dev(kv_scale, "kv_scale", torch.float32, 3)
+    _dev(kv_rope, "kv_rope", torch.bfloat16, 3)
+    _dev(block_table, "block_table", torch.int32, 2)
+    _dev(topk_idx, "topk_idx", torch.int32, 2)
+    P, epb, d_nope = kv_fp8.shape
+    d_rope = kv_rope.shape[2]
+    T, top_k = topk_idx.shape
+    if out is None:
+        out = torch.empty((T, top_k, d_nope + d_rope), dtype=torch.bfloat16, device=kv_fp8.device)
+    _dev(out, "out", torch.bfloat16, 3)
+    check(_lib.load().indexer_gather_kv(
+        _ptr(kv_fp8), _ptr(kv_scale), _ptr(kv_rope), _ptr(block_table), _row_stride(block_table), _ptr(topk_idx), T,
+        top_k, epb, block_table.shape[1], P, d_nope, d_rope, group, _ptr(out), _stream()))
+    return out
+
+
+def qsa_gather(k_cache, v_cache, block_table, sel, *, k_out: Optional[torch.Tensor] = None,
+               v_out: Optional[torch.Tensor] = None):
+    """(k_out, v_out) [n_sel, nkv, hd]: the cache rows of the selected token positions."""
+    _dev(k_cache, "k_cache", (torch.bfloat16, torch.float16), 4)
+    _dev(v_cache, "v_cache", k_cache.dtype, 4)
+    _dev(block_table, "block_table", torch.int32, 1)
+    _dev(sel, "sel", torch.int32, 1)
+    _, block_size, nkv, hd = k_cache.shape
+    n_sel = sel.shape[0]
+    if k_out is None:
+        k_out = torch.empty((n_sel, nkv, hd), dtype=k_cache.dtype, device=k_cache.device)
+    if v_out is None:
+        v_out = torch.empty((n_sel, nkv, hd), dtype=k_cache.dtype, device=k_cache.device)
+    check(_lib.load().qsa_gather(_ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(sel), _ptr(k_out),
+                                 _ptr(v_out), n_sel, block_size, nkv, hd, _stream()))
+    return k_out, v_out
 
 
 def qsa_block_pool(raw_keys, k_norm_w, block_keys, *, first_block: int, n_new: int, ratio: int, rot: int,
@@ -193,7 +236,7 @@ def qsa_score_rows(q, block_keys, *, first_pos: int, ratio: int, n_blocks_max: O
     if out is None:
         out = torch.empty((rows, nb), dtype=torch.float32, device=q.device)
     _dev(out, "out", torch.float32, 2)
-    check(_lib.load().qsa_score_rows(_ptr(q), _ptr(block_keys), _ptr(out), rows, nb, first_pos, out.stride(0), ratio,
+    check(_lib.load().qsa_score_rows(_ptr(q), _ptr(block_keys), _ptr(out), rows, nb, first_pos, _row_stride(out), ratio,
                                      n_heads, hd, PRECISION[precision], _stream()))
     return out
 

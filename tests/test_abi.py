@@ -88,3 +88,27 @@ def test_workspace_sizes_are_device_independent():
     fused = lib.indexer_score_topk_workspace_size(32, 4096, 64, 2048)
     assert fused >= 32 * 262144 * 4 + big
     assert lib.indexer_topk_workspace_size(0, 10, 10) == 0
+
+
+def test_gather_argument_checks_without_gpu():
+    lib = _lib.load()
+    g = lambda **o: lib.indexer_gather_kv(*[dict(fp8=256, sc=512, rope=1024, bt=2048, bts=8, idx=4096, T=2, k=4,
+                                                  epb=16, max_lb=8, P=8, dn=512, dr=64, grp=128, out=8192)
+                                             .__or__(o)[n] for n in ("fp8", "sc", "rope", "bt", "bts", "idx", "T",
+                                                                     "k", "epb", "max_lb", "P", "dn", "dr", "grp",
+                                                                     "out")], None)
+    assert g(T=0) == _lib.IDX_OK                         # no work: no launch
+    assert g(out=None) == _lib.IDX_ERR_NULL
+    assert g(dn=500) == _lib.IDX_ERR_UNSUPPORTED          # d_nope not a multiple of 16
+    assert g(grp=96) == _lib.IDX_ERR_UNSUPPORTED          # group not dividing d_nope
+    assert g(dr=4) == _lib.IDX_ERR_UNSUPPORTED
+    assert g(bts=4) == _lib.IDX_ERR_SHAPE
+    assert g(rope=None, dr=0, T=0) == _lib.IDX_OK          # no rope part: no rope pointer needed
+    assert g(out=8200) == _lib.IDX_ERR_SHAPE              # misaligned output
+    q = lambda **o: lib.qsa_gather(*[dict(k=256, v=512, bt=1024, sel=2048, ko=4096, vo=8192, n=3, bs=16, nkv=2,
+                                          hd=128).__or__(o)[n] for n in ("k", "v", "bt", "sel", "ko", "vo", "n", "bs",
+                                                                         "nkv", "hd")], None)
+    assert q(n=0) == _lib.IDX_OK
+    assert q(sel=None) == _lib.IDX_ERR_NULL
+    assert q(hd=3, nkv=1) == _lib.IDX_ERR_UNSUPPORTED
+    assert q(bs=0) == _lib.IDX_ERR_SHAPE

@@ -99,3 +99,24 @@ def make_qsa_gather(name, seed, n_blocks, block_size, nkv, hd, n_sel) -> QsaGath
     sel = np.sort(r_s.choice(n_blocks * block_size, size=n_sel, replace=False)).astype(np.int32)
     return QsaGatherWorkload(name=name, n_blocks=n_blocks, block_size=block_size, nkv=nkv, hd=hd, k_cache=k,
                              v_cache=v, block_table=bt, sel=sel)
+
+
+def _gather_long_decode():
+    """The long-context decode shape (32 queries, 4096 pages of 64 entries, valid lengths
+    U{131072..262144}, top_k 2048) over a KV pool of 512 FP8 dims (fp32 scale per 128)
+    and 64 bf16 rope dims per entry."""
+    return make_gather("gather_T32_k2048", [6], T=32, P=8192, epb=64, max_lb=4096, top_k=2048, d_nope=512,
+                       d_rope=64, group=128, valid_lens=_rng([6], 1).integers(131072, 262145, size=32))
+
+
+def _qsa_gather_decode():
+    """One query's selection in the QSA prefill shape: 256 blocks of 16 tokens (4096
+    positions) gathered from a paged bf16 K/V cache of 262144 tokens (4096 pages of 64),
+    4 KV heads of 128 dims."""
+    return make_qsa_gather("qsa_gather_4096", [7], n_blocks=4096, block_size=64, nkv=4, hd=128, n_sel=4096)
+
+
+GATHER_WORKLOADS = {
+    "gather_T32_k2048": _gather_long_decode,
+    "qsa_gather_4096": _qsa_gather_decode,
+}
