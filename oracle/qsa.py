@@ -9,7 +9,10 @@ Sources ([qsa.rs] doc comments of the launchers):
 * qsa_qprep / qsa_qprep_rows: per head, RMSNorm scaled by ``1 + w``, then partial
   RoPE at the row position ``first_pos + row``; q is read from rows of width
   ``qkw`` of the projection.
-* qsa_score: ``scores[b] = sum_h relu(q_h . k_b) / sqrt(hd)``.
+* qsa_score: ``scores[b] = sum_h relu(q_h . k_b) / sqrt(hd)`` for the ``n_blocks``
+  blocks a decode query scores (every block it is given: no causal cut).
+* qsa_qprep: one decode query, per head RMSNorm scaled by ``1 + w`` then partial RoPE
+  at the query's position ``pos``.
 * qsa_score_rows: per-row block scores; blocks at or past the row's count of
   complete blocks score -inf.
 
@@ -103,3 +106,17 @@ def score_rows(q, block_keys, first_pos, ratio, chunk: int = 8192):
             dots = q[r] @ k[a:b].T
             out[r, a:b] = np.maximum(dots, 0.0).sum(axis=0) * inv
     return out, valid
+
+
+def qprep(q_in, q_norm_w, n_heads, hd, rot, pos, theta, eps):
+    """One decode query [n_heads, hd] float64 from its projection q_in [n_heads * hd]:
+    per head RMSNorm * (1 + w), then RoPE at position ``pos``."""
+    q = np.asarray(q_in, dtype=np.float64)[: n_heads * hd].reshape(n_heads, hd)
+    return rope(rms_norm(q, q_norm_w, eps), np.full(n_heads, pos), rot, theta)
+
+
+def score_blocks(q, block_keys, n_blocks):
+    """Decode scores [n_blocks]: sum_h relu(q[h] . k_b) / sqrt(hd) for b < n_blocks."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(block_keys, dtype=np.float64)[:n_blocks]
+    return np.maximum(q @ k.T, 0.0).sum(axis=0) / np.sqrt(float(q.shape[-1]))

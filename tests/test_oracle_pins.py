@@ -435,6 +435,33 @@ def test_block_pool_rotates_at_the_block_first_position():
         np.testing.assert_allclose(got[i], [o0, o1, o2, o3], rtol=1e-13, atol=1e-14)
 
 
+def test_qprep_decode_query_hand_worked():
+    # the projection row (0,3,0,4 | -1,-1,1,1) of the hand-worked prefill case, now a single
+    # decode query at position 6 with no extra columns; same normalisation and rotation
+    got = qsa.qprep(np.array([0, 3, 0, 4, -1, -1, 1, 1], dtype=np.float64), np.array([0.0, 0.5, -0.5, 1.0]),
+                    2, 4, 4, 6, 100.0, 0.0)
+    for h, (n0, n1, n2, n3) in enumerate([(0.0, 1.8, 0.0, 3.2), (-1.0, -1.5, 0.5, 2.0)]):
+        o0, o2 = _rot(n0, n2, 6.0)
+        o1, o3 = _rot(n1, n3, 0.6)
+        np.testing.assert_allclose(got[h], [o0, o1, o2, o3], rtol=1e-13, atol=1e-14)
+
+
+def test_score_blocks_brute_force_and_no_causal_cut():
+    rng = np.random.default_rng(6)
+    H, hd, nb = 3, 16, 12
+    q = rng.standard_normal((H, hd))
+    k = rng.standard_normal((nb + 5, hd))        # the table is longer than the blocks scored
+    got = qsa.score_blocks(q, k, nb)
+    assert got.shape == (nb,)
+    for b in range(nb):
+        exp = sum(max(0.0, math.fsum(q[h, d] * k[b, d] for d in range(hd))) for h in range(H)) / 4.0
+        assert got[b] == pytest.approx(exp, rel=1e-13)
+    # a prefill row whose complete-block count is nb scores the same blocks
+    rows, valid = qsa.score_rows(q[None], k[:nb], first_pos=nb * 4 - 1, ratio=4)
+    assert valid.tolist() == [nb]
+    np.testing.assert_allclose(rows[0], got, rtol=1e-14)
+
+
 def test_complete_blocks_literal():
     # positions 14..18 with 4 tokens per block: tokens 0..15 fill blocks 0..3 at position 15
     assert qsa.complete_blocks(14, 5, 4, 100).tolist() == [3, 4, 4, 4, 4]
