@@ -43,6 +43,8 @@ WORKLOADS = {
     # diagnostic, not a configuration: the long-decode shape with every row on its own
     # pages of a 604 MB pool, so that every key byte read comes from DRAM
     "hbm_true_T32_S262144": "diag",
+    # one decode query of the QSA workload (its last prefill position) over all its blocks
+    "qsa_decode": "qsa_decode",
     # the selected-entry gathers that consume the top-k (workloads/gather.py)
     "gather_T32_k2048": "gather",
     "qsa_gather_4096": "gather",
@@ -300,6 +302,100 @@ def run_qsa(args, w):
     print(json.dumps(out), flush=True)
 
 
+def run_qsa_decode(args):
+    """One QSA decode step on the QSA workload's cache: the new block pooled (n_new = 1),
+    the query prepared at its position, its scores over every complete block, the top-k."""
+    import torch
+
+    import sparse_attention_lightning_block_amd as salb
+    from workloads import make
+    from workloads.device import bf16_tensor
+
+    w = make(5)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    raw = bf16_tensor(w.raw_keys).to(dev)
+    kw = torch.from_numpy(w.k_norm_w).to(dev)
+    qw = torch.from_numpy(w.q_norm_w).to(dev)
+    keys = torch.empty((w.n_blocks, w.hd), dtype=torch.float32, device=dev)
+    salb.qsa_block_pool(raw, kw, keys, first_block=0, n_new=w.n_blocks, ratio=w.ratio, rot=w.rot, theta=w.theta,
+                        eps=w.eps)
+    r = w.rows - 1
+    pos = w.first_pos + r
+    nb = min(w.n_blocks, (pos + 1) // w.ratio)
+    q_in = bf16_tensor(w.qk[r]).to(dev)
+    q = torch.empty((w.n_heads, w.hd), dtype=torch.float32, device=dev)
+    sc = torch.empty((1, nb), dtype=torch.float32, device=dev)
+    idx = torch.empty((1, w.top_k), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(256, salb.indexer_topk_workspace_size(1, nb, w.top_k)), dtype=torch.uint8, device=dev)
+
+    def pool():
+        salb.qsa_block_pool(raw, kw, keys, first_block=nb - 1, n_new=1, ratio=w.ratio, rot=w.rot, theta=w.theta,
+                            eps=w.eps)
+
+    def prep():
+        salb.qsa_qprep(q_in, qw, n_heads=w.n_heads, hd=w.hd, pos=pos, rot=w.rot, theta=w.theta, eps=w.eps, out=q)
+
+    def score():
+        salb.qsa_score(q, keys, n_blocks=nb, out=sc[0])
+
+    def select():
+        salb.indexer_topk_select(sc, w.top_k, workspace=ws, out_idx=idx)
+
+    def step():
+        pool()
+        prep()
+        score()
+        select()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step, stage = timed_steps(torch, make_step(torch, [step], args.graph), 1, args.steps)
+    pool_ms, prep_ms, score_ms, select_ms = (back_to_back_ms(torch, f, args.steps) for f in (pool, prep, score, select))
+    key_bytes = nb * w.hd * 4 + w.n_heads * w.hd * 4 + nb * 4
+    gbs = key_bytes / (score_ms / 1e3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": nb / (ms_per_step / 1e3),
+        "unit": "scores/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "qsa_decode", "pos": int(pos), "blocks": int(nb), "heads": w.n_heads, "hd": w.hd,
+                   "top_k": w.top_k, "launch": "hip_graph" if args.graph else "eager"},
+        "step_ms": {"p10": float(np.percentile(stage[0], 10)), "p50": float(np.median(stage[0])),
+                    "p90": float(np.percentile(stage[0], 90))},
+        "stage_ms": {"pool_one_block": pool_ms, "qprep": prep_ms, "score": score_ms, "select": select_ms},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "qsa_decode_score_kernel",
+                     "kernel_avg_us": round(score_ms * 1e3, 2), "bytes_per_launch": int(key_bytes),
+                     "flops_per_launch": int(2 * nb * w.n_heads * w.hd)},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_qsa_decode(w, r, pos, nb),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_qsa_decode(w, r, pos, nb):
+    """The oracle decode step (query prep, scores over the pooled keys, full-sort top-k);
+    the pooled keys come from the oracle too, outside the timed part."""
+    from oracle import indexer, qsa
+
+    keys = qsa.block_pool(indexer.upcast(w.raw_keys, "bf16"), w.k_norm_w, 0, nb, w.ratio, w.rot, w.theta, w.eps)
+    t0 = time.perf_counter()
+    q = qsa.qprep(indexer.upcast(w.qk[r], "bf16"), w.q_norm_w, w.n_heads, w.hd, w.rot, pos, w.theta, w.eps)
+    indexer.topk(qsa.score_blocks(q, keys, nb), w.top_k)
+    dt = time.perf_counter() - t0
+    return {"value": nb / dt, "unit": "scores/s", "cores": int(len(os.sched_getaffinity(0))), "kind": "oracle",
+            "sample": f"one decode query over {nb} blocks (prep, float64 scores, full-sort top-k): {dt:.3f} s"}
+
+
 def run_gather(args, name):
     """The selected-entry gathers: one step is one gather call, timed back to back."""
     import torch
@@ -414,6 +510,9 @@ def main():
     from workloads.device import to_dev
     from workloads import make, make_diag
 
+    if WORKLOADS[args.workload] == "qsa_decode":
+        run_qsa_decode(args)
+        return
     if WORKLOADS[args.workload] == "gather":
         run_gather(args, args.workload)
         return

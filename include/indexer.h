@@ -259,6 +259,29 @@ int qsa_qprep_rows(const uint16_t* qk, const float* q_norm_w, float* q_out,
                    uint32_t rot, float theta, float eps, hipStream_t stream);
 
 /*
+ * qsa_qprep -- one decode query ([qsa.rs] qsa_qprep): per head h,
+ *     q_out[h, :] = RoPE(x / sqrt(mean(x^2) + eps) * (1 + q_norm_w), pos),  x = q_in[h*hd .. h*hd+hd-1]
+ * i.e. qsa_qprep_rows for one row at position pos, read from a projection of n_heads * hd.
+ *  q_in   [n_heads * hd] bf16 (uint16 bit patterns), 16-byte aligned
+ *  q_out  [n_heads, hd] fp32 output, 16-byte aligned
+ */
+int qsa_qprep(const uint16_t* q_in, const float* q_norm_w, float* q_out, uint32_t n_heads, uint32_t hd,
+              uint32_t rot, uint32_t pos, float theta, float eps, hipStream_t stream);
+
+/*
+ * qsa_score -- decode scores of one query over n_blocks blocks ([qsa.rs] qsa_score):
+ *     scores[b] = sum_h ReLU(q[h,:] . block_keys[b,:]) / sqrt(hd)     b < n_blocks
+ * (every block given is scored; the caller passes the query's complete blocks).  fp32
+ * arithmetic, within ~1e-5 relative of the exact value.
+ *  q          [n_heads, hd] fp32, 16-byte aligned
+ *  block_keys [>= n_blocks, hd] fp32, 16-byte aligned
+ *  scores     [n_blocks] fp32 output (may be NULL when n_blocks is 0: nothing is launched)
+ * Supported: hd in {64, 128, 256}, 1 <= n_heads <= 64.
+ */
+int qsa_score(const float* q, const float* block_keys, float* scores, uint32_t n_blocks, uint32_t n_heads,
+              uint32_t hd, hipStream_t stream);
+
+/*
  * qsa_score_rows -- QSA block scores ([qsa.rs] qsa_score, qsa_score_rows, qsa_score_rows_tc):
  *     scores[r, b] = sum_h ReLU(q[r,h,:] . block_keys[b,:]) / sqrt(hd)   for b < nb_r
  *     scores[r, b] = -inf                                              for nb_r <= b < n_blocks_max

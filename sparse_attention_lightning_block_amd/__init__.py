@@ -13,7 +13,9 @@ from .ops import (  # noqa: F401
     indexer_topk_workspace_size,
     qsa_block_pool,
     qsa_gather,
+    qsa_qprep,
     qsa_qprep_rows,
+    qsa_score,
     qsa_score_rows,
 )
 from ._lib import IDX_ERR_DATA, IDX_F_VALIDATE, IndexerError, load  # noqa: F401

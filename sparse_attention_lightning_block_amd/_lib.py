@@ -51,6 +51,8 @@ SIGNATURES = {
     "qsa_gather": (_I, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _P]),
     "qsa_block_pool": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _F, _F, _P]),
     "qsa_qprep_rows": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _F, _F, _P]),
+    "qsa_qprep": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _F, _F, _P]),
+    "qsa_score": (_I, [_P, _P, _P, _U32, _U32, _U32, _P]),
     "qsa_score_rows": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _I, _P]),
     "indexer_debug_dequant": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
 }

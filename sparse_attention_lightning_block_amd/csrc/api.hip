@@ -384,6 +384,30 @@ int qsa_qprep_rows(const uint16_t* qk, const float* q_norm_w, float* q_out, uint
   return ok();
 }
 
+int qsa_qprep(const uint16_t* q_in, const float* q_norm_w, float* q_out, uint32_t n_heads, uint32_t hd,
+              uint32_t rot, uint32_t pos, float theta, float eps, hipStream_t stream) {
+  if (!q_in || !q_norm_w || !q_out) return fail(IDX_ERR_NULL, "q_in, q_norm_w and q_out are required");
+  if (n_heads < 1 || n_heads > 65535) return fail(IDX_ERR_SHAPE, "n_heads %u out of range", n_heads);
+  if (hd != 64 && hd != 128 && hd != 256) return fail(IDX_ERR_UNSUPPORTED, "hd %u (supported: 64, 128, 256)", hd);
+  // one row of qsa_qprep_rows at position pos, read from a projection row of n_heads * hd
+  return qsa_qprep_rows(q_in, q_norm_w, q_out, 1, pos, n_heads * hd, n_heads, hd, rot, theta, eps, stream);
+}
+
+int qsa_score(const float* q, const float* block_keys, float* scores, uint32_t n_blocks, uint32_t n_heads,
+              uint32_t hd, hipStream_t stream) {
+  if (!q || !block_keys || (!scores && n_blocks > 0))
+    return fail(IDX_ERR_NULL, "q, block_keys and (for n_blocks > 0) scores are required");
+  if (hd != 64 && hd != 128 && hd != 256) return fail(IDX_ERR_UNSUPPORTED, "hd %u (supported: 64, 128, 256)", hd);
+  if (n_heads < 1 || n_heads > 64) return fail(IDX_ERR_UNSUPPORTED, "n_heads %u (supported: 1..64)", n_heads);
+  if (n_blocks > 0x7fffffffu) return fail(IDX_ERR_SHAPE, "n_blocks too large");
+  if (!aligned(q, 16) || !aligned(block_keys, 16) || !aligned(scores, 4))
+    return fail(IDX_ERR_SHAPE, "q and block_keys must be 16-byte aligned");
+  if (n_blocks == 0) return ok();
+  hipError_t e = salb::launch_qsa_decode_score(q, block_keys, scores, n_blocks, n_heads, hd, stream);
+  if (e != hipSuccess) return hip_fail(e, "QSA decode score launch");
+  return ok();
+}
+
 int qsa_score_rows(const float* q, const float* block_keys, float* scores, uint32_t rows, uint32_t n_blocks_max,
                    uint32_t first_pos, uint32_t score_stride, uint32_t ratio, uint32_t n_heads, uint32_t hd,
                    int precision, hipStream_t stream) {

@@ -85,6 +85,8 @@ hipError_t launch_qprep_rows(const uint16_t* qk, const float* qw, float* out, ui
                              uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t hd, uint32_t rot,
                              float theta, float eps, hipStream_t st);
 bool qsa_score_uses_mfma(int precision, uint32_t n_heads, uint32_t hd);
+hipError_t launch_qsa_decode_score(const float* q, const float* keys, float* scores, uint32_t nb, uint32_t n_heads,
+                                   uint32_t hd, hipStream_t st);
 hipError_t launch_qsa_score(const float* q, const float* keys, float* scores, uint32_t rows, uint32_t nb,
                             uint32_t first_pos, uint32_t stride, uint32_t ratio, uint32_t n_heads, uint32_t hd,
                             int precision, hipStream_t st);

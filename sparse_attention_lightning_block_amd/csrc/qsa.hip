@@ -422,6 +422,57 @@ __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const float
   }
 }
 
+// ------------------------------------------------------------------ decode scores
+
+// One decode query against n_blocks block keys ([qsa.rs] qsa_score), fp32.  A 256-thread
+// workgroup takes 64 consecutive blocks, one per lane, whose key stays in registers;
+// the four waves split the heads (wave w takes heads w, w + 4, ...), reading the query
+// from LDS (every lane the same address: broadcast reads), and the four partial head
+// sums meet in LDS.  Four independent accumulators per dot product keep the FMA chains
+// short.  One query is far below the MFMA ridge (2 * heads flops per key byte), so the
+// VALU does the arithmetic.
+template <int HD>
+__global__ __launch_bounds__(256) void qsa_decode_score_kernel(const float* __restrict__ q,
+                                                               const float* __restrict__ keys,
+                                                               float* __restrict__ scores, uint32_t nb,
+                                                               uint32_t n_heads, float out_scale) {
+  extern __shared__ __align__(16) float qs[];  // [n_heads * HD]
+  __shared__ float part[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (uint32_t i = tid * 4; i < n_heads * HD; i += 1024)
+    *reinterpret_cast<float4v*>(qs + i) = *reinterpret_cast<const float4v*>(q + i);
+  const uint32_t b = blockIdx.x * 64 + lane;
+  const uint32_t bc = b < nb ? b : nb - 1;  // lanes past the last block re-read it; not stored
+  float k[HD];
+  const float* kp = keys + (int64_t)bc * HD;
+#pragma unroll
+  for (int d = 0; d < HD; d += 4) {
+    const float4v v = *reinterpret_cast<const float4v*>(kp + d);
+    k[d] = v[0];
+    k[d + 1] = v[1];
+    k[d + 2] = v[2];
+    k[d + 3] = v[3];
+  }
+  __syncthreads();
+  float acc = 0.0f;
+  for (uint32_t h = wave; h < n_heads; h += 4) {
+    const float* qh = qs + h * HD;
+    float d0 = 0.0f, d1 = 0.0f, d2 = 0.0f, d3 = 0.0f;
+#pragma unroll
+    for (int d = 0; d < HD; d += 4) {
+      const float4v x = *reinterpret_cast<const float4v*>(qh + d);
+      d0 = fmaf(x[0], k[d], d0);
+      d1 = fmaf(x[1], k[d + 1], d1);
+      d2 = fmaf(x[2], k[d + 2], d2);
+      d3 = fmaf(x[3], k[d + 3], d3);
+    }
+    acc += fmaxf((d0 + d1) + (d2 + d3), 0.0f);
+  }
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && b < nb) scores[b] = ((part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane])) * out_scale;
+}
+
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_block_pool(const uint16_t* raw, const float* kw, float* out, uint32_t first_block,
@@ -485,6 +536,29 @@ static hipError_t launch_qsa_mfma(const float* q, const float* keys, float* scor
   const dim3 grid(n_groups * kXcds);
   hipLaunchKernelGGL((qsa_score_mfma_kernel<HD, NH>), grid, dim3(kQsaThreads), 0, st, q, keys, scores, rows, nb,
                      first_pos, stride, ratio, chunk, n_groups, 1.0f / sqrtf((float)HD));
+  return hipGetLastError();
+}
+
+hipError_t launch_qsa_decode_score(const float* q, const float* keys, float* scores, uint32_t nb, uint32_t n_heads,
+                                   uint32_t hd, hipStream_t st) {
+  const dim3 grid((nb + 63) / 64);
+  const size_t lds = (size_t)n_heads * hd * 4;
+  const float sc = 1.0f / sqrtf((float)hd);
+  hipError_t e;
+  switch (hd) {
+    case 64:
+      if ((e = ensure_lds(reinterpret_cast<const void*>(qsa_decode_score_kernel<64>), lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL(qsa_decode_score_kernel<64>, grid, dim3(256), lds, st, q, keys, scores, nb, n_heads, sc);
+      break;
+    case 128:
+      if ((e = ensure_lds(reinterpret_cast<const void*>(qsa_decode_score_kernel<128>), lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL(qsa_decode_score_kernel<128>, grid, dim3(256), lds, st, q, keys, scores, nb, n_heads, sc);
+      break;
+    default:
+      if ((e = ensure_lds(reinterpret_cast<const void*>(qsa_decode_score_kernel<256>), lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL(qsa_decode_score_kernel<256>, grid, dim3(256), lds, st, q, keys, scores, nb, n_heads, sc);
+      break;
+  }
   return hipGetLastError();
 }
 

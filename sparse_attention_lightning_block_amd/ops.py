@@ -226,6 +226,36 @@ def qsa_qprep_rows(qk, q_norm_w, *, n_heads: int, hd: int, first_pos: int, rot: 
     return out
 
 
+def qsa_qprep(q_in, q_norm_w, *, n_heads: int, hd: int, pos: int, rot: int, theta: float, eps: float,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One prepared decode query [n_heads, hd] fp32 from its bf16 projection [n_heads * hd]."""
+    _dev(q_in, "q_in", torch.bfloat16, 1)
+    _dev(q_norm_w, "q_norm_w", torch.float32, 1)
+    if q_in.shape[0] < n_heads * hd:
+        raise ValueError("q_in holds fewer than n_heads * hd values")
+    if out is None:
+        out = torch.empty((n_heads, hd), dtype=torch.float32, device=q_in.device)
+    _dev(out, "out", torch.float32, 2)
+    check(_lib.load().qsa_qprep(_ptr(q_in), _ptr(q_norm_w), _ptr(out), n_heads, hd, rot, pos, theta, eps,
+                                _stream()))
+    return out
+
+
+def qsa_score(q, block_keys, *, n_blocks: Optional[int] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode scores [n_blocks] fp32 of one prepared query [n_heads, hd] over the block keys."""
+    _dev(q, "q", torch.float32, 2)
+    _dev(block_keys, "block_keys", torch.float32, 2)
+    n_heads, hd = q.shape
+    nb = block_keys.shape[0] if n_blocks is None else n_blocks
+    if nb > block_keys.shape[0]:
+        raise ValueError("n_blocks exceeds the block-key table")
+    if out is None:
+        out = torch.empty((nb,), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32, 1)
+    check(_lib.load().qsa_score(_ptr(q), _ptr(block_keys), _ptr(out), nb, n_heads, hd, _stream()))
+    return out
+
+
 def qsa_score_rows(q, block_keys, *, first_pos: int, ratio: int, n_blocks_max: Optional[int] = None,
                    precision: str = "mfma", out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """scores [rows, n_blocks_max] fp32 with -inf past each row's complete blocks."""

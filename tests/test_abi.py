@@ -112,3 +112,13 @@ def test_gather_argument_checks_without_gpu():
     assert q(sel=None) == _lib.IDX_ERR_NULL
     assert q(hd=3, nkv=1) == _lib.IDX_ERR_UNSUPPORTED
     assert q(bs=0) == _lib.IDX_ERR_SHAPE
+
+
+def test_qsa_decode_argument_checks_without_gpu():
+    lib = _lib.load()
+    assert lib.qsa_qprep(None, 16, 32, 32, 128, 64, 7, 1e4, 1e-6, None) == _lib.IDX_ERR_NULL
+    assert lib.qsa_qprep(16, 16, 32, 32, 100, 64, 7, 1e4, 1e-6, None) == _lib.IDX_ERR_UNSUPPORTED
+    assert lib.qsa_qprep(16, 16, 32, 32, 128, 65, 7, 1e4, 1e-6, None) == _lib.IDX_ERR_SHAPE     # odd rot
+    assert lib.qsa_score(16, 32, 48, 10, 65, 128, None) == _lib.IDX_ERR_UNSUPPORTED             # 65 heads
+    assert lib.qsa_score(16, 32, 48, 0, 32, 128, None) == _lib.IDX_OK                           # no blocks
+    assert lib.qsa_score(16, 40, 48, 10, 32, 128, None) == _lib.IDX_ERR_SHAPE                   # misaligned keys

@@ -28,7 +28,7 @@ def test_key_stream_bytes_per_entry():
 
 
 def test_workloads_cover_the_five_configurations():
-    configs = sorted(v for v in bench.WORKLOADS.values() if v not in ("diag", "gather"))
+    configs = sorted(v for v in bench.WORKLOADS.values() if isinstance(v, int))
     assert configs == [1, 2, 3, 4, 5]
     assert bench.WORKLOADS["decode_T8_S65536"] == 2
     assert set(bench.COLD_WORKLOADS) <= set(bench.WORKLOADS)

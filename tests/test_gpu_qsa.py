@@ -135,3 +135,78 @@ def test_chain_end_to_end_reduced():
         err = np.abs(got[r, :v].astype(np.float64) - ref[r, :v])
         assert np.all(err <= tol), f"row {r}: max err {err.max()}"
         check_topk(gi[r], gv[r], ref[r, :v], None, w.top_k, "fp32", f"qsa chain row {r}", tol=tol)
+
+
+# ------------------------------------------------------------------ decode (one query)
+
+def _decode_case(w, r, keys_d):
+    """Prepared query of projection row r as a decode query at position first_pos + r, its
+    scores over the complete blocks and their top-k, all on the GPU."""
+    pos = w.first_pos + r
+    nb = min(w.n_blocks, (pos + 1) // w.ratio)
+    q_in = _bf16(w.qk[r]).cuda()
+    q = salb.qsa_qprep(q_in, torch.from_numpy(w.q_norm_w).cuda(), n_heads=w.n_heads, hd=w.hd, pos=pos, rot=w.rot,
+                       theta=w.theta, eps=w.eps)
+    sc = salb.qsa_score(q, keys_d, n_blocks=nb)
+    idx, val = salb.indexer_topk_select(sc[None, :], w.top_k, with_scores=True)
+    torch.cuda.synchronize()
+    return pos, nb, q.cpu().numpy().astype(np.float64), sc.cpu().numpy(), idx[0].cpu().numpy(), val[0].cpu().numpy()
+
+
+@pytest.mark.parametrize("r", [0, 17, 39])
+def test_decode_query_reduced(r):
+    """qsa_qprep, qsa_score and the top-k of one decode query: the prepared query against
+    the oracle; the scores against the oracle on the GPU's own pooled keys and query (FP32
+    rule), and end to end against the oracle chain from the bf16 inputs."""
+    w = make(5, reduced=1)
+    keys_d = _pool_all(w)
+    pos, nb, q, sc, gi, gv = _decode_case(w, r, keys_d)
+    qo = qsa.qprep(indexer.upcast(w.qk[r], "bf16"), w.q_norm_w, w.n_heads, w.hd, w.rot, pos, w.theta, w.eps)
+    _check_vectors(q, qo, "decode qprep")
+    keys = keys_d.cpu().numpy().astype(np.float64)
+    ref = qsa.score_blocks(q, keys, nb)
+    A = np.abs(q).sum(axis=0) @ np.abs(keys[:nb]).T / np.sqrt(w.hd)
+    err = np.abs(sc.astype(np.float64) - ref)
+    assert np.all(err <= S_REL * np.abs(ref) + S_ABS_A * A), f"max err {err.max()}"
+    check_topk(gi, gv, ref, None, w.top_k, "fp32", f"decode {r}", tol=S_REL * np.abs(ref) + S_ABS_A * A)
+    keys_o = qsa.block_pool(indexer.upcast(w.raw_keys, "bf16"), w.k_norm_w, 0, w.n_blocks, w.ratio, w.rot, w.theta,
+                            w.eps)
+    ref_o = qsa.score_blocks(qo, keys_o, nb)
+    A_o = np.abs(qo).sum(axis=0) @ np.abs(keys_o[:nb]).T / np.sqrt(w.hd)
+    assert np.all(np.abs(sc - ref_o) <= S_REL * np.abs(ref_o) + CHAIN_ABS_A * A_o)
+
+
+def test_decode_query_full_size():
+    """The last prefill position of the QSA workload as a decode query: 32768 complete
+    blocks, top 256, against the oracle chain from the bf16 inputs."""
+    w = make(5)
+    keys_d = _pool_all(w)
+    r = w.rows - 1
+    pos, nb, q, sc, gi, gv = _decode_case(w, r, keys_d)
+    assert nb == w.n_blocks
+    qo = qsa.qprep(indexer.upcast(w.qk[r], "bf16"), w.q_norm_w, w.n_heads, w.hd, w.rot, pos, w.theta, w.eps)
+    _check_vectors(q, qo, "decode qprep full")
+    keys_o = qsa.block_pool(indexer.upcast(w.raw_keys, "bf16"), w.k_norm_w, 0, w.n_blocks, w.ratio, w.rot, w.theta,
+                            w.eps)
+    ref = qsa.score_blocks(qo, keys_o, nb)
+    A = np.abs(qo).sum(axis=0) @ np.abs(keys_o).T / np.sqrt(w.hd)
+    tol = S_REL * np.abs(ref) + CHAIN_ABS_A * A
+    err = np.abs(sc.astype(np.float64) - ref)
+    assert np.all(err <= tol), f"max err {err.max()}"
+    check_topk(gi, gv, ref, None, w.top_k, "fp32", "decode full", tol=tol)
+
+
+def test_decode_score_partial_table_and_empty():
+    """Only the n_blocks given are scored (the table may be longer); n_blocks = 0 launches
+    nothing."""
+    w = make(5, reduced=1)
+    keys_d = _pool_all(w)
+    q = torch.randn(w.n_heads, w.hd, dtype=torch.float32, device="cuda")
+    out = torch.full((w.n_blocks,), 9.0, dtype=torch.float32, device="cuda")
+    salb.qsa_score(q, keys_d, n_blocks=100, out=out[:100])
+    salb.qsa_score(q, keys_d, n_blocks=0, out=out[:0])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(got[100:] == 9.0)
+    ref = qsa.score_blocks(q.cpu().numpy().astype(np.float64), keys_d.cpu().numpy().astype(np.float64), 100)
+    assert np.allclose(got[:100], ref, rtol=1e-5, atol=1e-5 * np.abs(ref).max())
