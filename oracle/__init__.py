@@ -20,9 +20,11 @@ described on:
   qsa_score_rows, qsa_score_rows_tc).
 
 Modules:
-  nvfp4    -- E2M1 / E4M3 decode, block-table resolution, key dequantisation.
-  indexer  -- I[t,s] = sum_h w[t,h] * ReLU(q[t,h] . k[s]) and the total-order top-k.
-  qsa      -- block pooling, RMSNorm, partial RoPE, query prep and row scores.
+  nvfp4     -- E2M1 / E4M3 decode, block-table resolution, key dequantisation.
+  indexer   -- I[t,s] = sum_h w[t,h] * ReLU(q[t,h] . k[s]) and the total-order top-k.
+  qsa       -- block pooling, RMSNorm, partial RoPE, query prep, row and decode scores.
+  gather    -- the selected entries as dense tiles (FP8 + BF16 pool, QSA K/V rows).
+  attention -- prefill attention over the selected blocks plus the incomplete tail.
 """
 
-from . import nvfp4, indexer, qsa  # noqa: F401
+from . import attention, gather, indexer, nvfp4, qsa  # noqa: F401
