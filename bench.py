@@ -45,6 +45,8 @@ WORKLOADS = {
     "hbm_true_T32_S262144": "diag",
     # one decode query of the QSA workload (its last prefill position) over all its blocks
     "qsa_decode": "qsa_decode",
+    # attention of the QSA prefill rows over their selected blocks (workloads/attention.py)
+    "qsa_prefill_attn": "attention",
     # the selected-entry gathers that consume the top-k (workloads/gather.py)
     "gather_T32_k2048": "gather",
     "qsa_gather_4096": "gather",
@@ -396,6 +398,109 @@ def cpu_baseline_qsa_decode(w, r, pos, nb):
             "sample": f"one decode query over {nb} blocks (prep, float64 scores, full-sort top-k): {dt:.3f} s"}
 
 
+def run_attention(args):
+    """Block-sparse prefill attention of the QSA prefill rows: one step is one call."""
+    import torch
+
+    import sparse_attention_lightning_block_amd as salb
+    from oracle import attention
+    from workloads.attention import qsa_prefill_attention
+    from workloads.device import bf16_tensor
+
+    w = qsa_prefill_attention()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q = bf16_tensor(w.q).to(dev)
+    k = bf16_tensor(w.k_cache).to(dev)
+    v = bf16_tensor(w.v_cache).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    lists = torch.from_numpy(w.lists).to(dev)
+    out = torch.empty((w.rows, w.nq, w.hd), dtype=torch.float32, device=dev)
+
+    def step():
+        salb.qsa_prefill_attn(q, k, v, bt, lists, first_pos=w.first_pos, ratio=w.ratio, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step, stage = timed_steps(torch, make_step(torch, [step], args.graph), 1, args.steps)
+    kern_ms = back_to_back_ms(torch, step, args.steps)
+    n_pos = [attention.attended_positions(w.lists[r], w.first_pos, r, w.ratio).size for r in range(w.rows)]
+    pairs = int(np.sum(n_pos)) * w.nq                    # (row, head, position) triples
+    flops = 4.0 * pairs * w.hd                           # q.k and p.v, 2 flops per multiply-add
+    per_stream = int(np.sum(n_pos)) * w.nkv * w.hd * 2 * 2 + w.rows * w.nq * w.hd * (2 + 4)
+    blocks = set()
+    for r in range(w.rows):
+        blocks.update((attention.attended_positions(w.lists[r], w.first_pos, r, w.ratio) // w.block_size).tolist())
+    unique = len(blocks) * w.block_size * w.nkv * w.hd * 2 * 2 + w.rows * w.nq * w.hd * (2 + 4)
+    kern_s = kern_ms / 1e3
+    ridge = MFMA_F16_PEAK_TFLOPS / (HBM_PEAK_GBS / 1e3)
+    mfma_bound = flops / unique > ridge
+    tf = flops / kern_s / 1e12
+    # below the ridge the binding traffic is what each row must gather: its own listed
+    # blocks (lists are per row, and the cache is larger than the last-level cache)
+    gbs = per_stream / kern_s / 1e9
+    out_line = {
+        "metric": METRIC,
+        "value": pairs / (ms_per_step / 1e3),
+        "unit": "query-head x position pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qsa_prefill_attn", "rows": w.rows, "first_pos": w.first_pos, "ratio": w.ratio,
+                   "topk": w.topk, "nq": w.nq, "nkv": w.nkv, "hd": w.hd, "block_size": w.block_size,
+                   "launch": "hip_graph" if args.graph else "eager"},
+        "step_ms": {"p10": float(np.percentile(stage[0], 10)), "p50": float(np.median(stage[0])),
+                    "p90": float(np.percentile(stage[0], 90))},
+        "roofline": {
+            "bound": "mfma" if mfma_bound else "hbm",
+            "achieved": round(tf, 2) if mfma_bound else round(gbs, 1),
+            "peak": MFMA_F16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "frac": round((tf / MFMA_F16_PEAK_TFLOPS) if mfma_bound else (gbs / HBM_PEAK_GBS), 4),
+            "traffic": None, "kernel": "prefill_attn_kernel", "kernel_avg_us": round(kern_ms * 1e3, 2),
+            "flops_per_launch": int(flops), "bytes_per_launch": int(per_stream), "unique_bytes_per_launch": int(unique),
+            "ai_unique": round(flops / unique, 1), "ridge": round(ridge, 1),
+            "fractions": {"mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                          "hbm_unique": round(unique / kern_s / 1e9 / HBM_PEAK_GBS, 4),
+                          "hbm_per_stream": round(per_stream / kern_s / 1e9 / HBM_PEAK_GBS, 4)},
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_attention(w, pairs),
+    }
+    print(json.dumps(out_line), flush=True)
+
+
+def cpu_baseline_attention(w, pairs_all, budget_s=15.0):
+    """The oracle attention on whole rows until the budget is used."""
+    from oracle import attention, indexer
+
+    done_pairs, rows = 0, 0
+    t0 = time.perf_counter()
+    for r in range(w.rows):
+        pos = attention.attended_positions(w.lists[r], w.first_pos, r, w.ratio)
+        logical = np.unique(pos // w.block_size)
+        pages = w.block_table[logical]
+        bt = np.zeros(w.block_table.shape, dtype=np.int64)
+        bt[logical] = np.arange(logical.size)
+        attention.prefill_attn(indexer.upcast(w.q[r:r + 1], "bf16"), indexer.upcast(w.k_cache[pages], "bf16"),
+                               indexer.upcast(w.v_cache[pages], "bf16"), bt, w.lists[r:r + 1], w.first_pos + r, w.ratio,
+                               w.block_size, w.nkv, w.hd ** -0.5)
+        done_pairs += pos.size * w.nq
+        rows += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_pairs / dt, "unit": "query-head x position pairs/s",
+            "cores": int(len(os.sched_getaffinity(0))), "kind": "oracle",
+            "sample": f"{rows} of {w.rows} rows ({done_pairs} pairs), float64 numpy: {dt:.2f} s"}
+
+
 def run_gather(args, name):
     """The selected-entry gathers: one step is one gather call, timed back to back."""
     import torch
@@ -512,6 +617,9 @@ def main():
 
     if WORKLOADS[args.workload] == "qsa_decode":
         run_qsa_decode(args)
+        return
+    if WORKLOADS[args.workload] == "attention":
+        run_attention(args)
         return
     if WORKLOADS[args.workload] == "gather":
         run_gather(args, args.workload)

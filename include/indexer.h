@@ -224,6 +224,33 @@ int qsa_gather(const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* 
                hipStream_t stream);
 
 /*
+ * qsa_prefill_attn -- block-sparse prefill attention over the selected blocks
+ * ([qsa.rs] qsa_prefill_attn: per row and query head, attention over exactly the blocks
+ * of the row's list plus the incomplete tail, read from the paged cache):
+ *   row r at pos = first_pos + r has nb = floor((pos + 1) / ratio) complete blocks;
+ *   it attends positions [ratio*b, ratio*b + ratio) of every list entry 0 <= b < nb
+ *   (-1 and other entries are skipped) and the tail [ratio*nb, pos];
+ *   attn_out[r, h, :] = sum_j softmax_j(inv_sqrt_d * q[r, h] . k_j) * v_j,
+ *   with k_j, v_j of KV head h / (nq / nkv) at cache page block_table[j / block_size],
+ *   slot j % block_size; a row that attends nothing gets zeros.
+ * Scores and the softmax in fp32 (q . k from bf16 inputs on the matrix cores), the
+ * probabilities rounded to fp16 for the value product.
+ *  q           [rows, nq, hd] bf16 (uint16 bit patterns), 16-byte aligned
+ *  k_cache,    [pages, block_size, nkv, hd] bf16, 16-byte aligned
+ *  v_cache
+ *  block_table [> (first_pos + rows - 1) / block_size] int32 (one sequence); the cache
+ *              rows it names, page * block_size + slot, must be below 2^31
+ *  lists       [rows, topk] int32 (a top-k of complete blocks, -1 padded); NULL if topk = 0
+ *  attn_out    [rows, nq, hd] fp32 output
+ * Supported: hd 64 or 128; nkv dividing nq with nq / nkv <= 16; topk * ratio small
+ * enough for a workgroup's LDS (about 25000 positions at hd 128).
+ */
+int qsa_prefill_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* block_table,
+                     const int32_t* lists, float* attn_out, uint32_t rows, uint32_t first_pos, uint32_t topk,
+                     uint32_t ratio, uint32_t block_size, uint32_t nq, uint32_t nkv, uint32_t hd, float inv_sqrt_d,
+                     hipStream_t stream);
+
+/*
  * qsa_block_pool -- pooled QSA block keys ([qsa.rs] qsa_block_pool).
  *
  * For b in [first_block, first_block + n_new):

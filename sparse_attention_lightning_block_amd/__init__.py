@@ -13,6 +13,7 @@ from .ops import (  # noqa: F401
     indexer_topk_workspace_size,
     qsa_block_pool,
     qsa_gather,
+    qsa_prefill_attn,
     qsa_qprep,
     qsa_qprep_rows,
     qsa_score,

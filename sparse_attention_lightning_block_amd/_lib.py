@@ -49,6 +49,7 @@ SIGNATURES = {
                                         _P, _P, _P]),
     "indexer_gather_kv": (_I, [_P, _P, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "qsa_gather": (_I, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _P]),
+    "qsa_prefill_attn": (_I, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _F, _P]),
     "qsa_block_pool": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _F, _F, _P]),
     "qsa_qprep_rows": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _F, _F, _P]),
     "qsa_qprep": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _F, _F, _P]),

@@ -348,6 +348,35 @@ int qsa_gather(const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* 
   return ok();
 }
 
+int qsa_prefill_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* block_table,
+                     const int32_t* lists, float* attn_out, uint32_t rows, uint32_t first_pos, uint32_t topk,
+                     uint32_t ratio, uint32_t block_size, uint32_t nq, uint32_t nkv, uint32_t hd, float inv_sqrt_d,
+                     hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !attn_out || (topk > 0 && !lists))
+    return fail(IDX_ERR_NULL, "q, k_cache, v_cache, block_table, attn_out and (for topk > 0) lists are required");
+  if (hd != 64 && hd != 128) return fail(IDX_ERR_UNSUPPORTED, "hd %u (supported: 64, 128)", hd);
+  if (nkv < 1 || nq < nkv || nq % nkv || nq / nkv > 16)
+    return fail(IDX_ERR_UNSUPPORTED, "nq %u / nkv %u: nkv must divide nq with at most 16 query heads per KV head", nq,
+                nkv);
+  if (ratio < 1 || block_size < 1) return fail(IDX_ERR_SHAPE, "ratio and block_size must be >= 1");
+  if (topk > 65536 || (uint64_t)topk * ratio + ratio > (1u << 24))
+    return fail(IDX_ERR_UNSUPPORTED, "topk %u * ratio %u too large", topk, ratio);
+  if ((uint64_t)rows * nkv > 0x7fffffffull || (uint64_t)first_pos + rows > 0x7fffffffull)
+    return fail(IDX_ERR_SHAPE, "rows / positions out of range");
+  const size_t lds = salb::prefill_attn_lds_bytes((int)topk, (int)ratio, (int)hd);
+  if (lds > 160 * 1024 - 2048)
+    return fail(IDX_ERR_UNSUPPORTED, "topk %u * ratio %u positions do not fit the workgroup's LDS", topk, ratio);
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(attn_out, 4) ||
+      !aligned(block_table, 4) || !aligned(lists, 4))
+    return fail(IDX_ERR_SHAPE, "q and the caches must be 16-byte aligned");
+  if (rows == 0) return ok();
+  hipError_t e = salb::launch_prefill_attn(q, k_cache, v_cache, block_table, lists, attn_out, (int)rows, first_pos,
+                                           (int)topk, (int)ratio, (int)block_size, (int)nq, (int)nkv, (int)hd,
+                                           inv_sqrt_d, stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  return ok();
+}
+
 int qsa_block_pool(const uint16_t* raw_keys, const float* k_norm_w, float* block_keys, uint32_t first_block,
                    uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot, float theta, float eps,
                    hipStream_t stream) {

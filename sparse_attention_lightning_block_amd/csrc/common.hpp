@@ -33,7 +33,9 @@ __device__ __forceinline__ uint32_t ord_key(float v) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Inverse of ord_key on its image; key 0 (every NaN) gives the canonical quiet NaN.
 __device__ __forceinline__ float ord_to_float(uint32_t k) {
+  if (k == 0u) return __uint_as_float(0x7fc00000u);
   uint32_t b = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
   return __uint_as_float(b);
 }

@@ -77,6 +77,12 @@ hipError_t launch_qsa_gather(const uint16_t* k, const uint16_t* v, const int32_t
                              uint16_t* k_out, uint16_t* v_out, int n_sel, int block_size, int nkv, int hd,
                              hipStream_t st);
 
+// Block-sparse prefill attention (attention.hip).
+size_t prefill_attn_lds_bytes(int topk, int ratio, int hd);
+hipError_t launch_prefill_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* bt,
+                               const int32_t* lists, float* out, int rows, int64_t first_pos, int topk, int ratio,
+                               int block_size, int nq, int nkv, int hd, float inv_sqrt_d, hipStream_t st);
+
 // QSA (qsa.hip).
 hipError_t launch_block_pool(const uint16_t* raw, const float* kw, float* out, uint32_t first_block,
                              uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot, float theta,

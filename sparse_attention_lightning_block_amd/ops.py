@@ -198,6 +198,34 @@ def qsa_gather(k_cache, v_cache, block_table, sel, *, k_out: Optional[torch.Tens
     return k_out, v_out
 
 
+def qsa_prefill_attn(q, k_cache, v_cache, block_table, lists, *, first_pos: int, ratio: int,
+                     inv_sqrt_d: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Attention of each prefill row over its listed blocks plus its incomplete tail:
+    [rows, nq, hd] fp32 from bf16 q [rows, nq, hd] and paged bf16 caches [pages, bs, nkv, hd]."""
+    _dev(q, "q", torch.bfloat16, 3)
+    _dev(k_cache, "k_cache", torch.bfloat16, 4)
+    _dev(v_cache, "v_cache", torch.bfloat16, 4)
+    _dev(block_table, "block_table", torch.int32, 1)
+    rows, nq, hd = q.shape
+    _, block_size, nkv, hd_k = k_cache.shape
+    if hd_k != hd or v_cache.shape != k_cache.shape:
+        raise ValueError("q, k_cache and v_cache must agree on hd and the caches on their shape")
+    if lists is not None:
+        _dev(lists, "lists", torch.int32, 2)
+        if lists.shape[0] != rows:
+            raise ValueError("lists must have one row per query row")
+    topk = 0 if lists is None else lists.shape[1]
+    if inv_sqrt_d is None:
+        inv_sqrt_d = hd ** -0.5
+    if out is None:
+        out = torch.empty((rows, nq, hd), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32, 3)
+    check(_lib.load().qsa_prefill_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(lists),
+                                       _ptr(out), rows, first_pos, topk, ratio, block_size, nq, nkv, hd, inv_sqrt_d,
+                                       _stream()))
+    return out
+
+
 def qsa_block_pool(raw_keys, k_norm_w, block_keys, *, first_block: int, n_new: int, ratio: int, rot: int,
                    theta: float, eps: float) -> torch.Tensor:
     """Writes block_keys[first_block : first_block + n_new] (fp32) from bf16 raw keys."""

@@ -453,3 +453,31 @@ def test_one_workspace_serves_every_shape():
         w = (w2, w3)[it % 2]
         got = salb.indexer_score_topk(**to_dev(w), top_k=w.top_k, precision="mfma", workspace=ws)[0]
         assert torch.equal(got, fused_ref[w.name]), (it, w.name)
+
+
+def test_nan_scores_rank_last_on_both_selects():
+    """A NaN global scale makes every score of that page NaN.  The fused entry and the
+    split entries must both rank NaN below every number: bit-equal indices and scores
+    (NaN reported as the canonical quiet NaN), and no NaN entry selected while enough
+    numbers remain."""
+    w = make(3, reduced=1)
+    w.key_gscale = w.key_gscale.copy()
+    page = int(w.block_table[0, 3])
+    w.key_gscale[page] = np.nan
+    d = to_dev(w)
+    a_idx, a_val = salb.indexer_score_topk(**d, top_k=w.top_k, precision="mfma", with_scores=True)
+    rows = salb.indexer_score_rows(**d, n_cols=w.max_lb * w.epb, precision="mfma")
+    b_idx, b_val = salb.indexer_topk_select(rows, w.top_k, valid_lens=d["valid_lens"], with_scores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a_idx, b_idx)
+    assert torch.equal(a_val.view(torch.int32), b_val.view(torch.int32))
+    gi = _row(a_idx)
+    nan_entries = set(range(3 * w.epb, 4 * w.epb))
+    for t in range(w.T):
+        v = int(w.valid_lens[t])
+        if v - w.epb >= w.top_k:     # enough finite scores: none of the NaN page is chosen
+            assert not (set(gi[t].tolist()) & nan_entries), t
+    ref, amag = oracle_rows(w)
+    for t in range(w.T):
+        fin = np.isfinite(ref[t])
+        assert np.isnan(ref[t][~fin]).all()
