@@ -299,7 +299,9 @@ int qsa_qprep(const uint16_t* q_in, const float* q_norm_w, float* q_out, uint32_
  * qsa_score -- decode scores of one query over n_blocks blocks ([qsa.rs] qsa_score):
  *     scores[b] = sum_h ReLU(q[h,:] . block_keys[b,:]) / sqrt(hd)     b < n_blocks
  * (every block given is scored; the caller passes the query's complete blocks).  fp32
- * arithmetic, within ~1e-5 relative of the exact value.
+ * arithmetic, within ~1e-5 relative of the exact value: on the fp32 matrix cores
+ * (fp32 products and accumulation) when n_heads is 16, 32, 48 or 64 and hd is 64 or
+ * 128, else on the vector ALUs.
  *  q          [n_heads, hd] fp32, 16-byte aligned
  *  block_keys [>= n_blocks, hd] fp32, 16-byte aligned
  *  scores     [n_blocks] fp32 output (may be NULL when n_blocks is 0: nothing is launched)

@@ -62,6 +62,21 @@ __device__ __forceinline__ float row_sum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Sum over all 64 lanes, the same total in every lane: butterflies within quads and
+// 16-lane rows through DPP (quad permutes, then the half-row and row mirrors, which
+// pair a lane with one holding the other quad's or half's sum), then across the rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_f32<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_f32<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_f32<0x141>(x);  // row_half_mirror
+  x += dpp_f32<0x140>(x);  // row_mirror
+  return row_sum4(x);
+}
+
 // Four values per lane, x0..x3; lane i of row r (lanes 16 r .. 16 r + 15) returns the
 // sum of x_r over lane i of all four rows -- four butterflies' worth of sums, each
 // kept by one row, in three row swaps.  The 32-lane swap of (x0, x2) leaves the lower

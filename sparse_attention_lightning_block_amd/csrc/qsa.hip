@@ -21,6 +21,23 @@ namespace salb {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// Cosine and sine of a RoPE angle (fp64).  The angle is first reduced by the nearest
+// multiple of 2*pi, with 2*pi split into three doubles and each product taken by an fma
+// (exact to ~3e-16 rad for angles below 2^32), so that the library sine and cosine see
+// |x| <= ~3.4: at long-prefill positions the raw angle reaches ~5e5 rad, where they
+// would take their slow large-argument reduction.
+__device__ __forceinline__ void rope_cos_sin(double angle, double& c, double& s) {
+  constexpr double kInv2Pi = 0.15915494309189535;
+  constexpr double k2PiHi = 0x1.921fb54442d18p+2;
+  constexpr double k2PiMid = 0x1.1a62633145c07p-52;
+  constexpr double k2PiLo = -0x1.f1976b7ed8fbcp-108;
+  const double k = rint(angle * kInv2Pi);
+  double r = fma(-k, k2PiHi, angle);
+  r = fma(-k, k2PiMid, r);
+  r = fma(-k, k2PiLo, r);
+  sincos(r, &s, &c);
+}
+
 // ------------------------------------------------------------------ block pool
 
 // Eight pooled blocks per 256-thread workgroup, 32 threads per block.  Thread j of a
@@ -96,7 +113,7 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const uint16_t* __restr
   for (int i = j; i < half; i += TPB) {
     const double inv_freq = pow((double)theta, -2.0 * (double)i / (double)rot);
     double sn, c;
-    sincos((double)b * (double)ratio * inv_freq, &sn, &c);
+    rope_cos_sin((double)b * (double)ratio * inv_freq, c, sn);
     cs[bi][i][0] = c;
     cs[bi][i][1] = sn;
   }
@@ -124,24 +141,30 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const uint16_t* __restr
 
 // ------------------------------------------------------------------ query prep
 
-// One 256-thread workgroup per row, all heads: the row's raw values go to LDS, a
-// wave computes each head's RMSNorm factor, the rotation angles (fp64) are formed
-// once per pair for the row and shared by its heads, then every thread writes 8
-// output dims at a time.
+// One 1024-thread workgroup per row, all heads: the row's raw values go to LDS, each of
+// the 16 waves computes the RMSNorm factor of every 16th head (a wave-wide sum on the
+// VALU), the rotation angles (fp64) are formed once per pair for the row and shared by
+// its heads, and the outputs are written one element per thread in order (consecutive
+// lanes read consecutive LDS words and store consecutive floats).  A decode query is a
+// single row, so the heads are spread over as many waves as one workgroup holds.
+constexpr int kQprepThreads = 1024;
+
 template <int HD>
-__global__ __launch_bounds__(256) void qprep_rows_kernel(const uint16_t* __restrict__ qk,
-                                                        const float* __restrict__ qw, float* __restrict__ out,
-                                                        uint32_t first_pos, uint32_t qkw, uint32_t n_heads,
-                                                        int rot, float theta, float eps) {
+__global__ __launch_bounds__(kQprepThreads) void qprep_rows_kernel(const uint16_t* __restrict__ qk,
+                                                                   const float* __restrict__ qw,
+                                                                   float* __restrict__ out, uint32_t first_pos,
+                                                                   uint32_t qkw, uint32_t n_heads, int rot,
+                                                                   float theta, float eps) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* xr = reinterpret_cast<float*>(smem);                          // [n_heads * HD] raw values
   float* hinv = xr + n_heads * HD;                                     // [n_heads]
   double* cs = reinterpret_cast<double*>(hinv + ((n_heads + 3) & ~3));  // [HD / 2][2]
+  constexpr int kWaves = kQprepThreads / 64;
   const uint32_t r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int groups = (int)n_heads * HD / 8;
+  const int n = (int)n_heads * HD;
   const uint16_t* src = qk + (int64_t)r * qkw;
-  for (int g = tid; g < groups; g += 256) {
+  for (int g = tid; g < n / 8; g += kQprepThreads) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(src + 8 * g);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -151,45 +174,41 @@ __global__ __launch_bounds__(256) void qprep_rows_kernel(const uint16_t* __restr
   }
   const int half = rot >> 1;
   const double pos = (double)first_pos + (double)r;
-  for (int i = tid; i < half; i += 256) {
+  for (int i = tid; i < half; i += kQprepThreads) {
     const double inv_freq = pow((double)theta, -2.0 * (double)i / (double)rot);
     double sn, c;
-    sincos(pos * inv_freq, &sn, &c);
+    rope_cos_sin(pos * inv_freq, c, sn);
     cs[2 * i] = c;
     cs[2 * i + 1] = sn;
   }
   __syncthreads();
-  for (uint32_t h = wave; h < n_heads; h += 4) {
+  for (uint32_t h = wave; h < n_heads; h += kWaves) {
     float ss = 0.0f;
+#pragma unroll
     for (int d = lane; d < HD; d += 64) {
       const float x = xr[h * HD + d];
       ss += x * x;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    ss = wave_sum(ss);
     if (lane == 0) hinv[h] = 1.0f / sqrtf(ss / (float)HD + eps);
   }
   __syncthreads();
-  auto norm = [&](int h, int d) -> float { return xr[h * HD + d] * hinv[h] * (1.0f + qw[d]); };
-  for (int g = tid; g < groups; g += 256) {
-    const int h = (8 * g) / HD, d0 = (8 * g) % HD;
-    float o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int d = d0 + i;
-      if (d < half) {
-        const double a = norm(h, d), bb = norm(h, d + half);
-        o[i] = (float)(a * cs[2 * d] - bb * cs[2 * d + 1]);
-      } else if (d < rot) {
-        const double a = norm(h, d - half), bb = norm(h, d);
-        o[i] = (float)(a * cs[2 * (d - half) + 1] + bb * cs[2 * (d - half)]);
-      } else {
-        o[i] = norm(h, d);
-      }
+  float* dst = out + (int64_t)r * n;
+  for (int e = tid; e < n; e += kQprepThreads) {
+    const int h = e / HD, d = e % HD;
+    const float hv = hinv[h];
+    auto norm = [&](int dd) -> float { return xr[h * HD + dd] * hv * (1.0f + qw[dd]); };
+    float o;
+    if (d < half) {
+      const double a = norm(d), bb = norm(d + half);
+      o = (float)(a * cs[2 * d] - bb * cs[2 * d + 1]);
+    } else if (d < rot) {
+      const double a = norm(d - half), bb = norm(d);
+      o = (float)(a * cs[2 * (d - half) + 1] + bb * cs[2 * (d - half)]);
+    } else {
+      o = norm(d);
     }
-    float* dst = out + ((int64_t)r * n_heads + h) * HD + d0;
-    *reinterpret_cast<float4v*>(dst) = float4v{o[0], o[1], o[2], o[3]};
-    *reinterpret_cast<float4v*>(dst + 4) = float4v{o[4], o[5], o[6], o[7]};
+    dst[e] = o;
   }
 }
 
@@ -473,6 +492,74 @@ __global__ __launch_bounds__(256) void qsa_decode_score_kernel(const float* __re
   if (wave == 0 && b < nb) scores[b] = ((part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane])) * out_scale;
 }
 
+// The same scores on the fp32 matrix cores (v_mfma_f32_16x16x4_f32: fp32 products and
+// fp32 accumulation), for head counts that are a multiple of 16 (at most 64) and hd 64 or
+// 128.  Each wave takes UPW units of 16 consecutive blocks and computes the 16-head x
+// 16-block tiles S^T[h, b] = q[h, :] . k[b, :].  Lane l (column c = l % 16, lane group
+// g = l / 16) holds, in both operands, the dims [g * HD/4, (g + 1) * HD/4): MFMA step s
+// takes dim g * HD/4 + s from every group, so the steps and the four groups together
+// cover each dim once.  The A operand is head m * 16 + c of the query, the B operand
+// block b0 + c; the result leaves block b0 + c in lane column c with heads 4g .. 4g + 3
+// of the tile in its four values.  ReLU, the sum over those heads and the head tiles in
+// the lane, then the sum over the four lane groups; ×1/√hd.  Loads: each lane reads
+// 128-byte (hd 128) runs of its block and of the query, all issued before the first MFMA.
+template <int HD, int MT, int UPW>
+__global__ __launch_bounds__(256) void qsa_decode_score_mfma_kernel(const float* __restrict__ q,
+                                                                    const float* __restrict__ keys,
+                                                                    float* __restrict__ scores, uint32_t nb,
+                                                                    float out_scale) {
+  constexpr int KS = HD / 4;  // MFMA steps = dims per lane group
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const uint32_t units = (nb + 15) / 16;
+  const uint32_t u0 = (blockIdx.x * 4 + wave) * UPW;
+  if (u0 >= units) return;  // a whole wave leaves; the kernel has no barrier
+  float kb[UPW][KS];
+#pragma unroll
+  for (int u = 0; u < UPW; ++u) {
+    const uint32_t b = (u0 + u) * 16 + c;
+    const float* src = keys + (int64_t)(b < nb ? b : nb - 1) * HD + g * KS;  // past the end: re-read, not stored
+#pragma unroll
+    for (int s = 0; s < KS; s += 4) {
+      const float4v v = *reinterpret_cast<const float4v*>(src + s);
+      kb[u][s] = v[0];
+      kb[u][s + 1] = v[1];
+      kb[u][s + 2] = v[2];
+      kb[u][s + 3] = v[3];
+    }
+  }
+  float qa[MT][KS];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const float* src = q + (m * 16 + c) * HD + g * KS;
+#pragma unroll
+    for (int s = 0; s < KS; s += 4) {
+      const float4v v = *reinterpret_cast<const float4v*>(src + s);
+      qa[m][s] = v[0];
+      qa[m][s + 1] = v[1];
+      qa[m][s + 2] = v[2];
+      qa[m][s + 3] = v[3];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UPW; ++u) {
+    float4v acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[m][s], kb[u][s], acc[m], 0, 0, 0);
+    float part = 0.0f;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      part += (fmaxf(acc[m][0], 0.0f) + fmaxf(acc[m][1], 0.0f)) + (fmaxf(acc[m][2], 0.0f) + fmaxf(acc[m][3], 0.0f));
+    part = row_sum4(part);
+    const uint32_t b = (u0 + u) * 16 + c;
+    if (g == 0 && b < nb) scores[b] = part * out_scale;
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_block_pool(const uint16_t* raw, const float* kw, float* out, uint32_t first_block,
@@ -508,18 +595,18 @@ hipError_t launch_qprep_rows(const uint16_t* qk, const float* qw, float* out, ui
   switch (hd) {
     case 64:
       if ((e = ensure_lds(reinterpret_cast<const void*>(qprep_rows_kernel<64>), lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(qprep_rows_kernel<64>, dim3(rows), dim3(256), lds, st, qk, qw, out, first_pos, qkw, n_heads,
-                         (int)rot, theta, eps);
+      hipLaunchKernelGGL(qprep_rows_kernel<64>, dim3(rows), dim3(kQprepThreads), lds, st, qk, qw, out, first_pos,
+                         qkw, n_heads, (int)rot, theta, eps);
       break;
     case 128:
       if ((e = ensure_lds(reinterpret_cast<const void*>(qprep_rows_kernel<128>), lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(qprep_rows_kernel<128>, dim3(rows), dim3(256), lds, st, qk, qw, out, first_pos, qkw, n_heads,
-                         (int)rot, theta, eps);
+      hipLaunchKernelGGL(qprep_rows_kernel<128>, dim3(rows), dim3(kQprepThreads), lds, st, qk, qw, out, first_pos,
+                         qkw, n_heads, (int)rot, theta, eps);
       break;
     default:
       if ((e = ensure_lds(reinterpret_cast<const void*>(qprep_rows_kernel<256>), lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(qprep_rows_kernel<256>, dim3(rows), dim3(256), lds, st, qk, qw, out, first_pos, qkw, n_heads,
-                         (int)rot, theta, eps);
+      hipLaunchKernelGGL(qprep_rows_kernel<256>, dim3(rows), dim3(kQprepThreads), lds, st, qk, qw, out, first_pos,
+                         qkw, n_heads, (int)rot, theta, eps);
       break;
   }
   return hipGetLastError();
@@ -539,11 +626,47 @@ static hipError_t launch_qsa_mfma(const float* q, const float* keys, float* scor
   return hipGetLastError();
 }
 
+template <int HD, int MT>
+static hipError_t launch_decode_mfma(const float* q, const float* keys, float* scores, uint32_t nb, float sc,
+                                     hipStream_t st) {
+  // two 16-block units per wave once that still leaves a wave per SIMD (1024 SIMDs)
+  const uint32_t units = (nb + 15) / 16;
+  if (units >= 2048) {
+    const dim3 grid((units + 7) / 8);
+    hipLaunchKernelGGL((qsa_decode_score_mfma_kernel<HD, MT, 2>), grid, dim3(256), 0, st, q, keys, scores, nb, sc);
+  } else {
+    const dim3 grid((units + 3) / 4);
+    hipLaunchKernelGGL((qsa_decode_score_mfma_kernel<HD, MT, 1>), grid, dim3(256), 0, st, q, keys, scores, nb, sc);
+  }
+  return hipGetLastError();
+}
+
+bool qsa_decode_uses_mfma(uint32_t n_heads, uint32_t hd) {
+  return (hd == 64 || hd == 128) && n_heads % 16 == 0 && n_heads >= 16 && n_heads <= 64;
+}
+
 hipError_t launch_qsa_decode_score(const float* q, const float* keys, float* scores, uint32_t nb, uint32_t n_heads,
                                    uint32_t hd, hipStream_t st) {
+  const float sc = 1.0f / sqrtf((float)hd);
+  if (qsa_decode_uses_mfma(n_heads, hd)) {
+    const uint32_t mt = n_heads / 16;
+    if (hd == 64) {
+      switch (mt) {
+        case 1: return launch_decode_mfma<64, 1>(q, keys, scores, nb, sc, st);
+        case 2: return launch_decode_mfma<64, 2>(q, keys, scores, nb, sc, st);
+        case 3: return launch_decode_mfma<64, 3>(q, keys, scores, nb, sc, st);
+        default: return launch_decode_mfma<64, 4>(q, keys, scores, nb, sc, st);
+      }
+    }
+    switch (mt) {
+      case 1: return launch_decode_mfma<128, 1>(q, keys, scores, nb, sc, st);
+      case 2: return launch_decode_mfma<128, 2>(q, keys, scores, nb, sc, st);
+      case 3: return launch_decode_mfma<128, 3>(q, keys, scores, nb, sc, st);
+      default: return launch_decode_mfma<128, 4>(q, keys, scores, nb, sc, st);
+    }
+  }
   const dim3 grid((nb + 63) / 64);
   const size_t lds = (size_t)n_heads * hd * 4;
-  const float sc = 1.0f / sqrtf((float)hd);
   hipError_t e;
   switch (hd) {
     case 64:

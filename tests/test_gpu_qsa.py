@@ -210,3 +210,25 @@ def test_decode_score_partial_table_and_empty():
     assert np.all(got[100:] == 9.0)
     ref = qsa.score_blocks(q.cpu().numpy().astype(np.float64), keys_d.cpu().numpy().astype(np.float64), 100)
     assert np.allclose(got[:100], ref, rtol=1e-5, atol=1e-5 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("n_heads,hd,nb", [(16, 64, 1000), (48, 128, 777), (64, 128, 40001), (32, 128, 32785),
+                                           (5, 128, 300), (32, 256, 129), (16, 128, 7)])
+def test_decode_score_shapes(n_heads, hd, nb):
+    """qsa_score over the shapes of both kernels (matrix-core tiles for 16..64 heads in
+    steps of 16 at hd 64/128, one and two 16-block units per wave; the VALU kernel
+    otherwise), ragged block counts, seeded N(0, 1) inputs: the FP32 rule against the
+    oracle."""
+    rng = np.random.default_rng([5, n_heads, hd, nb])
+    q = rng.standard_normal((n_heads, hd)).astype(np.float32)
+    keys = rng.standard_normal((nb + 3, hd)).astype(np.float32)
+    out = torch.full((nb + 16,), 7.0, dtype=torch.float32, device="cuda")
+    salb.qsa_score(torch.from_numpy(q).cuda(), torch.from_numpy(keys).cuda(), n_blocks=nb, out=out[:nb])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(got[nb:] == 7.0)
+    q64, k64 = q.astype(np.float64), keys.astype(np.float64)
+    ref = qsa.score_blocks(q64, k64, nb)
+    A = np.abs(q64).sum(axis=0) @ np.abs(k64[:nb]).T / np.sqrt(hd)
+    err = np.abs(got[:nb].astype(np.float64) - ref)
+    assert np.all(err <= S_REL * np.abs(ref) + S_ABS_A * A), f"max err {err.max()}"
