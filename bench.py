@@ -33,6 +33,7 @@ METRIC = "query·key scores/s + ms per top-k=2048 call; % of HBM BW (decode) / M
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 VALU_F32_PEAK_TFLOPS = 157.3
+MFMA_F32_PEAK_TFLOPS = 157.3
 
 WORKLOADS = {
     "tiny_decode": 1,
@@ -353,7 +354,11 @@ def run_qsa_decode(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ms_per_step, stage = timed_steps(torch, make_step(torch, [step], args.graph), 1, args.steps)
+    # A decode step is a short chain of small kernels whose eager launches from Python
+    # take longer than the kernels run: the step is captured into one HIP graph and
+    # replayed (the eager rate is reported beside it).
+    ms_per_step, stage = timed_steps(torch, make_step(torch, [step], True), 1, args.steps)
+    ms_eager, _ = timed_steps(torch, make_step(torch, [step], False), 1, args.steps)
     pool_ms, prep_ms, score_ms, select_ms = (back_to_back_ms(torch, f, args.steps) for f in (pool, prep, score, select))
     key_bytes = nb * w.hd * 4 + w.n_heads * w.hd * 4 + nb * 4
     gbs = key_bytes / (score_ms / 1e3) / 1e9
@@ -371,7 +376,8 @@ def run_qsa_decode(args):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "qsa_decode", "pos": int(pos), "blocks": int(nb), "heads": w.n_heads, "hd": w.hd,
-                   "top_k": w.top_k, "launch": "hip_graph" if args.graph else "eager"},
+                   "top_k": w.top_k, "launch": "hip_graph"},
+        "ms_per_step_eager": ms_eager,
         "step_ms": {"p10": float(np.percentile(stage[0], 10)), "p50": float(np.median(stage[0])),
                     "p90": float(np.percentile(stage[0], 90))},
         "stage_ms": {"pool_one_block": pool_ms, "qprep": prep_ms, "score": score_ms, "select": select_ms},
@@ -744,15 +750,21 @@ def csa_roofline(w, score_s, precision):
     per_stream, unique = csa_bytes(w)
     traffic = scorer_traffic(w.name) if precision == "mfma" else None
     tflops = flops / score_s / 1e12
-    ridge = MFMA_F16_PEAK_TFLOPS / (HBM_PEAK_GBS / 1e3)
+    # the matrix peak of the path's own operand type: fp16 for the MFMA path, fp32 for FP32
+    mpeak = MFMA_F16_PEAK_TFLOPS if precision == "mfma" else MFMA_F32_PEAK_TFLOPS
+    ridge = mpeak / (HBM_PEAK_GBS / 1e3)
     ai_unique = flops / unique
     frac = {
-        "mfma": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+        "mfma": round(tflops / mpeak, 4),
         "hbm_per_stream": round(per_stream / score_s / 1e9 / HBM_PEAK_GBS, 4),
         "hbm_unique": round(unique / score_s / 1e9 / HBM_PEAK_GBS, 4),
         "hbm_counter": None if traffic is None else round(traffic / score_s / 1e9 / HBM_PEAK_GBS, 4),
     }
-    if precision != "mfma":
+    # the FP32 path runs on the fp32 matrix cores at D 64/128 (the vector ALUs otherwise)
+    f32_mfma = precision != "mfma" and w.D in (64, 128)
+    if f32_mfma:
+        bound, achieved, peak, unit = "mfma", tflops, MFMA_F32_PEAK_TFLOPS, "TFLOP/s"
+    elif precision != "mfma":
         bound, achieved, peak, unit = "alu", tflops, VALU_F32_PEAK_TFLOPS, "TFLOP/s"
     elif ai_unique > ridge:
         bound, achieved, peak, unit = "mfma", tflops, MFMA_F16_PEAK_TFLOPS, "TFLOP/s"
@@ -766,7 +778,7 @@ def csa_roofline(w, score_s, precision):
         "frac": round(achieved / peak, 4),
         "traffic": traffic,
         "kernel": ("score_mfma_group_kernel" if w.T >= 4 else "score_mfma_split_kernel") if precision == "mfma"
-        else "score_f32_kernel",
+        else "score_f32mfma_kernel" if f32_mfma else "score_f32_kernel",
         "kernel_avg_us": round(score_s * 1e6, 2),
         "flops_per_launch": int(flops),
         "bytes_per_launch": int(per_stream),

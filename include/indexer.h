@@ -66,7 +66,8 @@ extern "C" {
 #define IDX_DTYPE_BF16 1
 
 /* arithmetic of the dot products */
-#define IDX_PREC_FP32 0   /* fp32 vector FMAs; scores within ~1e-5 relative of the exact value */
+#define IDX_PREC_FP32 0   /* fp32 products and sums (the fp32 matrix cores at D 64/128, vector
+                             FMAs at D 256); scores within ~1e-5 relative of the exact value */
 #define IDX_PREC_MFMA 1   /* fp16 matrix cores with fp32 accumulation; q rounded to 11 bits
                              after a per-head power-of-two prescale, NVFP4 code values exact */
 

@@ -27,8 +27,9 @@
 //        from sixteen rows on), one per wave; when the rows resolve the chunk to the
 //        same pages, each 64-key tile is decoded once into LDS (every thread decodes
 //        a 1/G slice of a key) and read by all the waves.
-//  * score_f32_kernel (IDX_PREC_FP32): one key per lane, fp32 FMAs with q read
-//    through the scalar cache, for results within ~1e-5 relative.
+//  * score_f32mfma_kernel (IDX_PREC_FP32, D 64/128): the same contraction in fp32 on
+//    the fp32 matrix cores, for results within ~1e-5 relative; score_f32_kernel (D 256):
+//    one key per lane, fp32 FMAs with q read through the scalar cache.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -797,6 +798,117 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs a) {
   out_row[s] = score;
 }
 
+// FP32 scores on the fp32 matrix cores (IDX_PREC_FP32 at D 64 or 128, up to 64 heads):
+// every wave streams 16-key steps of one row.  v_mfma_f32_16x16x4_f32 takes 16 heads x
+// 4 dims of q (A) and 4 dims x 16 keys of exact NVFP4 code values (B), fp32 products and
+// sums.  Lane (c, g) = (lane % 16, lane / 16) holds, in both operands, the dims
+// [g D/4, (g + 1) D/4): MFMA step s takes dim g D/4 + s from every lane group, so each
+// lane decodes one contiguous D/8-byte slice of its key (key c of the step).  The
+// epilogue is the vector kernel's, w * max(g * dot, 0) per head: lane (c, g) holds heads
+// 16 mt + 4 g + i of key c, summed in the lane and then over the four lane groups.
+template <int MT, int D>
+__global__ __launch_bounds__(256) void score_f32mfma_kernel(ScoreArgs a) {
+  constexpr int KS = D / 4;   // MFMA steps = dims per lane group
+  constexpr int NB = D / 8;   // code bytes of a lane's slice
+  constexpr int NG = KS / 16; // 16-dim scale groups in it
+  static_assert(D == 64 || D == 128, "head dim");
+  zero_side_words(a, 256);
+  const XcdTile tile = score_tile(a, a.T);
+  if (tile.chunk >= a.n_chunks) return;
+  const int t = tile.row;
+  const int valid = a.valid_lens[t];
+  const int s_begin = tile.chunk * a.chunk;
+  const int s_lim = a.write_tail ? a.n_cols : valid;
+  if (s_begin >= s_lim) return;
+  const int s_end = min(s_begin + a.chunk, s_lim);
+  const int s_vend = min(s_end, valid);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  float* out_row = a.scores + (int64_t)t * a.score_stride;
+  for (int s = max(s_vend, s_begin) + tid; s < s_end; s += 256) out_row[s] = -INFINITY;
+  if (s_vend <= s_begin) return;
+
+  // A operands q[16 mt + c][g KS + s] and the weights of accumulator rows 16 mt + 4 g + i
+  float qa[MT][KS];
+  float wr[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int h = 16 * mt + c;
+    const int64_t base = ((int64_t)t * a.H + h) * D + g * KS;
+#pragma unroll
+    for (int s = 0; s < KS; s += 8) {
+      if (h >= a.H) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qa[mt][s + e] = 0.0f;
+      } else if (a.q_bf16) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) + base + s);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qa[mt][s + 2 * e] = __uint_as_float(v[e] << 16);
+          qa[mt][s + 2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+        }
+      } else {
+        const float* src = reinterpret_cast<const float*>(a.q) + base + s;
+        const float4v v0 = *reinterpret_cast<const float4v*>(src);
+        const float4v v1 = *reinterpret_cast<const float4v*>(src + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qa[mt][s + e] = v0[e];
+          qa[mt][s + 4 + e] = v1[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hr = 16 * mt + 4 * g + i;
+      wr[mt][i] = hr < a.H ? a.w[(int64_t)t * a.H + hr] : 0.0f;
+    }
+  }
+  const int32_t* bt_row = a.bt + (int64_t)t * a.bt_stride;
+  for (int s0 = s_begin + 16 * wave; s0 < s_vend; s0 += 64) {
+    // key c of the step (keys past the valid end re-read the last valid one; not stored)
+    const int s = min(s0 + c, s_vend - 1);
+    const uint32_t lb = div_epb((uint32_t)s, a.epb_magic);
+    const int p = bt_row[lb];
+    const int64_t e = (int64_t)p * a.epb + (s - (int)lb * a.epb);
+    const float gs = a.gscale[p];
+    const uint8_t* kp = a.keys + e * (D / 2) + g * NB;
+    const uint8_t* sp = a.kscale + e * (D / 16) + g * NG;
+    uint32_t words[NB / 4];
+    if constexpr (NB == 16) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(kp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) words[i] = v[i];
+    } else {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(kp);
+      words[0] = v[0];
+      words[1] = v[1];
+    }
+    float kb[KS];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const float sc = e4m3_to_f32(sp[j]);
+      decode8_f32(words[2 * j], sc, kb + 16 * j);
+      decode8_f32(words[2 * j + 1], sc, kb + 16 * j + 8);
+    }
+    float4v acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[mt][k], kb[k], acc[mt], 0, 0, 0);
+    float part = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part = fmaf(wr[mt][i], fmaxf(gs * acc[mt][i], 0.0f), part);
+    part = row_sum4(part);
+    if (g == 0 && s0 + c < s_vend) out_row[s0 + c] = part;
+  }
+}
+
 // ------------------------------------------------------------------ debug dequant
 
 template <int D>
@@ -891,6 +1003,20 @@ static hipError_t launch_f32_d(const ScoreArgs& a, int blocks, hipStream_t st) {
   return a.q_bf16 ? launch_f32_q<D, 1>(a, blocks, st) : launch_f32_q<D, 0>(a, blocks, st);
 }
 
+template <int D>
+static hipError_t launch_f32mfma_d(const ScoreArgs& a, int blocks, hipStream_t st) {
+  switch ((a.H + 15) / 16) {
+    case 1: hipLaunchKernelGGL((score_f32mfma_kernel<1, D>), dim3(blocks), dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((score_f32mfma_kernel<2, D>), dim3(blocks), dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((score_f32mfma_kernel<3, D>), dim3(blocks), dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((score_f32mfma_kernel<4, D>), dim3(blocks), dim3(256), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+// The FP32 path runs on the fp32 matrix cores for D 64/128 and up to 64 heads.
+static bool f32_uses_mfma(const ScoreArgs& a) { return (a.D == 64 || a.D == 128) && a.H <= 64; }
+
 // Keys per workgroup: enough workgroups to fill the chip a few times over
 // (`target`), multiples of 64, between 256 and 4096, and few enough block-table
 // entries per chunk (<= 500) for the LDS page lists.
@@ -913,6 +1039,9 @@ hipError_t launch_score_rows(ScoreArgs a, int precision, hipStream_t st) {
   if (precision == 1) {
     a.chunk = chunk_keys(units, a.n_cols, a.epb, group ? SALB_GROUP_WGS : SALB_SPLIT_WGS);
     a.pid_cap = a.chunk / a.epb + 2;
+  } else if (f32_uses_mfma(a)) {
+    a.chunk = chunk_keys(units, a.n_cols, a.epb, SALB_SPLIT_WGS);
+    a.pid_cap = 0;
   } else {
     a.chunk = 256;
     a.pid_cap = 0;
@@ -949,6 +1078,8 @@ hipError_t launch_score_rows(ScoreArgs a, int precision, hipStream_t st) {
       default: return launch_mfma_d<256>(a, (int)blocks, group, st);
     }
   }
+  if (f32_uses_mfma(a))
+    return a.D == 64 ? launch_f32mfma_d<64>(a, (int)blocks, st) : launch_f32mfma_d<128>(a, (int)blocks, st);
   switch (a.D) {
     case 64: return launch_f32_d<64>(a, (int)blocks, st);
     case 128: return launch_f32_d<128>(a, (int)blocks, st);

@@ -64,4 +64,7 @@ def test_roofline_bound_follows_the_unique_byte_intensity():
     # the scores are the same in both)
     assert shared["bytes_per_launch"] == own["bytes_per_launch"]
     assert own["unique_bytes_per_launch"] > 3 * shared["unique_bytes_per_launch"]
-    assert bench.csa_roofline(wl("shared"), 10e-6, "fp32")["bound"] == "alu"
+    # the FP32 path at D 128 runs on the fp32 matrix cores: its own peak, 157.3 TFLOP/s
+    f32 = bench.csa_roofline(wl("shared"), 10e-6, "fp32")
+    assert f32["bound"] == "mfma" and f32["peak"] == 157.3 and f32["kernel"] == "score_f32mfma_kernel"
+    assert f32["frac"] == pytest.approx(flops / 10e-6 / 1e12 / 157.3, rel=1e-3)

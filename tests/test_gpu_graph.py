@@ -124,3 +124,49 @@ def test_fused_entry_graph_replays_match_eager(cfg, reduced):
         # eager work between replays, on the same workspace (another shape)
         salb.indexer_score_topk(**od, top_k=other.top_k, precision="mfma", workspace=ws)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n_blocks", [700, 32768])
+def test_qsa_decode_step_graph_replays_match_eager(n_blocks):
+    """One QSA decode step (the new block pooled, the query prepared, its scores over
+    all blocks on the matrix cores, the top-k through the long-row select when the row
+    is long) captured once and replayed: bit-equal to the eager step every time."""
+    w = make(5, reduced=0 if n_blocks > 700 else 1)
+    nb = min(n_blocks, w.n_blocks)
+    raw = torch.from_numpy(w.raw_keys.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    kw = torch.from_numpy(w.k_norm_w).cuda()
+    qw = torch.from_numpy(w.q_norm_w).cuda()
+    q_in = torch.from_numpy(w.qk[w.rows - 1].view(np.int16).copy()).view(torch.bfloat16).cuda()
+    pos = nb * w.ratio - 1
+    keys = torch.empty((w.n_blocks, w.hd), dtype=torch.float32, device="cuda")
+    salb.qsa_block_pool(raw, kw, keys, first_block=0, n_new=nb, ratio=w.ratio, rot=w.rot, theta=w.theta, eps=w.eps)
+    q = torch.empty((w.n_heads, w.hd), dtype=torch.float32, device="cuda")
+    sc = torch.empty((1, nb), dtype=torch.float32, device="cuda")
+    idx = torch.empty((1, w.top_k), dtype=torch.int32, device="cuda")
+    val = torch.empty((1, w.top_k), dtype=torch.float32, device="cuda")
+    ws = torch.full((max(256, salb.indexer_topk_workspace_size(1, nb, w.top_k)),), 0x5A, dtype=torch.uint8,
+                    device="cuda")
+
+    def step():
+        salb.qsa_block_pool(raw, kw, keys, first_block=nb - 1, n_new=1, ratio=w.ratio, rot=w.rot, theta=w.theta,
+                            eps=w.eps)
+        salb.qsa_qprep(q_in, qw, n_heads=w.n_heads, hd=w.hd, pos=pos, rot=w.rot, theta=w.theta, eps=w.eps, out=q)
+        salb.qsa_score(q, keys, n_blocks=nb, out=sc[0])
+        salb.indexer_topk_select(sc, w.top_k, workspace=ws, out_idx=idx, out_scores=val)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (keys, q, sc, idx, val)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (q, sc, val):
+            t.fill_(2.5)
+        idx.fill_(-3)
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((keys, q, sc, idx, val), ref):
+            assert torch.equal(got.view(torch.int32), want.view(torch.int32)), rep
+        step()  # eager work between replays
+        torch.cuda.synchronize()
