@@ -322,7 +322,12 @@ int qsa_score(const float* q, const float* block_keys, float* scores, uint32_t n
  * Supported: hd in {64, 128, 256}, 1 <= n_heads <= 64; precision IDX_PREC_FP32 or IDX_PREC_MFMA.
  * IDX_PREC_MFMA runs on the fp16 matrix cores (q and keys rounded to fp16, fp32
  * accumulation; within 2e-3 of the row's largest score) when hd is 64 or 128 and
- * n_heads is 16, 32 or 64, and on the fp32 path (~1e-5 relative) otherwise.
+ * n_heads is 16, 32 or 64, and on the fp32 path (~1e-5 relative) otherwise.  The fp16
+ * rounding takes the values as they are, with no prescale: it assumes every |q| and
+ * |block_keys| element is below 65504 and that elements below 2^-14 (fp16's normal
+ * range) carry a negligible share of a score -- which holds for the RMSNorm outputs of
+ * qsa_block_pool and qsa_qprep_rows (elements of order sqrt(hd) * |1 + w|).  Other
+ * inputs belong on IDX_PREC_FP32.
  */
 int qsa_score_rows(const float* q, const float* block_keys, float* scores,
                    uint32_t rows, uint32_t n_blocks_max, uint32_t first_pos, uint32_t score_stride,
