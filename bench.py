@@ -232,8 +232,12 @@ def run_qsa(args, w):
     kw = torch.from_numpy(w.k_norm_w).to(dev)
     qk = torch.from_numpy(w.qk.view(np.int16).copy()).view(torch.bfloat16).to(dev)
     qw = torch.from_numpy(w.q_norm_w).to(dev)
-    keys = torch.empty((w.n_blocks, w.hd), dtype=torch.float32, device=dev)
-    q = torch.empty((w.rows, w.n_heads, w.hd), dtype=torch.float32, device=dev)
+    # the matrix-core path stores the pooled keys and prepared queries in fp16, the values
+    # its MFMAs multiply (the same scores, bit for bit, as from fp32 storage)
+    mfma = args.precision == "mfma" and w.hd in (64, 128) and w.n_heads in (16, 32, 64)
+    sdt = torch.float16 if mfma else torch.float32
+    keys = torch.empty((w.n_blocks, w.hd), dtype=sdt, device=dev)
+    q = torch.empty((w.rows, w.n_heads, w.hd), dtype=sdt, device=dev)
     scores = torch.empty((w.rows, w.n_blocks), dtype=torch.float32, device=dev)
     idx = torch.empty((w.rows, w.top_k), dtype=torch.int32, device=dev)
     ws = torch.zeros(max(1, salb.indexer_topk_workspace_size(w.rows, w.n_blocks, w.top_k)), dtype=torch.uint8,
@@ -266,10 +270,8 @@ def run_qsa(args, w):
     flops = 2.0 * pairs * w.n_heads * w.hd
     score_s = score_avg / 1e3
     tf = flops / score_s / 1e12
-    # the library's QSA scorer takes the matrix cores for hd 64/128 with 16, 32 or 64 heads
-    mfma = args.precision == "mfma" and w.hd in (64, 128) and w.n_heads in (16, 32, 64)
     peak = MFMA_F16_PEAK_TFLOPS if mfma else VALU_F32_PEAK_TFLOPS
-    pool_bytes = w.n_blocks * w.ratio * w.hd * 2 + w.n_blocks * w.hd * 4
+    pool_bytes = w.n_blocks * w.ratio * w.hd * 2 + w.n_blocks * w.hd * keys.element_size()
     out = {
         "metric": METRIC,
         "value": pairs / (ms_per_step / 1e3),
@@ -285,7 +287,8 @@ def run_qsa(args, w):
         "data": "synthetic",
         "config": {"workload": w.name, "rows": w.rows, "heads": w.n_heads, "hd": w.hd, "raw_keys": w.n_blocks * w.ratio,
                    "ratio": w.ratio, "blocks": w.n_blocks, "top_k": w.top_k, "pairs": pairs,
-                   "precision": args.precision, "launch": "hip_graph" if args.graph else "eager"},
+                   "precision": args.precision, "storage": "f16" if mfma else "f32",
+                   "launch": "hip_graph" if args.graph else "eager"},
         "step_ms": {"p50": float(np.median(prep_ms + score_ms + select_ms))},
         "stage_ms": {"pool_and_qprep": prep_avg, "score": score_avg, "select": select_avg},
         "roofline": {

@@ -271,6 +271,17 @@ int qsa_block_pool(const uint16_t* raw_keys, const float* k_norm_w, float* block
                    float theta, float eps, hipStream_t stream);
 
 /*
+ * qsa_block_pool_f16 -- qsa_block_pool with fp16 block keys: each fp32 result rounded to
+ * nearest even, the values the matrix-core scorer multiplies (qsa_score_rows_f16 reads
+ * them as they are; qsa_score_rows with IDX_PREC_MFMA rounds fp32 keys to the same
+ * values).  block_keys [>= first_block+n_new, hd] fp16 (uint16 bit patterns), 16-byte
+ * aligned; everything else as qsa_block_pool.
+ */
+int qsa_block_pool_f16(const uint16_t* raw_keys, const float* k_norm_w, uint16_t* block_keys,
+                       uint32_t first_block, uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot,
+                       float theta, float eps, hipStream_t stream);
+
+/*
  * qsa_qprep_rows -- prefill query prep ([qsa.rs] qsa_qprep_rows, qsa_qprep).
  *
  * For row r and head h: x = qk[r, h*hd .. h*hd+hd-1];
@@ -285,6 +296,15 @@ int qsa_block_pool(const uint16_t* raw_keys, const float* k_norm_w, float* block
 int qsa_qprep_rows(const uint16_t* qk, const float* q_norm_w, float* q_out,
                    uint32_t rows, uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t hd,
                    uint32_t rot, float theta, float eps, hipStream_t stream);
+
+/*
+ * qsa_qprep_rows_f16 -- qsa_qprep_rows with fp16 output (each fp32 result rounded to
+ * nearest even; the query values the matrix-core scorer multiplies).  q_out
+ * [rows, n_heads, hd] fp16 (uint16 bit patterns), 16-byte aligned.
+ */
+int qsa_qprep_rows_f16(const uint16_t* qk, const float* q_norm_w, uint16_t* q_out,
+                       uint32_t rows, uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t hd,
+                       uint32_t rot, float theta, float eps, hipStream_t stream);
 
 /*
  * qsa_qprep -- one decode query ([qsa.rs] qsa_qprep): per head h,
@@ -332,6 +352,17 @@ int qsa_score(const float* q, const float* block_keys, float* scores, uint32_t n
 int qsa_score_rows(const float* q, const float* block_keys, float* scores,
                    uint32_t rows, uint32_t n_blocks_max, uint32_t first_pos, uint32_t score_stride,
                    uint32_t ratio, uint32_t n_heads, uint32_t hd, int precision, hipStream_t stream);
+
+/*
+ * qsa_score_rows_f16 -- qsa_score_rows on the fp16 matrix cores from fp16 q [rows, n_heads,
+ * hd] and block keys [n_blocks_max, hd] (uint16 bit patterns, 16-byte aligned), as
+ * written by qsa_qprep_rows_f16 and qsa_block_pool_f16: the same scores, bit for bit, as
+ * qsa_score_rows with IDX_PREC_MFMA on the fp32 tensors those calls round, with half the
+ * query and key bytes.  Supported: hd in {64, 128}, n_heads in {16, 32, 64}.
+ */
+int qsa_score_rows_f16(const uint16_t* q, const uint16_t* block_keys, float* scores,
+                       uint32_t rows, uint32_t n_blocks_max, uint32_t first_pos, uint32_t score_stride,
+                       uint32_t ratio, uint32_t n_heads, uint32_t hd, hipStream_t stream);
 
 /*
  * indexer_debug_dequant -- test hook for the NVFP4 decoders used by the scorers.

@@ -51,10 +51,13 @@ SIGNATURES = {
     "qsa_gather": (_I, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _P]),
     "qsa_prefill_attn": (_I, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _F, _P]),
     "qsa_block_pool": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _F, _F, _P]),
+    "qsa_block_pool_f16": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _F, _F, _P]),
     "qsa_qprep_rows": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _F, _F, _P]),
+    "qsa_qprep_rows_f16": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _F, _F, _P]),
     "qsa_qprep": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _F, _F, _P]),
     "qsa_score": (_I, [_P, _P, _P, _U32, _U32, _U32, _P]),
     "qsa_score_rows": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _I, _P]),
+    "qsa_score_rows_f16": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _P]),
     "indexer_debug_dequant": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
 }
 

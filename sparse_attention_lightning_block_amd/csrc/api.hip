@@ -377,9 +377,11 @@ int qsa_prefill_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t*
   return ok();
 }
 
-int qsa_block_pool(const uint16_t* raw_keys, const float* k_norm_w, float* block_keys, uint32_t first_block,
-                   uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot, float theta, float eps,
-                   hipStream_t stream) {
+extern "C++" {
+template <typename OutT>
+static int block_pool_impl(const uint16_t* raw_keys, const float* k_norm_w, OutT* block_keys, uint32_t first_block,
+                           uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot, float theta, float eps,
+                           hipStream_t stream) {
   if (!raw_keys || !k_norm_w || !block_keys) return fail(IDX_ERR_NULL, "raw_keys, k_norm_w and block_keys are required");
   if (hd != 64 && hd != 128 && hd != 256) return fail(IDX_ERR_UNSUPPORTED, "hd %u (supported: 64, 128, 256)", hd);
   if (rot > hd || (rot & 1)) return fail(IDX_ERR_SHAPE, "rot %u must be even and <= hd", rot);
@@ -388,15 +390,32 @@ int qsa_block_pool(const uint16_t* raw_keys, const float* k_norm_w, float* block
   if (!aligned(raw_keys, 16) || !aligned(block_keys, 16) || !aligned(k_norm_w, 4))
     return fail(IDX_ERR_SHAPE, "raw_keys and block_keys must be 16-byte aligned");
   if (n_new == 0) return ok();
-  hipError_t e = salb::launch_block_pool(raw_keys, k_norm_w, block_keys, first_block, n_new, ratio, hd, rot, theta,
-                                         eps, stream);
+  hipError_t e = salb::launch_block_pool<OutT>(raw_keys, k_norm_w, block_keys, first_block, n_new, ratio, hd, rot,
+                                               theta, eps, stream);
   if (e != hipSuccess) return hip_fail(e, "block pool launch");
   return ok();
 }
+}  // extern "C++"
 
-int qsa_qprep_rows(const uint16_t* qk, const float* q_norm_w, float* q_out, uint32_t rows, uint32_t first_pos,
-                   uint32_t qkw, uint32_t n_heads, uint32_t hd, uint32_t rot, float theta, float eps,
+int qsa_block_pool(const uint16_t* raw_keys, const float* k_norm_w, float* block_keys, uint32_t first_block,
+                   uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot, float theta, float eps,
                    hipStream_t stream) {
+  return block_pool_impl<float>(raw_keys, k_norm_w, block_keys, first_block, n_new, ratio, hd, rot, theta, eps,
+                                stream);
+}
+
+int qsa_block_pool_f16(const uint16_t* raw_keys, const float* k_norm_w, uint16_t* block_keys, uint32_t first_block,
+                       uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot, float theta, float eps,
+                       hipStream_t stream) {
+  return block_pool_impl<_Float16>(raw_keys, k_norm_w, reinterpret_cast<_Float16*>(block_keys), first_block, n_new,
+                                   ratio, hd, rot, theta, eps, stream);
+}
+
+extern "C++" {
+template <typename OutT>
+static int qprep_rows_impl(const uint16_t* qk, const float* q_norm_w, OutT* q_out, uint32_t rows, uint32_t first_pos,
+                           uint32_t qkw, uint32_t n_heads, uint32_t hd, uint32_t rot, float theta, float eps,
+                           hipStream_t stream) {
   if (!qk || !q_norm_w || !q_out) return fail(IDX_ERR_NULL, "qk, q_norm_w and q_out are required");
   if (hd != 64 && hd != 128 && hd != 256) return fail(IDX_ERR_UNSUPPORTED, "hd %u (supported: 64, 128, 256)", hd);
   if (rot > hd || (rot & 1)) return fail(IDX_ERR_SHAPE, "rot %u must be even and <= hd", rot);
@@ -407,10 +426,24 @@ int qsa_qprep_rows(const uint16_t* qk, const float* q_norm_w, float* q_out, uint
   if (qkw % 8 != 0 || !aligned(qk, 16) || !aligned(q_out, 16) || !aligned(q_norm_w, 4))
     return fail(IDX_ERR_SHAPE, "qk and q_out must be 16-byte aligned and qkw a multiple of 8");
   if (rows == 0) return ok();
-  hipError_t e = salb::launch_qprep_rows(qk, q_norm_w, q_out, rows, first_pos, qkw, n_heads, hd, rot, theta, eps,
-                                         stream);
+  hipError_t e = salb::launch_qprep_rows<OutT>(qk, q_norm_w, q_out, rows, first_pos, qkw, n_heads, hd, rot, theta,
+                                               eps, stream);
   if (e != hipSuccess) return hip_fail(e, "query prep launch");
   return ok();
+}
+}  // extern "C++"
+
+int qsa_qprep_rows(const uint16_t* qk, const float* q_norm_w, float* q_out, uint32_t rows, uint32_t first_pos,
+                   uint32_t qkw, uint32_t n_heads, uint32_t hd, uint32_t rot, float theta, float eps,
+                   hipStream_t stream) {
+  return qprep_rows_impl<float>(qk, q_norm_w, q_out, rows, first_pos, qkw, n_heads, hd, rot, theta, eps, stream);
+}
+
+int qsa_qprep_rows_f16(const uint16_t* qk, const float* q_norm_w, uint16_t* q_out, uint32_t rows, uint32_t first_pos,
+                       uint32_t qkw, uint32_t n_heads, uint32_t hd, uint32_t rot, float theta, float eps,
+                       hipStream_t stream) {
+  return qprep_rows_impl<_Float16>(qk, q_norm_w, reinterpret_cast<_Float16*>(q_out), rows, first_pos, qkw, n_heads,
+                                   hd, rot, theta, eps, stream);
 }
 
 int qsa_qprep(const uint16_t* q_in, const float* q_norm_w, float* q_out, uint32_t n_heads, uint32_t hd,
@@ -453,6 +486,26 @@ int qsa_score_rows(const float* q, const float* block_keys, float* scores, uint3
   if (rows == 0 || n_blocks_max == 0) return ok();
   hipError_t e = salb::launch_qsa_score(q, block_keys, scores, rows, n_blocks_max, first_pos, score_stride, ratio,
                                         n_heads, hd, precision, stream);
+  if (e != hipSuccess) return hip_fail(e, "QSA score launch");
+  return ok();
+}
+
+int qsa_score_rows_f16(const uint16_t* q, const uint16_t* block_keys, float* scores, uint32_t rows,
+                       uint32_t n_blocks_max, uint32_t first_pos, uint32_t score_stride, uint32_t ratio,
+                       uint32_t n_heads, uint32_t hd, hipStream_t stream) {
+  if (!q || !block_keys || !scores) return fail(IDX_ERR_NULL, "q, block_keys and scores are required");
+  if (hd != 64 && hd != 128) return fail(IDX_ERR_UNSUPPORTED, "hd %u (fp16 inputs: 64 or 128)", hd);
+  if (n_heads != 16 && n_heads != 32 && n_heads != 64)
+    return fail(IDX_ERR_UNSUPPORTED, "n_heads %u (fp16 inputs: 16, 32 or 64)", n_heads);
+  if (ratio < 1) return fail(IDX_ERR_SHAPE, "ratio must be >= 1");
+  if (score_stride < n_blocks_max) return fail(IDX_ERR_SHAPE, "score_stride < n_blocks_max");
+  if (n_blocks_max >= (uint32_t)kMaxCols) return fail(IDX_ERR_UNSUPPORTED, "n_blocks_max must be < 2^24");
+  if (!aligned(q, 16) || !aligned(block_keys, 16) || !aligned(scores, 4))
+    return fail(IDX_ERR_SHAPE, "q and block_keys must be 16-byte aligned");
+  if (rows == 0 || n_blocks_max == 0) return ok();
+  hipError_t e = salb::launch_qsa_score_f16(reinterpret_cast<const _Float16*>(q),
+                                            reinterpret_cast<const _Float16*>(block_keys), scores, rows, n_blocks_max,
+                                            first_pos, score_stride, ratio, n_heads, hd, stream);
   if (e != hipSuccess) return hip_fail(e, "QSA score launch");
   return ok();
 }

@@ -84,12 +84,18 @@ hipError_t launch_prefill_attn(const uint16_t* q, const uint16_t* k, const uint1
                                int block_size, int nq, int nkv, int hd, float inv_sqrt_d, hipStream_t st);
 
 // QSA (qsa.hip).
-hipError_t launch_block_pool(const uint16_t* raw, const float* kw, float* out, uint32_t first_block,
+// OutT float or _Float16 (fp16 storage, each fp32 result rounded to nearest even)
+template <typename OutT>
+hipError_t launch_block_pool(const uint16_t* raw, const float* kw, OutT* out, uint32_t first_block,
                              uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot, float theta,
                              float eps, hipStream_t st);
-hipError_t launch_qprep_rows(const uint16_t* qk, const float* qw, float* out, uint32_t rows,
+template <typename OutT>
+hipError_t launch_qprep_rows(const uint16_t* qk, const float* qw, OutT* out, uint32_t rows,
                              uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t hd, uint32_t rot,
                              float theta, float eps, hipStream_t st);
+hipError_t launch_qsa_score_f16(const _Float16* q, const _Float16* keys, float* scores, uint32_t rows, uint32_t nb,
+                                uint32_t first_pos, uint32_t stride, uint32_t ratio, uint32_t n_heads, uint32_t hd,
+                                hipStream_t st);
 bool qsa_score_uses_mfma(int precision, uint32_t n_heads, uint32_t hd);
 hipError_t launch_qsa_decode_score(const float* q, const float* keys, float* scores, uint32_t nb, uint32_t n_heads,
                                    uint32_t hd, hipStream_t st);

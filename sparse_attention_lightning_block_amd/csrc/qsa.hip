@@ -47,9 +47,9 @@ __device__ __forceinline__ void rope_cos_sin(double angle, double& c, double& s)
 // column groups, and the rotation pairs through LDS.  The rotation angle and its
 // sine and cosine are evaluated in fp64 (at long-prefill positions an fp32 angle is
 // off by ~0.03 rad), once per (block, pair).
-template <int HD>
+template <int HD, typename OutT>
 __global__ __launch_bounds__(256) void block_pool_kernel(const uint16_t* __restrict__ raw,
-                                                         const float* __restrict__ kw, float* __restrict__ out,
+                                                         const float* __restrict__ kw, OutT* __restrict__ out,
                                                          uint32_t first_block, uint32_t n_new, uint32_t ratio,
                                                          int rot, float theta, float eps) {
   constexpr int TPB = 32;           // threads per block
@@ -133,9 +133,16 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const uint16_t* __restr
         o[i] = xs[bi][d];
       }
     }
-    float* dst = out + (int64_t)b * HD + cg * 8;
-    *reinterpret_cast<float4v*>(dst) = float4v{o[0], o[1], o[2], o[3]};
-    *reinterpret_cast<float4v*>(dst + 4) = float4v{o[4], o[5], o[6], o[7]};
+    OutT* dst = out + (int64_t)b * HD + cg * 8;
+    if constexpr (sizeof(OutT) == 4) {
+      *reinterpret_cast<float4v*>(dst) = float4v{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<float4v*>(dst + 4) = float4v{o[4], o[5], o[6], o[7]};
+    } else {  // fp16 storage: each fp32 result rounded to nearest even
+      half8v h;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = (_Float16)o[i];
+      *reinterpret_cast<half8v*>(dst) = h;
+    }
   }
 }
 
@@ -149,10 +156,10 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const uint16_t* __restr
 // single row, so the heads are spread over as many waves as one workgroup holds.
 constexpr int kQprepThreads = 1024;
 
-template <int HD>
+template <int HD, typename OutT>
 __global__ __launch_bounds__(kQprepThreads) void qprep_rows_kernel(const uint16_t* __restrict__ qk,
                                                                    const float* __restrict__ qw,
-                                                                   float* __restrict__ out, uint32_t first_pos,
+                                                                   OutT* __restrict__ out, uint32_t first_pos,
                                                                    uint32_t qkw, uint32_t n_heads, int rot,
                                                                    float theta, float eps) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -193,7 +200,7 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_rows_kernel(const uint16_
     if (lane == 0) hinv[h] = 1.0f / sqrtf(ss / (float)HD + eps);
   }
   __syncthreads();
-  float* dst = out + (int64_t)r * n;
+  OutT* dst = out + (int64_t)r * n;
   for (int e = tid; e < n; e += kQprepThreads) {
     const int h = e / HD, d = e % HD;
     const float hv = hinv[h];
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_rows_kernel(const uint16_
     } else {
       o = norm(d);
     }
-    dst[e] = o;
+    dst[e] = (OutT)o;  // fp16 storage: rounded to nearest even
   }
 }
 
@@ -266,9 +273,9 @@ __global__ __launch_bounds__(256) void qsa_score_f32_kernel(const float* __restr
 // fp16 range; the accumulation is fp32.
 constexpr int kQsaThreads = 512;
 
-template <int HD, int NH>
-__global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const float* __restrict__ q,
-                                                                     const float* __restrict__ keys,
+template <int HD, int NH, typename InT>
+__global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const InT* __restrict__ q,
+                                                                     const InT* __restrict__ keys,
                                                                      float* __restrict__ scores, uint32_t rows,
                                                                      uint32_t nb, uint32_t first_pos,
                                                                      uint32_t stride, uint32_t ratio,
@@ -324,13 +331,17 @@ __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const float
     for (int kk = 0; kk < KW; ++kk) {
       half8v a;
       if (r < (int)rows) {
-        const float* src = q + ((int64_t)r * NH + h) * HD + 32 * kk + 8 * quarter;
-        const float4v x0 = *reinterpret_cast<const float4v*>(src);
-        const float4v x1 = *reinterpret_cast<const float4v*>(src + 4);
+        const InT* src = q + ((int64_t)r * NH + h) * HD + 32 * kk + 8 * quarter;
+        if constexpr (sizeof(InT) == 2) {
+          a = *reinterpret_cast<const half8v*>(src);
+        } else {
+          const float4v x0 = *reinterpret_cast<const float4v*>(src);
+          const float4v x1 = *reinterpret_cast<const float4v*>(src + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = (_Float16)x0[e];
-          a[4 + e] = (_Float16)x1[e];
+          for (int e = 0; e < 4; ++e) {
+            a[e] = (_Float16)x0[e];
+            a[4 + e] = (_Float16)x1[e];
+          }
         }
       } else {
 #pragma unroll
@@ -356,25 +367,33 @@ __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const float
   // LDS rows start on distinct bank groups: conflict-free tile writes
   static_assert(LPK == 8 && NT % 64 == 0, "loader map");
   const int lk = (tid & 7) | ((tid >> 6) << 3), lpart = (tid >> 3) & 7;
-  // keys past kend are clamped onto the last one (their scores are masked at the store)
-  const float* kbase = keys + lpart * FPL;
-  auto load_tile = [&](int64_t k0, float4v (&st)[FPL / 4]) {
+  // keys past kend are clamped onto the last one (their scores are masked at the store).
+  // A loader thread's slice is FPL elements: FPL / 4 float4 loads of fp32 keys
+  // (converted on the way into LDS), or FPL / 8 16-byte loads of fp16 keys (copied).
+  constexpr int SV = sizeof(InT) == 4 ? FPL / 4 : FPL / 8;  // 16-byte vectors per slice
+  typedef u32x4 Stage[SV];
+  const InT* kbase = keys + lpart * FPL;
+  auto load_tile = [&](int64_t k0, Stage& st) {
     const int64_t kk = min(k0 + lk, kend - 1);
-    const float* src = kbase + kk * HD;
+    const InT* src = kbase + kk * HD;
 #pragma unroll
-    for (int j = 0; j < FPL / 4; ++j) st[j] = *reinterpret_cast<const float4v*>(src + 4 * j);
+    for (int j = 0; j < SV; ++j) st[j] = *reinterpret_cast<const u32x4*>(src + (16 / sizeof(InT)) * j);
   };
-  auto store_tile = [&](int buf, const float4v (&st)[FPL / 4]) {
+  auto store_tile = [&](int buf, const Stage& st) {
     _Float16* dst = &kb[buf][lk * BLD + lpart * FPL];
 #pragma unroll
     for (int j = 0; j < FPL / 8; ++j) {
-      half8v h;
+      if constexpr (sizeof(InT) == 2) {
+        *reinterpret_cast<u32x4*>(dst + 8 * j) = st[j];
+      } else {
+        half8v h;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[e] = (_Float16)st[2 * j][e];
-        h[4 + e] = (_Float16)st[2 * j + 1][e];
+        for (int e = 0; e < 4; ++e) {
+          h[e] = (_Float16)__uint_as_float(st[2 * j][e]);
+          h[4 + e] = (_Float16)__uint_as_float(st[2 * j + 1][e]);
+        }
+        *reinterpret_cast<half8v*>(dst + 8 * j) = h;
       }
-      *reinterpret_cast<half8v*>(dst + 8 * j) = h;
     }
   };
   // multiply one LDS tile, reduce the heads, write the scores
@@ -420,7 +439,7 @@ __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const float
 
   // two register stages: tile j + 2 loads while tile j multiplies and tile j + 1
   // waits for its LDS buffer
-  float4v sa[FPL / 4], sb[FPL / 4];
+  Stage sa, sb;
   load_tile(c0, sa);
   load_tile(c0 + TILE, sb);
   store_tile(0, sa);
@@ -562,21 +581,22 @@ __global__ __launch_bounds__(256) void qsa_decode_score_mfma_kernel(const float*
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_block_pool(const uint16_t* raw, const float* kw, float* out, uint32_t first_block,
+template <typename OutT>
+hipError_t launch_block_pool(const uint16_t* raw, const float* kw, OutT* out, uint32_t first_block,
                              uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot, float theta,
                              float eps, hipStream_t st) {
   const dim3 grid((n_new + 7) / 8);
   switch (hd) {
     case 64:
-      hipLaunchKernelGGL(block_pool_kernel<64>, grid, dim3(256), 0, st, raw, kw, out, first_block, n_new, ratio,
+      hipLaunchKernelGGL((block_pool_kernel<64, OutT>), grid, dim3(256), 0, st, raw, kw, out, first_block, n_new, ratio,
                          (int)rot, theta, eps);
       break;
     case 128:
-      hipLaunchKernelGGL(block_pool_kernel<128>, grid, dim3(256), 0, st, raw, kw, out, first_block, n_new, ratio,
+      hipLaunchKernelGGL((block_pool_kernel<128, OutT>), grid, dim3(256), 0, st, raw, kw, out, first_block, n_new, ratio,
                          (int)rot, theta, eps);
       break;
     default:
-      hipLaunchKernelGGL(block_pool_kernel<256>, grid, dim3(256), 0, st, raw, kw, out, first_block, n_new, ratio,
+      hipLaunchKernelGGL((block_pool_kernel<256, OutT>), grid, dim3(256), 0, st, raw, kw, out, first_block, n_new, ratio,
                          (int)rot, theta, eps);
       break;
   }
@@ -587,33 +607,34 @@ size_t qprep_lds_bytes(uint32_t n_heads, uint32_t hd) {
   return (size_t)4 * n_heads * hd + (size_t)4 * ((n_heads + 3) & ~3u) + (size_t)8 * hd;
 }
 
-hipError_t launch_qprep_rows(const uint16_t* qk, const float* qw, float* out, uint32_t rows,
+template <typename OutT>
+hipError_t launch_qprep_rows(const uint16_t* qk, const float* qw, OutT* out, uint32_t rows,
                              uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t hd, uint32_t rot,
                              float theta, float eps, hipStream_t st) {
   const size_t lds = qprep_lds_bytes(n_heads, hd);
   hipError_t e;
   switch (hd) {
     case 64:
-      if ((e = ensure_lds(reinterpret_cast<const void*>(qprep_rows_kernel<64>), lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(qprep_rows_kernel<64>, dim3(rows), dim3(kQprepThreads), lds, st, qk, qw, out, first_pos,
+      if ((e = ensure_lds(reinterpret_cast<const void*>(qprep_rows_kernel<64, OutT>), lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL((qprep_rows_kernel<64, OutT>), dim3(rows), dim3(kQprepThreads), lds, st, qk, qw, out, first_pos,
                          qkw, n_heads, (int)rot, theta, eps);
       break;
     case 128:
-      if ((e = ensure_lds(reinterpret_cast<const void*>(qprep_rows_kernel<128>), lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(qprep_rows_kernel<128>, dim3(rows), dim3(kQprepThreads), lds, st, qk, qw, out, first_pos,
+      if ((e = ensure_lds(reinterpret_cast<const void*>(qprep_rows_kernel<128, OutT>), lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL((qprep_rows_kernel<128, OutT>), dim3(rows), dim3(kQprepThreads), lds, st, qk, qw, out, first_pos,
                          qkw, n_heads, (int)rot, theta, eps);
       break;
     default:
-      if ((e = ensure_lds(reinterpret_cast<const void*>(qprep_rows_kernel<256>), lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(qprep_rows_kernel<256>, dim3(rows), dim3(kQprepThreads), lds, st, qk, qw, out, first_pos,
+      if ((e = ensure_lds(reinterpret_cast<const void*>(qprep_rows_kernel<256, OutT>), lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL((qprep_rows_kernel<256, OutT>), dim3(rows), dim3(kQprepThreads), lds, st, qk, qw, out, first_pos,
                          qkw, n_heads, (int)rot, theta, eps);
       break;
   }
   return hipGetLastError();
 }
 
-template <int HD, int NH>
-static hipError_t launch_qsa_mfma(const float* q, const float* keys, float* scores, uint32_t rows, uint32_t nb,
+template <int HD, int NH, typename InT>
+static hipError_t launch_qsa_mfma(const InT* q, const InT* keys, float* scores, uint32_t rows, uint32_t nb,
                                   uint32_t first_pos, uint32_t stride, uint32_t ratio, hipStream_t st) {
   constexpr uint32_t kRowsPerGroup = (kQsaThreads / 64) * (64 / NH);
   const uint32_t n_groups = (rows + kRowsPerGroup - 1) / kRowsPerGroup;
@@ -621,7 +642,7 @@ static hipError_t launch_qsa_mfma(const float* q, const float* keys, float* scor
   uint32_t chunk = (nb + kXcds - 1) / kXcds;
   chunk = (chunk + 63) / 64 * 64;
   const dim3 grid(n_groups * kXcds);
-  hipLaunchKernelGGL((qsa_score_mfma_kernel<HD, NH>), grid, dim3(kQsaThreads), 0, st, q, keys, scores, rows, nb,
+  hipLaunchKernelGGL((qsa_score_mfma_kernel<HD, NH, InT>), grid, dim3(kQsaThreads), 0, st, q, keys, scores, rows, nb,
                      first_pos, stride, ratio, chunk, n_groups, 1.0f / sqrtf((float)HD));
   return hipGetLastError();
 }
@@ -687,6 +708,34 @@ hipError_t launch_qsa_decode_score(const float* q, const float* keys, float* sco
 
 bool qsa_score_uses_mfma(int precision, uint32_t n_heads, uint32_t hd) {
   return precision == 1 && (hd == 64 || hd == 128) && (n_heads == 16 || n_heads == 32 || n_heads == 64);
+}
+
+template hipError_t launch_block_pool<float>(const uint16_t*, const float*, float*, uint32_t, uint32_t, uint32_t,
+                                             uint32_t, uint32_t, float, float, hipStream_t);
+template hipError_t launch_block_pool<_Float16>(const uint16_t*, const float*, _Float16*, uint32_t, uint32_t,
+                                                uint32_t, uint32_t, uint32_t, float, float, hipStream_t);
+template hipError_t launch_qprep_rows<float>(const uint16_t*, const float*, float*, uint32_t, uint32_t, uint32_t,
+                                             uint32_t, uint32_t, uint32_t, float, float, hipStream_t);
+template hipError_t launch_qprep_rows<_Float16>(const uint16_t*, const float*, _Float16*, uint32_t, uint32_t,
+                                                uint32_t, uint32_t, uint32_t, uint32_t, float, float, hipStream_t);
+
+// fp16 q and block keys (the storage of qsa_qprep_rows_f16 / qsa_block_pool_f16): the
+// matrix-core scorer only, which rounds fp32 inputs to exactly these values itself.
+hipError_t launch_qsa_score_f16(const _Float16* q, const _Float16* keys, float* scores, uint32_t rows, uint32_t nb,
+                                uint32_t first_pos, uint32_t stride, uint32_t ratio, uint32_t n_heads, uint32_t hd,
+                                hipStream_t st) {
+  if (hd == 64) {
+    switch (n_heads) {
+      case 16: return launch_qsa_mfma<64, 16>(q, keys, scores, rows, nb, first_pos, stride, ratio, st);
+      case 32: return launch_qsa_mfma<64, 32>(q, keys, scores, rows, nb, first_pos, stride, ratio, st);
+      default: return launch_qsa_mfma<64, 64>(q, keys, scores, rows, nb, first_pos, stride, ratio, st);
+    }
+  }
+  switch (n_heads) {
+    case 16: return launch_qsa_mfma<128, 16>(q, keys, scores, rows, nb, first_pos, stride, ratio, st);
+    case 32: return launch_qsa_mfma<128, 32>(q, keys, scores, rows, nb, first_pos, stride, ratio, st);
+    default: return launch_qsa_mfma<128, 64>(q, keys, scores, rows, nb, first_pos, stride, ratio, st);
+  }
 }
 
 hipError_t launch_qsa_score(const float* q, const float* keys, float* scores, uint32_t rows, uint32_t nb,

@@ -228,29 +228,34 @@ def qsa_prefill_attn(q, k_cache, v_cache, block_table, lists, *, first_pos: int,
 
 def qsa_block_pool(raw_keys, k_norm_w, block_keys, *, first_block: int, n_new: int, ratio: int, rot: int,
                    theta: float, eps: float) -> torch.Tensor:
-    """Writes block_keys[first_block : first_block + n_new] (fp32) from bf16 raw keys."""
+    """Writes block_keys[first_block : first_block + n_new] from bf16 raw keys: fp32, or fp16
+    (each fp32 result rounded to nearest even) when block_keys is a float16 tensor."""
     _dev(raw_keys, "raw_keys", torch.bfloat16, 2)
     _dev(k_norm_w, "k_norm_w", torch.float32, 1)
-    _dev(block_keys, "block_keys", torch.float32, 2)
+    f16 = block_keys.dtype == torch.float16
+    _dev(block_keys, "block_keys", torch.float16 if f16 else torch.float32, 2)
     hd = raw_keys.shape[1]
     if (first_block + n_new) * ratio > raw_keys.shape[0] or first_block + n_new > block_keys.shape[0]:
         raise ValueError("block range exceeds the raw keys or the block-key table")
-    check(_lib.load().qsa_block_pool(_ptr(raw_keys), _ptr(k_norm_w), _ptr(block_keys), first_block, n_new, ratio, hd,
-                                     rot, theta, eps, _stream()))
+    fn = _lib.load().qsa_block_pool_f16 if f16 else _lib.load().qsa_block_pool
+    check(fn(_ptr(raw_keys), _ptr(k_norm_w), _ptr(block_keys), first_block, n_new, ratio, hd, rot, theta, eps,
+             _stream()))
     return block_keys
 
 
 def qsa_qprep_rows(qk, q_norm_w, *, n_heads: int, hd: int, first_pos: int, rot: int, theta: float, eps: float,
-                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Prepared queries [rows, n_heads, hd] fp32 from bf16 projection rows qk [rows, qkw]."""
+                   out: Optional[torch.Tensor] = None, dtype=torch.float32) -> torch.Tensor:
+    """Prepared queries [rows, n_heads, hd] from bf16 projection rows qk [rows, qkw]: fp32, or
+    fp16 (rounded to nearest even) for dtype (or out) float16."""
     _dev(qk, "qk", torch.bfloat16, 2)
     _dev(q_norm_w, "q_norm_w", torch.float32, 1)
     rows, qkw = qk.shape
     if out is None:
-        out = torch.empty((rows, n_heads, hd), dtype=torch.float32, device=qk.device)
-    _dev(out, "out", torch.float32, 3)
-    check(_lib.load().qsa_qprep_rows(_ptr(qk), _ptr(q_norm_w), _ptr(out), rows, first_pos, qkw, n_heads, hd, rot,
-                                     theta, eps, _stream()))
+        out = torch.empty((rows, n_heads, hd), dtype=dtype, device=qk.device)
+    f16 = out.dtype == torch.float16
+    _dev(out, "out", torch.float16 if f16 else torch.float32, 3)
+    fn = _lib.load().qsa_qprep_rows_f16 if f16 else _lib.load().qsa_qprep_rows
+    check(fn(_ptr(qk), _ptr(q_norm_w), _ptr(out), rows, first_pos, qkw, n_heads, hd, rot, theta, eps, _stream()))
     return out
 
 
@@ -286,16 +291,24 @@ def qsa_score(q, block_keys, *, n_blocks: Optional[int] = None, out: Optional[to
 
 def qsa_score_rows(q, block_keys, *, first_pos: int, ratio: int, n_blocks_max: Optional[int] = None,
                    precision: str = "mfma", out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """scores [rows, n_blocks_max] fp32 with -inf past each row's complete blocks."""
-    _dev(q, "q", torch.float32, 3)
-    _dev(block_keys, "block_keys", torch.float32, 2)
+    """scores [rows, n_blocks_max] fp32 with -inf past each row's complete blocks.  fp16 q and
+    block keys (the storage of the *_f16 pool and prep) take the matrix-core scorer."""
+    f16 = q.dtype == torch.float16
+    _dev(q, "q", torch.float16 if f16 else torch.float32, 3)
+    _dev(block_keys, "block_keys", torch.float16 if f16 else torch.float32, 2)
     rows, n_heads, hd = q.shape
     nb = block_keys.shape[0] if n_blocks_max is None else n_blocks_max
     if out is None:
         out = torch.empty((rows, nb), dtype=torch.float32, device=q.device)
     _dev(out, "out", torch.float32, 2)
-    check(_lib.load().qsa_score_rows(_ptr(q), _ptr(block_keys), _ptr(out), rows, nb, first_pos, _row_stride(out), ratio,
-                                     n_heads, hd, PRECISION[precision], _stream()))
+    if f16:
+        if precision != "mfma":
+            raise ValueError("fp16 q and block keys are scored on the matrix cores (precision='mfma')")
+        check(_lib.load().qsa_score_rows_f16(_ptr(q), _ptr(block_keys), _ptr(out), rows, nb, first_pos,
+                                             _row_stride(out), ratio, n_heads, hd, _stream()))
+    else:
+        check(_lib.load().qsa_score_rows(_ptr(q), _ptr(block_keys), _ptr(out), rows, nb, first_pos, _row_stride(out),
+                                         ratio, n_heads, hd, PRECISION[precision], _stream()))
     return out
 
 

@@ -122,3 +122,19 @@ def test_qsa_decode_argument_checks_without_gpu():
     assert lib.qsa_score(16, 32, 48, 10, 65, 128, None) == _lib.IDX_ERR_UNSUPPORTED             # 65 heads
     assert lib.qsa_score(16, 32, 48, 0, 32, 128, None) == _lib.IDX_OK                           # no blocks
     assert lib.qsa_score(16, 40, 48, 10, 32, 128, None) == _lib.IDX_ERR_SHAPE                   # misaligned keys
+
+
+def test_qsa_fp16_storage_argument_checks_without_gpu():
+    lib = _lib.load()
+    assert lib.qsa_block_pool_f16(None, 16, 32, 0, 1, 16, 128, 64, 1e4, 1e-6, None) == _lib.IDX_ERR_NULL
+    assert lib.qsa_block_pool_f16(16, 16, 32, 0, 1, 16, 100, 64, 1e4, 1e-6, None) == _lib.IDX_ERR_UNSUPPORTED
+    assert lib.qsa_block_pool_f16(16, 16, 40, 0, 1, 16, 128, 64, 1e4, 1e-6, None) == _lib.IDX_ERR_SHAPE
+    assert lib.qsa_block_pool_f16(16, 16, 32, 0, 0, 16, 128, 64, 1e4, 1e-6, None) == _lib.IDX_OK
+    assert lib.qsa_qprep_rows_f16(16, 16, 32, 4, 0, 100, 1, 128, 64, 1e4, 1e-6, None) == _lib.IDX_ERR_SHAPE
+    assert lib.qsa_qprep_rows_f16(16, 16, 32, 0, 0, 128, 1, 128, 64, 1e4, 1e-6, None) == _lib.IDX_OK
+    # fp16 inputs take the matrix-core scorer only: hd 64/128, 16/32/64 heads
+    assert lib.qsa_score_rows_f16(16, 32, 48, 4, 64, 0, 64, 16, 32, 256, None) == _lib.IDX_ERR_UNSUPPORTED
+    assert lib.qsa_score_rows_f16(16, 32, 48, 4, 64, 0, 64, 16, 8, 128, None) == _lib.IDX_ERR_UNSUPPORTED
+    assert lib.qsa_score_rows_f16(16, 32, 48, 4, 64, 0, 32, 16, 32, 128, None) == _lib.IDX_ERR_SHAPE
+    assert lib.qsa_score_rows_f16(None, 32, 48, 4, 64, 0, 64, 16, 32, 128, None) == _lib.IDX_ERR_NULL
+    assert lib.qsa_score_rows_f16(16, 32, 48, 0, 64, 0, 64, 16, 32, 128, None) == _lib.IDX_OK

@@ -232,3 +232,41 @@ def test_decode_score_shapes(n_heads, hd, nb):
     A = np.abs(q64).sum(axis=0) @ np.abs(k64[:nb]).T / np.sqrt(hd)
     err = np.abs(got[:nb].astype(np.float64) - ref)
     assert np.all(err <= S_REL * np.abs(ref) + S_ABS_A * A), f"max err {err.max()}"
+
+
+@pytest.mark.parametrize("reduced,n_heads,hd", [(1, 32, 128), (1, 16, 64), (1, 64, 128), (0, 32, 128)])
+def test_fp16_storage_is_the_mfma_path_bit_for_bit(reduced, n_heads, hd):
+    """qsa_block_pool_f16 and qsa_qprep_rows_f16 store exactly the fp16 roundings of the
+    fp32 results (torch's round-to-nearest-even .half()), and qsa_score_rows_f16 on them
+    returns the fp32-input matrix-core scores bit for bit."""
+    w = make(5, reduced=reduced)
+    rng = np.random.default_rng([5, 16, n_heads, hd])
+    if (n_heads, hd) != (w.n_heads, w.hd):      # other shapes: seeded bf16 projections and raw keys
+        raw_np = rng.standard_normal((w.n_blocks * w.ratio, hd)).astype(np.float32)
+        qk_np = rng.standard_normal((w.rows, n_heads * hd)).astype(np.float32)
+        raw = torch.from_numpy(raw_np).to(torch.bfloat16).cuda()
+        qk = torch.from_numpy(qk_np).to(torch.bfloat16).cuda()
+        kw = torch.from_numpy(rng.normal(0, 0.1, hd).astype(np.float32)).cuda()
+        qw = torch.from_numpy(rng.normal(0, 0.1, hd).astype(np.float32)).cuda()
+        rot = min(w.rot, hd)
+    else:
+        raw = _bf16(w.raw_keys).cuda()
+        qk = _bf16(w.qk).cuda()
+        kw = torch.from_numpy(w.k_norm_w).cuda()
+        qw = torch.from_numpy(w.q_norm_w).cuda()
+        rot = w.rot
+    k32 = torch.empty((w.n_blocks, hd), dtype=torch.float32, device="cuda")
+    k16 = torch.empty((w.n_blocks, hd), dtype=torch.float16, device="cuda")
+    for keys in (k32, k16):
+        salb.qsa_block_pool(raw, kw, keys, first_block=0, n_new=w.n_blocks, ratio=w.ratio, rot=rot, theta=w.theta,
+                            eps=w.eps)
+    kwargs = dict(n_heads=n_heads, hd=hd, first_pos=w.first_pos, rot=rot, theta=w.theta, eps=w.eps)
+    q32 = salb.qsa_qprep_rows(qk, qw, **kwargs)
+    q16 = salb.qsa_qprep_rows(qk, qw, dtype=torch.float16, **kwargs)
+    torch.cuda.synchronize()
+    assert torch.equal(k16.view(torch.int16), k32.half().view(torch.int16))
+    assert torch.equal(q16.view(torch.int16), q32.half().view(torch.int16))
+    s32 = salb.qsa_score_rows(q32, k32, first_pos=w.first_pos, ratio=w.ratio, precision="mfma")
+    s16 = salb.qsa_score_rows(q16, k16, first_pos=w.first_pos, ratio=w.ratio, precision="mfma")
+    torch.cuda.synchronize()
+    assert torch.equal(s16.view(torch.int32), s32.view(torch.int32))
