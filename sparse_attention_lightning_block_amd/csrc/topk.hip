@@ -55,8 +55,7 @@ constexpr int kRowMax = 32 * kRowThreads;  // 8192: one-workgroup rows
 constexpr int kRowThreadsWide = 1024;
 constexpr int kRowMaxWide = 32 * kRowThreadsWide;  // 32768
 constexpr int kWideRowsMin = 256;
-constexpr int kRowThreadsLds = 512;    // persistent rows kept in LDS: 64 entries per thread
-constexpr int kPersistentWgs = 256;    // one workgroup per CU (the row fills its LDS)
+constexpr int kRowThreadsReg = 512;    // many rows of up to 32768 entries: 64 per thread in registers
 constexpr int kBucketMax = 48;           // crowded bucket: sorting network instead
 constexpr int kHistCopies = kXcds;       // one global histogram per XCD
 constexpr int kMaxWaves = 1024 / kWave;  // widest workgroup of the select kernels
@@ -430,10 +429,6 @@ struct FinishLds {
   uint32_t* hist;
 };
 
-// LDS of a row's order keys held by a one-workgroup select (16-byte multiple).
-__host__ __device__ __forceinline__ size_t row_keys_lds_bytes(int n_cols) {
-  return ((size_t)n_cols * 4 + 15) & ~(size_t)15;
-}
 
 __device__ __forceinline__ FinishLds carve(unsigned char* smem, int top_k) {
   const int p = pow2_at_least(top_k);
@@ -547,150 +542,139 @@ __global__ __launch_bounds__(NT, (NT == kRowThreads && PER <= 16) ? 5 : 1) void 
   finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, mx, mn, sh, kbase);
 }
 
-// Rows too long for registers (up to 32768 entries), one at a time per workgroup
-// (a persistent grid, one workgroup per CU, each taking every grid-th row, longest
-// first).  While a row is selected, the loads of the workgroup's next row are in
-// flight into registers (64 entries per thread).  The row's order keys go to LDS once,
-// with their range.  One histogram pass over a 12-bit
-// digit of the key relative to the row's smallest (the digit spans the row's actual
-// range) finds the bin of the K-th entry; the entries from that bin up -- K plus the
-// rest of the bin -- are compacted into an LDS candidate list, where the radix select
-// finishes and the winners are gathered.  A bin crowded past the list's capacity falls
-// back to radix passes over the whole row.  Thread t owns the runs of four entries
-// 4 (t + m NT) .. + 3 of the LDS row, read as 16-byte words, eight in flight per pass.
+// Rows of up to 32768 entries when there are many (one 512-thread workgroup per row,
+// longest rows first, several workgroups per CU so that one's loads overlap another's
+// passes).  The row stays in registers as order keys (entry i NT + t in register i of
+// thread t, 64 per thread, coalesced loads).  Its range comes from one wave and block
+// reduction; one histogram pass over a 12-bit digit of the key relative to the row's
+// smallest (the digit spans the row's actual range) finds the bin of the K-th entry;
+// the entries from that bin up -- K plus the rest of the bin -- are compacted into an
+// LDS candidate list (one LDS atomic per wave and register, the lanes placed by their
+// rank in the wave's ballot), where the radix select finishes and the winners are
+// gathered.  A bin crowded past the list's capacity falls back to radix passes over
+// the row read again from memory.
 template <int NT>
-__global__ __launch_bounds__(NT) void select_rows_lds_kernel(SelArgs a, int rows) {
+__global__ __launch_bounds__(NT) void select_rows_reg_kernel(SelArgs a, int rows) {
   constexpr int PF = kRowMaxWide / NT;  // a row's entries per thread
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ SelShared sh;
   __shared__ uint32_t s_kmx[NT / kWave], s_kmn[NT / kWave];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const size_t key_bytes = row_keys_lds_bytes(kRowMaxWide);
-  uint32_t* lkey = reinterpret_cast<uint32_t*>(smem);
-  uint64_t* cand = reinterpret_cast<uint64_t*>(smem + key_bytes);
-  FinishLds f = carve(smem + key_bytes + (size_t)a.cand_cap * 8, a.top_k);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(smem);
+  FinishLds f = carve(smem + (size_t)a.cand_cap * 8, a.top_k);
+  const int row = rows - 1 - (int)blockIdx.x;  // causal rows grow with the index: longest first
+  const int n = row_valid(a, row);
+  const int K = n < a.top_k ? n : a.top_k;
 
-  float x[PF];  // the next row, entry i * NT + tid in x[i]
-  auto fetch = [&](int r) {
-    const int nr = row_valid(a, r);
-    const float* src = a.scores + (int64_t)r * a.score_stride;
-    const int last = nr > 0 ? nr - 1 : 0;  // past the valid entries: re-read valid memory
+  const float* src = a.scores + (int64_t)row * a.score_stride;
+  uint32_t key[PF];
+  {
+    const int last = n > 0 ? n - 1 : 0;  // past the valid entries: re-read valid memory
 #pragma unroll
-    for (int i = 0; i < PF; ++i) x[i] = src[min(i * NT + tid, last)];
+    for (int i = 0; i < PF; ++i) key[i] = ord_key(src[min(i * NT + tid, last)]);
+  }
+  uint32_t kmx = 0u, kmn = ~0u;
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const bool v = i * NT + tid < n;
+    kmx = v && key[i] > kmx ? key[i] : kmx;
+    kmn = v && key[i] < kmn ? key[i] : kmn;
+  }
+  kmx = wave_max(kmx);
+  kmn = ~wave_max(~kmn);
+  if (lane == 0) {
+    s_kmx[wave] = kmx;
+    s_kmn[wave] = kmn;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NT / kWave; ++w) {
+    kmx = s_kmx[w] > kmx ? s_kmx[w] : kmx;
+    kmn = s_kmn[w] < kmn ? s_kmn[w] : kmn;
+  }
+  const uint32_t kbase = kmn;
+  // every valid entry of the row as its composite, read again from memory: only the
+  // rare paths use it (a crowded bin past the candidate list, rows no longer than
+  // top_k), so the registers of the row are free after the compaction
+  auto each_row = [&](auto&& fn) {
+    for (int e = tid; e < n; e += NT) fn(composite(ord_key(src[e]) - kbase, (uint32_t)e));
   };
-  if ((int)blockIdx.x >= rows) return;
-  fetch(rows - 1 - (int)blockIdx.x);
-  for (int idx = blockIdx.x; idx < rows; idx += gridDim.x) {
-    const int row = rows - 1 - idx;  // causal rows grow with the index: longest first
-    const int n = row_valid(a, row);
-    const int K = n < a.top_k ? n : a.top_k;
-    __syncthreads();  // the previous row is done with the LDS
-
-    // the row's keys into LDS (slots past n hold values never read) and their range
-    uint32_t kmx = 0u, kmn = ~0u;
+  int C = -1;  // candidates in the list (-1: the whole row is the candidate set)
+  auto each_cand = [&](auto&& fn) {
+    for (int i = tid; i < C; i += NT) fn(cand[i]);
+  };
+  uint64_t thr = 0ull;
+  if (K < n) {
+    const uint32_t span = kmx - kbase;
+    const int bits = span ? 32 - __clz(span) : 1;
+    const int shift = bits > kDigit ? bits - kDigit : 0;
+    clear_bins<NT>(f.hist);
+    if (tid == 0) sh.fill = 0u;
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      const uint32_t k = ord_key(x[i]);
-      lkey[i * NT + tid] = k;
-      const bool v = i * NT + tid < n;
-      kmx = v && k > kmx ? k : kmx;
-      kmn = v && k < kmn ? k : kmn;
-    }
-    if (idx + (int)gridDim.x < rows) fetch(rows - 1 - (idx + (int)gridDim.x));
-    kmx = wave_max(kmx);
-    kmn = ~wave_max(~kmn);
-    if (lane == 0) {
-      s_kmx[wave] = kmx;
-      s_kmn[wave] = kmn;
+      if (i * NT >= n) break;
+      if (i * NT + tid < n) atomicAdd(&f.hist[(key[i] - kbase) >> shift], 1u);
     }
     __syncthreads();
+    uint32_t h[kBins / NT];
+    load_bins<NT>(f.hist, h);
+    find_digit<NT>(h, (uint32_t)K, sh);
+    const uint32_t b1 = sh.digit, gt = sh.gt, cnt = sh.cnt;
+    const uint64_t prefix = (uint64_t)b1 << (32 + shift);
+    if (gt + cnt <= (uint32_t)a.cand_cap) {
+      const uint32_t kthr = kbase + (b1 << shift);  // smallest key of bin b1
 #pragma unroll
-    for (int w = 0; w < NT / kWave; ++w) {
-      kmx = s_kmx[w] > kmx ? s_kmx[w] : kmx;
-      kmn = s_kmn[w] < kmn ? s_kmn[w] : kmn;
-    }
-    auto each_key = [&](auto&& fn) {
-      const uint4* lk4 = reinterpret_cast<const uint4*>(lkey);
-      for (int m0 = 0; m0 * 4 * NT < n; m0 += 8) {
-        uint4 v[8];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const int w = (m0 + m) * NT + tid;
-          v[m] = 4 * w < n ? lk4[w] : uint4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const int e = 4 * ((m0 + m) * NT + tid);
-          if (e < n) fn(v[m].x, e);
-          if (e + 1 < n) fn(v[m].y, e + 1);
-          if (e + 2 < n) fn(v[m].z, e + 2);
-          if (e + 3 < n) fn(v[m].w, e + 3);
+      for (int i = 0; i < PF; ++i) {
+        if (i * NT >= n) break;
+        const int e = i * NT + tid;
+        const bool pick = e < n && key[i] >= kthr;
+        const uint64_t m = __ballot(pick);
+        if (m != 0ull) {
+          const int leader = __ffsll((unsigned long long)m) - 1;
+          uint32_t base = 0u;
+          if (lane == leader) base = atomicAdd(&sh.fill, (uint32_t)__popcll(m));
+          base = __builtin_amdgcn_readlane(base, leader);
+          const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          if (pick) cand[base + below] = composite(key[i] - kbase, (uint32_t)e);
         }
       }
-    };
-    const uint32_t kbase = kmn;
-    auto each_row = [&](auto&& fn) { each_key([&](uint32_t k, int e) { fn(composite(k - kbase, (uint32_t)e)); }); };
-    int C = -1;  // candidates in the list (-1: the whole row is the candidate set)
-    auto each_cand = [&](auto&& fn) {
-      for (int i = tid; i < C; i += NT) fn(cand[i]);
-    };
-    uint64_t thr = 0ull;
-    if (K < n) {
-      const uint32_t span = kmx - kbase;
-      const int bits = span ? 32 - __clz(span) : 1;
-      const int shift = bits > kDigit ? bits - kDigit : 0;
-      clear_bins<NT>(f.hist);
-      if (tid == 0) sh.fill = 0u;
       __syncthreads();
-      each_key([&](uint32_t k, int) { atomicAdd(&f.hist[(k - kbase) >> shift], 1u); });
-      __syncthreads();
-      uint32_t h[kBins / NT];
-      load_bins<NT>(f.hist, h);
-      find_digit<NT>(h, (uint32_t)K, sh);
-      const uint32_t b1 = sh.digit, gt = sh.gt, cnt = sh.cnt;
-      const uint64_t prefix = (uint64_t)b1 << (32 + shift);
-      if (gt + cnt <= (uint32_t)a.cand_cap) {
-        const uint32_t kthr = kbase + (b1 << shift);  // smallest key of bin b1
-        each_key([&](uint32_t k, int e) {
-          if (k >= kthr) cand[atomicAdd(&sh.fill, 1u)] = composite(k - kbase, (uint32_t)e);
-        });
-        __syncthreads();
-        C = (int)(gt + cnt);
-        if (gt + cnt == (uint32_t)K)
-          thr = prefix;  // the bin is taken whole
-        else
-          thr = radix_select<NT>(each_cand, prefix, (uint64_t)(kBins - 1) << (32 + shift), (uint32_t)K - gt,
-                                 31 + shift, f.hist, sh);
-      } else {
-        thr = radix_select<NT>(each_row, prefix, (uint64_t)(kBins - 1) << (32 + shift), (uint32_t)K - gt, 31 + shift,
-                               f.hist, sh);
-      }
-    }
-    // gather the winners
-    auto each = [&](auto&& fn) {
-      if (C >= 0)
-        each_cand(fn);
+      C = (int)(gt + cnt);
+      if (gt + cnt == (uint32_t)K)
+        thr = prefix;  // the bin is taken whole
       else
-        each_row(fn);
-    };
-    uint32_t mine = 0;
-    uint64_t mx = 0ull, mn = ~0ull;
-    each([&](uint64_t c) {
-      if (c >= thr) {
-        ++mine;
-        mx = c > mx ? c : mx;
-        mn = c < mn ? c : mn;
-      }
-    });
-    uint32_t off = block_suffix_minmax<NT>(mine, mx, mn, sh);
-    each([&](uint64_t c) {
-      if (c >= thr && off < (uint32_t)K) f.sortbuf[off++] = c;  // exactly K are selected
-    });
-    __syncthreads();
-    int32_t* oi = a.out_idx + (int64_t)row * a.top_k;
-    float* os = a.out_scores ? a.out_scores + (int64_t)row * a.top_k : nullptr;
-    finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, mx, mn, sh, kbase);
+        thr = radix_select<NT>(each_cand, prefix, (uint64_t)(kBins - 1) << (32 + shift), (uint32_t)K - gt,
+                               31 + shift, f.hist, sh);
+    } else {
+      thr = radix_select<NT>(each_row, prefix, (uint64_t)(kBins - 1) << (32 + shift), (uint32_t)K - gt, 31 + shift,
+                             f.hist, sh);
+    }
   }
+  // gather the winners
+  auto each = [&](auto&& fn) {
+    if (C >= 0)
+      each_cand(fn);
+    else
+      each_row(fn);
+  };
+  uint32_t mine = 0;
+  uint64_t mx = 0ull, mn = ~0ull;
+  each([&](uint64_t c) {
+    if (c >= thr) {
+      ++mine;
+      mx = c > mx ? c : mx;
+      mn = c < mn ? c : mn;
+    }
+  });
+  uint32_t off = block_suffix_minmax<NT>(mine, mx, mn, sh);
+  each([&](uint64_t c) {
+    if (c >= thr && off < (uint32_t)K) f.sortbuf[off++] = c;  // exactly K are selected
+  });
+  __syncthreads();
+  int32_t* oi = a.out_idx + (int64_t)row * a.top_k;
+  float* os = a.out_scores ? a.out_scores + (int64_t)row * a.top_k : nullptr;
+  finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, mx, mn, sh, kbase);
 }
 
 // ------------------------------------------------------------------ long rows
@@ -964,6 +948,8 @@ static WsLayout ws_layout(int rows, int chunks, int chunk) {
 
 constexpr size_t kLdsMax = 160 * 1024;
 constexpr size_t kStaticLdsReserve = 1024;  // static LDS of the one-workgroup row kernels
+// dynamic LDS of a register-row workgroup: two per CU
+constexpr size_t kRegRowLds = kLdsMax / 2 - kStaticLdsReserve;
 
 bool plan_select(int rows, int n_cols, int top_k, SelectPlan* p) {
   if (top_k < 1 || top_k > kMaxTopK) return false;
@@ -985,14 +971,15 @@ bool plan_select(int rows, int n_cols, int top_k, SelectPlan* p) {
     p->chunks = 1;
     p->bytes = 0;
   } else if (rows >= kWideRowsMin && n_cols <= kRowMaxWide &&
-             p->lds + row_keys_lds_bytes(kRowMaxWide) + kStaticLdsReserve <= kLdsMax) {
-    p->two_pass = 0;  // persistent workgroups, the row's keys in LDS, then a candidate list
-    p->row_nt = kRowThreadsLds;
+             p->lds + (size_t)16 * top_k <= kRegRowLds) {
+    // one workgroup per row, the row in registers; the LDS candidate list takes what
+    // two workgroups per CU leave (at least twice top_k)
+    p->two_pass = 0;
+    p->row_nt = kRowThreadsReg;
     p->per = 0;
-    const size_t fixed = p->lds + row_keys_lds_bytes(kRowMaxWide);
-    const size_t cap = (kLdsMax - kStaticLdsReserve - fixed) / 8;
+    const size_t cap = (kRegRowLds - p->lds) / 8;
     p->cand_cap = (int)(cap < (size_t)kRowMaxWide ? cap : (size_t)kRowMaxWide) & ~1;  // keeps 16-byte alignment
-    p->lds = fixed + (size_t)p->cand_cap * 8;
+    p->lds += (size_t)p->cand_cap * 8;
     p->chunks = 1;
     p->bytes = 0;
   } else {
@@ -1031,11 +1018,10 @@ static hipError_t launch_rows(const SelArgs& a, const SelectPlan& p, hipStream_t
 }
 
 template <int NT>
-static hipError_t launch_rows_lds(const SelArgs& a, const SelectPlan& p, hipStream_t st) {
-  hipError_t e = set_lds(select_rows_lds_kernel<NT>, p.lds);
+static hipError_t launch_rows_reg(const SelArgs& a, const SelectPlan& p, hipStream_t st) {
+  hipError_t e = set_lds(select_rows_reg_kernel<NT>, p.lds);
   if (e != hipSuccess) return e;
-  const int grid = p.rows < kPersistentWgs ? p.rows : kPersistentWgs;
-  hipLaunchKernelGGL((select_rows_lds_kernel<NT>), dim3(grid), dim3(NT), p.lds, st, a, p.rows);
+  hipLaunchKernelGGL((select_rows_reg_kernel<NT>), dim3(p.rows), dim3(NT), p.lds, st, a, p.rows);
   return hipGetLastError();
 }
 
@@ -1088,7 +1074,7 @@ hipError_t launch_select(const SelectPlan& p, const float* scores, int64_t score
   a.out_scores = out_scores;
   a.cand_cap = p.cand_cap;
   if (!p.two_pass) {
-    if (p.row_nt == kRowThreadsLds) return launch_rows_lds<kRowThreadsLds>(a, p, st);
+    if (p.row_nt == kRowThreadsReg) return launch_rows_reg<kRowThreadsReg>(a, p, st);
     if (p.row_nt == kRowThreadsWide) return launch_rows<kRowThreadsWide, 16>(a, p, st);
     switch (p.per) {
       case 4: return launch_rows<kRowThreads, 4>(a, p, st);

@@ -183,9 +183,11 @@ def test_topk_select_exact(n_cols, k):
 
 @pytest.mark.parametrize("n_cols,k", [(12000, 256), (30000, 256), (32768, 2048), (20000, 1)])
 def test_topk_select_many_long_rows(n_cols, k):
-    """Many rows (one workgroup per row of 1024 threads: entries in registers up to 16384
-    columns, in LDS up to 32768): exact against the oracle on sampled rows, with ties,
-    empty rows, rows shorter than k and full rows; set rules on every row."""
+    """Many rows (one workgroup per row: 1024 threads with 16 entries each in registers up
+    to 16384 columns, 512 threads with 64 each up to 32768; a row of one repeated value
+    overflows the candidate list and takes the radix passes over the row): exact against
+    the oracle on sampled rows, with ties, empty rows, rows shorter than k and full rows;
+    set rules on every row."""
     rng = np.random.default_rng(n_cols + 7 * k)
     rows = 300
     s = rng.standard_normal((rows, n_cols)).astype(np.float32)
