@@ -17,10 +17,10 @@
 //   * longer rows run as a pipeline of three launches (kernel boundaries order
 //     them; no grid-wide fences, which write back the whole L2 on this chip):
 //     every workgroup of a (chunk, row) grid adds its chunk's LDS histogram of the
-//     top 12 order-key bits (the bins that can hold the row's K-th entry) into one
-//     of eight global copies (one per XCD, so contended atomics stay in one L2),
-//     which the call zeroes first (a clearing launch, or the scorer launch that
-//     precedes the select in the fused path);
+//     top 12 order-key bits (its nonzero bins) into one of eight global copies (one
+//     per XCD, so contended atomics stay in one L2), which the call zeroes first (a
+//     clearing launch, or the scorer launch that precedes the select in the fused
+//     path);
 //     the (chunk, row) grid then finds the bin holding the K-th entry from the
 //     copies (scanning down from the row's highest bin) and writes every entry at
 //     or above that bin to the chunk's own candidate slots; one workgroup per row
@@ -687,7 +687,6 @@ template <int PER>
 __global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelArgs a) {
   constexpr int NT = kChunkThreads;
   __shared__ __align__(16) uint32_t hist[kBins];
-  __shared__ SelShared sh;
   __shared__ uint32_t top_bin;
   const int row = blockIdx.y;
   const int tid = threadIdx.x;
@@ -717,24 +716,14 @@ __global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelArgs a) {
   mk = wave_max(mk);
   if ((tid & 63) == 0) atomicMax(&top_bin, mk);
   __syncthreads();
-  // The row's K-th entry is at least the chunk's K-th entry, so bins below the
-  // latter's never hold it and are not needed above it: they are not flushed.
-  const int K = n < a.top_k ? n : a.top_k;
-  const int m = n - lo < PER * NT ? n - lo : PER * NT;
-  uint32_t low = 0;
-  if (m > K) {
-    uint32_t h[kBins / NT];
-    load_bins<NT>(hist, h);
-    find_digit<NT>(h, (uint32_t)K, sh);
-    low = sh.digit;
-  }
+  // every nonzero bin is flushed (a chunk's scores occupy few bins)
   const int copy = (blockIdx.y * gridDim.x + blockIdx.x) % kHistCopies;
   uint32_t* gh = a.ghist + ((int64_t)row * kHistCopies + copy) * kBins;
 #pragma unroll
   for (int q = 0; q < kBins / NT; ++q) {
     const int b = q * NT + tid;
     const uint32_t v = hist[b];
-    if (v && (uint32_t)b >= low) atomicAdd(&gh[b], v);
+    if (v) atomicAdd(&gh[b], v);
   }
   if (tid == 0) atomicMax(&a.gmax[(int64_t)row * kHistCopies + copy], top_bin);
 }
@@ -759,6 +748,14 @@ __global__ __launch_bounds__(kChunkThreads) void select_filter_kernel(SelArgs a)
     return;
   }
   const int K = n < a.top_k ? n : a.top_k;
+  // the chunk's scores are loaded first: their latency overlaps the search for the bin
+  const float* src = a.scores + (int64_t)row * a.score_stride;
+  uint32_t key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lo + i * NT + tid;
+    key[i] = e < n ? ord_key(src[e]) : 0u;
+  }
   RowInfo info{0u, 0u, (uint32_t)n, 0u};  // K == n: every entry is a candidate
   if (K < n) {
     const uint32_t* gm = a.gmax + (int64_t)row * kHistCopies;
@@ -797,14 +794,11 @@ __global__ __launch_bounds__(kChunkThreads) void select_filter_kernel(SelArgs a)
     if (tid == 0) a.ccount[slot] = 0u;
     return;
   }
-  const float* src = a.scores + (int64_t)row * a.score_stride;
   const uint32_t bin = info.bin;
-  uint32_t key[PER];
   uint32_t mine = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lo + i * NT + tid;
-    key[i] = e < n ? ord_key(src[e]) : 0u;
     mine += (e < n && (key[i] >> (32 - kDigit)) >= bin);
   }
   uint32_t pos = block_suffix<NT>(mine, sh);
