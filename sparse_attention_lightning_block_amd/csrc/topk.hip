@@ -14,6 +14,9 @@
 //     row in registers, finds the K-th composite with 12-bit-digit LDS histogram
 //     passes (stopping once the digit bin of the K-th entry is taken whole),
 //     gathers the winners and sorts them;
+//   * many rows (256 or more) of up to 32768 entries: one workgroup per row as well,
+//     1024 threads with 16 entries each in registers up to 16384 entries, 512 threads
+//     with 64 each beyond (one histogram pass, then an LDS candidate list);
 //   * longer rows run as a pipeline of three launches (kernel boundaries order
 //     them; no grid-wide fences, which write back the whole L2 on this chip):
 //     every workgroup of a (chunk, row) grid adds its chunk's LDS histogram of the
