@@ -326,6 +326,40 @@ def test_fused_entry_balanced_split():
         check_topk(gi[t], gv[t], ref[t], amag[t], 256, "mfma", f"fused balanced t{t}")
 
 
+# ------------------------------------------------------------------ FP32 path shapes
+
+FP32_SHAPES = [
+    # T, H, D, epb, table, q dtype: the FP32 kernel each one reaches
+    (5, 16, 64, 16, "shared", "f32"),      # fp32 matrix cores, one head tile, hd 64
+    (3, 48, 128, 7, "shared", "bf16"),     # three head tiles, steps crossing pages, bf16 q
+    (9, 32, 128, 64, "per_row", "f32"),    # two head tiles, rows on their own pages
+    (4, 64, 256, 32, "shared", "f32"),     # hd 256: the vector kernel
+    (2, 5, 256, 16, "per_row", "bf16"),    # vector kernel, a partial head group
+]
+
+
+@pytest.mark.parametrize("T,H,D,epb,table,qdt", FP32_SHAPES)
+def test_fp32_path_shapes(T, H, D, epb, table, qdt):
+    """IDX_PREC_FP32 over the head counts and key widths of both of its kernels (the fp32
+    matrix cores at hd 64/128, the vector ALUs at 256), fp32 and bf16 q, shared and
+    per-row tables: scores by the FP32 rule and the top-k against the oracle."""
+    max_lb = -(-1700 // epb)
+    w = csa(f"fp32_{T}_{H}_{D}_{table}", [97, T, H, D], T=T, H=H, D=D, epb=epb, P=max_lb * 2 + 3, max_lb=max_lb,
+            top_k=40, valid_lens=lambda rng, n: rng.integers(1, max_lb * epb + 1, size=n), dist="gauss",
+            q_dtype=qdt, w_scale=1 / H, table=table)
+    d = to_dev(w)
+    n_cols = max_lb * epb
+    rows = salb.indexer_score_rows(**d, n_cols=n_cols, precision="fp32")
+    idx, val = salb.indexer_score_topk(**d, top_k=40, precision="fp32", with_scores=True)
+    torch.cuda.synchronize()
+    gr, gi, gv = _row(rows), _row(idx), _row(val)
+    ref, amag = oracle_rows(w)
+    for t in range(T):
+        check_scores(gr[t], ref[t], amag[t], "fp32", f"fp32 shape T{T} H{H} D{D} t{t}")
+        assert np.all(np.isneginf(gr[t, int(w.valid_lens[t]):]))
+        check_topk(gi[t], gv[t], ref[t], amag[t], 40, "fp32", f"fp32 shape T{T} H{H} D{D} t{t}")
+
+
 # ------------------------------------------------------------------ signs of g and w
 
 SIGN_SHAPES = [
