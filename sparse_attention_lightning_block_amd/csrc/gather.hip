@@ -9,9 +9,10 @@
 //    selected positions' K and V rows ([nkv, hd] each) copied into [n_sel, nkv, hd].
 //
 // Both are pure data movement, bound by HBM.  The work is a flat list of (output row,
-// 16-byte chunk) items; every thread takes four items spread by the grid size and
-// issues all their dependent loads (index, block-table entry, data) before any store,
-// so that enough independent requests are in flight.
+// 16-byte chunk) items, one per thread: the grid covers every item (up to 16384
+// workgroups; beyond that a grid-stride loop), so that the chains of dependent loads
+// (index, block-table entry, data) of many threads are in flight at once -- more
+// threads with one chain each measured faster than fewer threads with four.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -20,7 +21,7 @@
 namespace salb {
 
 constexpr int kGatherThreads = 256;
-constexpr int kGatherItems = 4;  // items per thread and pass
+constexpr int kGatherItems = 1;  // items per thread and pass
 
 // One rounding of the exact product a * s to bfloat16 (round to nearest, ties to even).
 // p = RN32(a * s) and e = a * s - p (exact through the fma) decide it: bfloat16's ties
@@ -171,9 +172,8 @@ __global__ __launch_bounds__(kGatherThreads) void qsa_gather_kernel(QsaGatherArg
 }
 
 static unsigned gather_grid(int64_t n_items) {
-  // enough workgroups for eight per CU, each thread taking about four items per pass
   const int64_t want = (n_items + (int64_t)kGatherThreads * kGatherItems - 1) / ((int64_t)kGatherThreads * kGatherItems);
-  return (unsigned)(want < 2048 ? (want > 0 ? want : 1) : 2048);
+  return (unsigned)(want < 16384 ? (want > 0 ? want : 1) : 16384);
 }
 
 hipError_t launch_gather_kv(const uint8_t* fp8, const float* scale, const uint16_t* rope, const int32_t* bt,
