@@ -300,6 +300,11 @@ __device__ __forceinline__ void wave_stream(const ScoreArgs& a, const half8v (&A
                                             int s_begin, int s_vend, int first, int stride, float* out_row,
                                             int lane) {
   constexpr int KW = D / 32;
+  // the wave's bounds in scalar registers: every branch and trip count below is scalar
+  s_begin = __builtin_amdgcn_readfirstlane(s_begin);
+  s_vend = __builtin_amdgcn_readfirstlane(s_vend);
+  first = __builtin_amdgcn_readfirstlane(first);
+  stride = __builtin_amdgcn_readfirstlane(stride);
   const int n_vg = (s_vend - s_begin + 15) >> 4;
   if (first >= n_vg) return;
   const int col = lane & 15, quarter = lane >> 4;
@@ -348,36 +353,71 @@ __device__ __forceinline__ void wave_stream(const ScoreArgs& a, const half8v (&A
   float4v AC0[MT], AC1[MT];
   zero_acc<MT>(AC1);
   int gi = first;
+  // issued in ring order (the scheduler may not reorder them): the waits in the loop
+  // count on step u's loads being older than those of the steps after it
 #pragma unroll
-  for (int u = 0; u < kRing - 1; ++u) load_step(gi + u * stride, R[u], G[u]);
-  int s_prev = 0x3fffffff;  // nothing pending: its stores are masked off
-  float g_prev = 0.0f;
-  bool last_ac1 = false, done = false;
-  for (;;) {
+  for (int u = 0; u < kRing - 1; ++u) {
+    load_step(gi + u * stride, R[u], G[u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Four steps make a group: each step leaves its in-lane head sum times the key's
+  // |global scale| in p[q] (q = its place in the group), and once the group is complete
+  // the four are reduced over the lane quarters together, so that lane (col, q) ends
+  // with key col of step q and the group leaves in one store.  sg is the first key of
+  // the group's step 0 (a value past s_vend masks the whole store: nothing pending yet).
+  float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f, p3 = 0.0f;
+  float g_last = 0.0f;  // |global scale| of the last step's key (its ring slot is reloaded first)
+  int sg = 0x3fffffff;
+  auto flush = [&]() {
+    const float sc = row_transpose_sum4(p0, p1, p2, p3);
+    const int s = sg + quarter * stride * 16 + col;
+    if (s < s_vend) out_row[s] = sc;
+  };
+  // kRing steps per trip and a single exit (the trip count): steps past this wave's last
+  // only reload the ring.  A loop left from the middle of its body would reach its header
+  // on paths with other loads outstanding, and the waits placed there would drain the ring.
+  const int n_mine = (n_vg - first + stride - 1) / stride;  // >= 1
+  const int n_trips = (n_mine + kRing - 1) / kRing;
+  for (int trip = 0; trip < n_trips; ++trip) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
-      // the step before u left its scores in AC1 when u is even, in AC0 when odd
-      if (gi >= n_vg) {
-        last_ac1 = (u & 1) == 0;
-        done = true;
-        break;
-      }
       load_step(gi + (kRing - 1) * stride, R[(u + kRing - 1) % kRing], G[(u + kRing - 1) % kRing]);
-      if (u & 1) {
-        compute(R[u], G[u], AC1);
-        epilogue<MT>(AC0, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
-      } else {
-        compute(R[u], G[u], AC0);
-        epilogue<MT>(AC1, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
+      if (gi < n_vg) {
+        // step u multiplies into AC0 when u is even, into AC1 when odd, beside the head
+        // sum of the step before it
+        float prev;
+        if (u & 1) {
+          compute(R[u], G[u], AC1);
+          prev = g_last * head_part<MT>(AC0, wr);
+        } else {
+          compute(R[u], G[u], AC0);
+          prev = g_last * head_part<MT>(AC1, wr);
+        }
+        switch ((u + 3) & 3) {
+          case 0: p0 = prev; break;
+          case 1: p1 = prev; break;
+          case 2: p2 = prev; break;
+          default: p3 = prev; break;
+        }
+        if ((u & 3) == 0) {  // the step before completed a group
+          flush();
+          sg = s_begin + gi * 16;
+        }
+        g_last = fabsf(G[u]);
       }
-      s_prev = s_begin + gi * 16;
-      g_prev = G[u];
       gi += stride;
     }
-    if (done) break;
   }
-  if (last_ac1) epilogue<MT>(AC1, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
-  else epilogue<MT>(AC0, wr, fabsf(g_prev), s_prev, s_vend, out_row, lane);
+  // the last step's head sum (its accumulators by the parity of its ring slot), then
+  // its group; the group's places past it hold keys past s_vend and are masked
+  const int u_last = (n_mine - 1) % kRing;
+  const float pl = g_last * ((u_last & 1) ? head_part<MT>(AC1, wr) : head_part<MT>(AC0, wr));
+  const int q_last = u_last & 3;
+  p0 = q_last == 0 ? pl : p0;
+  p1 = q_last == 1 ? pl : p1;
+  p2 = q_last == 2 ? pl : p2;
+  p3 = q_last == 3 ? pl : p3;
+  flush();
 }
 
 // Loads the page ids and global scales of logical blocks lb0 .. lb0 + n - 1 of row t.
@@ -865,31 +905,45 @@ __global__ __launch_bounds__(256) void score_f32mfma_kernel(ScoreArgs a) {
     }
   }
   const int32_t* bt_row = a.bt + (int64_t)t * a.bt_stride;
-  for (int s0 = s_begin + 16 * wave; s0 < s_vend; s0 += 64) {
-    // key c of the step (keys past the valid end re-read the last valid one; not stored)
-    const int s = min(s0 + c, s_vend - 1);
+  // Step i of this wave covers keys s_begin + 16 wave + 64 i + (0..15).  Its loads run
+  // ahead of the matrix work: the table entry two steps ahead, the codes, the scales and
+  // the global scale one step ahead (keys past the valid end re-read the last valid one;
+  // their scores are not stored).
+  const int w0 = __builtin_amdgcn_readfirstlane(s_begin + 16 * wave);
+  const int n_steps = w0 < s_vend ? (s_vend - w0 + 63) / 64 : 0;
+  struct KeyRaw {
+    uint32_t words[NB / 4];
+    uint32_t sc;  // the slice's NG scale bytes
+    float gs;
+  };
+  auto key_of = [&](int i) { return min(w0 + 64 * i + c, s_vend - 1); };
+  auto entry_of = [&](int i) { return bt_row[div_epb((uint32_t)key_of(i), a.epb_magic)]; };
+  auto load_key = [&](int i, int p, KeyRaw& r) {
+    const int s = key_of(i);
     const uint32_t lb = div_epb((uint32_t)s, a.epb_magic);
-    const int p = bt_row[lb];
     const int64_t e = (int64_t)p * a.epb + (s - (int)lb * a.epb);
-    const float gs = a.gscale[p];
     const uint8_t* kp = a.keys + e * (D / 2) + g * NB;
     const uint8_t* sp = a.kscale + e * (D / 16) + g * NG;
-    uint32_t words[NB / 4];
     if constexpr (NB == 16) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(kp);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) words[i] = v[i];
+      for (int k = 0; k < 4; ++k) r.words[k] = v[k];
+      r.sc = *reinterpret_cast<const uint16_t*>(sp);
     } else {
       const u32x2 v = *reinterpret_cast<const u32x2*>(kp);
-      words[0] = v[0];
-      words[1] = v[1];
+      r.words[0] = v[0];
+      r.words[1] = v[1];
+      r.sc = *sp;
     }
+    r.gs = a.gscale[p];
+  };
+  auto compute_store = [&](int i, const KeyRaw& r) {
     float kb[KS];
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
-      const float sc = e4m3_to_f32(sp[j]);
-      decode8_f32(words[2 * j], sc, kb + 16 * j);
-      decode8_f32(words[2 * j + 1], sc, kb + 16 * j + 8);
+      const float sc = e4m3_to_f32((r.sc >> (8 * j)) & 0xffu);
+      decode8_f32(r.words[2 * j], sc, kb + 16 * j);
+      decode8_f32(r.words[2 * j + 1], sc, kb + 16 * j + 8);
     }
     float4v acc[MT];
 #pragma unroll
@@ -903,9 +957,35 @@ __global__ __launch_bounds__(256) void score_f32mfma_kernel(ScoreArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part = fmaf(wr[mt][i], fmaxf(gs * acc[mt][i], 0.0f), part);
+      for (int q = 0; q < 4; ++q) part = fmaf(wr[mt][q], fmaxf(r.gs * acc[mt][q], 0.0f), part);
     part = row_sum4(part);
-    if (g == 0 && s0 + c < s_vend) out_row[s0 + c] = part;
+    // every lane stores its column's total; columns past the valid end were computed on
+    // the last valid key (clamped above), so they write that key's own score to its slot
+    out_row[key_of(i)] = part;
+  };
+  if (n_steps == 0) return;
+  // two steps per trip and a single exit; the loads are issued in pipeline order
+  const int pa = entry_of(0);
+  int pb = entry_of(1);  // table entry of step i + 1
+  int pc = entry_of(2);  // ... of step i + 2
+  __builtin_amdgcn_sched_barrier(0);
+  KeyRaw r0;  // step i
+  load_key(0, pa, r0);
+  __builtin_amdgcn_sched_barrier(0);
+  // (the scheduling barriers keep each step's loads ahead of the matrix work before them)
+  for (int i = 0; i < n_steps; i += 2) {
+    KeyRaw r1;
+    load_key(i + 1, pb, r1);
+    const int pd = entry_of(i + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_store(i, r0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_key(i + 2, pc, r0);
+    pc = entry_of(i + 4);
+    pb = pd;
+    __builtin_amdgcn_sched_barrier(0);
+    compute_store(i + 1, r1);  // past the last step: its scores are not stored
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
