@@ -8,11 +8,14 @@
 //  * qsa_gather ([qsa.rs] "metrale_model_layers/layers/ops/qsa.rs", qsa_gather): the
 //    selected positions' K and V rows ([nkv, hd] each) copied into [n_sel, nkv, hd].
 //
-// Both are pure data movement, bound by HBM.  The work is a flat list of (output row,
-// 16-byte chunk) items, one per thread: the grid covers every item (up to 16384
-// workgroups; beyond that a grid-stride loop), so that the chains of dependent loads
-// (index, block-table entry, data) of many threads are in flight at once -- more
-// threads with one chain each measured faster than fewer threads with four.
+// Both are pure data movement, bound by HBM.  The FP8 gather's work is a flat list of
+// (output row, 16-byte chunk) items, one per thread: the grid covers every item (up to
+// 16384 workgroups; beyond that a grid-stride loop), so that the chains of dependent
+// loads (index, block-table entry, data) of many threads are in flight at once -- more
+// threads with one chain each measured faster than fewer threads with four, and faster
+// than one wave per row (its 40 busy lanes of 64 carry all of a row's conversions).  The
+// QSA gather, a plain copy, takes one wave per selected position: the position and its
+// table entry are loaded once per row, and every lane copies 16-byte chunks.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -21,7 +24,7 @@
 namespace salb {
 
 constexpr int kGatherThreads = 256;
-constexpr int kGatherItems = 1;  // items per thread and pass
+constexpr int kGatherItems = 1;  // items per thread and pass of the FP8 gather
 
 // One rounding of the exact product a * s to bfloat16 (round to nearest, ties to even).
 // p = RN32(a * s) and e = a * s - p (exact through the fma) decide it: bfloat16's ties
@@ -56,6 +59,9 @@ struct GatherKvArgs {
   int cpr_nope, cpr;  // chunks per row: d_nope / 16 FP8 chunks, then d_rope / 8 rope chunks
   uint64_t epb_magic;
 };
+
+// Rows per wave and pass of the QSA gather (its waves copy whole rows).
+constexpr int kRowsPerWave = 2;
 
 __global__ __launch_bounds__(kGatherThreads) void gather_kv_kernel(GatherKvArgs a) {
   const int64_t step = (int64_t)gridDim.x * kGatherThreads;
@@ -137,42 +143,58 @@ struct QsaGatherArgs {
   const int32_t* sel;
   uint16_t* k_out;
   uint16_t* v_out;
-  int64_t n_items;  // n_sel * 2 * cpr
+  int64_t n_items;  // n_sel
   int block_size, row_elems, cpr;  // row_elems = nkv * hd; cpr = row_elems / 8
 };
 
+// One wave per selected position, kRowsPerWave at a time: the position's table entry
+// is loaded once (the same address in every lane), and the lanes copy the K and V rows
+// in 16-byte chunks.
 __global__ __launch_bounds__(kGatherThreads) void qsa_gather_kernel(QsaGatherArgs a) {
-  const int64_t step = (int64_t)gridDim.x * kGatherThreads;
-  for (int64_t base = (int64_t)blockIdx.x * kGatherThreads + threadIdx.x; base < a.n_items;
-       base += step * kGatherItems) {
-    int64_t item[kGatherItems], src[kGatherItems], dst[kGatherItems];
-    int kv[kGatherItems];
+  constexpr int WPB = kGatherThreads / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * WPB + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n_rows = a.n_items;  // n_sel
+  const int64_t step = (int64_t)gridDim.x * WPB * kRowsPerWave;
+  for (int64_t r0 = wave * kRowsPerWave; r0 < n_rows; r0 += step) {
+    int64_t src[kRowsPerWave];
 #pragma unroll
-    for (int u = 0; u < kGatherItems; ++u) {
-      item[u] = base + u * step;
-      const int64_t it = item[u] < a.n_items ? item[u] : 0;
-      const int64_t r = it / (2 * a.cpr);             // selected slot
-      const int rest = (int)(it - r * 2 * a.cpr);
-      kv[u] = rest >= a.cpr;                          // 0: K, 1: V
-      const int c = rest - kv[u] * a.cpr;
-      const uint32_t pos = (uint32_t)a.sel[r];
+    for (int u = 0; u < kRowsPerWave; ++u) {
+      const int64_t r = r0 + u < n_rows ? r0 + u : n_rows - 1;  // past the end: re-read the last, not stored
+      const uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane(a.sel[r]);
       const uint32_t lb = pos / (uint32_t)a.block_size;
-      const int64_t phys = a.bt[lb];
-      src[u] = (phys * a.block_size + (pos - lb * (uint32_t)a.block_size)) * a.row_elems + c * 8;
-      dst[u] = r * a.row_elems + c * 8;
+      const int64_t phys = __builtin_amdgcn_readfirstlane(a.bt[lb]);
+      src[u] = (phys * a.block_size + (pos - lb * (uint32_t)a.block_size)) * a.row_elems;
     }
-    u32x4 x[kGatherItems];
+    for (int c = lane; c < a.cpr; c += 64) {
+      u32x4 xk[kRowsPerWave], xv[kRowsPerWave];
 #pragma unroll
-    for (int u = 0; u < kGatherItems; ++u)
-      if (item[u] < a.n_items) x[u] = *reinterpret_cast<const u32x4*>((kv[u] ? a.v : a.k) + src[u]);
+      for (int u = 0; u < kRowsPerWave; ++u) {
+        xk[u] = *reinterpret_cast<const u32x4*>(a.k + src[u] + c * 8);
+        xv[u] = *reinterpret_cast<const u32x4*>(a.v + src[u] + c * 8);
+      }
 #pragma unroll
-    for (int u = 0; u < kGatherItems; ++u)
-      if (item[u] < a.n_items) *reinterpret_cast<u32x4*>((kv[u] ? a.v_out : a.k_out) + dst[u]) = x[u];
+      for (int u = 0; u < kRowsPerWave; ++u) {
+        if (r0 + u >= n_rows) continue;
+        const int64_t dst = (r0 + u) * a.row_elems + c * 8;
+        *reinterpret_cast<u32x4*>(a.k_out + dst) = xk[u];
+        *reinterpret_cast<u32x4*>(a.v_out + dst) = xv[u];
+      }
+    }
   }
 }
 
+// Workgroups for one item per thread (at most 16384; beyond that a grid-stride loop).
 static unsigned gather_grid(int64_t n_items) {
   const int64_t want = (n_items + (int64_t)kGatherThreads * kGatherItems - 1) / ((int64_t)kGatherThreads * kGatherItems);
+  return (unsigned)(want < 16384 ? (want > 0 ? want : 1) : 16384);
+}
+
+// Workgroups for one wave per kRowsPerWave rows (at most 16384; beyond that the waves
+// loop over the rows).
+static unsigned gather_rows_grid(int64_t n_rows) {
+  const int64_t waves = (n_rows + kRowsPerWave - 1) / kRowsPerWave;
+  const int64_t want = (waves + kGatherThreads / 64 - 1) / (kGatherThreads / 64);
   return (unsigned)(want < 16384 ? (want > 0 ? want : 1) : 16384);
 }
 
@@ -214,8 +236,8 @@ hipError_t launch_qsa_gather(const uint16_t* k, const uint16_t* v, const int32_t
   a.block_size = block_size;
   a.row_elems = nkv * hd;
   a.cpr = a.row_elems / 8;
-  a.n_items = (int64_t)n_sel * 2 * a.cpr;
-  hipLaunchKernelGGL(qsa_gather_kernel, dim3(gather_grid(a.n_items)), dim3(kGatherThreads), 0, st, a);
+  a.n_items = n_sel;  // selected positions, one wave each
+  hipLaunchKernelGGL(qsa_gather_kernel, dim3(gather_rows_grid(a.n_items)), dim3(kGatherThreads), 0, st, a);
   return hipGetLastError();
 }
 
