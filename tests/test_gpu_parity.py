@@ -407,6 +407,31 @@ def test_negative_gscale_and_weights(T, table, epb, precision):
         check_topk(gi[t], gv[t], ref[t], amag[t], 48, precision, f"signs T{T} {table} t{t}")
 
 
+# ------------------------------------------------------------------ streaming tails
+
+@pytest.mark.parametrize("T,table,epb", [(8, "disjoint", 64), (3, "disjoint", 16), (2, "shared", 7)])
+def test_stream_tails(T, table, epb):
+    """The streaming scorers run whole eight-step trips and store four 16-key steps at a
+    time: valid lengths cover every count of steps modulo eight (and a partial last step)
+    for per-wave streams of eight rows on their own pages, and for the one-row split
+    scorer (its four waves take every fourth step)."""
+    lens = [16 * k + r for k, r in zip(range(T), (1, 16, 15, 7, 16, 3, 9, 16))]
+    if T < 4:
+        lens = [1000, 61, 16][:T]
+    max_lb = -(-max(lens) // epb) + 1
+    w = csa(f"tails_{T}_{epb}", [94, T, epb], T=T, H=64, D=128, epb=epb, P=max_lb * T + 3, max_lb=max_lb,
+            top_k=8, valid_lens=np.array(lens), dist="gauss", w_scale=1 / 64, table=table)
+    d = to_dev(w)
+    n_cols = max_lb * epb
+    rows = salb.indexer_score_rows(**d, n_cols=n_cols, precision="mfma")
+    torch.cuda.synchronize()
+    gr = _row(rows)
+    ref, amag = oracle_rows(w)
+    for t in range(T):
+        check_scores(gr[t], ref[t], amag[t], "mfma", f"tails T{T} t{t}")
+        assert np.all(np.isneginf(gr[t, lens[t]:])), t
+
+
 # ------------------------------------------------------------------ IDX_F_VALIDATE
 
 def test_validate_accepts_in_range_data():
