@@ -68,12 +68,12 @@ COLD_SPAN_BYTES = 2 * 256 * 2**20
 TRAFFIC_COPY_FACTOR = {"FETCH_SIZE": 1.9998, "WRITE_SIZE": 1.0}
 SCORER_SOURCES = {"csa": ['score.hip', 'nvfp4.hpp', 'common.hpp', 'internal.hpp'], "qsa": ['qsa.hip', 'common.hpp', 'internal.hpp']}
 SCORER_TRAFFIC = {   # workload: (sources, sha, FETCH_SIZE KiB, WRITE_SIZE KiB per dispatch)
-    "tiny_decode": ("csa", "27f7be8fd0abd273", 81.7, 16.0),
-    "decode_T8_S65536": ("csa", "27f7be8fd0abd273", 3551.8, 2048.0),
-    "long_decode_T32_S262144": ("csa", "27f7be8fd0abd273", 33768.6, 32776.0),
-    "prefill_T4096": ("csa", "27f7be8fd0abd273", 35446.6, 65690.5),
+    "tiny_decode": ("csa", "52f41720cf47e45b", 81.7, 16.0),
+    "decode_T8_S65536": ("csa", "52f41720cf47e45b", 3551.8, 2048.0),
+    "long_decode_T32_S262144": ("csa", "52f41720cf47e45b", 33768.6, 32776.0),
+    "prefill_T4096": ("csa", "52f41720cf47e45b", 35446.6, 65690.5),
     "qsa_prefill": ("qsa", "f0e5c69d978aa9b9", 81956.7, 262424.0),
-    "hbm_true_T32_S262144": ("csa", "27f7be8fd0abd273", 229531.4, 32776.1),
+    "hbm_true_T32_S262144": ("csa", "52f41720cf47e45b", 229531.4, 32776.1),
 }
 
 

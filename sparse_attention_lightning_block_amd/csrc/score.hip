@@ -16,13 +16,14 @@
 //    an instruction is a fixed permutation of the head dims applied to both
 //    operands, chosen so that every lane's key slice is contiguous.  The epilogue
 //    applies ReLU, the head weights and the per-page global scale to the fp32
-//    accumulators, reduces the heads (in-lane, then two row swaps on the VALU) and
-//    writes one score per key.  q is prescaled per head by a power of two so that its fp16
+//    accumulators, reduces the heads in the lane and then over the lane quarters with
+//    row swaps on the VALU (four 16-key steps together: three swaps), and writes the
+//    four steps' 64 scores in one store.  q is prescaled per head by a power of two so that its fp16
 //    rounding is relative (11 bits); the inverse power is folded into the head
 //    weight, which keeps the result identical up to that rounding.
 //      - score_mfma_split_kernel (fewer than four rows): every wave streams its own
-//        keys of the row; each lane decodes its 16-byte slice of one key straight
-//        into the B operand (no LDS trip).
+//        keys of the row through a ring of eight raw steps; each lane decodes its
+//        16-byte slice of one key straight into the B operand (no LDS trip).
 //      - score_mfma_group_kernel (four rows or more): four rows per workgroup (eight
 //        from sixteen rows on), one per wave; when the rows resolve the chunk to the
 //        same pages, each 64-key tile is decoded once into LDS (every thread decodes
