@@ -438,23 +438,26 @@ __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const InT* 
   };
 
   // two register stages: tile j + 2 loads while tile j multiplies and tile j + 1
-  // waits for its LDS buffer
+  // waits for its LDS buffer.  Two tiles per trip and a single exit: the loads are
+  // unconditional (past the last tile they re-read the clamped last key), so every path
+  // into the loop header has the same loads outstanding and the waits there only wait
+  // for the tile they need.
   Stage sa, sb;
   load_tile(c0, sa);
   load_tile(c0 + TILE, sb);
   store_tile(0, sa);
   __syncthreads();
-  for (int64_t k0 = c0; k0 < kend; k0 += 2 * TILE) {
-    // tile k0 is in buffer 0, tile k0 + TILE in sb
-    if (k0 + 2 * TILE < kend) load_tile(k0 + 2 * TILE, sa);
+  const int n_tiles = (int)((kend - c0 + TILE - 1) / TILE);
+  for (int j = 0; j < n_tiles; j += 2) {
+    const int64_t k0 = c0 + (int64_t)j * TILE;
+    // tile j is in buffer 0, tile j + 1 in sb
+    load_tile(k0 + 2 * TILE, sa);
     do_tile(0, k0);
-    if (k0 + TILE >= kend) break;
     store_tile(1, sb);
     __syncthreads();
-    // tile k0 + TILE is in buffer 1, tile k0 + 2 TILE in sa
-    if (k0 + 3 * TILE < kend) load_tile(k0 + 3 * TILE, sb);
-    do_tile(1, k0 + TILE);
-    if (k0 + 2 * TILE >= kend) break;
+    // tile j + 1 is in buffer 1, tile j + 2 in sa
+    load_tile(k0 + 3 * TILE, sb);
+    if (j + 1 < n_tiles) do_tile(1, k0 + TILE);
     store_tile(0, sa);
     __syncthreads();
   }
