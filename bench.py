@@ -309,8 +309,9 @@ def run_qsa(args, w):
 
 
 def run_qsa_decode(args):
-    """One QSA decode step on the QSA workload's cache: the new block pooled (n_new = 1),
-    the query prepared at its position, its scores over every complete block, the top-k."""
+    """One QSA decode step on the QSA workload's cache: the new block pooled (n_new = 1) and
+    the query prepared at its position (one launch), its scores over every complete block,
+    the top-k."""
     import torch
 
     import sparse_attention_lightning_block_amd as salb
@@ -342,6 +343,13 @@ def run_qsa_decode(args):
     def prep():
         salb.qsa_qprep(q_in, qw, n_heads=w.n_heads, hd=w.hd, pos=pos, rot=w.rot, theta=w.theta, eps=w.eps, out=q)
 
+    q_rows, q_out = q_in.view(1, -1), q.view(1, w.n_heads, w.hd)
+
+    def prep_one_launch():  # both of the above in one launch
+        salb.qsa_decode_prep(raw, kw, keys, q_rows, qw, first_block=nb - 1, n_new=1, ratio=w.ratio,
+                             n_heads=w.n_heads, hd=w.hd, first_pos=pos, rot=w.rot, theta=w.theta, eps=w.eps,
+                             out=q_out)
+
     def score():
         salb.qsa_score(q, keys, n_blocks=nb, out=sc[0])
 
@@ -349,8 +357,7 @@ def run_qsa_decode(args):
         salb.indexer_topk_select(sc, w.top_k, workspace=ws, out_idx=idx)
 
     def step():
-        pool()
-        prep()
+        prep_one_launch()
         score()
         select()
 
@@ -362,7 +369,8 @@ def run_qsa_decode(args):
     # replayed (the eager rate is reported beside it).
     ms_per_step, stage = timed_steps(torch, make_step(torch, [step], True), 1, args.steps)
     ms_eager, _ = timed_steps(torch, make_step(torch, [step], False), 1, args.steps)
-    pool_ms, prep_ms, score_ms, select_ms = (back_to_back_ms(torch, f, args.steps) for f in (pool, prep, score, select))
+    pool_ms, prep_ms, fused_ms, score_ms, select_ms = (back_to_back_ms(torch, f, args.steps)
+                                                       for f in (pool, prep, prep_one_launch, score, select))
     key_bytes = nb * w.hd * 4 + w.n_heads * w.hd * 4 + nb * 4
     gbs = key_bytes / (score_ms / 1e3) / 1e9
     out = {
@@ -383,7 +391,8 @@ def run_qsa_decode(args):
         "ms_per_step_eager": ms_eager,
         "step_ms": {"p10": float(np.percentile(stage[0], 10)), "p50": float(np.median(stage[0])),
                     "p90": float(np.percentile(stage[0], 90))},
-        "stage_ms": {"pool_one_block": pool_ms, "qprep": prep_ms, "score": score_ms, "select": select_ms},
+        "stage_ms": {"prep_one_launch": fused_ms, "score": score_ms, "select": select_ms,
+                     "pool_one_block_alone": pool_ms, "qprep_alone": prep_ms},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "qsa_decode_score_kernel",
                      "kernel_avg_us": round(score_ms * 1e3, 2), "bytes_per_launch": int(key_bytes),

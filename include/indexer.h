@@ -317,6 +317,19 @@ int qsa_qprep(const uint16_t* q_in, const float* q_norm_w, float* q_out, uint32_
               uint32_t rot, uint32_t pos, float theta, float eps, hipStream_t stream);
 
 /*
+ * qsa_decode_prep -- a decode step's inputs in one launch: qsa_block_pool of blocks
+ * [first_block, first_block + n_new) into block_keys and qsa_qprep_rows of rows
+ * [0, rows) (positions first_pos + r) into q_out, both fp32.  The arguments, layouts,
+ * checks and results are those of the two calls, bit for bit (the same arithmetic);
+ * the two write disjoint outputs, so one launch replaces two.  Returns IDX_OK without a
+ * launch when n_new and rows are both 0.
+ */
+int qsa_decode_prep(const uint16_t* raw_keys, const float* k_norm_w, float* block_keys, uint32_t first_block,
+                    uint32_t n_new, uint32_t ratio, const uint16_t* qk, const float* q_norm_w, float* q_out,
+                    uint32_t rows, uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t hd, uint32_t rot,
+                    float theta, float eps, hipStream_t stream);
+
+/*
  * qsa_score -- decode scores of one query over n_blocks blocks ([qsa.rs] qsa_score):
  *     scores[b] = sum_h ReLU(q[h,:] . block_keys[b,:]) / sqrt(hd)     b < n_blocks
  * (every block given is scored; the caller passes the query's complete blocks).  fp32

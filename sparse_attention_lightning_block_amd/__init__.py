@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     indexer_topk_select,
     indexer_topk_workspace_size,
     qsa_block_pool,
+    qsa_decode_prep,
     qsa_gather,
     qsa_prefill_attn,
     qsa_qprep,

@@ -55,6 +55,8 @@ SIGNATURES = {
     "qsa_qprep_rows": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _F, _F, _P]),
     "qsa_qprep_rows_f16": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _F, _F, _P]),
     "qsa_qprep": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _F, _F, _P]),
+    "qsa_decode_prep": (_I, [_P, _P, _P, _U32, _U32, _U32, _P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _F, _F,
+                             _P]),
     "qsa_score": (_I, [_P, _P, _P, _U32, _U32, _U32, _P]),
     "qsa_score_rows": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _I, _P]),
     "qsa_score_rows_f16": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _P]),

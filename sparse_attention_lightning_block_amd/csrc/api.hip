@@ -378,10 +378,8 @@ int qsa_prefill_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t*
 }
 
 extern "C++" {
-template <typename OutT>
-static int block_pool_impl(const uint16_t* raw_keys, const float* k_norm_w, OutT* block_keys, uint32_t first_block,
-                           uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot, float theta, float eps,
-                           hipStream_t stream) {
+static int block_pool_check(const uint16_t* raw_keys, const float* k_norm_w, const void* block_keys,
+                            uint32_t first_block, uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot) {
   if (!raw_keys || !k_norm_w || !block_keys) return fail(IDX_ERR_NULL, "raw_keys, k_norm_w and block_keys are required");
   if (hd != 64 && hd != 128 && hd != 256) return fail(IDX_ERR_UNSUPPORTED, "hd %u (supported: 64, 128, 256)", hd);
   if (rot > hd || (rot & 1)) return fail(IDX_ERR_SHAPE, "rot %u must be even and <= hd", rot);
@@ -389,6 +387,29 @@ static int block_pool_impl(const uint16_t* raw_keys, const float* k_norm_w, OutT
   if ((uint64_t)first_block + n_new > 0x7fffffffull) return fail(IDX_ERR_SHAPE, "block range too large");
   if (!aligned(raw_keys, 16) || !aligned(block_keys, 16) || !aligned(k_norm_w, 4))
     return fail(IDX_ERR_SHAPE, "raw_keys and block_keys must be 16-byte aligned");
+  return IDX_OK;
+}
+
+static int qprep_check(const uint16_t* qk, const float* q_norm_w, const void* q_out, uint32_t qkw, uint32_t n_heads,
+                       uint32_t hd, uint32_t rot) {
+  if (!qk || !q_norm_w || !q_out) return fail(IDX_ERR_NULL, "qk, q_norm_w and q_out are required");
+  if (hd != 64 && hd != 128 && hd != 256) return fail(IDX_ERR_UNSUPPORTED, "hd %u (supported: 64, 128, 256)", hd);
+  if (rot > hd || (rot & 1)) return fail(IDX_ERR_SHAPE, "rot %u must be even and <= hd", rot);
+  if (n_heads < 1 || n_heads > 65535) return fail(IDX_ERR_SHAPE, "n_heads %u out of range", n_heads);
+  if ((uint64_t)n_heads * hd > qkw) return fail(IDX_ERR_SHAPE, "qkw %u < n_heads * hd", qkw);
+  if ((uint64_t)n_heads * hd > 32768)
+    return fail(IDX_ERR_UNSUPPORTED, "n_heads * hd = %llu (supported: <= 32768)", (unsigned long long)n_heads * hd);
+  if (qkw % 8 != 0 || !aligned(qk, 16) || !aligned(q_out, 16) || !aligned(q_norm_w, 4))
+    return fail(IDX_ERR_SHAPE, "qk and q_out must be 16-byte aligned and qkw a multiple of 8");
+  return IDX_OK;
+}
+
+template <typename OutT>
+static int block_pool_impl(const uint16_t* raw_keys, const float* k_norm_w, OutT* block_keys, uint32_t first_block,
+                           uint32_t n_new, uint32_t ratio, uint32_t hd, uint32_t rot, float theta, float eps,
+                           hipStream_t stream) {
+  int rc;
+  if ((rc = block_pool_check(raw_keys, k_norm_w, block_keys, first_block, n_new, ratio, hd, rot)) != IDX_OK) return rc;
   if (n_new == 0) return ok();
   hipError_t e = salb::launch_block_pool<OutT>(raw_keys, k_norm_w, block_keys, first_block, n_new, ratio, hd, rot,
                                                theta, eps, stream);
@@ -416,15 +437,8 @@ template <typename OutT>
 static int qprep_rows_impl(const uint16_t* qk, const float* q_norm_w, OutT* q_out, uint32_t rows, uint32_t first_pos,
                            uint32_t qkw, uint32_t n_heads, uint32_t hd, uint32_t rot, float theta, float eps,
                            hipStream_t stream) {
-  if (!qk || !q_norm_w || !q_out) return fail(IDX_ERR_NULL, "qk, q_norm_w and q_out are required");
-  if (hd != 64 && hd != 128 && hd != 256) return fail(IDX_ERR_UNSUPPORTED, "hd %u (supported: 64, 128, 256)", hd);
-  if (rot > hd || (rot & 1)) return fail(IDX_ERR_SHAPE, "rot %u must be even and <= hd", rot);
-  if (n_heads < 1 || n_heads > 65535) return fail(IDX_ERR_SHAPE, "n_heads %u out of range", n_heads);
-  if ((uint64_t)n_heads * hd > qkw) return fail(IDX_ERR_SHAPE, "qkw %u < n_heads * hd", qkw);
-  if ((uint64_t)n_heads * hd > 32768)
-    return fail(IDX_ERR_UNSUPPORTED, "n_heads * hd = %llu (supported: <= 32768)", (unsigned long long)n_heads * hd);
-  if (qkw % 8 != 0 || !aligned(qk, 16) || !aligned(q_out, 16) || !aligned(q_norm_w, 4))
-    return fail(IDX_ERR_SHAPE, "qk and q_out must be 16-byte aligned and qkw a multiple of 8");
+  int rc;
+  if ((rc = qprep_check(qk, q_norm_w, q_out, qkw, n_heads, hd, rot)) != IDX_OK) return rc;
   if (rows == 0) return ok();
   hipError_t e = salb::launch_qprep_rows<OutT>(qk, q_norm_w, q_out, rows, first_pos, qkw, n_heads, hd, rot, theta,
                                                eps, stream);
@@ -444,6 +458,21 @@ int qsa_qprep_rows_f16(const uint16_t* qk, const float* q_norm_w, uint16_t* q_ou
                        hipStream_t stream) {
   return qprep_rows_impl<_Float16>(qk, q_norm_w, reinterpret_cast<_Float16*>(q_out), rows, first_pos, qkw, n_heads,
                                    hd, rot, theta, eps, stream);
+}
+
+int qsa_decode_prep(const uint16_t* raw_keys, const float* k_norm_w, float* block_keys, uint32_t first_block,
+                    uint32_t n_new, uint32_t ratio, const uint16_t* qk, const float* q_norm_w, float* q_out,
+                    uint32_t rows, uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t hd, uint32_t rot,
+                    float theta, float eps, hipStream_t stream) {
+  int rc;
+  if ((rc = block_pool_check(raw_keys, k_norm_w, block_keys, first_block, n_new, ratio, hd, rot)) != IDX_OK) return rc;
+  if ((rc = qprep_check(qk, q_norm_w, q_out, qkw, n_heads, hd, rot)) != IDX_OK) return rc;
+  if ((uint64_t)rows + (n_new + 31) / 32 > 0x7fffffffull) return fail(IDX_ERR_SHAPE, "rows %u too large", rows);
+  if (n_new == 0 && rows == 0) return ok();
+  hipError_t e = salb::launch_decode_prep(raw_keys, k_norm_w, block_keys, first_block, n_new, ratio, qk, q_norm_w,
+                                          q_out, rows, first_pos, qkw, n_heads, hd, rot, theta, eps, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode prep launch");
+  return ok();
 }
 
 int qsa_qprep(const uint16_t* q_in, const float* q_norm_w, float* q_out, uint32_t n_heads, uint32_t hd,

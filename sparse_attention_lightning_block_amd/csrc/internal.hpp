@@ -93,6 +93,11 @@ template <typename OutT>
 hipError_t launch_qprep_rows(const uint16_t* qk, const float* qw, OutT* out, uint32_t rows,
                              uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t hd, uint32_t rot,
                              float theta, float eps, hipStream_t st);
+// The query rows' prep and the new blocks' pooling (fp32 outputs) in one launch.
+hipError_t launch_decode_prep(const uint16_t* raw, const float* kw, float* block_keys, uint32_t first_block,
+                              uint32_t n_new, uint32_t ratio, const uint16_t* qk, const float* qw, float* q_out,
+                              uint32_t rows, uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t hd,
+                              uint32_t rot, float theta, float eps, hipStream_t st);
 hipError_t launch_qsa_score_f16(const _Float16* q, const _Float16* keys, float* scores, uint32_t rows, uint32_t nb,
                                 uint32_t first_pos, uint32_t stride, uint32_t ratio, uint32_t n_heads, uint32_t hd,
                                 hipStream_t st);

@@ -47,22 +47,34 @@ __device__ __forceinline__ void rope_cos_sin(double angle, double& c, double& s)
 // column groups, and the rotation pairs through LDS.  The rotation angle and its
 // sine and cosine are evaluated in fp64 (at long-prefill positions an fp32 angle is
 // off by ~0.03 rad), once per (block, pair).
+constexpr int kPoolTPB = 32;                  // threads per pooled block
+constexpr int kPoolNBW = 256 / kPoolTPB;      // blocks per 256-thread group
+
+// LDS of one 256-thread pooling group: the normalised block rows and the rotation
+// pairs' cosines and sines.
+template <int HD>
+struct PoolLds {
+  float xs[kPoolNBW][HD];
+  double cs[kPoolNBW][HD / 2][2];
+};
+
+// The pooling of one 256-thread group (group index grp: blocks first_block + 8 grp ..
+// + 7 below n_new).  Every thread of the workgroup calls it (it holds one barrier).
 template <int HD, typename OutT>
-__global__ __launch_bounds__(256) void block_pool_kernel(const uint16_t* __restrict__ raw,
-                                                         const float* __restrict__ kw, OutT* __restrict__ out,
-                                                         uint32_t first_block, uint32_t n_new, uint32_t ratio,
-                                                         int rot, float theta, float eps) {
-  constexpr int TPB = 32;           // threads per block
-  constexpr int NBW = 256 / TPB;    // blocks per workgroup
+__device__ __forceinline__ void pool_group(const uint16_t* __restrict__ raw, const float* __restrict__ kw,
+                                           OutT* __restrict__ out, uint32_t first_block, uint32_t n_new,
+                                           uint32_t ratio, int rot, float theta, float eps, uint32_t grp, int tid,
+                                           PoolLds<HD>& lds) {
+  constexpr int TPB = kPoolTPB;     // threads per block
+  constexpr int NBW = kPoolNBW;     // blocks per group
   constexpr int CG = HD / 8;        // 16-byte column groups per raw row
   constexpr int RC = TPB / CG;      // raw-row classes (threads per column group)
   static_assert(RC >= 1 && TPB % CG == 0, "head_dim");
-  __shared__ float xs[NBW][HD];
-  __shared__ double cs[NBW][HD / 2][2];
-  const int tid = threadIdx.x;
+  auto& xs = lds.xs;
+  auto& cs = lds.cs;
   const int bi = tid / TPB, j = tid % TPB;
   const int cg = j % CG, rc = j / CG;
-  const uint32_t nb_local = blockIdx.x * NBW + bi;
+  const uint32_t nb_local = grp * NBW + bi;
   const bool live = nb_local < n_new;
   const uint32_t b = first_block + nb_local;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -110,12 +122,14 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const uint16_t* __restr
     for (int i = 0; i < 8; ++i) xs[bi][cg * 8 + i] = m[i] * inv * (1.0f + kw[cg * 8 + i]);
   }
   const int half = rot >> 1;
-  for (int i = j; i < half; i += TPB) {
-    const double inv_freq = pow((double)theta, -2.0 * (double)i / (double)rot);
-    double sn, c;
-    rope_cos_sin((double)b * (double)ratio * inv_freq, c, sn);
-    cs[bi][i][0] = c;
-    cs[bi][i][1] = sn;
+  if (live) {  // blocks past n_new skip the fp64 angle evaluation (their outputs are not stored)
+    for (int i = j; i < half; i += TPB) {
+      const double inv_freq = pow((double)theta, -2.0 * (double)i / (double)rot);
+      double sn, c;
+      rope_cos_sin((double)b * (double)ratio * inv_freq, c, sn);
+      cs[bi][i][0] = c;
+      cs[bi][i][1] = sn;
+    }
   }
   __syncthreads();
   if (live && rc == 0) {
@@ -146,6 +160,15 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const uint16_t* __restr
   }
 }
 
+template <int HD, typename OutT>
+__global__ __launch_bounds__(256) void block_pool_kernel(const uint16_t* __restrict__ raw,
+                                                         const float* __restrict__ kw, OutT* __restrict__ out,
+                                                         uint32_t first_block, uint32_t n_new, uint32_t ratio,
+                                                         int rot, float theta, float eps) {
+  __shared__ PoolLds<HD> lds;
+  pool_group<HD, OutT>(raw, kw, out, first_block, n_new, ratio, rot, theta, eps, blockIdx.x, threadIdx.x, lds);
+}
+
 // ------------------------------------------------------------------ query prep
 
 // One 1024-thread workgroup per row, all heads: the row's raw values go to LDS, each of
@@ -156,18 +179,15 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const uint16_t* __restr
 // single row, so the heads are spread over as many waves as one workgroup holds.
 constexpr int kQprepThreads = 1024;
 
+// The prep of row r by one kQprepThreads workgroup (smem: qprep_lds_bytes).
 template <int HD, typename OutT>
-__global__ __launch_bounds__(kQprepThreads) void qprep_rows_kernel(const uint16_t* __restrict__ qk,
-                                                                   const float* __restrict__ qw,
-                                                                   OutT* __restrict__ out, uint32_t first_pos,
-                                                                   uint32_t qkw, uint32_t n_heads, int rot,
-                                                                   float theta, float eps) {
-  extern __shared__ __align__(16) unsigned char smem[];
+__device__ __forceinline__ void qprep_row(const uint16_t* __restrict__ qk, const float* __restrict__ qw,
+                                          OutT* __restrict__ out, uint32_t r, uint32_t first_pos, uint32_t qkw,
+                                          uint32_t n_heads, int rot, float theta, float eps, unsigned char* smem) {
   float* xr = reinterpret_cast<float*>(smem);                          // [n_heads * HD] raw values
   float* hinv = xr + n_heads * HD;                                     // [n_heads]
   double* cs = reinterpret_cast<double*>(hinv + ((n_heads + 3) & ~3));  // [HD / 2][2]
   constexpr int kWaves = kQprepThreads / 64;
-  const uint32_t r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = (int)n_heads * HD;
   const uint16_t* src = qk + (int64_t)r * qkw;
@@ -217,6 +237,37 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_rows_kernel(const uint16_
     }
     dst[e] = (OutT)o;  // fp16 storage: rounded to nearest even
   }
+}
+
+template <int HD, typename OutT>
+__global__ __launch_bounds__(kQprepThreads) void qprep_rows_kernel(const uint16_t* __restrict__ qk,
+                                                                   const float* __restrict__ qw,
+                                                                   OutT* __restrict__ out, uint32_t first_pos,
+                                                                   uint32_t qkw, uint32_t n_heads, int rot,
+                                                                   float theta, float eps) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  qprep_row<HD, OutT>(qk, qw, out, blockIdx.x, first_pos, qkw, n_heads, rot, theta, eps, smem);
+}
+
+// A decode step's inputs in one launch: workgroups [0, rows) prepare the query rows;
+// the others pool the new blocks, four 256-thread groups each (the same arithmetic as
+// qprep_rows_kernel and block_pool_kernel, so the outputs are bit-identical to theirs).
+template <int HD>
+__global__ __launch_bounds__(kQprepThreads) void decode_prep_kernel(
+    const uint16_t* __restrict__ raw, const float* __restrict__ kw, float* __restrict__ block_keys,
+    uint32_t first_block, uint32_t n_new, uint32_t ratio, const uint16_t* __restrict__ qk,
+    const float* __restrict__ qw, float* __restrict__ q_out, uint32_t rows, uint32_t first_pos, uint32_t qkw,
+    uint32_t n_heads, int rot, float theta, float eps) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  if (blockIdx.x < rows) {  // uniform over the workgroup
+    qprep_row<HD, float>(qk, qw, q_out, blockIdx.x, first_pos, qkw, n_heads, rot, theta, eps, smem);
+    return;
+  }
+  constexpr int kGroups = kQprepThreads / 256;
+  const int g = threadIdx.x / 256;
+  PoolLds<HD>* lds = reinterpret_cast<PoolLds<HD>*>(smem) + g;
+  pool_group<HD, float>(raw, kw, block_keys, first_block, n_new, ratio, rot, theta, eps,
+                        (blockIdx.x - rows) * kGroups + g, threadIdx.x % 256, *lds);
 }
 
 // ------------------------------------------------------------------ row scores (fp32)
@@ -608,6 +659,40 @@ hipError_t launch_block_pool(const uint16_t* raw, const float* kw, OutT* out, ui
 
 size_t qprep_lds_bytes(uint32_t n_heads, uint32_t hd) {
   return (size_t)4 * n_heads * hd + (size_t)4 * ((n_heads + 3) & ~3u) + (size_t)8 * hd;
+}
+
+template <int HD>
+static hipError_t launch_decode_prep_hd(const uint16_t* raw, const float* kw, float* block_keys, uint32_t first_block,
+                                        uint32_t n_new, uint32_t ratio, const uint16_t* qk, const float* qw,
+                                        float* q_out, uint32_t rows, uint32_t first_pos, uint32_t qkw,
+                                        uint32_t n_heads, uint32_t rot, float theta, float eps, hipStream_t st) {
+  constexpr uint32_t kBlocksPerWg = (kQprepThreads / 256) * kPoolNBW;
+  const size_t pool_lds = (size_t)(kQprepThreads / 256) * sizeof(PoolLds<HD>);
+  const size_t q_lds = qprep_lds_bytes(n_heads, HD);
+  const size_t lds = q_lds > pool_lds ? q_lds : pool_lds;
+  const hipError_t e = ensure_lds(reinterpret_cast<const void*>(decode_prep_kernel<HD>), lds);
+  if (e != hipSuccess) return e;
+  const uint32_t grid = rows + (n_new + kBlocksPerWg - 1) / kBlocksPerWg;
+  hipLaunchKernelGGL((decode_prep_kernel<HD>), dim3(grid), dim3(kQprepThreads), lds, st, raw, kw, block_keys,
+                     first_block, n_new, ratio, qk, qw, q_out, rows, first_pos, qkw, n_heads, (int)rot, theta, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_prep(const uint16_t* raw, const float* kw, float* block_keys, uint32_t first_block,
+                              uint32_t n_new, uint32_t ratio, const uint16_t* qk, const float* qw, float* q_out,
+                              uint32_t rows, uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t hd,
+                              uint32_t rot, float theta, float eps, hipStream_t st) {
+  switch (hd) {
+    case 64:
+      return launch_decode_prep_hd<64>(raw, kw, block_keys, first_block, n_new, ratio, qk, qw, q_out, rows, first_pos,
+                                       qkw, n_heads, rot, theta, eps, st);
+    case 128:
+      return launch_decode_prep_hd<128>(raw, kw, block_keys, first_block, n_new, ratio, qk, qw, q_out, rows,
+                                        first_pos, qkw, n_heads, rot, theta, eps, st);
+    default:
+      return launch_decode_prep_hd<256>(raw, kw, block_keys, first_block, n_new, ratio, qk, qw, q_out, rows,
+                                        first_pos, qkw, n_heads, rot, theta, eps, st);
+  }
 }
 
 template <typename OutT>

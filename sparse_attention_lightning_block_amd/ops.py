@@ -259,6 +259,30 @@ def qsa_qprep_rows(qk, q_norm_w, *, n_heads: int, hd: int, first_pos: int, rot: 
     return out
 
 
+def qsa_decode_prep(raw_keys, k_norm_w, block_keys, qk, q_norm_w, *, first_block: int, n_new: int, ratio: int,
+                    n_heads: int, hd: int, first_pos: int, rot: int, theta: float, eps: float,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """qsa_block_pool (fp32 block keys) and qsa_qprep_rows (fp32 queries) in one launch: writes
+    block_keys[first_block : first_block + n_new] and returns the prepared rows of qk."""
+    _dev(raw_keys, "raw_keys", torch.bfloat16, 2)
+    _dev(k_norm_w, "k_norm_w", torch.float32, 1)
+    _dev(block_keys, "block_keys", torch.float32, 2)
+    _dev(qk, "qk", torch.bfloat16, 2)
+    _dev(q_norm_w, "q_norm_w", torch.float32, 1)
+    if raw_keys.shape[1] != hd or block_keys.shape[1] != hd:
+        raise ValueError("raw_keys and block_keys must have hd columns")
+    if (first_block + n_new) * ratio > raw_keys.shape[0] or first_block + n_new > block_keys.shape[0]:
+        raise ValueError("block range exceeds the raw keys or the block-key table")
+    rows, qkw = qk.shape
+    if out is None:
+        out = torch.empty((rows, n_heads, hd), dtype=torch.float32, device=qk.device)
+    _dev(out, "out", torch.float32, 3)
+    check(_lib.load().qsa_decode_prep(_ptr(raw_keys), _ptr(k_norm_w), _ptr(block_keys), first_block, n_new, ratio,
+                                      _ptr(qk), _ptr(q_norm_w), _ptr(out), rows, first_pos, qkw, n_heads, hd, rot,
+                                      theta, eps, _stream()))
+    return out
+
+
 def qsa_qprep(q_in, q_norm_w, *, n_heads: int, hd: int, pos: int, rot: int, theta: float, eps: float,
               out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One prepared decode query [n_heads, hd] fp32 from its bf16 projection [n_heads * hd]."""

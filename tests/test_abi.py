@@ -124,6 +124,24 @@ def test_qsa_decode_argument_checks_without_gpu():
     assert lib.qsa_score(16, 40, 48, 10, 32, 128, None) == _lib.IDX_ERR_SHAPE                   # misaligned keys
 
 
+def test_qsa_decode_prep_argument_checks_without_gpu():
+    """The one-launch decode prep applies both calls' checks before any HIP call."""
+    lib = _lib.load()
+    good = (16, 16, 32, 0, 1, 16, 48, 16, 64, 1, 0, 4096, 32, 128, 64, 1e4, 1e-6, None)
+    bad = list(good); bad[0] = None                      # raw_keys
+    assert lib.qsa_decode_prep(*bad) == _lib.IDX_ERR_NULL
+    bad = list(good); bad[7] = None                      # q_norm_w
+    assert lib.qsa_decode_prep(*bad) == _lib.IDX_ERR_NULL
+    bad = list(good); bad[13] = 100                      # hd
+    assert lib.qsa_decode_prep(*bad) == _lib.IDX_ERR_UNSUPPORTED
+    bad = list(good); bad[11] = 100                      # qkw < n_heads * hd
+    assert lib.qsa_decode_prep(*bad) == _lib.IDX_ERR_SHAPE
+    bad = list(good); bad[2] = 40                        # block_keys misaligned
+    assert lib.qsa_decode_prep(*bad) == _lib.IDX_ERR_SHAPE
+    empty = list(good); empty[4] = 0; empty[9] = 0       # nothing to do: no launch
+    assert lib.qsa_decode_prep(*empty) == _lib.IDX_OK
+
+
 def test_qsa_fp16_storage_argument_checks_without_gpu():
     lib = _lib.load()
     assert lib.qsa_block_pool_f16(None, 16, 32, 0, 1, 16, 128, 64, 1e4, 1e-6, None) == _lib.IDX_ERR_NULL

@@ -128,8 +128,8 @@ def test_fused_entry_graph_replays_match_eager(cfg, reduced):
 
 @pytest.mark.parametrize("n_blocks", [700, 32768])
 def test_qsa_decode_step_graph_replays_match_eager(n_blocks):
-    """One QSA decode step (the new block pooled, the query prepared, its scores over
-    all blocks on the matrix cores, the top-k through the long-row select when the row
+    """One QSA decode step (the new block pooled and the query prepared in one launch,
+    its scores over all blocks on the matrix cores, the top-k through the long-row select when the row
     is long) captured once and replayed: bit-equal to the eager step every time."""
     w = make(5, reduced=0 if n_blocks > 700 else 1)
     nb = min(n_blocks, w.n_blocks)
@@ -147,10 +147,10 @@ def test_qsa_decode_step_graph_replays_match_eager(n_blocks):
     ws = torch.full((max(256, salb.indexer_topk_workspace_size(1, nb, w.top_k)),), 0x5A, dtype=torch.uint8,
                     device="cuda")
 
-    def step():
-        salb.qsa_block_pool(raw, kw, keys, first_block=nb - 1, n_new=1, ratio=w.ratio, rot=w.rot, theta=w.theta,
-                            eps=w.eps)
-        salb.qsa_qprep(q_in, qw, n_heads=w.n_heads, hd=w.hd, pos=pos, rot=w.rot, theta=w.theta, eps=w.eps, out=q)
+    def step():  # the new block and the query in one launch, as the benchmark's step
+        salb.qsa_decode_prep(raw, kw, keys, q_in.view(1, -1), qw, first_block=nb - 1, n_new=1, ratio=w.ratio,
+                             n_heads=w.n_heads, hd=w.hd, first_pos=pos, rot=w.rot, theta=w.theta, eps=w.eps,
+                             out=q.view(1, w.n_heads, w.hd))
         salb.qsa_score(q, keys, n_blocks=nb, out=sc[0])
         salb.indexer_topk_select(sc, w.top_k, workspace=ws, out_idx=idx, out_scores=val)
 

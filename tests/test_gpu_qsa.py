@@ -88,6 +88,40 @@ def test_qprep_rows_reduced():
     _check_vectors(q, ref, "qprep")
 
 
+@pytest.mark.parametrize("first_block,n_new,rows", [(100, 1, 1), (3, 45, 7), (0, 0, 2), (60, 33, 1)])
+def test_decode_prep_is_pool_and_qprep_bit_for_bit(first_block, n_new, rows):
+    """The one-launch decode prep writes exactly what qsa_block_pool and qsa_qprep_rows
+    write (one new block and one query, many blocks and rows, no new block), leaves the
+    other blocks untouched, and matches the oracle."""
+    w = make(5, reduced=1)
+    raw = _bf16(w.raw_keys).cuda()
+    kw = torch.from_numpy(w.k_norm_w).cuda()
+    qw = torch.from_numpy(w.q_norm_w).cuda()
+    qk = _bf16(w.qk[:rows]).cuda() if rows else torch.empty((0, w.qk.shape[1]), dtype=torch.bfloat16, device="cuda")
+    fp = w.first_pos + 5
+    a_keys = torch.full((w.n_blocks, w.hd), 7.0, dtype=torch.float32, device="cuda")
+    b_keys = a_keys.clone()
+    a_q = salb.qsa_decode_prep(raw, kw, a_keys, qk, qw, first_block=first_block, n_new=n_new, ratio=w.ratio,
+                               n_heads=w.n_heads, hd=w.hd, first_pos=fp, rot=w.rot, theta=w.theta, eps=w.eps)
+    salb.qsa_block_pool(raw, kw, b_keys, first_block=first_block, n_new=n_new, ratio=w.ratio, rot=w.rot,
+                        theta=w.theta, eps=w.eps)
+    b_q = (salb.qsa_qprep_rows(qk, qw, n_heads=w.n_heads, hd=w.hd, first_pos=fp, rot=w.rot, theta=w.theta, eps=w.eps)
+           if rows else torch.empty((0, w.n_heads, w.hd), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(a_keys.view(torch.int32), b_keys.view(torch.int32))
+    assert torch.equal(a_q.view(torch.int32), b_q.view(torch.int32))
+    got = a_keys.cpu().numpy()
+    assert np.all(got[:first_block] == 7.0) and np.all(got[first_block + n_new:] == 7.0)
+    if n_new:
+        ref = qsa.block_pool(indexer.upcast(w.raw_keys, "bf16"), w.k_norm_w, first_block, n_new, w.ratio, w.rot,
+                             w.theta, w.eps)
+        _check_vectors(got[first_block:first_block + n_new], ref, "decode prep pool")
+    if rows:
+        ref = qsa.qprep_rows(indexer.upcast(w.qk[:rows], "bf16"), w.q_norm_w, rows, fp, w.n_heads * w.hd, w.n_heads,
+                             w.hd, w.rot, w.theta, w.eps)
+        _check_vectors(a_q.cpu().numpy(), ref, "decode prep qprep")
+
+
 @pytest.mark.parametrize("precision", ["fp32", "mfma"])
 def test_score_rows_and_topk_reduced(precision):
     """Scores from the GPU's own pooled keys and prepared queries (the same fp32 inputs on
