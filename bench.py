@@ -72,7 +72,7 @@ SCORER_TRAFFIC = {   # workload: (sources, sha, FETCH_SIZE KiB, WRITE_SIZE KiB p
     "decode_T8_S65536": ("csa", "52f41720cf47e45b", 3551.8, 2048.0),
     "long_decode_T32_S262144": ("csa", "52f41720cf47e45b", 33768.6, 32776.0),
     "prefill_T4096": ("csa", "52f41720cf47e45b", 35446.6, 65690.5),
-    "qsa_prefill": ("qsa", "fe8e8a21c6afafee", 81957.7, 262424.2),
+    "qsa_prefill": ("qsa", "e78330d1767c1a9e", 81962.3, 262424.1),
     "hbm_true_T32_S262144": ("csa", "52f41720cf47e45b", 229531.4, 32776.1),
 }
 
