@@ -310,8 +310,8 @@ def run_qsa(args, w):
 
 def run_qsa_decode(args):
     """One QSA decode step on the QSA workload's cache: the new block pooled (n_new = 1) and
-    the query prepared at its position (one launch), its scores over every complete block,
-    the top-k."""
+    the query prepared at its position (one launch), then its scores over every complete
+    block and their top-k (qsa_score_topk)."""
     import torch
 
     import sparse_attention_lightning_block_amd as salb
@@ -335,6 +335,7 @@ def run_qsa_decode(args):
     sc = torch.empty((1, nb), dtype=torch.float32, device=dev)
     idx = torch.empty((1, w.top_k), dtype=torch.int32, device=dev)
     ws = torch.empty(max(256, salb.indexer_topk_workspace_size(1, nb, w.top_k)), dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(max(256, salb.qsa_score_topk_workspace_size(nb, w.top_k)), dtype=torch.uint8, device=dev)
 
     def pool():
         salb.qsa_block_pool(raw, kw, keys, first_block=nb - 1, n_new=1, ratio=w.ratio, rot=w.rot, theta=w.theta,
@@ -356,10 +357,12 @@ def run_qsa_decode(args):
     def select():
         salb.indexer_topk_select(sc, w.top_k, workspace=ws, out_idx=idx)
 
+    def score_topk():  # both of the above, the scores in the workspace (one launch fewer)
+        salb.qsa_score_topk(q, keys, w.top_k, n_blocks=nb, workspace=ws2, out_idx=idx)
+
     def step():
         prep_one_launch()
-        score()
-        select()
+        score_topk()
 
     for _ in range(args.warmup):
         step()
@@ -369,8 +372,8 @@ def run_qsa_decode(args):
     # replayed (the eager rate is reported beside it).
     ms_per_step, stage = timed_steps(torch, make_step(torch, [step], True), 1, args.steps)
     ms_eager, _ = timed_steps(torch, make_step(torch, [step], False), 1, args.steps)
-    pool_ms, prep_ms, fused_ms, score_ms, select_ms = (back_to_back_ms(torch, f, args.steps)
-                                                       for f in (pool, prep, prep_one_launch, score, select))
+    pool_ms, prep_ms, fused_ms, score_ms, select_ms, st_ms = (
+        back_to_back_ms(torch, f, args.steps) for f in (pool, prep, prep_one_launch, score, select, score_topk))
     key_bytes = nb * w.hd * 4 + w.n_heads * w.hd * 4 + nb * 4
     gbs = key_bytes / (score_ms / 1e3) / 1e9
     out = {
@@ -391,8 +394,8 @@ def run_qsa_decode(args):
         "ms_per_step_eager": ms_eager,
         "step_ms": {"p10": float(np.percentile(stage[0], 10)), "p50": float(np.median(stage[0])),
                     "p90": float(np.percentile(stage[0], 90))},
-        "stage_ms": {"prep_one_launch": fused_ms, "score": score_ms, "select": select_ms,
-                     "pool_one_block_alone": pool_ms, "qprep_alone": prep_ms},
+        "stage_ms": {"prep_one_launch": fused_ms, "score_topk": st_ms, "score_alone": score_ms,
+                     "select_alone": select_ms, "pool_one_block_alone": pool_ms, "qprep_alone": prep_ms},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "qsa_decode_score_kernel",
                      "kernel_avg_us": round(score_ms * 1e3, 2), "bytes_per_launch": int(key_bytes),

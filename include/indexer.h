@@ -345,6 +345,21 @@ int qsa_score(const float* q, const float* block_keys, float* scores, uint32_t n
               uint32_t hd, hipStream_t stream);
 
 /*
+ * qsa_score_topk -- qsa_score of one decode query over n_blocks blocks, then the top_k
+ * of those scores as indexer_topk_select of one row with every block valid: the same
+ * indices and scores, bit for bit, as the two calls.  The scores live in the workspace
+ * and the score launch also clears the select's counters, so the call takes one launch
+ * fewer than the two.  top_k slots past n_blocks get -1 (and -inf).
+ *  workspace  >= qsa_score_topk_workspace_size(n_blocks, top_k) bytes, 256-byte aligned,
+ *             any contents (NULL allowed when the size is 0)
+ * Errors as qsa_score and indexer_topk_select; IDX_ERR_WORKSPACE when it is too small.
+ */
+size_t qsa_score_topk_workspace_size(uint32_t n_blocks, int top_k);
+int qsa_score_topk(const float* q, const float* block_keys, uint32_t n_blocks, uint32_t n_heads, uint32_t hd,
+                   int top_k, int32_t* topk_idx, float* topk_scores, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/*
  * qsa_score_rows -- QSA block scores ([qsa.rs] qsa_score, qsa_score_rows, qsa_score_rows_tc):
  *     scores[r, b] = sum_h ReLU(q[r,h,:] . block_keys[b,:]) / sqrt(hd)   for b < nb_r
  *     scores[r, b] = -inf                                              for nb_r <= b < n_blocks_max

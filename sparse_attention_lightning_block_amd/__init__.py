@@ -19,5 +19,7 @@ from .ops import (  # noqa: F401
     qsa_qprep_rows,
     qsa_score,
     qsa_score_rows,
+    qsa_score_topk,
+    qsa_score_topk_workspace_size,
 )
 from ._lib import IDX_ERR_DATA, IDX_F_VALIDATE, IndexerError, load  # noqa: F401

@@ -43,6 +43,8 @@ SIGNATURES = {
     "indexer_topk_workspace_size": (_SZ, [_I, _I, _I]),
     "indexer_topk_select": (_I, [_P, _I64, _P, _I64, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "indexer_score_topk_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "qsa_score_topk_workspace_size": (_SZ, [_U32, _I]),
+    "qsa_score_topk": (_I, [_P, _P, _U32, _U32, _U32, _I, _P, _P, _P, _SZ, _P]),
     "indexer_score_topk": (_I, [_P, _I, _P, _P, _P, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _I, _I, _U32, _P, _P,
                                 _P, _SZ, _P]),
     "indexer_score_topk_noalloc": (_I, [_P, _I, _P, _P, _P, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _I, _I, _U32,

@@ -494,8 +494,48 @@ int qsa_score(const float* q, const float* block_keys, float* scores, uint32_t n
   if (!aligned(q, 16) || !aligned(block_keys, 16) || !aligned(scores, 4))
     return fail(IDX_ERR_SHAPE, "q and block_keys must be 16-byte aligned");
   if (n_blocks == 0) return ok();
-  hipError_t e = salb::launch_qsa_decode_score(q, block_keys, scores, n_blocks, n_heads, hd, stream);
+  hipError_t e = salb::launch_qsa_decode_score(q, block_keys, scores, n_blocks, n_heads, hd, nullptr, 0, stream);
   if (e != hipSuccess) return hip_fail(e, "QSA decode score launch");
+  return ok();
+}
+
+size_t qsa_score_topk_workspace_size(uint32_t n_blocks, int top_k) {
+  if (n_blocks == 0 || n_blocks > 0x7fffffffu || top_k <= 0) return 0;
+  salb::SelectPlan p;
+  if (!salb::plan_select(1, (int)n_blocks, top_k, &p)) return 0;
+  return round_up((size_t)n_blocks * 4, 256) + p.bytes;
+}
+
+int qsa_score_topk(const float* q, const float* block_keys, uint32_t n_blocks, uint32_t n_heads, uint32_t hd,
+                   int top_k, int32_t* topk_idx, float* topk_scores, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  if (!q || !block_keys || !topk_idx) return fail(IDX_ERR_NULL, "q, block_keys and topk_idx are required");
+  if (hd != 64 && hd != 128 && hd != 256) return fail(IDX_ERR_UNSUPPORTED, "hd %u (supported: 64, 128, 256)", hd);
+  if (n_heads < 1 || n_heads > 64) return fail(IDX_ERR_UNSUPPORTED, "n_heads %u (supported: 1..64)", n_heads);
+  if (n_blocks > 0x7fffffffu || (int64_t)n_blocks >= kMaxCols)
+    return fail(IDX_ERR_UNSUPPORTED, "n_blocks %u (supported: < 2^24)", n_blocks);
+  if (!aligned(q, 16) || !aligned(block_keys, 16)) return fail(IDX_ERR_SHAPE, "q and block_keys must be 16-byte aligned");
+  int rc = check_select(1, (int)n_blocks, top_k, (int64_t)n_blocks, 0);
+  if (rc) return rc;
+  if (n_blocks == 0) {  // no block: every slot is padding (the select alone writes it)
+    return indexer_topk_select(nullptr, 0, nullptr, 0, 0, 1, 0, top_k, topk_idx, topk_scores, workspace,
+                               workspace_bytes, stream);
+  }
+  salb::SelectPlan p;
+  if (!salb::plan_select(1, (int)n_blocks, top_k, &p)) return fail(IDX_ERR_UNSUPPORTED, "top_k %d is not supported", top_k);
+  const size_t score_bytes = round_up((size_t)n_blocks * 4, 256);
+  const size_t need = score_bytes + p.bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(IDX_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(IDX_ERR_SHAPE, "workspace must be 256-byte aligned");
+  float* sc = static_cast<float*>(workspace);
+  unsigned char* sel_ws = static_cast<unsigned char*>(workspace) + score_bytes;
+  // the score launch also zeroes the select's counters (no clearing launch)
+  hipError_t e = salb::launch_qsa_decode_score(q, block_keys, sc, n_blocks, n_heads, hd, reinterpret_cast<uint4*>(sel_ws),
+                                               (int64_t)(salb::select_counter_bytes(p) / 16), stream);
+  if (e != hipSuccess) return hip_fail(e, "QSA decode score launch");
+  e = salb::launch_select(p, sc, (int64_t)n_blocks, nullptr, 0, 0, topk_idx, topk_scores, sel_ws, true, stream);
+  if (e != hipSuccess) return hip_fail(e, "select kernel launch");
   return ok();
 }
 

@@ -102,8 +102,9 @@ hipError_t launch_qsa_score_f16(const _Float16* q, const _Float16* keys, float* 
                                 uint32_t first_pos, uint32_t stride, uint32_t ratio, uint32_t n_heads, uint32_t hd,
                                 hipStream_t st);
 bool qsa_score_uses_mfma(int precision, uint32_t n_heads, uint32_t hd);
+// zero_ptr / zero_n16: 16-byte words the launch also zeroes (0 words: none)
 hipError_t launch_qsa_decode_score(const float* q, const float* keys, float* scores, uint32_t nb, uint32_t n_heads,
-                                   uint32_t hd, hipStream_t st);
+                                   uint32_t hd, uint4* zero_ptr, int64_t zero_n16, hipStream_t st);
 hipError_t launch_qsa_score(const float* q, const float* keys, float* scores, uint32_t rows, uint32_t nb,
                             uint32_t first_pos, uint32_t stride, uint32_t ratio, uint32_t n_heads, uint32_t hd,
                             int precision, hipStream_t st);

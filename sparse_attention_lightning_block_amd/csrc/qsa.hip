@@ -516,6 +516,15 @@ __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const InT* 
 
 // ------------------------------------------------------------------ decode scores
 
+// Zeroes n16 16-byte words at p over the whole grid (a fused score + top-k call clears
+// the select's counters in its score launch instead of a launch of its own).
+__device__ __forceinline__ void zero_words(uint4* p, int64_t n16) {
+  if (n16 == 0) return;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += step)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 // One decode query against n_blocks block keys ([qsa.rs] qsa_score), fp32.  A 256-thread
 // workgroup takes 64 consecutive blocks, one per lane, whose key stays in registers;
 // the four waves split the heads (wave w takes heads w, w + 4, ...), reading the query
@@ -527,7 +536,9 @@ template <int HD>
 __global__ __launch_bounds__(256) void qsa_decode_score_kernel(const float* __restrict__ q,
                                                                const float* __restrict__ keys,
                                                                float* __restrict__ scores, uint32_t nb,
-                                                               uint32_t n_heads, float out_scale) {
+                                                               uint32_t n_heads, float out_scale,
+                                                               uint4* __restrict__ zero_ptr, int64_t zero_n16) {
+  zero_words(zero_ptr, zero_n16);
   extern __shared__ __align__(16) float qs[];  // [n_heads * HD]
   __shared__ float part[4][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -580,7 +591,9 @@ template <int HD, int MT, int UPW>
 __global__ __launch_bounds__(256) void qsa_decode_score_mfma_kernel(const float* __restrict__ q,
                                                                     const float* __restrict__ keys,
                                                                     float* __restrict__ scores, uint32_t nb,
-                                                                    float out_scale) {
+                                                                    float out_scale, uint4* __restrict__ zero_ptr,
+                                                                    int64_t zero_n16) {
+  zero_words(zero_ptr, zero_n16);
   constexpr int KS = HD / 4;  // MFMA steps = dims per lane group
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -737,15 +750,17 @@ static hipError_t launch_qsa_mfma(const InT* q, const InT* keys, float* scores, 
 
 template <int HD, int MT>
 static hipError_t launch_decode_mfma(const float* q, const float* keys, float* scores, uint32_t nb, float sc,
-                                     hipStream_t st) {
+                                     uint4* zero_ptr, int64_t zero_n16, hipStream_t st) {
   // two 16-block units per wave once that still leaves a wave per SIMD (1024 SIMDs)
   const uint32_t units = (nb + 15) / 16;
   if (units >= 2048) {
     const dim3 grid((units + 7) / 8);
-    hipLaunchKernelGGL((qsa_decode_score_mfma_kernel<HD, MT, 2>), grid, dim3(256), 0, st, q, keys, scores, nb, sc);
+    hipLaunchKernelGGL((qsa_decode_score_mfma_kernel<HD, MT, 2>), grid, dim3(256), 0, st, q, keys, scores, nb, sc,
+                       zero_ptr, zero_n16);
   } else {
     const dim3 grid((units + 3) / 4);
-    hipLaunchKernelGGL((qsa_decode_score_mfma_kernel<HD, MT, 1>), grid, dim3(256), 0, st, q, keys, scores, nb, sc);
+    hipLaunchKernelGGL((qsa_decode_score_mfma_kernel<HD, MT, 1>), grid, dim3(256), 0, st, q, keys, scores, nb, sc,
+                       zero_ptr, zero_n16);
   }
   return hipGetLastError();
 }
@@ -755,23 +770,23 @@ bool qsa_decode_uses_mfma(uint32_t n_heads, uint32_t hd) {
 }
 
 hipError_t launch_qsa_decode_score(const float* q, const float* keys, float* scores, uint32_t nb, uint32_t n_heads,
-                                   uint32_t hd, hipStream_t st) {
+                                   uint32_t hd, uint4* zero_ptr, int64_t zero_n16, hipStream_t st) {
   const float sc = 1.0f / sqrtf((float)hd);
   if (qsa_decode_uses_mfma(n_heads, hd)) {
     const uint32_t mt = n_heads / 16;
     if (hd == 64) {
       switch (mt) {
-        case 1: return launch_decode_mfma<64, 1>(q, keys, scores, nb, sc, st);
-        case 2: return launch_decode_mfma<64, 2>(q, keys, scores, nb, sc, st);
-        case 3: return launch_decode_mfma<64, 3>(q, keys, scores, nb, sc, st);
-        default: return launch_decode_mfma<64, 4>(q, keys, scores, nb, sc, st);
+        case 1: return launch_decode_mfma<64, 1>(q, keys, scores, nb, sc, zero_ptr, zero_n16, st);
+        case 2: return launch_decode_mfma<64, 2>(q, keys, scores, nb, sc, zero_ptr, zero_n16, st);
+        case 3: return launch_decode_mfma<64, 3>(q, keys, scores, nb, sc, zero_ptr, zero_n16, st);
+        default: return launch_decode_mfma<64, 4>(q, keys, scores, nb, sc, zero_ptr, zero_n16, st);
       }
     }
     switch (mt) {
-      case 1: return launch_decode_mfma<128, 1>(q, keys, scores, nb, sc, st);
-      case 2: return launch_decode_mfma<128, 2>(q, keys, scores, nb, sc, st);
-      case 3: return launch_decode_mfma<128, 3>(q, keys, scores, nb, sc, st);
-      default: return launch_decode_mfma<128, 4>(q, keys, scores, nb, sc, st);
+      case 1: return launch_decode_mfma<128, 1>(q, keys, scores, nb, sc, zero_ptr, zero_n16, st);
+      case 2: return launch_decode_mfma<128, 2>(q, keys, scores, nb, sc, zero_ptr, zero_n16, st);
+      case 3: return launch_decode_mfma<128, 3>(q, keys, scores, nb, sc, zero_ptr, zero_n16, st);
+      default: return launch_decode_mfma<128, 4>(q, keys, scores, nb, sc, zero_ptr, zero_n16, st);
     }
   }
   const dim3 grid((nb + 63) / 64);
@@ -780,15 +795,18 @@ hipError_t launch_qsa_decode_score(const float* q, const float* keys, float* sco
   switch (hd) {
     case 64:
       if ((e = ensure_lds(reinterpret_cast<const void*>(qsa_decode_score_kernel<64>), lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(qsa_decode_score_kernel<64>, grid, dim3(256), lds, st, q, keys, scores, nb, n_heads, sc);
+      hipLaunchKernelGGL(qsa_decode_score_kernel<64>, grid, dim3(256), lds, st, q, keys, scores, nb, n_heads, sc,
+                         zero_ptr, zero_n16);
       break;
     case 128:
       if ((e = ensure_lds(reinterpret_cast<const void*>(qsa_decode_score_kernel<128>), lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(qsa_decode_score_kernel<128>, grid, dim3(256), lds, st, q, keys, scores, nb, n_heads, sc);
+      hipLaunchKernelGGL(qsa_decode_score_kernel<128>, grid, dim3(256), lds, st, q, keys, scores, nb, n_heads, sc,
+                         zero_ptr, zero_n16);
       break;
     default:
       if ((e = ensure_lds(reinterpret_cast<const void*>(qsa_decode_score_kernel<256>), lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(qsa_decode_score_kernel<256>, grid, dim3(256), lds, st, q, keys, scores, nb, n_heads, sc);
+      hipLaunchKernelGGL(qsa_decode_score_kernel<256>, grid, dim3(256), lds, st, q, keys, scores, nb, n_heads, sc,
+                         zero_ptr, zero_n16);
       break;
   }
   return hipGetLastError();

@@ -313,6 +313,34 @@ def qsa_score(q, block_keys, *, n_blocks: Optional[int] = None, out: Optional[to
     return out
 
 
+def qsa_score_topk_workspace_size(n_blocks: int, top_k: int) -> int:
+    return int(_lib.load().qsa_score_topk_workspace_size(n_blocks, top_k))
+
+
+def qsa_score_topk(q, block_keys, top_k: int, *, n_blocks: Optional[int] = None, with_scores: bool = False,
+                   workspace: Optional[torch.Tensor] = None, out_idx: Optional[torch.Tensor] = None,
+                   out_scores: Optional[torch.Tensor] = None):
+    """(idx [top_k] int32, scores [top_k] fp32 or None): the top_k blocks of one prepared
+    decode query [n_heads, hd] over the first n_blocks block keys (qsa_score, then the
+    select, with the scores kept in the workspace)."""
+    _dev(q, "q", torch.float32, 2)
+    _dev(block_keys, "block_keys", torch.float32, 2)
+    n_heads, hd = q.shape
+    nb = block_keys.shape[0] if n_blocks is None else n_blocks
+    if nb > block_keys.shape[0]:
+        raise ValueError("n_blocks exceeds the block-key table")
+    dev = q.device
+    if out_idx is None:
+        out_idx = torch.empty((top_k,), dtype=torch.int32, device=dev)
+    if with_scores and out_scores is None:
+        out_scores = torch.empty((top_k,), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(qsa_score_topk_workspace_size(nb, top_k), 256), dtype=torch.uint8, device=dev)
+    check(_lib.load().qsa_score_topk(_ptr(q), _ptr(block_keys), nb, n_heads, hd, top_k, _ptr(out_idx),
+                                     _ptr(out_scores), _ptr(workspace), workspace.numel(), _stream()))
+    return out_idx, out_scores
+
+
 def qsa_score_rows(q, block_keys, *, first_pos: int, ratio: int, n_blocks_max: Optional[int] = None,
                    precision: str = "mfma", out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """scores [rows, n_blocks_max] fp32 with -inf past each row's complete blocks.  fp16 q and

@@ -142,6 +142,20 @@ def test_qsa_decode_prep_argument_checks_without_gpu():
     assert lib.qsa_decode_prep(*empty) == _lib.IDX_OK
 
 
+def test_qsa_score_topk_argument_checks_without_gpu():
+    lib = _lib.load()
+    n = lib.qsa_score_topk_workspace_size(32768, 256)
+    assert n >= 32768 * 4 and n % 256 == 0
+    assert lib.qsa_score_topk_workspace_size(0, 256) == 0
+    assert lib.qsa_score_topk_workspace_size(100, 0) == 0
+    assert lib.qsa_score_topk(None, 16, 100, 32, 128, 8, 16, None, 256, 1 << 20, None) == _lib.IDX_ERR_NULL
+    assert lib.qsa_score_topk(16, 16, 100, 32, 100, 8, 16, None, 256, 1 << 20, None) == _lib.IDX_ERR_UNSUPPORTED
+    assert lib.qsa_score_topk(16, 16, 100, 65, 128, 8, 16, None, 256, 1 << 20, None) == _lib.IDX_ERR_UNSUPPORTED
+    assert lib.qsa_score_topk(16, 16, 100, 32, 128, 0, 16, None, 256, 1 << 20, None) == _lib.IDX_ERR_UNSUPPORTED
+    # a workspace too small for the scores: rejected before any HIP call
+    assert lib.qsa_score_topk(16, 16, 32768, 32, 128, 256, 16, None, 256, 1024, None) == _lib.IDX_ERR_WORKSPACE
+
+
 def test_qsa_fp16_storage_argument_checks_without_gpu():
     lib = _lib.load()
     assert lib.qsa_block_pool_f16(None, 16, 32, 0, 1, 16, 128, 64, 1e4, 1e-6, None) == _lib.IDX_ERR_NULL

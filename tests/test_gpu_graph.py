@@ -129,8 +129,9 @@ def test_fused_entry_graph_replays_match_eager(cfg, reduced):
 @pytest.mark.parametrize("n_blocks", [700, 32768])
 def test_qsa_decode_step_graph_replays_match_eager(n_blocks):
     """One QSA decode step (the new block pooled and the query prepared in one launch,
-    its scores over all blocks on the matrix cores, the top-k through the long-row select when the row
-    is long) captured once and replayed: bit-equal to the eager step every time."""
+    then qsa_score_topk: its scores over all blocks on the matrix cores and the top-k,
+    through the long-row select when the row is long, its counters cleared by the score
+    launch) captured once and replayed: bit-equal to the eager step every time."""
     w = make(5, reduced=0 if n_blocks > 700 else 1)
     nb = min(n_blocks, w.n_blocks)
     raw = torch.from_numpy(w.raw_keys.view(np.int16).copy()).view(torch.bfloat16).cuda()
@@ -141,32 +142,30 @@ def test_qsa_decode_step_graph_replays_match_eager(n_blocks):
     keys = torch.empty((w.n_blocks, w.hd), dtype=torch.float32, device="cuda")
     salb.qsa_block_pool(raw, kw, keys, first_block=0, n_new=nb, ratio=w.ratio, rot=w.rot, theta=w.theta, eps=w.eps)
     q = torch.empty((w.n_heads, w.hd), dtype=torch.float32, device="cuda")
-    sc = torch.empty((1, nb), dtype=torch.float32, device="cuda")
     idx = torch.empty((1, w.top_k), dtype=torch.int32, device="cuda")
     val = torch.empty((1, w.top_k), dtype=torch.float32, device="cuda")
-    ws = torch.full((max(256, salb.indexer_topk_workspace_size(1, nb, w.top_k)),), 0x5A, dtype=torch.uint8,
+    ws = torch.full((max(256, salb.qsa_score_topk_workspace_size(nb, w.top_k)),), 0x5A, dtype=torch.uint8,
                     device="cuda")
 
     def step():  # the new block and the query in one launch, as the benchmark's step
         salb.qsa_decode_prep(raw, kw, keys, q_in.view(1, -1), qw, first_block=nb - 1, n_new=1, ratio=w.ratio,
                              n_heads=w.n_heads, hd=w.hd, first_pos=pos, rot=w.rot, theta=w.theta, eps=w.eps,
                              out=q.view(1, w.n_heads, w.hd))
-        salb.qsa_score(q, keys, n_blocks=nb, out=sc[0])
-        salb.indexer_topk_select(sc, w.top_k, workspace=ws, out_idx=idx, out_scores=val)
+        salb.qsa_score_topk(q, keys, w.top_k, n_blocks=nb, workspace=ws, out_idx=idx[0], out_scores=val[0])
 
     step()
     torch.cuda.synchronize()
-    ref = [t.clone() for t in (keys, q, sc, idx, val)]
+    ref = [t.clone() for t in (keys, q, idx, val)]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
     for rep in range(3):
-        for t in (q, sc, val):
+        for t in (q, val):
             t.fill_(2.5)
         idx.fill_(-3)
         g.replay()
         torch.cuda.synchronize()
-        for got, want in zip((keys, q, sc, idx, val), ref):
+        for got, want in zip((keys, q, idx, val), ref):
             assert torch.equal(got.view(torch.int32), want.view(torch.int32)), rep
         step()  # eager work between replays
         torch.cuda.synchronize()

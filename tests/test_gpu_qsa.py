@@ -122,6 +122,34 @@ def test_decode_prep_is_pool_and_qprep_bit_for_bit(first_block, n_new, rows):
         _check_vectors(a_q.cpu().numpy(), ref, "decode prep qprep")
 
 
+@pytest.mark.parametrize("nb", [0, 5, 700, 32768])
+def test_score_topk_is_score_then_select_bit_for_bit(nb):
+    """qsa_score_topk (scores in the workspace, the select's counters cleared by the score
+    launch) against qsa_score followed by indexer_topk_select: the same indices and
+    scores, bit for bit, from a workspace full of garbage, twice in a row; fewer blocks
+    than top_k pads with -1 / -inf."""
+    w = make(5, reduced=0 if nb > 1000 else 1)
+    nb = min(nb, w.n_blocks)
+    keys = _pool_all(w)
+    r = w.rows - 1
+    q = salb.qsa_qprep(_bf16(w.qk[r]).cuda(), torch.from_numpy(w.q_norm_w).cuda(), n_heads=w.n_heads, hd=w.hd,
+                       pos=w.first_pos + r, rot=w.rot, theta=w.theta, eps=w.eps)
+    ws = torch.full((max(256, salb.qsa_score_topk_workspace_size(nb, w.top_k)),), 0x5A, dtype=torch.uint8,
+                    device="cuda")
+    for _ in range(2):
+        a_idx, a_val = salb.qsa_score_topk(q, keys, w.top_k, n_blocks=nb, with_scores=True, workspace=ws)
+        if nb:
+            sc = salb.qsa_score(q, keys, n_blocks=nb)
+            b_idx, b_val = salb.indexer_topk_select(sc.view(1, nb), w.top_k, with_scores=True)
+        torch.cuda.synchronize()
+        if nb:
+            assert torch.equal(a_idx, b_idx[0]) and torch.equal(a_val.view(torch.int32), b_val[0].view(torch.int32))
+        k = min(nb, w.top_k)
+        assert torch.all(a_idx[k:] == -1) and torch.all(torch.isneginf(a_val[k:]))
+        assert torch.all(a_idx[:k] >= 0) and torch.all(a_idx[:k] < max(nb, 1))
+        ws.fill_(0xA5)
+
+
 @pytest.mark.parametrize("precision", ["fp32", "mfma"])
 def test_score_rows_and_topk_reduced(precision):
     """Scores from the GPU's own pooled keys and prepared queries (the same fp32 inputs on
