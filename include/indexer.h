@@ -291,7 +291,8 @@ int qsa_block_pool_f16(const uint16_t* raw_keys, const float* k_norm_w, uint16_t
  *  q_norm_w [hd] fp32
  *  q_out    [rows, n_heads, hd] fp32 output, 16-byte aligned
  * RoPE as in qsa_block_pool.
- * Supported: hd in {64, 128, 256}, rot even and <= hd, n_heads * hd <= 32768.
+ * Supported: hd in {64, 128, 256}, rot even and <= hd, n_heads * hd <= 32768, and
+ * rows * ceil(n_heads * hd / 1024) < 2^31 (the launch grid; IDX_ERR_SHAPE otherwise).
  */
 int qsa_qprep_rows(const uint16_t* qk, const float* q_norm_w, float* q_out,
                    uint32_t rows, uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t hd,

@@ -390,6 +390,10 @@ static int block_pool_check(const uint16_t* raw_keys, const float* k_norm_w, con
   return IDX_OK;
 }
 
+// Workgroups per query row at the smallest slice the query prep launches (128 chunks of
+// 8 dims): bounds the launch grid.
+static uint64_t qprep_slices(uint32_t n_heads, uint32_t hd) { return ((uint64_t)n_heads * hd / 8 + 127) / 128; }
+
 static int qprep_check(const uint16_t* qk, const float* q_norm_w, const void* q_out, uint32_t qkw, uint32_t n_heads,
                        uint32_t hd, uint32_t rot) {
   if (!qk || !q_norm_w || !q_out) return fail(IDX_ERR_NULL, "qk, q_norm_w and q_out are required");
@@ -439,6 +443,8 @@ static int qprep_rows_impl(const uint16_t* qk, const float* q_norm_w, OutT* q_ou
                            hipStream_t stream) {
   int rc;
   if ((rc = qprep_check(qk, q_norm_w, q_out, qkw, n_heads, hd, rot)) != IDX_OK) return rc;
+  if ((uint64_t)rows * qprep_slices(n_heads, hd) > 0x7fffffffull)
+    return fail(IDX_ERR_SHAPE, "rows %u too large", rows);
   if (rows == 0) return ok();
   hipError_t e = salb::launch_qprep_rows<OutT>(qk, q_norm_w, q_out, rows, first_pos, qkw, n_heads, hd, rot, theta,
                                                eps, stream);
@@ -467,7 +473,8 @@ int qsa_decode_prep(const uint16_t* raw_keys, const float* k_norm_w, float* bloc
   int rc;
   if ((rc = block_pool_check(raw_keys, k_norm_w, block_keys, first_block, n_new, ratio, hd, rot)) != IDX_OK) return rc;
   if ((rc = qprep_check(qk, q_norm_w, q_out, qkw, n_heads, hd, rot)) != IDX_OK) return rc;
-  if ((uint64_t)rows + (n_new + 31) / 32 > 0x7fffffffull) return fail(IDX_ERR_SHAPE, "rows %u too large", rows);
+  if ((uint64_t)rows * qprep_slices(n_heads, hd) + (n_new + 7) / 8 > 0x7fffffffull)
+    return fail(IDX_ERR_SHAPE, "rows %u too large", rows);
   if (n_new == 0 && rows == 0) return ok();
   hipError_t e = salb::launch_decode_prep(raw_keys, k_norm_w, block_keys, first_block, n_new, ratio, qk, q_norm_w,
                                           q_out, rows, first_pos, qkw, n_heads, hd, rot, theta, eps, stream);

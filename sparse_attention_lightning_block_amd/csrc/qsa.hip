@@ -70,37 +70,60 @@ __device__ __forceinline__ void pool_group(const uint16_t* __restrict__ raw, con
   constexpr int CG = HD / 8;        // 16-byte column groups per raw row
   constexpr int RC = TPB / CG;      // raw-row classes (threads per column group)
   static_assert(RC >= 1 && TPB % CG == 0, "head_dim");
+  constexpr int B = RC >= 4 ? 4 : 8;  // raw rows per thread in flight
   auto& xs = lds.xs;
   auto& cs = lds.cs;
   const int bi = tid / TPB, j = tid % TPB;
   const int cg = j % CG, rc = j / CG;
   const uint32_t nb_local = grp * NBW + bi;
   const bool live = nb_local < n_new;
-  const uint32_t b = first_block + nb_local;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (live) {
-    const uint16_t* base = raw + (int64_t)b * ratio * HD + cg * 8;
-    uint32_t r = rc;
-    for (; r + 3 * RC < ratio; r += 4 * RC) {
-      u32x4 v[4];
+  // blocks past n_new re-read the last new block and store nothing
+  const uint32_t b = first_block + (live ? nb_local : n_new - 1);
+  const uint16_t* base = raw + (int64_t)b * ratio * HD + cg * 8;
+  // Raw rows r0 + u RC + rc (u < B) of this thread's column group: all B loads are issued
+  // before any is used; rows past the block re-read its last row and add nothing.
+  auto load_batch = [&](uint32_t r0, u32x4 (&v)[B]) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const u32x4*>(base + (int64_t)(r + u * RC) * HD);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += __uint_as_float(v[u][i] << 16);
-          acc[2 * i + 1] += __uint_as_float(v[u][i] & 0xffff0000u);
-        }
+    for (int u = 0; u < B; ++u) {
+      const uint32_t r = min(r0 + (uint32_t)(u * RC + rc), ratio - 1);
+      v[u] = *reinterpret_cast<const u32x4*>(base + (int64_t)r * HD);
     }
-    for (; r < ratio; r += RC) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(base + (int64_t)r * HD);
+  };
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  auto add_batch = [&](uint32_t r0, const u32x4 (&v)[B]) {
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const bool ok = r0 + (uint32_t)(u * RC + rc) < ratio;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += __uint_as_float(v[i] << 16);
-        acc[2 * i + 1] += __uint_as_float(v[i] & 0xffff0000u);
+        const float lo = acc[2 * i] + __uint_as_float(v[u][i] << 16);
+        const float hi = acc[2 * i + 1] + __uint_as_float(v[u][i] & 0xffff0000u);
+        acc[2 * i] = ok ? lo : acc[2 * i];
+        acc[2 * i + 1] = ok ? hi : acc[2 * i + 1];
       }
     }
+  };
+  u32x4 v[B];
+  load_batch(0, v);
+  float wk[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) wk[i] = kw[cg * 8 + i];
+  __builtin_amdgcn_sched_barrier(0);
+  const int half = rot >> 1;
+  if (live) {  // the rotation angles while the loads are in flight (dead blocks skip them)
+    for (int i = j; i < half; i += TPB) {
+      const double inv_freq = pow((double)theta, -2.0 * (double)i / (double)rot);
+      double sn, c;
+      rope_cos_sin((double)b * (double)ratio * inv_freq, c, sn);
+      cs[bi][i][0] = c;
+      cs[bi][i][1] = sn;
+    }
+  }
+  add_batch(0, v);
+  const uint32_t n_more = (ratio - 1) / (uint32_t)(B * RC);  // further batches, uniform
+  for (uint32_t p = 1; p <= n_more; ++p) {
+    load_batch(p * B * RC, v);
+    add_batch(p * B * RC, v);
   }
   // sum the raw-row classes (lanes j ^ CG, j ^ 2 CG, ... of the same block)
 #pragma unroll
@@ -119,17 +142,7 @@ __device__ __forceinline__ void pool_group(const uint16_t* __restrict__ raw, con
   const float inv = 1.0f / sqrtf(ss / (float)HD + eps);
   if (rc == 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xs[bi][cg * 8 + i] = m[i] * inv * (1.0f + kw[cg * 8 + i]);
-  }
-  const int half = rot >> 1;
-  if (live) {  // blocks past n_new skip the fp64 angle evaluation (their outputs are not stored)
-    for (int i = j; i < half; i += TPB) {
-      const double inv_freq = pow((double)theta, -2.0 * (double)i / (double)rot);
-      double sn, c;
-      rope_cos_sin((double)b * (double)ratio * inv_freq, c, sn);
-      cs[bi][i][0] = c;
-      cs[bi][i][1] = sn;
-    }
+    for (int i = 0; i < 8; ++i) xs[bi][cg * 8 + i] = m[i] * inv * (1.0f + wk[i]);
   }
   __syncthreads();
   if (live && rc == 0) {
@@ -171,103 +184,129 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const uint16_t* __restr
 
 // ------------------------------------------------------------------ query prep
 
-// One 1024-thread workgroup per row, all heads: the row's raw values go to LDS, each of
-// the 16 waves computes the RMSNorm factor of every 16th head (a wave-wide sum on the
-// VALU), the rotation angles (fp64) are formed once per pair for the row and shared by
-// its heads, and the outputs are written one element per thread in order (consecutive
-// lanes read consecutive LDS words and store consecutive floats).  A decode query is a
-// single row, so the heads are spread over as many waves as one workgroup holds.
-constexpr int kQprepThreads = 1024;
+// A row is cut into slices of SL 16-byte chunks (SL a multiple of 64 chunks, so a slice
+// holds whole heads), one workgroup per (row, slice) and one chunk per thread: thread t
+// owns the 8 dims of chunk s SL + t, and a head's HD / 8 chunks sit in consecutive lanes
+// of one wave, so the head's RMSNorm sum of squares is a lane-swap tree with no LDS or
+// barrier.  The chunk and norm-weight loads are issued before the rotation angles are
+// evaluated (fp64, once per pair and workgroup), so the angle work overlaps their
+// latency; the normalised values meet their rotation partners through LDS after the
+// one barrier, and each chunk leaves as 16-byte stores.  The arithmetic of a chunk does
+// not depend on the slicing or the workgroup size, so every launch shape gives the same
+// bits.  A decode row spreads over several CUs; a prefill keeps many slices in flight
+// per CU.
 
-// The prep of row r by one kQprepThreads workgroup (smem: qprep_lds_bytes).
-template <int HD, typename OutT>
-__device__ __forceinline__ void qprep_row(const uint16_t* __restrict__ qk, const float* __restrict__ qw,
-                                          OutT* __restrict__ out, uint32_t r, uint32_t first_pos, uint32_t qkw,
-                                          uint32_t n_heads, int rot, float theta, float eps, unsigned char* smem) {
-  float* xr = reinterpret_cast<float*>(smem);                          // [n_heads * HD] raw values
-  float* hinv = xr + n_heads * HD;                                     // [n_heads]
-  double* cs = reinterpret_cast<double*>(hinv + ((n_heads + 3) & ~3));  // [HD / 2][2]
-  constexpr int kWaves = kQprepThreads / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = (int)n_heads * HD;
-  const uint16_t* src = qk + (int64_t)r * qkw;
-  for (int g = tid; g < n / 8; g += kQprepThreads) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(src + 8 * g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xr[8 * g + 2 * i] = __uint_as_float(v[i] << 16);
-      xr[8 * g + 2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
-    }
-  }
+// The prep of chunks [s SL, s SL + SL) of row r by threads [0, SL) of the workgroup
+// (the others only take part in the barrier).  smem: qprep_lds_bytes(SL, hd).
+template <int HD, typename OutT, int SL>
+__device__ __forceinline__ void qprep_slice(const uint16_t* __restrict__ qk, const float* __restrict__ qw,
+                                            OutT* __restrict__ out, uint32_t r, uint32_t s, uint32_t first_pos,
+                                            uint32_t qkw, uint32_t n_heads, int rot, float theta, float eps,
+                                            int tid, unsigned char* smem) {
+  constexpr int CG = HD / 8;  // chunks per head
+  static_assert(SL % 64 == 0 && 64 % CG == 0, "whole heads per wave");
+  const int n_chunks = (int)n_heads * CG;
+  float* xs = reinterpret_cast<float*>(smem);           // [SL * 8] normalised values of the slice
+  double* cs = reinterpret_cast<double*>(xs + SL * 8);  // [HD / 2][2] cosine, sine
+  const int c = (int)s * SL + tid;                      // this thread's chunk
+  const bool mine = tid < SL && c < n_chunks;
+  const int d0 = (tid % CG) * 8;                        // its dims d0 .. d0 + 7 of its head
   const int half = rot >> 1;
-  const double pos = (double)first_pos + (double)r;
-  for (int i = tid; i < half; i += kQprepThreads) {
-    const double inv_freq = pow((double)theta, -2.0 * (double)i / (double)rot);
-    double sn, c;
-    rope_cos_sin(pos * inv_freq, c, sn);
-    cs[2 * i] = c;
-    cs[2 * i + 1] = sn;
-  }
-  __syncthreads();
-  for (uint32_t h = wave; h < n_heads; h += kWaves) {
-    float ss = 0.0f;
+  // lanes past the row re-read its last chunk and store nothing
+  const u32x4 v = *reinterpret_cast<const u32x4*>(qk + (int64_t)r * qkw + 8 * min(c, n_chunks - 1));
+  float wq[8];
 #pragma unroll
-    for (int d = lane; d < HD; d += 64) {
-      const float x = xr[h * HD + d];
-      ss += x * x;
+  for (int i = 0; i < 8; ++i) wq[i] = qw[d0 + i];
+  __builtin_amdgcn_sched_barrier(0);
+  if (tid < SL) {  // the row's rotation angles, while the loads are in flight
+    const double pos = (double)first_pos + (double)r;
+    for (int i = tid; i < half; i += SL) {
+      const double inv_freq = pow((double)theta, -2.0 * (double)i / (double)rot);
+      double sn, cn;
+      rope_cos_sin(pos * inv_freq, cn, sn);
+      cs[2 * i] = cn;
+      cs[2 * i + 1] = sn;
     }
-    ss = wave_sum(ss);
-    if (lane == 0) hinv[h] = 1.0f / sqrtf(ss / (float)HD + eps);
+  }
+  float x[8], ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(v[i] << 16);
+    x[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
+#pragma unroll
+  for (int off = 1; off < CG; off <<= 1) ss += __shfl_xor(ss, off);
+  const float hv = 1.0f / sqrtf(ss / (float)HD + eps);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = x[i] * hv * (1.0f + wq[i]);
+  if (mine) {
+    float* xd = xs + 8 * tid;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xd[i] = x[i];
   }
   __syncthreads();
-  OutT* dst = out + (int64_t)r * n;
-  for (int e = tid; e < n; e += kQprepThreads) {
-    const int h = e / HD, d = e % HD;
-    const float hv = hinv[h];
-    auto norm = [&](int dd) -> float { return xr[h * HD + dd] * hv * (1.0f + qw[dd]); };
-    float o;
+  if (!mine) return;
+  const float* xh = xs + (tid / CG) * HD;  // this thread's head in the slice
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int d = d0 + i;
     if (d < half) {
-      const double a = norm(d), bb = norm(d + half);
-      o = (float)(a * cs[2 * d] - bb * cs[2 * d + 1]);
+      const double a = x[i], bb = xh[d + half];
+      o[i] = (float)(a * cs[2 * d] - bb * cs[2 * d + 1]);
     } else if (d < rot) {
-      const double a = norm(d - half), bb = norm(d);
-      o = (float)(a * cs[2 * (d - half) + 1] + bb * cs[2 * (d - half)]);
+      const double a = xh[d - half], bb = x[i];
+      o[i] = (float)(a * cs[2 * (d - half) + 1] + bb * cs[2 * (d - half)]);
     } else {
-      o = norm(d);
+      o[i] = x[i];
     }
-    dst[e] = (OutT)o;  // fp16 storage: rounded to nearest even
+  }
+  OutT* dc = out + (int64_t)r * n_chunks * 8 + 8 * c;
+  if constexpr (sizeof(OutT) == 4) {
+    *reinterpret_cast<float4v*>(dc) = float4v{o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<float4v*>(dc + 4) = float4v{o[4], o[5], o[6], o[7]};
+  } else {  // fp16 storage: each fp32 result rounded to nearest even
+    half8v h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = (_Float16)o[i];
+    *reinterpret_cast<half8v*>(dc) = h;
   }
 }
 
-template <int HD, typename OutT>
-__global__ __launch_bounds__(kQprepThreads) void qprep_rows_kernel(const uint16_t* __restrict__ qk,
-                                                                   const float* __restrict__ qw,
-                                                                   OutT* __restrict__ out, uint32_t first_pos,
-                                                                   uint32_t qkw, uint32_t n_heads, int rot,
-                                                                   float theta, float eps) {
+// One (row, slice) per workgroup of SL threads: workgroup g takes row g / n_slices.
+template <int HD, typename OutT, int SL>
+__global__ __launch_bounds__(SL) void qprep_rows_kernel(const uint16_t* __restrict__ qk,
+                                                        const float* __restrict__ qw, OutT* __restrict__ out,
+                                                        uint32_t first_pos, uint32_t qkw, uint32_t n_heads,
+                                                        uint32_t n_slices, int rot, float theta, float eps) {
   extern __shared__ __align__(16) unsigned char smem[];
-  qprep_row<HD, OutT>(qk, qw, out, blockIdx.x, first_pos, qkw, n_heads, rot, theta, eps, smem);
+  qprep_slice<HD, OutT, SL>(qk, qw, out, blockIdx.x / n_slices, blockIdx.x % n_slices, first_pos, qkw, n_heads, rot,
+                            theta, eps, threadIdx.x, smem);
 }
 
-// A decode step's inputs in one launch: workgroups [0, rows) prepare the query rows;
-// the others pool the new blocks, four 256-thread groups each (the same arithmetic as
-// qprep_rows_kernel and block_pool_kernel, so the outputs are bit-identical to theirs).
+// A decode step's inputs in one launch: workgroups [0, rows n_slices) prepare the query
+// rows, kQprepDecodeSlice chunks each; the others pool the new blocks, one 256-thread
+// group each (the same arithmetic as qprep_rows_kernel and block_pool_kernel, so the
+// outputs are bit-identical to theirs).
+constexpr int kQprepDecodeSlice = 128;
+
 template <int HD>
-__global__ __launch_bounds__(kQprepThreads) void decode_prep_kernel(
+__global__ __launch_bounds__(256) void decode_prep_kernel(
     const uint16_t* __restrict__ raw, const float* __restrict__ kw, float* __restrict__ block_keys,
     uint32_t first_block, uint32_t n_new, uint32_t ratio, const uint16_t* __restrict__ qk,
-    const float* __restrict__ qw, float* __restrict__ q_out, uint32_t rows, uint32_t first_pos, uint32_t qkw,
-    uint32_t n_heads, int rot, float theta, float eps) {
+    const float* __restrict__ qw, float* __restrict__ q_out, uint32_t rows, uint32_t n_slices, uint32_t first_pos,
+    uint32_t qkw, uint32_t n_heads, int rot, float theta, float eps) {
   extern __shared__ __align__(16) unsigned char smem[];
-  if (blockIdx.x < rows) {  // uniform over the workgroup
-    qprep_row<HD, float>(qk, qw, q_out, blockIdx.x, first_pos, qkw, n_heads, rot, theta, eps, smem);
+  const uint32_t n_q = rows * n_slices;
+  if (blockIdx.x < n_q) {  // uniform over the workgroup
+    qprep_slice<HD, float, kQprepDecodeSlice>(qk, qw, q_out, blockIdx.x / n_slices, blockIdx.x % n_slices,
+                                              first_pos, qkw, n_heads, rot, theta, eps, threadIdx.x, smem);
     return;
   }
-  constexpr int kGroups = kQprepThreads / 256;
-  const int g = threadIdx.x / 256;
-  PoolLds<HD>* lds = reinterpret_cast<PoolLds<HD>*>(smem) + g;
-  pool_group<HD, float>(raw, kw, block_keys, first_block, n_new, ratio, rot, theta, eps,
-                        (blockIdx.x - rows) * kGroups + g, threadIdx.x % 256, *lds);
+  pool_group<HD, float>(raw, kw, block_keys, first_block, n_new, ratio, rot, theta, eps, blockIdx.x - n_q,
+                        threadIdx.x, *reinterpret_cast<PoolLds<HD>*>(smem));
 }
 
 // ------------------------------------------------------------------ row scores (fp32)
@@ -670,24 +709,20 @@ hipError_t launch_block_pool(const uint16_t* raw, const float* kw, OutT* out, ui
   return hipGetLastError();
 }
 
-size_t qprep_lds_bytes(uint32_t n_heads, uint32_t hd) {
-  return (size_t)4 * n_heads * hd + (size_t)4 * ((n_heads + 3) & ~3u) + (size_t)8 * hd;
-}
+static size_t qprep_lds_bytes(uint32_t slice, uint32_t hd) { return (size_t)32 * slice + (size_t)8 * hd; }
 
 template <int HD>
 static hipError_t launch_decode_prep_hd(const uint16_t* raw, const float* kw, float* block_keys, uint32_t first_block,
                                         uint32_t n_new, uint32_t ratio, const uint16_t* qk, const float* qw,
                                         float* q_out, uint32_t rows, uint32_t first_pos, uint32_t qkw,
                                         uint32_t n_heads, uint32_t rot, float theta, float eps, hipStream_t st) {
-  constexpr uint32_t kBlocksPerWg = (kQprepThreads / 256) * kPoolNBW;
-  const size_t pool_lds = (size_t)(kQprepThreads / 256) * sizeof(PoolLds<HD>);
-  const size_t q_lds = qprep_lds_bytes(n_heads, HD);
+  const uint32_t n_slices = (n_heads * (HD / 8) + kQprepDecodeSlice - 1) / kQprepDecodeSlice;
+  const size_t pool_lds = sizeof(PoolLds<HD>);
+  const size_t q_lds = qprep_lds_bytes(kQprepDecodeSlice, HD);
   const size_t lds = q_lds > pool_lds ? q_lds : pool_lds;
-  const hipError_t e = ensure_lds(reinterpret_cast<const void*>(decode_prep_kernel<HD>), lds);
-  if (e != hipSuccess) return e;
-  const uint32_t grid = rows + (n_new + kBlocksPerWg - 1) / kBlocksPerWg;
-  hipLaunchKernelGGL((decode_prep_kernel<HD>), dim3(grid), dim3(kQprepThreads), lds, st, raw, kw, block_keys,
-                     first_block, n_new, ratio, qk, qw, q_out, rows, first_pos, qkw, n_heads, (int)rot, theta, eps);
+  const uint32_t grid = rows * n_slices + (n_new + kPoolNBW - 1) / kPoolNBW;
+  hipLaunchKernelGGL((decode_prep_kernel<HD>), dim3(grid), dim3(256), lds, st, raw, kw, block_keys, first_block, n_new,
+                     ratio, qk, qw, q_out, rows, n_slices, first_pos, qkw, n_heads, (int)rot, theta, eps);
   return hipGetLastError();
 }
 
@@ -708,30 +743,39 @@ hipError_t launch_decode_prep(const uint16_t* raw, const float* kw, float* block
   }
 }
 
+// Slices of 256 chunks when the rows alone fill the chip several times over, else of 128
+// (a short decode batch spreads over more CUs).
+template <int HD, typename OutT>
+static hipError_t launch_qprep_rows_hd(const uint16_t* qk, const float* qw, OutT* out, uint32_t rows,
+                                       uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t rot, float theta,
+                                       float eps, hipStream_t st) {
+  const uint32_t n_chunks = n_heads * (HD / 8);
+  if ((uint64_t)rows * ((n_chunks + 255) / 256) >= 1024) {
+    const uint32_t n_slices = (n_chunks + 255) / 256;
+    hipLaunchKernelGGL((qprep_rows_kernel<HD, OutT, 256>), dim3(rows * n_slices), dim3(256),
+                       qprep_lds_bytes(256, HD), st, qk, qw, out, first_pos, qkw, n_heads, n_slices, (int)rot, theta,
+                       eps);
+  } else {
+    const uint32_t n_slices = (n_chunks + 127) / 128;
+    hipLaunchKernelGGL((qprep_rows_kernel<HD, OutT, 128>), dim3(rows * n_slices), dim3(128),
+                       qprep_lds_bytes(128, HD), st, qk, qw, out, first_pos, qkw, n_heads, n_slices, (int)rot, theta,
+                       eps);
+  }
+  return hipGetLastError();
+}
+
 template <typename OutT>
 hipError_t launch_qprep_rows(const uint16_t* qk, const float* qw, OutT* out, uint32_t rows,
                              uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t hd, uint32_t rot,
                              float theta, float eps, hipStream_t st) {
-  const size_t lds = qprep_lds_bytes(n_heads, hd);
-  hipError_t e;
   switch (hd) {
     case 64:
-      if ((e = ensure_lds(reinterpret_cast<const void*>(qprep_rows_kernel<64, OutT>), lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL((qprep_rows_kernel<64, OutT>), dim3(rows), dim3(kQprepThreads), lds, st, qk, qw, out, first_pos,
-                         qkw, n_heads, (int)rot, theta, eps);
-      break;
+      return launch_qprep_rows_hd<64, OutT>(qk, qw, out, rows, first_pos, qkw, n_heads, rot, theta, eps, st);
     case 128:
-      if ((e = ensure_lds(reinterpret_cast<const void*>(qprep_rows_kernel<128, OutT>), lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL((qprep_rows_kernel<128, OutT>), dim3(rows), dim3(kQprepThreads), lds, st, qk, qw, out, first_pos,
-                         qkw, n_heads, (int)rot, theta, eps);
-      break;
+      return launch_qprep_rows_hd<128, OutT>(qk, qw, out, rows, first_pos, qkw, n_heads, rot, theta, eps, st);
     default:
-      if ((e = ensure_lds(reinterpret_cast<const void*>(qprep_rows_kernel<256, OutT>), lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL((qprep_rows_kernel<256, OutT>), dim3(rows), dim3(kQprepThreads), lds, st, qk, qw, out, first_pos,
-                         qkw, n_heads, (int)rot, theta, eps);
-      break;
+      return launch_qprep_rows_hd<256, OutT>(qk, qw, out, rows, first_pos, qkw, n_heads, rot, theta, eps, st);
   }
-  return hipGetLastError();
 }
 
 template <int HD, int NH, typename InT>

@@ -9,6 +9,7 @@ import sparse_attention_lightning_block_amd as salb
 from oracle import indexer, qsa
 from tests.parity import MFMA_ROWMAX, check_topk
 from workloads import make
+from workloads.configs import qsa as qsa_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +87,56 @@ def test_qprep_rows_reduced():
     ref = qsa.qprep_rows(indexer.upcast(w.qk, "bf16"), w.q_norm_w, w.rows, w.first_pos, w.n_heads * w.hd, w.n_heads,
                          w.hd, w.rot, w.theta, w.eps)
     _check_vectors(q, ref, "qprep")
+
+
+# (n_heads, hd, rot, ratio, rows, qkw padding, first_pos): every head size, rotations
+# narrower than hd and none, odd ratios, head counts that leave a slice of the query
+# prep partly empty, and enough rows for both slice widths (256 chunks once the rows
+# fill 1024 workgroups, else 128)
+_SHAPES = [
+    (3, 64, 64, 4, 5, 8, 17),
+    (5, 256, 128, 7, 9, 0, 500000),
+    (1, 128, 0, 16, 3, 0, 40),
+    (64, 128, 96, 3, 300, 0, 262000),
+    (40, 64, 62, 16, 7, 16, 123457),
+    (24, 128, 128, 2, 2000, 0, 9),
+]
+
+
+@pytest.mark.parametrize("n_heads,hd,rot,ratio,rows,pad,first_pos", _SHAPES)
+def test_pool_and_qprep_shapes(n_heads, hd, rot, ratio, rows, pad, first_pos):
+    """Block pool and query prep against the oracle over head sizes, rotation widths and
+    slicings; projection rows padded with NaN bits (a read past n_heads * hd shows); the
+    one-launch decode prep and the fp16 outputs bit-identical to the fp32 calls."""
+    nb = 37
+    w = qsa_workload("qsa_shapes", [11, n_heads, hd, rows], n_tok=nb * ratio, hd=hd, ratio=ratio, rows=rows,
+                     n_heads=n_heads, top_k=1, rot=rot, first_pos=first_pos)
+    qk_bits = np.concatenate([w.qk, np.full((rows, pad), 0x7FC0, dtype=np.uint16)], axis=1)
+    raw, kw = _bf16(w.raw_keys).cuda(), torch.from_numpy(w.k_norm_w).cuda()
+    qk, qw = _bf16(qk_bits).cuda(), torch.from_numpy(w.q_norm_w).cuda()
+    kwargs = dict(ratio=ratio, rot=rot, theta=w.theta, eps=w.eps)
+    keys = torch.full((nb, hd), 7.0, dtype=torch.float32, device="cuda")
+    salb.qsa_block_pool(raw, kw, keys, first_block=2, n_new=nb - 2, **kwargs)
+    q = salb.qsa_qprep_rows(qk, qw, n_heads=n_heads, hd=hd, first_pos=first_pos, rot=rot, theta=w.theta, eps=w.eps)
+    got_keys, got_q = keys.cpu().numpy(), q.cpu().numpy()
+    assert np.all(got_keys[:2] == 7.0)
+    ref_keys = qsa.block_pool(indexer.upcast(w.raw_keys, "bf16"), w.k_norm_w, 2, nb - 2, ratio, rot, w.theta, w.eps)
+    _check_vectors(got_keys[2:], ref_keys, "block pool")
+    ref_q = qsa.qprep_rows(indexer.upcast(qk_bits, "bf16"), w.q_norm_w, rows, first_pos, n_heads * hd + pad,
+                           n_heads, hd, rot, w.theta, w.eps)
+    _check_vectors(got_q, ref_q, "qprep")
+    # the fused decode prep and the fp16 outputs give the same bits
+    keys2 = torch.full((nb, hd), 7.0, dtype=torch.float32, device="cuda")
+    q2 = salb.qsa_decode_prep(raw, kw, keys2, qk, qw, first_block=2, n_new=nb - 2, n_heads=n_heads, hd=hd,
+                              first_pos=first_pos, **kwargs)
+    assert torch.equal(keys2.view(torch.int32), keys.view(torch.int32))
+    assert torch.equal(q2.view(torch.int32), q.view(torch.int32))
+    keys16 = torch.zeros((nb, hd), dtype=torch.float16, device="cuda")
+    salb.qsa_block_pool(raw, kw, keys16, first_block=2, n_new=nb - 2, **kwargs)
+    q16 = salb.qsa_qprep_rows(qk, qw, n_heads=n_heads, hd=hd, first_pos=first_pos, rot=rot, theta=w.theta,
+                              eps=w.eps, dtype=torch.float16)
+    assert torch.equal(keys16[2:].view(torch.int16), keys[2:].half().view(torch.int16))
+    assert torch.equal(q16.view(torch.int16), q.half().view(torch.int16))
 
 
 @pytest.mark.parametrize("first_block,n_new,rows", [(100, 1, 1), (3, 45, 7), (0, 0, 2), (60, 33, 1)])
