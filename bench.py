@@ -72,7 +72,8 @@ SCORER_TRAFFIC = {   # workload: (sources, sha, FETCH_SIZE KiB, WRITE_SIZE KiB p
     "decode_T8_S65536": ("csa", "52f41720cf47e45b", 3551.8, 2048.0),
     "long_decode_T32_S262144": ("csa", "52f41720cf47e45b", 33768.6, 32776.0),
     "prefill_T4096": ("csa", "52f41720cf47e45b", 35446.6, 65690.5),
-    "qsa_prefill": ("qsa", "e78330d1767c1a9e", 81962.3, 262424.1),
+    "qsa_prefill": ("qsa", "26fe8f199fe8fcff", 81962.3, 262424.1),
+    "qsa_decode": ("qsa", "26fe8f199fe8fcff", 8278.0, 230.9),
     "hbm_true_T32_S262144": ("csa", "52f41720cf47e45b", 229531.4, 32776.1),
 }
 
@@ -401,7 +402,8 @@ def run_qsa_decode(args):
         "stage_ms": {"prep_one_launch": fused_ms, "score_topk": st_ms, "score_alone": score_ms,
                      "select_alone": select_ms, "pool_one_block_alone": pool_ms, "qprep_alone": prep_ms},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "qsa_decode_score_kernel",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": scorer_traffic("qsa_decode"),
+                     "kernel": "qsa_decode_score_mfma_kernel",
                      "kernel_avg_us": round(score_ms * 1e3, 2), "bytes_per_launch": int(key_bytes),
                      "flops_per_launch": int(2 * nb * w.n_heads * w.hd)},
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_qsa_decode(w, r, pos, nb),

@@ -181,13 +181,13 @@ def test_topk_select_exact(n_cols, k):
         assert np.array_equal(gv[r][:kk], o_val[:kk].astype(np.float32))
 
 
-@pytest.mark.parametrize("n_cols,k", [(12000, 256), (30000, 256), (32768, 2048), (20000, 1)])
+@pytest.mark.parametrize("n_cols,k", [(12000, 256), (30000, 256), (32768, 2048), (20000, 1), (32768, 512)])
 def test_topk_select_many_long_rows(n_cols, k):
     """Many rows (one workgroup per row: 1024 threads with 16 entries each in registers up
     to 16384 columns, 512 threads with 64 each up to 32768; a row of one repeated value
     overflows the candidate list and takes the radix passes over the row): exact against
-    the oracle on sampled rows, with ties, empty rows, rows shorter than k and full rows;
-    set rules on every row."""
+    the oracle on sampled rows, with ties, empty rows, rows shorter than k, a row of
+    k + 1 entries and full rows; set rules on every row."""
     rng = np.random.default_rng(n_cols + 7 * k)
     rows = 300
     s = rng.standard_normal((rows, n_cols)).astype(np.float32)
@@ -197,7 +197,7 @@ def test_topk_select_many_long_rows(n_cols, k):
     s[3, ::3] = -np.inf
     valid = rng.integers(0, n_cols + 1, rows).astype(np.int32)
     valid[:4] = n_cols
-    valid[4], valid[5], valid[6] = 0, max(0, k - 3), k
+    valid[4], valid[5], valid[6], valid[7] = 0, max(0, k - 3), k, k + 1
     idx, val = salb.indexer_topk_select(torch.from_numpy(s).cuda(), k, valid_lens=torch.from_numpy(valid).cuda(),
                                         with_scores=True)
     gi, gv = _row(idx), _row(val)
