@@ -42,6 +42,7 @@
 namespace salb {
 
 constexpr int kDigit = 12;
+constexpr int kRankSortMax = 64;  // winners sorted by a plain rank count up to this many
 constexpr int kBins = 1 << kDigit;       // 4096 histogram bins
 constexpr int kTopShift = 64 - kDigit;   // first digit: the score's top 12 order bits
 constexpr int kRowThreads = 256;         // one-workgroup rows
@@ -337,8 +338,10 @@ __device__ __forceinline__ int pow2_at_least(int x) {
 
 // Sorts the K winners in sortbuf[0, K) (capacity pow2_at_least(K)) and writes the
 // row's output: K indices (and scores) in selection order, then -1 (and -inf) up
-// to top_k.  mx and mn are the largest and smallest winner; grp holds K entries;
-// hist holds kBins + 4 counters.
+// to top_k.  Up to kRankSortMax winners each find their place by counting the larger
+// ones; more are bucketed by their top bits and ranked within the bucket (a sorting
+// network when a bucket is crowded).  mx and mn are the largest and smallest winner;
+// grp holds K entries; hist holds kBins + 4 counters.  The kernel ends after it.
 template <int NT>
 __device__ void finish_row(uint64_t* sortbuf, uint64_t* grp, uint32_t* hist, int K, int top_k, int32_t* oi,
                            float* os, uint64_t mx, uint64_t mn, SelShared& sh, uint32_t kbase = 0u) {
@@ -353,6 +356,22 @@ __device__ void finish_row(uint64_t* sortbuf, uint64_t* grp, uint32_t* hist, int
       const uint64_t c = sortbuf[0];
       oi[0] = (int32_t)(~(uint32_t)c);
       if (os) os[0] = ord_to_float((uint32_t)(c >> 32) + kbase);
+    }
+    return;
+  }
+  if (K <= kRankSortMax) {
+    // Few winners: each one's place is the count of larger winners (composites are
+    // distinct), read with broadcast LDS loads -- one pass, no barrier or atomic.
+    for (int i = tid; i < K; i += NT) {
+      const uint64_t c = sortbuf[i];
+      uint32_t r = 0;
+      int j = 0;
+      for (; j + 4 <= K; j += 4)
+        r += (uint32_t)(sortbuf[j] > c) + (uint32_t)(sortbuf[j + 1] > c) + (uint32_t)(sortbuf[j + 2] > c) +
+             (uint32_t)(sortbuf[j + 3] > c);
+      for (; j < K; ++j) r += (uint32_t)(sortbuf[j] > c);
+      oi[r] = (int32_t)(~(uint32_t)c);
+      if (os) os[r] = ord_to_float((uint32_t)(c >> 32) + kbase);
     }
     return;
   }
