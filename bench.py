@@ -61,20 +61,21 @@ COLD_SPAN_BYTES = 2 * 256 * 2**20
 
 
 # HBM traffic of one scorer launch, from two rocprofv3 --pmc passes (FETCH_SIZE, then
-# WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for a plain
+# WRITE_SIZE, KiB per dispatch of the split entry's scorer, the launch the roofline
+# times) scaled by what the same counters read for a plain
 # 256 MiB copy (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0); the summaries are under
 # profiles/.  Valid only for the scorer sources they were taken with: a different
 # source hash reports null.
 TRAFFIC_COPY_FACTOR = {"FETCH_SIZE": 1.9998, "WRITE_SIZE": 1.0}
 SCORER_SOURCES = {"csa": ['score.hip', 'nvfp4.hpp', 'common.hpp', 'internal.hpp'], "qsa": ['qsa.hip', 'common.hpp', 'internal.hpp']}
 SCORER_TRAFFIC = {   # workload: (sources, sha, FETCH_SIZE KiB, WRITE_SIZE KiB per dispatch)
-    "tiny_decode": ("csa", "52f41720cf47e45b", 81.7, 16.0),
-    "decode_T8_S65536": ("csa", "52f41720cf47e45b", 3551.8, 2048.0),
-    "long_decode_T32_S262144": ("csa", "52f41720cf47e45b", 33768.6, 32776.0),
-    "prefill_T4096": ("csa", "52f41720cf47e45b", 35446.6, 65690.5),
-    "qsa_prefill": ("qsa", "26fe8f199fe8fcff", 81962.3, 262424.1),
-    "qsa_decode": ("qsa", "26fe8f199fe8fcff", 8278.0, 230.9),
-    "hbm_true_T32_S262144": ("csa", "52f41720cf47e45b", 229531.4, 32776.1),
+    "tiny_decode": ("csa", "2dba759cfc17e677", 81.7, 16.0),
+    "decode_T8_S65536": ("csa", "2dba759cfc17e677", 3552.0, 2048.0),
+    "long_decode_T32_S262144": ("csa", "2dba759cfc17e677", 33760.1, 32776.0),
+    "prefill_T4096": ("csa", "2dba759cfc17e677", 35446.6, 65690.6),
+    "qsa_prefill": ("qsa", "5e1f6904c0c9ea7b", 81958.7, 262424.2),
+    "qsa_decode": ("qsa", "5e1f6904c0c9ea7b", 8280.0, 231.3),
+    "hbm_true_T32_S262144": ("csa", "2dba759cfc17e677", 229531.2, 32776.1),
 }
 
 
