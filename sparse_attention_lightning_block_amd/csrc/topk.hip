@@ -566,8 +566,9 @@ __global__ __launch_bounds__(NT, (NT == kRowThreads && PER <= 16) ? 5 : 1) void 
 
 // Rows of up to 32768 entries when there are many (one 512-thread workgroup per row,
 // longest rows first, several workgroups per CU so that one's loads overlap another's
-// passes).  The row stays in registers as order keys (entry i NT + t in register i of
-// thread t, 64 per thread, coalesced loads).  Its range comes from one wave and block
+// passes).  The row stays in registers as order keys (64 per thread, coalesced loads:
+// four consecutive entries per 16-byte load where the row's alignment allows, else
+// entry i NT + t in register i of thread t).  Its range comes from one wave and block
 // reduction; one histogram pass over a 12-bit digit of the key relative to the row's
 // smallest (the digit spans the row's actual range) finds the bin of the K-th entry;
 // the entries from that bin up -- K plus the rest of the bin -- are compacted into an
@@ -575,9 +576,16 @@ __global__ __launch_bounds__(NT, (NT == kRowThreads && PER <= 16) ? 5 : 1) void 
 // rank in the wave's ballot), where the radix select finishes and the winners are
 // gathered.  A bin crowded past the list's capacity falls back to radix passes over
 // the row read again from memory.
-template <int NT>
+// VEC: each lane reads four consecutive entries per 16-byte load, register i of thread t
+// holding entry 4 ((i / 4) NT + t) + i % 4 (a quarter of the load instructions); only
+// for 16-byte aligned rows whose stride and n_cols are multiples of 4, so that every
+// vector lies inside its row.
+template <int NT, bool VEC>
 __global__ __launch_bounds__(NT) void select_rows_reg_kernel(SelArgs a, int rows) {
   constexpr int PF = kRowMaxWide / NT;  // a row's entries per thread
+  // entry of register i, and the first entry any thread holds in register i
+  auto ent = [&](int i) { return VEC ? 4 * ((i >> 2) * NT + (int)threadIdx.x) + (i & 3) : i * NT + (int)threadIdx.x; };
+  auto ent0 = [](int i) { return VEC ? 4 * (i >> 2) * NT : i * NT; };
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ SelShared sh;
   __shared__ uint32_t s_kmx[NT / kWave], s_kmn[NT / kWave];
@@ -592,13 +600,22 @@ __global__ __launch_bounds__(NT) void select_rows_reg_kernel(SelArgs a, int rows
   uint32_t key[PF];
   {
     const int last = n > 0 ? n - 1 : 0;  // past the valid entries: re-read valid memory
+    if constexpr (VEC) {
 #pragma unroll
-    for (int i = 0; i < PF; ++i) key[i] = ord_key(src[min(i * NT + tid, last)]);
+      for (int j = 0; j < PF / 4; ++j) {
+        const float4v v = *reinterpret_cast<const float4v*>(src + 4 * min(j * NT + tid, last >> 2));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) key[4 * j + q] = ord_key(v[q]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PF; ++i) key[i] = ord_key(src[min(i * NT + tid, last)]);
+    }
   }
   uint32_t kmx = 0u, kmn = ~0u;
 #pragma unroll
   for (int i = 0; i < PF; ++i) {
-    const bool v = i * NT + tid < n;
+    const bool v = ent(i) < n;
     kmx = v && key[i] > kmx ? key[i] : kmx;
     kmn = v && key[i] < kmn ? key[i] : kmn;
   }
@@ -635,8 +652,8 @@ __global__ __launch_bounds__(NT) void select_rows_reg_kernel(SelArgs a, int rows
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      if (i * NT >= n) break;
-      if (i * NT + tid < n) atomicAdd(&f.hist[(key[i] - kbase) >> shift], 1u);
+      if (ent0(i) >= n) break;
+      if (ent(i) < n) atomicAdd(&f.hist[(key[i] - kbase) >> shift], 1u);
     }
     __syncthreads();
     uint32_t h[kBins / NT];
@@ -648,8 +665,8 @@ __global__ __launch_bounds__(NT) void select_rows_reg_kernel(SelArgs a, int rows
       const uint32_t kthr = kbase + (b1 << shift);  // smallest key of bin b1
 #pragma unroll
       for (int i = 0; i < PF; ++i) {
-        if (i * NT >= n) break;
-        const int e = i * NT + tid;
+        if (ent0(i) >= n) break;
+        const int e = ent(i);
         const bool pick = e < n && key[i] >= kthr;
         const uint64_t m = __ballot(pick);
         if (m != 0ull) {
@@ -1038,9 +1055,13 @@ static hipError_t launch_rows(const SelArgs& a, const SelectPlan& p, hipStream_t
 
 template <int NT>
 static hipError_t launch_rows_reg(const SelArgs& a, const SelectPlan& p, hipStream_t st) {
-  hipError_t e = set_lds(select_rows_reg_kernel<NT>, p.lds);
+  const bool vec = a.score_stride % 4 == 0 && a.n_cols % 4 == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
+  hipError_t e = vec ? set_lds(select_rows_reg_kernel<NT, true>, p.lds) : set_lds(select_rows_reg_kernel<NT, false>, p.lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((select_rows_reg_kernel<NT>), dim3(p.rows), dim3(NT), p.lds, st, a, p.rows);
+  if (vec)
+    hipLaunchKernelGGL((select_rows_reg_kernel<NT, true>), dim3(p.rows), dim3(NT), p.lds, st, a, p.rows);
+  else
+    hipLaunchKernelGGL((select_rows_reg_kernel<NT, false>), dim3(p.rows), dim3(NT), p.lds, st, a, p.rows);
   return hipGetLastError();
 }
 

@@ -181,7 +181,7 @@ def test_topk_select_exact(n_cols, k):
         assert np.array_equal(gv[r][:kk], o_val[:kk].astype(np.float32))
 
 
-@pytest.mark.parametrize("n_cols,k", [(12000, 256), (30000, 256), (32768, 2048), (20000, 1), (32768, 512)])
+@pytest.mark.parametrize("n_cols,k", [(12000, 256), (30000, 256), (30002, 256), (32768, 2048), (20000, 1), (32768, 512)])
 def test_topk_select_many_long_rows(n_cols, k):
     """Many rows (one workgroup per row: 1024 threads with 16 entries each in registers up
     to 16384 columns, 512 threads with 64 each up to 32768; a row of one repeated value
