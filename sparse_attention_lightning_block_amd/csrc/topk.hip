@@ -463,9 +463,17 @@ __device__ __forceinline__ FinishLds carve(unsigned char* smem, int top_k) {
 
 // ------------------------------------------------------------------ short rows
 
+// Whether a row select may read its rows with 16-byte loads of four consecutive entries:
+// rows 16-byte aligned, stride and n_cols multiples of 4 (every vector then lies inside
+// its row).
+__host__ __forceinline__ bool rows_vec_ok(const SelArgs& a) {
+  return a.score_stride % 4 == 0 && a.n_cols % 4 == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
+}
+
 // One workgroup per row; entry e of the row sits in register i of thread t with
-// e = i * NT + t (coalesced loads).
-template <int NT, int PER>
+// e = i * NT + t, or with VEC (16-byte loads, a quarter of the load instructions)
+// e = 4 ((i / 4) NT + t) + i % 4.  Coalesced loads either way.
+template <int NT, int PER, bool VEC>
 __global__ __launch_bounds__(NT, (NT == kRowThreads && PER <= 16) ? 5 : 1) void select_rows_kernel(SelArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ SelShared sh;
@@ -476,19 +484,34 @@ __global__ __launch_bounds__(NT, (NT == kRowThreads && PER <= 16) ? 5 : 1) void 
   const float* src = a.scores + (int64_t)row * a.score_stride;
   FinishLds f = carve(smem, a.top_k);
 
+  // entry of register i, and the first entry any thread holds in register i
+  auto ent = [&](int i) { return VEC ? 4 * ((i >> 2) * NT + tid) + (i & 3) : i * NT + tid; };
+  auto ent0 = [](int i) { return VEC ? 4 * (i >> 2) * NT : i * NT; };
   uint32_t key[PER];
+  if constexpr (VEC) {
+    static_assert(PER % 4 == 0, "vector rows");
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = i * NT + tid;
-    key[i] = e < n ? ord_key(src[e]) : 0u;
+    for (int j = 0; j < PER / 4; ++j) {
+      const int v = j * NT + tid;
+      float4v x = {0.f, 0.f, 0.f, 0.f};
+      if (4 * v < n) x = *reinterpret_cast<const float4v*>(src + 4 * v);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) key[4 * j + q] = 4 * v + q < n ? ord_key(x[q]) : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = i * NT + tid;
+      key[i] = e < n ? ord_key(src[e]) : 0u;
+    }
   }
   // registers past the row's last entry are skipped on a wave-uniform branch: a short
   // row costs passes over its own length, not over the workgroup's capacity
   auto each_key = [&](auto&& fn) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      if (i * NT >= n) break;
-      const int e = i * NT + tid;
+      if (ent0(i) >= n) break;
+      const int e = ent(i);
       if (e < n) fn(key[i], e);
     }
   };
@@ -1047,15 +1070,19 @@ static hipError_t set_lds(K kernel, size_t bytes) {
 
 template <int NT, int PER>
 static hipError_t launch_rows(const SelArgs& a, const SelectPlan& p, hipStream_t st) {
-  hipError_t e = set_lds(select_rows_kernel<NT, PER>, p.lds);
+  const bool vec = rows_vec_ok(a);
+  hipError_t e = vec ? set_lds(select_rows_kernel<NT, PER, true>, p.lds) : set_lds(select_rows_kernel<NT, PER, false>, p.lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((select_rows_kernel<NT, PER>), dim3(p.rows), dim3(NT), p.lds, st, a);
+  if (vec)
+    hipLaunchKernelGGL((select_rows_kernel<NT, PER, true>), dim3(p.rows), dim3(NT), p.lds, st, a);
+  else
+    hipLaunchKernelGGL((select_rows_kernel<NT, PER, false>), dim3(p.rows), dim3(NT), p.lds, st, a);
   return hipGetLastError();
 }
 
 template <int NT>
 static hipError_t launch_rows_reg(const SelArgs& a, const SelectPlan& p, hipStream_t st) {
-  const bool vec = a.score_stride % 4 == 0 && a.n_cols % 4 == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
+  const bool vec = rows_vec_ok(a);
   hipError_t e = vec ? set_lds(select_rows_reg_kernel<NT, true>, p.lds) : set_lds(select_rows_reg_kernel<NT, false>, p.lds);
   if (e != hipSuccess) return e;
   if (vec)
