@@ -741,11 +741,42 @@ __global__ __launch_bounds__(NT) void select_rows_reg_kernel(SelArgs a, int rows
 
 // ------------------------------------------------------------------ long rows
 
+// A chunk's PER entries per thread from lo on, as order keys (0 past n): entry
+// lo + i NT + t in register i of thread t, or with VEC (16-byte loads of four
+// consecutive entries, a quarter of the load instructions) lo + 4 ((i / 4) NT + t) + i % 4.
+template <int PER, bool VEC>
+__device__ __forceinline__ int chunk_ent(int lo, int i) {
+  constexpr int NT = kChunkThreads;
+  return VEC ? lo + 4 * ((i >> 2) * NT + (int)threadIdx.x) + (i & 3) : lo + i * NT + (int)threadIdx.x;
+}
+
+template <int PER, bool VEC>
+__device__ __forceinline__ void load_chunk(const float* src, int lo, int n, uint32_t (&key)[PER]) {
+  constexpr int NT = kChunkThreads;
+  if constexpr (VEC) {
+    static_assert(PER % 4 == 0, "vector chunks");
+#pragma unroll
+    for (int j = 0; j < PER / 4; ++j) {
+      const int e0 = lo + 4 * (j * NT + (int)threadIdx.x);
+      float4v x = {0.f, 0.f, 0.f, 0.f};
+      if (e0 < n) x = *reinterpret_cast<const float4v*>(src + e0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) key[4 * j + q] = e0 + q < n ? ord_key(x[q]) : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lo + i * NT + (int)threadIdx.x;
+      key[i] = e < n ? ord_key(src[e]) : 0u;
+    }
+  }
+}
+
 // Stage 1: the chunk's histogram of the top 12 order-key bits, added into the
 // global copy of the XCD the workgroup runs on (workgroups are dealt to the eight
 // XCDs round robin by linear index), and the chunk's highest bin into that copy's
 // row maximum.
-template <int PER>
+template <int PER, bool VEC>
 __global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelArgs a) {
   constexpr int NT = kChunkThreads;
   __shared__ __align__(16) uint32_t hist[kBins];
@@ -756,21 +787,17 @@ __global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelArgs a) {
   const int lo = blockIdx.x * (PER * NT);
   if (lo >= n) return;
   const float* src = a.scores + (int64_t)row * a.score_stride;
-  float x[PER];  // every load in flight before the first LDS atomic
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lo + i * NT + tid;
-    x[i] = e < n ? src[e] : 0.0f;
-  }
+  uint32_t key[PER];  // every load in flight before the first LDS atomic
+  load_chunk<PER, VEC>(src, lo, n, key);
   clear_bins<NT>(hist);
   if (tid == 0) top_bin = 0u;
   __syncthreads();
   uint32_t mk = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int e = lo + i * NT + tid;
+    const int e = chunk_ent<PER, VEC>(lo, i);
     if (e < n) {
-      const uint32_t b = ord_key(x[i]) >> (32 - kDigit);
+      const uint32_t b = key[i] >> (32 - kDigit);
       atomicAdd(&hist[b], 1u);
       mk = b > mk ? b : mk;
     }
@@ -796,7 +823,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelArgs a) {
 // candidate slots (their order does not matter: the composites are ordered later)
 // and the chunk's count to ccount.  The first chunk of the row also records the
 // bin for the last stage.
-template <int PER>
+template <int PER, bool VEC>
 __global__ __launch_bounds__(kChunkThreads) void select_filter_kernel(SelArgs a) {
   constexpr int NT = kChunkThreads;
   __shared__ SelShared sh;
@@ -813,11 +840,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_filter_kernel(SelArgs a)
   // the chunk's scores are loaded first: their latency overlaps the search for the bin
   const float* src = a.scores + (int64_t)row * a.score_stride;
   uint32_t key[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lo + i * NT + tid;
-    key[i] = e < n ? ord_key(src[e]) : 0u;
-  }
+  load_chunk<PER, VEC>(src, lo, n, key);
   RowInfo info{0u, 0u, (uint32_t)n, 0u};  // K == n: every entry is a candidate
   if (K < n) {
     const uint32_t* gm = a.gmax + (int64_t)row * kHistCopies;
@@ -860,7 +883,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_filter_kernel(SelArgs a)
   uint32_t mine = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int e = lo + i * NT + tid;
+    const int e = chunk_ent<PER, VEC>(lo, i);
     mine += (e < n && (key[i] >> (32 - kDigit)) >= bin);
   }
   uint32_t pos = block_suffix<NT>(mine, sh);
@@ -868,7 +891,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_filter_kernel(SelArgs a)
   uint64_t* cd = a.cand + slot * (PER * NT);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int e = lo + i * NT + tid;
+    const int e = chunk_ent<PER, VEC>(lo, i);
     if (e < n && (key[i] >> (32 - kDigit)) >= bin && pos < (uint32_t)(PER * NT))
       cd[pos++] = composite(key[i], (uint32_t)e);
   }
@@ -1105,9 +1128,15 @@ static hipError_t launch_pipeline(const SelArgs& a, const SelectPlan& p, bool co
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const dim3 grid(p.chunks, p.rows);
-  hipLaunchKernelGGL(select_hist_kernel<PER>, grid, dim3(kChunkThreads), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(select_filter_kernel<PER>, grid, dim3(kChunkThreads), 0, st, a);
+  if (rows_vec_ok(a)) {
+    hipLaunchKernelGGL((select_hist_kernel<PER, true>), grid, dim3(kChunkThreads), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((select_filter_kernel<PER, true>), grid, dim3(kChunkThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((select_hist_kernel<PER, false>), grid, dim3(kChunkThreads), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((select_filter_kernel<PER, false>), grid, dim3(kChunkThreads), 0, st, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.final_nt == kFinalThreads)
     hipLaunchKernelGGL((select_final_kernel<kFinalThreads, kFinalPer>), dim3(p.rows), dim3(kFinalThreads), p.lds, st,
