@@ -215,6 +215,40 @@ def test_topk_select_many_long_rows(n_cols, k):
             assert np.all(s[r, : valid[r]][~sel] <= gv[r, kk - 1]), r
 
 
+@pytest.mark.parametrize("rows,n_cols,k", [(8, 4096, 512), (300, 12000, 256), (300, 30000, 256), (4, 65536, 2048)])
+def test_topk_select_unaligned_rows(rows, n_cols, k):
+    """Rows that start 4 bytes past a 16-byte boundary with a stride of n_cols + 3 (the
+    scalar-load kernels: short rows, wide rows, register rows, long-row pipeline) select
+    exactly what the aligned rows (16-byte loads) select, and match the oracle."""
+    rng = np.random.default_rng(rows + n_cols + k)
+    s = rng.standard_normal((rows, n_cols)).astype(np.float32)
+    s[0, ::5] = 0.75                                    # ties
+    valid = rng.integers(k // 2, n_cols + 1, rows).astype(np.int32)
+    valid[0] = n_cols
+    base = torch.zeros((rows, n_cols + 3), dtype=torch.float32, device="cuda")
+    base[:, 1:1 + n_cols] = torch.from_numpy(s).cuda()
+    view = base[:, 1:1 + n_cols]
+    assert view.data_ptr() % 16 == 4 and view.stride(0) == n_cols + 3
+    vl = torch.from_numpy(valid).cuda()
+    # the Python binding takes contiguous tensors only: the strided rows go through the C ABI
+    from sparse_attention_lightning_block_amd import _lib
+    lib = _lib.load()
+    ws_bytes = max(int(lib.indexer_topk_workspace_size(rows, n_cols, k)), 256)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    gi_u = torch.empty((rows, k), dtype=torch.int32, device="cuda")
+    gv_u = torch.empty((rows, k), dtype=torch.float32, device="cuda")
+    _lib.check(lib.indexer_topk_select(view.data_ptr(), view.stride(0), vl.data_ptr(), 0, 0, rows, n_cols, k,
+                                       gi_u.data_ptr(), gv_u.data_ptr(), ws.data_ptr(), ws_bytes,
+                                       torch.cuda.current_stream().cuda_stream))
+    gi_a, gv_a = salb.indexer_topk_select(torch.from_numpy(s).cuda(), k, valid_lens=vl, with_scores=True)
+    assert torch.equal(gi_u, gi_a)
+    assert torch.equal(gv_u.view(torch.int32), gv_a.view(torch.int32))
+    gi = _row(gi_u)
+    for r in (0, rows - 1):
+        o_idx, _ = indexer.topk(s[r, : valid[r]].astype(np.float64), k)
+        assert gi[r].tolist() == o_idx.tolist(), r
+
+
 def test_topk_select_causal_rule():
     rng = np.random.default_rng(9)
     rows, nb, ratio, first = 5, 64, 16, 900
