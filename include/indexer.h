@@ -394,6 +394,50 @@ int qsa_score_rows_f16(const uint16_t* q, const uint16_t* block_keys, float* sco
                        uint32_t ratio, uint32_t n_heads, uint32_t hd, hipStream_t stream);
 
 /*
+ * qsa_score_select_f16 -- the QSA prefill's row scores and their top-k in one call
+ * ([qsa.rs] qsa_score_rows_tc and the causal valid count of qsa_score_rows): qsa_score_rows_f16 of
+ * rows [0, rows) over blocks [0, n_blocks) followed by indexer_topk_select with the valid
+ * count floor((first_pos + r + 1) / ratio), bit-identical to the two calls (indices and
+ * scores, ties included); the scores live only in the workspace.  For n_blocks <= 32768
+ * and top_k <= 512 the score launch also records the largest order key of every 16-block
+ * sub-tile, and the select reads only the sub-tiles whose maximum reaches the K-th
+ * largest sub-tile maximum (no winner lies elsewhere); otherwise the general select runs.
+ *  q, block_keys   as qsa_score_rows_f16 (fp16 bit patterns, 16-byte aligned)
+ *  topk_idx        [rows, top_k] int32 output (block indices, -1 past the valid count)
+ *  topk_scores     [rows, top_k] fp32 output or NULL (-inf past the valid count)
+ *  workspace       device scratch of qsa_score_select_f16_workspace_size(rows, n_blocks,
+ *                  top_k) bytes, 256-byte aligned, no initialisation needed
+ * Errors as qsa_score_rows_f16 and indexer_topk_select; IDX_ERR_WORKSPACE when it is too small.
+ */
+/*
+ * The two halves of qsa_score_select_f16, for callers that keep the scores:
+ *
+ * qsa_score_rows_f16_tmax -- qsa_score_rows_f16, and for every row r < rows and 16-block
+ * sub-tile s < ceil(n_blocks_max / 16) the largest order key of the sub-tile's stored
+ * scores into tile_max[r * tile_stride + s] (uint32; the order key maps a score's bits to
+ * an unsigned integer in score order, -0 as +0, every NaN to 0, the lowest; blocks past
+ * n_blocks_max count as 0).  tile_stride >= ceil(n_blocks_max / 16).
+ *
+ * qsa_select_tiles -- indexer_topk_select with the causal valid count (ratio >= 1) over
+ * those scores and tile maxima: the same output, bit for bit, reading only the sub-tiles
+ * that can hold a winner.  Supported: n_cols <= 32768, top_k <= 512; scores 16-byte
+ * aligned with score_stride a multiple of 4 and >= n_cols rounded up to 16 (whole
+ * sub-tiles are read); no workspace.
+ */
+int qsa_score_rows_f16_tmax(const uint16_t* q, const uint16_t* block_keys, float* scores, uint32_t* tile_max,
+                            uint32_t rows, uint32_t n_blocks_max, uint32_t first_pos, uint32_t score_stride,
+                            uint32_t tile_stride, uint32_t ratio, uint32_t n_heads, uint32_t hd, hipStream_t stream);
+int qsa_select_tiles(const float* scores, int64_t score_stride, const uint32_t* tile_max, int64_t tile_stride,
+                     int64_t first_pos, int ratio, int rows, int n_cols, int top_k, int32_t* topk_idx,
+                     float* topk_scores, hipStream_t stream);
+
+size_t qsa_score_select_f16_workspace_size(uint32_t rows, uint32_t n_blocks, int top_k);
+int qsa_score_select_f16(const uint16_t* q, const uint16_t* block_keys, uint32_t rows, uint32_t n_blocks,
+                         uint32_t first_pos, uint32_t ratio, uint32_t n_heads, uint32_t hd, int top_k,
+                         int32_t* topk_idx, float* topk_scores, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
  * indexer_debug_dequant -- test hook for the NVFP4 decoders used by the scorers.
  *
  * For the first n logical entries of one block-table row (addressing as in

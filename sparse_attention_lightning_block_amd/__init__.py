@@ -21,5 +21,9 @@ from .ops import (  # noqa: F401
     qsa_score_rows,
     qsa_score_topk,
     qsa_score_topk_workspace_size,
+    qsa_score_select_f16,
+    qsa_score_select_f16_workspace_size,
+    qsa_score_rows_f16_tmax,
+    qsa_select_tiles,
 )
 from ._lib import IDX_ERR_DATA, IDX_F_VALIDATE, IndexerError, load  # noqa: F401

@@ -45,6 +45,10 @@ SIGNATURES = {
     "indexer_score_topk_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "qsa_score_topk_workspace_size": (_SZ, [_U32, _I]),
     "qsa_score_topk": (_I, [_P, _P, _U32, _U32, _U32, _I, _P, _P, _P, _SZ, _P]),
+    "qsa_score_select_f16_workspace_size": (_SZ, [_U32, _U32, _I]),
+    "qsa_score_rows_f16_tmax": (_I, [_P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _P]),
+    "qsa_select_tiles": (_I, [_P, _I64, _P, _I64, _I64, _I, _I, _I, _I, _P, _P, _P]),
+    "qsa_score_select_f16": (_I, [_P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _I, _P, _P, _P, _SZ, _P]),
     "indexer_score_topk": (_I, [_P, _I, _P, _P, _P, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _I, _I, _U32, _P, _P,
                                 _P, _SZ, _P]),
     "indexer_score_topk_noalloc": (_I, [_P, _I, _P, _P, _P, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _I, _I, _U32,

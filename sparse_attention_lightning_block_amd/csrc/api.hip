@@ -586,6 +586,131 @@ int qsa_score_rows_f16(const uint16_t* q, const uint16_t* block_keys, float* sco
   return ok();
 }
 
+static int score_f16_check(const uint16_t* q, const uint16_t* block_keys, const float* scores, uint32_t n_heads,
+                           uint32_t hd, uint32_t ratio) {
+  if (!q || !block_keys || !scores) return fail(IDX_ERR_NULL, "q, block_keys and scores are required");
+  if (hd != 64 && hd != 128) return fail(IDX_ERR_UNSUPPORTED, "hd %u (fp16 inputs: 64 or 128)", hd);
+  if (n_heads != 16 && n_heads != 32 && n_heads != 64)
+    return fail(IDX_ERR_UNSUPPORTED, "n_heads %u (fp16 inputs: 16, 32 or 64)", n_heads);
+  if (ratio < 1 || ratio > 0x7fffffffu) return fail(IDX_ERR_SHAPE, "ratio must be >= 1");
+  if (!aligned(q, 16) || !aligned(block_keys, 16)) return fail(IDX_ERR_SHAPE, "q and block_keys must be 16-byte aligned");
+  return IDX_OK;
+}
+
+int qsa_score_rows_f16_tmax(const uint16_t* q, const uint16_t* block_keys, float* scores, uint32_t* tile_max,
+                            uint32_t rows, uint32_t n_blocks_max, uint32_t first_pos, uint32_t score_stride,
+                            uint32_t tile_stride, uint32_t ratio, uint32_t n_heads, uint32_t hd, hipStream_t stream) {
+  int rc = score_f16_check(q, block_keys, scores, n_heads, hd, ratio);
+  if (rc) return rc;
+  if (!tile_max) return fail(IDX_ERR_NULL, "tile_max is required");
+  if (score_stride < n_blocks_max) return fail(IDX_ERR_SHAPE, "score_stride < n_blocks_max");
+  if (tile_stride < (n_blocks_max + 15) / 16) return fail(IDX_ERR_SHAPE, "tile_stride < ceil(n_blocks_max / 16)");
+  if (n_blocks_max >= (uint32_t)kMaxCols) return fail(IDX_ERR_UNSUPPORTED, "n_blocks_max must be < 2^24");
+  if (!aligned(scores, 4) || !aligned(tile_max, 4)) return fail(IDX_ERR_SHAPE, "scores and tile_max must be 4-byte aligned");
+  if (rows == 0 || n_blocks_max == 0) return ok();
+  hipError_t e = salb::launch_qsa_score_f16(reinterpret_cast<const _Float16*>(q),
+                                            reinterpret_cast<const _Float16*>(block_keys), scores, rows, n_blocks_max,
+                                            first_pos, score_stride, ratio, n_heads, hd, stream, tile_max, tile_stride);
+  if (e != hipSuccess) return hip_fail(e, "QSA score launch");
+  return ok();
+}
+
+int qsa_select_tiles(const float* scores, int64_t score_stride, const uint32_t* tile_max, int64_t tile_stride,
+                     int64_t first_pos, int ratio, int rows, int n_cols, int top_k, int32_t* topk_idx,
+                     float* topk_scores, hipStream_t stream) {
+  int rc = check_select(rows, n_cols, top_k, score_stride, ratio);
+  if (rc) return rc;
+  if (!topk_idx) return fail(IDX_ERR_NULL, "topk_idx is required");
+  if (ratio < 1) return fail(IDX_ERR_SHAPE, "ratio must be >= 1 (the causal valid count)");
+  if (rows == 0) return ok();
+  if (!scores || !tile_max) return fail(IDX_ERR_NULL, "scores and tile_max are required");
+  if (!salb::tile_select_fits(n_cols, top_k))
+    return fail(IDX_ERR_UNSUPPORTED, "n_cols %d / top_k %d (supported: 1..32768 / 1..512)", n_cols, top_k);
+  if (score_stride % 4 != 0 || score_stride < (int64_t)((n_cols + 15) & ~15) || !aligned(scores, 16))
+    return fail(IDX_ERR_SHAPE, "scores must be 16-byte aligned, score_stride a multiple of 4 and >= n_cols rounded up to 16");
+  if (tile_stride < (n_cols + 15) / 16 || !aligned(tile_max, 4)) return fail(IDX_ERR_SHAPE, "tile_stride < ceil(n_cols / 16)");
+  hipError_t e = salb::launch_select_tiles(scores, score_stride, tile_max, tile_stride, first_pos, ratio, rows, n_cols,
+                                           top_k, topk_idx, topk_scores, stream);
+  if (e != hipSuccess) return hip_fail(e, "select kernel launch");
+  return ok();
+}
+
+// Workspace of qsa_score_select_f16: the scores (row stride n_blocks rounded up to 16),
+// then either the sub-tile maxima (the sub-tile select) or the general select's buffers.
+struct ScoreSelectLayout {
+  uint32_t sstride, tstride;
+  size_t scores, tmax, select, total;
+  bool tiles;
+};
+
+static bool score_select_layout(uint32_t rows, uint32_t n_blocks, int top_k, ScoreSelectLayout* l) {
+  l->sstride = (n_blocks + 15u) & ~15u;
+  l->tstride = l->sstride / 16;
+  l->tiles = salb::tile_select_fits((int)n_blocks, top_k);
+  l->scores = 0;
+  l->tmax = round_up((size_t)rows * l->sstride * 4, 256);
+  if (l->tiles) {
+    l->select = l->tmax;
+    l->total = l->tmax + round_up((size_t)rows * l->tstride * 4, 256);
+    return true;
+  }
+  salb::SelectPlan p;
+  if (!salb::plan_select((int)rows, (int)n_blocks, top_k, &p)) return false;
+  l->select = l->tmax;
+  l->total = l->tmax + p.bytes;
+  return true;
+}
+
+size_t qsa_score_select_f16_workspace_size(uint32_t rows, uint32_t n_blocks, int top_k) {
+  if (rows == 0 || n_blocks == 0 || (int64_t)n_blocks >= kMaxCols || rows > 0x7fffffffu || top_k <= 0) return 0;
+  ScoreSelectLayout l;
+  if (!score_select_layout(rows, n_blocks, top_k, &l)) return 0;
+  return l.total;
+}
+
+int qsa_score_select_f16(const uint16_t* q, const uint16_t* block_keys, uint32_t rows, uint32_t n_blocks,
+                         uint32_t first_pos, uint32_t ratio, uint32_t n_heads, uint32_t hd, int top_k,
+                         int32_t* topk_idx, float* topk_scores, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (!q || !block_keys || !topk_idx) return fail(IDX_ERR_NULL, "q, block_keys and topk_idx are required");
+  if (hd != 64 && hd != 128) return fail(IDX_ERR_UNSUPPORTED, "hd %u (fp16 inputs: 64 or 128)", hd);
+  if (n_heads != 16 && n_heads != 32 && n_heads != 64)
+    return fail(IDX_ERR_UNSUPPORTED, "n_heads %u (fp16 inputs: 16, 32 or 64)", n_heads);
+  if (ratio < 1 || ratio > 0x7fffffffu) return fail(IDX_ERR_SHAPE, "ratio must be >= 1");
+  if (rows > 0x7fffffffu) return fail(IDX_ERR_SHAPE, "rows %u out of range", rows);
+  if ((int64_t)n_blocks >= kMaxCols) return fail(IDX_ERR_UNSUPPORTED, "n_blocks must be < 2^24");
+  int rc = check_select((int)rows, (int)n_blocks, top_k, (int64_t)n_blocks, (int)ratio);
+  if (rc) return rc;
+  if (!aligned(q, 16) || !aligned(block_keys, 16)) return fail(IDX_ERR_SHAPE, "q and block_keys must be 16-byte aligned");
+  if (rows == 0) return ok();
+  if (n_blocks == 0)  // no block: every slot is padding (the select alone writes it)
+    return indexer_topk_select(nullptr, 0, nullptr, first_pos, (int)ratio, (int)rows, 0, top_k, topk_idx, topk_scores,
+                               workspace, workspace_bytes, stream);
+  ScoreSelectLayout l;
+  if (!score_select_layout(rows, n_blocks, top_k, &l)) return fail(IDX_ERR_UNSUPPORTED, "top_k %d is not supported", top_k);
+  if (!workspace || workspace_bytes < l.total)
+    return fail(IDX_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", l.total, workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(IDX_ERR_SHAPE, "workspace must be 256-byte aligned");
+  unsigned char* w = static_cast<unsigned char*>(workspace);
+  float* sc = reinterpret_cast<float*>(w + l.scores);
+  uint32_t* tm = l.tiles ? reinterpret_cast<uint32_t*>(w + l.tmax) : nullptr;
+  hipError_t e = salb::launch_qsa_score_f16(reinterpret_cast<const _Float16*>(q),
+                                            reinterpret_cast<const _Float16*>(block_keys), sc, rows, n_blocks,
+                                            first_pos, l.sstride, ratio, n_heads, hd, stream, tm, l.tstride);
+  if (e != hipSuccess) return hip_fail(e, "QSA score launch");
+  if (l.tiles) {
+    e = salb::launch_select_tiles(sc, l.sstride, tm, l.tstride, first_pos, (int)ratio, (int)rows, (int)n_blocks, top_k,
+                                  topk_idx, topk_scores, stream);
+  } else {
+    salb::SelectPlan p;
+    salb::plan_select((int)rows, (int)n_blocks, top_k, &p);
+    e = salb::launch_select(p, sc, l.sstride, nullptr, first_pos, (int)ratio, topk_idx, topk_scores, w + l.select,
+                            false, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "select kernel launch");
+  return ok();
+}
+
 int indexer_debug_dequant(const uint8_t* keys_fp4, const uint8_t* key_scale, const float* key_gscale,
                           const int32_t* block_table_row, int n, int D, int epb, int n_pages, int mode, float* out,
                           hipStream_t stream) {

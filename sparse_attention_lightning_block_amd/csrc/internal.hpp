@@ -63,6 +63,12 @@ struct SelectPlan {
 bool plan_select(int rows, int n_cols, int top_k, SelectPlan* p);
 // counters_zeroed: the first select_counter_bytes(p) bytes of ws were zeroed by an
 // earlier launch of this call on the same stream (else the select zeroes them itself).
+// The sub-tile select (rows of at most 32768 entries whose 16-entry sub-tiles come with
+// their largest order key; top_k <= 512; rows 16-byte aligned, stride a multiple of 16).
+bool tile_select_fits(int n_cols, int top_k);
+hipError_t launch_select_tiles(const float* scores, int64_t score_stride, const uint32_t* tmax, int64_t tmax_stride,
+                               int64_t first_pos, int ratio, int rows, int n_cols, int top_k, int32_t* out_idx,
+                               float* out_scores, hipStream_t st);
 hipError_t launch_select(const SelectPlan& p, const float* scores, int64_t score_stride,
                          const int32_t* valid_lens, int64_t first_pos, int ratio, int32_t* out_idx,
                          float* out_scores, void* ws, bool counters_zeroed, hipStream_t st);
@@ -98,9 +104,10 @@ hipError_t launch_decode_prep(const uint16_t* raw, const float* kw, float* block
                               uint32_t n_new, uint32_t ratio, const uint16_t* qk, const float* qw, float* q_out,
                               uint32_t rows, uint32_t first_pos, uint32_t qkw, uint32_t n_heads, uint32_t hd,
                               uint32_t rot, float theta, float eps, hipStream_t st);
+// tmax (nullable): [rows][tstride] order-key maxima of the 16-block sub-tiles.
 hipError_t launch_qsa_score_f16(const _Float16* q, const _Float16* keys, float* scores, uint32_t rows, uint32_t nb,
                                 uint32_t first_pos, uint32_t stride, uint32_t ratio, uint32_t n_heads, uint32_t hd,
-                                hipStream_t st);
+                                hipStream_t st, uint32_t* tmax = nullptr, uint32_t tstride = 0);
 bool qsa_score_uses_mfma(int precision, uint32_t n_heads, uint32_t hd);
 // zero_ptr / zero_n16: 16-byte words the launch also zeroes (0 words: none)
 hipError_t launch_qsa_decode_score(const float* q, const float* keys, float* scores, uint32_t nb, uint32_t n_heads,

@@ -363,16 +363,32 @@ __global__ __launch_bounds__(256) void qsa_score_f32_kernel(const float* __restr
 // at 32768 blocks) stay in that XCD's L2.  q and the keys come out of RMSNorm, so
 // their fp16 roundings are relative (2^-11) and the products stay far inside the
 // fp16 range; the accumulation is fp32.
+//
+// With TMAX the scorer also writes, for every row and 16-block sub-tile (a 16-lane row of
+// the wave), the largest order key of the sub-tile's stored scores (blocks past nb count
+// as key 0, the order key of NaN, which no score undercuts): the per-sub-tile bound a
+// select uses to skip most of a row.
 constexpr int kQsaThreads = 512;
 
-template <int HD, int NH, typename InT>
+// Maximum over the lanes of each 16-lane row, left in the row's last lane (row shifts
+// with 0 shifted in: 0 is below every order key that matters).
+__device__ __forceinline__ uint32_t row_max_last(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  return x;
+}
+
+template <int HD, int NH, typename InT, bool TMAX>
 __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const InT* __restrict__ q,
                                                                      const InT* __restrict__ keys,
                                                                      float* __restrict__ scores, uint32_t rows,
                                                                      uint32_t nb, uint32_t first_pos,
                                                                      uint32_t stride, uint32_t ratio,
                                                                      uint32_t chunk, uint32_t n_groups,
-                                                                     float out_scale) {
+                                                                     float out_scale, uint32_t* __restrict__ tmax,
+                                                                     uint32_t tstride) {
   constexpr int NT = kQsaThreads;
   constexpr int NW = NT / 64;     // waves
   constexpr int KW = HD / 32;     // K steps of 32 dims
@@ -401,13 +417,17 @@ __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const InT* 
   };
   const int64_t vmax = valid_of(r_last);
   const int64_t kend = c1 < vmax ? c1 : vmax;  // keys [c0, kend) are multiplied
-  // keys of the chunk past every row's valid count: -inf
+  // keys of the chunk past every row's valid count: -inf (and, with TMAX, the maxima of
+  // the sub-tiles past the last 64-key tile multiplied below: the order key of -inf)
   {
     const int64_t from = kend > c0 ? kend : c0;
+    const int64_t tfrom = kend > c0 ? c0 + (kend - c0 + 63) / 64 * 64 : c0;
     for (int rr = 0; rr < RPG; ++rr) {
       const int r = r0 + rr;
       if (r >= (int)rows) break;
       for (int64_t s = from + tid; s < c1; s += NT) scores[(int64_t)r * stride + s] = -INFINITY;
+      if constexpr (TMAX)
+        for (int64_t s = tfrom + 16 * tid; s < c1; s += 16 * NT) tmax[(int64_t)r * tstride + (s >> 4)] = ord_key(-INFINITY);
     }
   }
   if (kend <= c0) return;
@@ -525,7 +545,15 @@ __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const InT* 
         }
       }
       const float v = row_transpose_sum4(x[0], x[1], x[2], x[3]);
-      if (orow[rr] != nullptr && key < crel) orow[rr][key] = key < vrel[rr] ? v * out_scale : -INFINITY;
+      const float sv = key < vrel[rr] ? v * out_scale : -INFINITY;
+      if (orow[rr] != nullptr && key < crel) orow[rr][key] = sv;
+      if constexpr (TMAX) {
+        // sub-tile (k0 + 16 quarter) / 16 of the row; its last lane (col 15) stores
+        const uint32_t m = row_max_last(orow[rr] != nullptr && key < crel ? ord_key(sv) : 0u);
+        const int st0 = (int)(k0 - c0) + 16 * quarter;  // its first block, relative to c0
+        if (col == 15 && orow[rr] != nullptr && st0 < crel)
+          tmax[(int64_t)(r0 + wave * RPW + rr) * tstride + (uint32_t)((c0 + st0) >> 4)] = m;
+      }
     }
   };
 
@@ -782,15 +810,20 @@ hipError_t launch_qprep_rows(const uint16_t* qk, const float* qw, OutT* out, uin
 
 template <int HD, int NH, typename InT>
 static hipError_t launch_qsa_mfma(const InT* q, const InT* keys, float* scores, uint32_t rows, uint32_t nb,
-                                  uint32_t first_pos, uint32_t stride, uint32_t ratio, hipStream_t st) {
+                                  uint32_t first_pos, uint32_t stride, uint32_t ratio, hipStream_t st,
+                                  uint32_t* tmax = nullptr, uint32_t tstride = 0) {
   constexpr uint32_t kRowsPerGroup = (kQsaThreads / 64) * (64 / NH);
   const uint32_t n_groups = (rows + kRowsPerGroup - 1) / kRowsPerGroup;
   // one key chunk per XCD (a multiple of the 64-key tile)
   uint32_t chunk = (nb + kXcds - 1) / kXcds;
   chunk = (chunk + 63) / 64 * 64;
   const dim3 grid(n_groups * kXcds);
-  hipLaunchKernelGGL((qsa_score_mfma_kernel<HD, NH, InT>), grid, dim3(kQsaThreads), 0, st, q, keys, scores, rows, nb,
-                     first_pos, stride, ratio, chunk, n_groups, 1.0f / sqrtf((float)HD));
+  if (tmax)
+    hipLaunchKernelGGL((qsa_score_mfma_kernel<HD, NH, InT, true>), grid, dim3(kQsaThreads), 0, st, q, keys, scores, rows, nb,
+                     first_pos, stride, ratio, chunk, n_groups, 1.0f / sqrtf((float)HD), tmax, tstride);
+  else
+    hipLaunchKernelGGL((qsa_score_mfma_kernel<HD, NH, InT, false>), grid, dim3(kQsaThreads), 0, st, q, keys, scores, rows, nb,
+                     first_pos, stride, ratio, chunk, n_groups, 1.0f / sqrtf((float)HD), nullptr, 0u);
   return hipGetLastError();
 }
 
@@ -875,18 +908,18 @@ template hipError_t launch_qprep_rows<_Float16>(const uint16_t*, const float*, _
 // matrix-core scorer only, which rounds fp32 inputs to exactly these values itself.
 hipError_t launch_qsa_score_f16(const _Float16* q, const _Float16* keys, float* scores, uint32_t rows, uint32_t nb,
                                 uint32_t first_pos, uint32_t stride, uint32_t ratio, uint32_t n_heads, uint32_t hd,
-                                hipStream_t st) {
+                                hipStream_t st, uint32_t* tmax, uint32_t tstride) {
   if (hd == 64) {
     switch (n_heads) {
-      case 16: return launch_qsa_mfma<64, 16>(q, keys, scores, rows, nb, first_pos, stride, ratio, st);
-      case 32: return launch_qsa_mfma<64, 32>(q, keys, scores, rows, nb, first_pos, stride, ratio, st);
-      default: return launch_qsa_mfma<64, 64>(q, keys, scores, rows, nb, first_pos, stride, ratio, st);
+      case 16: return launch_qsa_mfma<64, 16>(q, keys, scores, rows, nb, first_pos, stride, ratio, st, tmax, tstride);
+      case 32: return launch_qsa_mfma<64, 32>(q, keys, scores, rows, nb, first_pos, stride, ratio, st, tmax, tstride);
+      default: return launch_qsa_mfma<64, 64>(q, keys, scores, rows, nb, first_pos, stride, ratio, st, tmax, tstride);
     }
   }
   switch (n_heads) {
-    case 16: return launch_qsa_mfma<128, 16>(q, keys, scores, rows, nb, first_pos, stride, ratio, st);
-    case 32: return launch_qsa_mfma<128, 32>(q, keys, scores, rows, nb, first_pos, stride, ratio, st);
-    default: return launch_qsa_mfma<128, 64>(q, keys, scores, rows, nb, first_pos, stride, ratio, st);
+    case 16: return launch_qsa_mfma<128, 16>(q, keys, scores, rows, nb, first_pos, stride, ratio, st, tmax, tstride);
+    case 32: return launch_qsa_mfma<128, 32>(q, keys, scores, rows, nb, first_pos, stride, ratio, st, tmax, tstride);
+    default: return launch_qsa_mfma<128, 64>(q, keys, scores, rows, nb, first_pos, stride, ratio, st, tmax, tstride);
   }
 }
 

@@ -90,6 +90,9 @@ struct SelArgs {
   RowInfo* info;     // [rows]
   uint32_t* ccount;  // [rows][chunks] candidates per chunk
   uint64_t* cand;    // [rows][chunks][chunk] candidate slots
+  // sub-tile select
+  const uint32_t* tmax;  // [rows][tmax_stride] order-key maximum of each 16-entry sub-tile
+  int64_t tmax_stride;
 };
 
 __device__ __forceinline__ int row_valid(const SelArgs& a, int row) {
@@ -739,6 +742,180 @@ __global__ __launch_bounds__(NT) void select_rows_reg_kernel(SelArgs a, int rows
   finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, mx, mn, sh, kbase);
 }
 
+// ------------------------------------------------------------------ sub-tile rows
+
+// Rows of up to 32768 entries whose 16-entry sub-tiles come with their largest order key
+// (written by the scorer beside the scores), top_k <= kTileSelMaxK, rows 16-byte aligned
+// with a stride that is a multiple of 16: one 256-thread workgroup per row, longest rows
+// first.  When K is at most the count of sub-tiles holding valid entries, the K-th largest
+// sub-tile maximum bounds the K-th largest entry from below (at least K sub-tiles, hence
+// at least K entries, reach it), so every winner lies in a sub-tile whose maximum reaches
+// it.  One histogram pass over the maxima (bins spanning their actual range) gives a bound
+// T at or below that maximum; only the sub-tiles reaching T are read, and their entries at
+// or above T form an LDS candidate list, where the radix select finishes and the winners
+// are gathered -- the same winners as a select over the whole row.  A list crowded past
+// its capacity (rows of many equal scores) falls back to radix passes over the whole row.
+constexpr int kTileSelThreads = 256;
+constexpr int kTileSelMaxK = 512;
+constexpr int kTileSelCand = 1920;                      // LDS candidate slots (four workgroups per CU)
+constexpr int kTileSelTiles = kRowMaxWide / 16;          // sub-tiles of the longest row: 2048
+
+template <int NT>
+__global__ __launch_bounds__(NT) void select_tiles_kernel(SelArgs a, int rows) {
+  constexpr int MPT = kTileSelTiles / NT;  // sub-tile maxima per thread
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ SelShared sh;
+  __shared__ uint32_t s_kmx[NT / kWave], s_kmn[NT / kWave];
+  __shared__ uint32_t s_tiles, s_cands;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  uint64_t* cand = reinterpret_cast<uint64_t*>(smem);                             // [kTileSelCand]
+  uint16_t* tlist = reinterpret_cast<uint16_t*>(cand + kTileSelCand);             // [kTileSelTiles]
+  FinishLds f = carve(reinterpret_cast<unsigned char*>(tlist + kTileSelTiles), a.top_k);
+  const int row = rows - 1 - (int)blockIdx.x;  // causal rows grow with the index: longest first
+  const int n = row_valid(a, row);
+  const int K = n < a.top_k ? n : a.top_k;
+  const float* src = a.scores + (int64_t)row * a.score_stride;
+
+  uint32_t kbase = 0u;  // composites hold keys relative to it
+  int C = -1;           // candidates in the list (-1: the whole row is the candidate set)
+  uint64_t thr = 0ull;
+  auto each_row = [&](auto&& fn) {
+    for (int e = tid; e < n; e += NT) fn(composite(ord_key(src[e]) - kbase, (uint32_t)e));
+  };
+  auto each_cand = [&](auto&& fn) {
+    for (int i = tid; i < C; i += NT) fn(cand[i]);
+  };
+  if (K < n) {
+    const int nt = (n + 15) >> 4;  // sub-tiles holding valid entries
+    const uint32_t* tm = a.tmax + (int64_t)row * a.tmax_stride;
+    uint32_t mk[MPT];
+#pragma unroll
+    for (int i = 0; i < MPT; ++i) {
+      const int j = i * NT + tid;
+      mk[i] = j < nt ? tm[j] : 0u;
+    }
+    // range of the maxima
+    uint32_t kmx = 0u, kmn = ~0u;
+#pragma unroll
+    for (int i = 0; i < MPT; ++i) {
+      const bool v = i * NT + tid < nt;
+      kmx = v && mk[i] > kmx ? mk[i] : kmx;
+      kmn = v && mk[i] < kmn ? mk[i] : kmn;
+    }
+    kmx = wave_max(kmx);
+    kmn = ~wave_max(~kmn);
+    if (lane == 0) {
+      s_kmx[wave] = kmx;
+      s_kmn[wave] = kmn;
+    }
+    if (tid == 0) {
+      s_tiles = 0u;
+      s_cands = 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) {
+      kmx = s_kmx[w] > kmx ? s_kmx[w] : kmx;
+      kmn = s_kmn[w] < kmn ? s_kmn[w] : kmn;
+    }
+    uint32_t T = 0u;  // every winner's key is >= T, and so is its sub-tile's maximum
+    if (K <= nt) {
+      const uint32_t span = kmx - kmn;
+      const int bits = span ? 32 - __clz(span) : 1;
+      const int shift = bits > kDigit ? bits - kDigit : 0;
+      clear_bins<NT>(f.hist);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < MPT; ++i)
+        if (i * NT + tid < nt) atomicAdd(&f.hist[(mk[i] - kmn) >> shift], 1u);
+      __syncthreads();
+      uint32_t h[kBins / NT];
+      load_bins<NT>(f.hist, h);
+      find_digit<NT>(h, (uint32_t)K, sh);  // the bin of the K-th largest maximum
+      T = kmn + (sh.digit << shift);
+    }
+    // the sub-tiles whose maximum reaches T, listed in LDS (ballot ranks)
+#pragma unroll
+    for (int i = 0; i < MPT; ++i) {
+      const int j = i * NT + tid;
+      const bool pick = j < nt && mk[i] >= T;
+      const uint64_t m = __ballot(pick);
+      if (m != 0ull) {
+        const int leader = __ffsll((unsigned long long)m) - 1;
+        uint32_t base = 0u;
+        if (lane == leader) base = atomicAdd(&s_tiles, (uint32_t)__popcll(m));
+        base = __builtin_amdgcn_readlane(base, leader);
+        const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (pick) tlist[base + below] = (uint16_t)j;
+      }
+    }
+    __syncthreads();
+    const int ct = (int)s_tiles;
+    // their entries at or above T: four lanes per sub-tile, 16 bytes each; the count runs
+    // on past the list's capacity, the writes stop at it
+    for (int w0 = 0; w0 < 4 * ct; w0 += NT) {
+      const int w = w0 + tid;
+      float4v x = {0.f, 0.f, 0.f, 0.f};
+      int e0 = 0;
+      if (w < 4 * ct) {
+        e0 = 16 * (int)tlist[w >> 2] + 4 * (w & 3);
+        x = *reinterpret_cast<const float4v*>(src + e0);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = e0 + q;
+        const uint32_t key = ord_key(x[q]);
+        const bool pick = w < 4 * ct && e < n && key >= T;
+        const uint64_t m = __ballot(pick);
+        if (m != 0ull) {
+          const int leader = __ffsll((unsigned long long)m) - 1;
+          uint32_t base = 0u;
+          if (lane == leader) base = atomicAdd(&s_cands, (uint32_t)__popcll(m));
+          base = __builtin_amdgcn_readlane(base, leader);
+          const uint32_t below =
+              __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          if (pick && base + below < (uint32_t)kTileSelCand) cand[base + below] = composite(key - T, (uint32_t)e);
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t nc = s_cands;
+    if (nc <= (uint32_t)kTileSelCand) {
+      C = (int)nc;  // >= K: every winner is listed
+      kbase = T;
+      const uint32_t rel = kmx - T;  // the largest relative key among the candidates
+      const int rbits = rel ? 32 - __clz(rel) : 1;
+      thr = radix_select<NT>(each_cand, 0ull, 0ull, (uint32_t)K, 31 + rbits, f.hist, sh);
+    } else {
+      thr = radix_select<NT>(each_row, 0ull, 0ull, (uint32_t)K, 63, f.hist, sh);
+    }
+  }
+  // gather the winners
+  auto each = [&](auto&& fn) {
+    if (C >= 0)
+      each_cand(fn);
+    else
+      each_row(fn);
+  };
+  uint32_t mine = 0;
+  uint64_t mx = 0ull, mn = ~0ull;
+  each([&](uint64_t c) {
+    if (c >= thr) {
+      ++mine;
+      mx = c > mx ? c : mx;
+      mn = c < mn ? c : mn;
+    }
+  });
+  uint32_t off = block_suffix_minmax<NT>(mine, mx, mn, sh);
+  each([&](uint64_t c) {
+    if (c >= thr && off < (uint32_t)K) f.sortbuf[off++] = c;  // exactly K are selected
+  });
+  __syncthreads();
+  int32_t* oi = a.out_idx + (int64_t)row * a.top_k;
+  float* os = a.out_scores ? a.out_scores + (int64_t)row * a.top_k : nullptr;
+  finish_row<NT>(f.sortbuf, f.grp, f.hist, K, a.top_k, oi, os, mx, mn, sh, kbase);
+}
+
 // ------------------------------------------------------------------ long rows
 
 // A chunk's PER entries per thread from lo on, as order keys (0 past n): entry
@@ -1152,6 +1329,32 @@ static hipError_t launch_pipeline(const SelArgs& a, const SelectPlan& p, bool co
 size_t select_counter_bytes(const SelectPlan& p) {
   if (!p.two_pass) return 0;
   return ws_layout(p.rows, p.chunks, p.per * kChunkThreads).info;
+}
+
+bool tile_select_fits(int n_cols, int top_k) {
+  return n_cols >= 1 && n_cols <= kRowMaxWide && top_k >= 1 && top_k <= kTileSelMaxK;
+}
+
+hipError_t launch_select_tiles(const float* scores, int64_t score_stride, const uint32_t* tmax, int64_t tmax_stride,
+                               int64_t first_pos, int ratio, int rows, int n_cols, int top_k, int32_t* out_idx,
+                               float* out_scores, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  SelArgs a{};
+  a.scores = scores;
+  a.score_stride = score_stride;
+  a.first_pos = first_pos;
+  a.ratio = ratio;
+  a.n_cols = n_cols;
+  a.top_k = top_k;
+  a.out_idx = out_idx;
+  a.out_scores = out_scores;
+  a.tmax = tmax;
+  a.tmax_stride = tmax_stride;
+  const size_t lds = (size_t)kTileSelCand * 8 + (size_t)kTileSelTiles * 2 + finish_lds_bytes(top_k);
+  hipError_t e = set_lds(select_tiles_kernel<kTileSelThreads>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((select_tiles_kernel<kTileSelThreads>), dim3(rows), dim3(kTileSelThreads), lds, st, a, rows);
+  return hipGetLastError();
 }
 
 hipError_t launch_select(const SelectPlan& p, const float* scores, int64_t score_stride,

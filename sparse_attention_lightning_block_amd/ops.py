@@ -341,6 +341,78 @@ def qsa_score_topk(q, block_keys, top_k: int, *, n_blocks: Optional[int] = None,
     return out_idx, out_scores
 
 
+def qsa_score_rows_f16_tmax(q, block_keys, *, first_pos: int, ratio: int, n_blocks_max: Optional[int] = None,
+                            out: Optional[torch.Tensor] = None, tile_max: Optional[torch.Tensor] = None):
+    """(scores [rows, S] fp32, tile_max [rows, S / 16] int32 holding uint32 order keys), S =
+    n_blocks_max rounded up to 16: qsa_score_rows of fp16 q and block keys, and the largest
+    order key of every 16-block sub-tile (columns past n_blocks_max are not written)."""
+    _dev(q, "q", torch.float16, 3)
+    _dev(block_keys, "block_keys", torch.float16, 2)
+    rows, n_heads, hd = q.shape
+    nb = block_keys.shape[0] if n_blocks_max is None else n_blocks_max
+    s16 = (nb + 15) // 16 * 16
+    if out is None:
+        out = torch.empty((rows, s16), dtype=torch.float32, device=q.device)
+    if tile_max is None:
+        tile_max = torch.empty((rows, s16 // 16), dtype=torch.int32, device=q.device)
+    _dev(out, "out", torch.float32, 2)
+    _dev(tile_max, "tile_max", torch.int32, 2)
+    check(_lib.load().qsa_score_rows_f16_tmax(_ptr(q), _ptr(block_keys), _ptr(out), _ptr(tile_max), rows, nb,
+                                              first_pos, _row_stride(out), _row_stride(tile_max), ratio, n_heads, hd,
+                                              _stream()))
+    return out, tile_max
+
+
+def qsa_select_tiles(scores, tile_max, top_k: int, *, n_cols: int, first_pos: int, ratio: int,
+                     with_scores: bool = False, out_idx: Optional[torch.Tensor] = None,
+                     out_scores: Optional[torch.Tensor] = None):
+    """(idx [rows, top_k] int32, scores [rows, top_k] fp32 or None): indexer_topk_select with the
+    causal count over scores and tile maxima from qsa_score_rows_f16_tmax, reading only the
+    sub-tiles that can hold a winner."""
+    _dev(scores, "scores", torch.float32, 2)
+    _dev(tile_max, "tile_max", torch.int32, 2)
+    rows = scores.shape[0]
+    dev = scores.device
+    if out_idx is None:
+        out_idx = torch.empty((rows, top_k), dtype=torch.int32, device=dev)
+    if with_scores and out_scores is None:
+        out_scores = torch.empty((rows, top_k), dtype=torch.float32, device=dev)
+    check(_lib.load().qsa_select_tiles(_ptr(scores), _row_stride(scores), _ptr(tile_max), _row_stride(tile_max),
+                                       first_pos, ratio, rows, n_cols, top_k, _ptr(out_idx), _ptr(out_scores),
+                                       _stream()))
+    return out_idx, out_scores
+
+
+def qsa_score_select_f16_workspace_size(rows: int, n_blocks: int, top_k: int) -> int:
+    return int(_lib.load().qsa_score_select_f16_workspace_size(rows, n_blocks, top_k))
+
+
+def qsa_score_select_f16(q, block_keys, top_k: int, *, first_pos: int, ratio: int, n_blocks: Optional[int] = None,
+                         with_scores: bool = False, workspace: Optional[torch.Tensor] = None,
+                         out_idx: Optional[torch.Tensor] = None, out_scores: Optional[torch.Tensor] = None):
+    """(idx [rows, top_k] int32, scores [rows, top_k] fp32 or None): the causal top_k blocks of
+    every fp16 prepared query row over the first n_blocks fp16 block keys (qsa_score_rows on
+    the matrix cores, then the select, with the scores kept in the workspace)."""
+    _dev(q, "q", torch.float16, 3)
+    _dev(block_keys, "block_keys", torch.float16, 2)
+    rows, n_heads, hd = q.shape
+    nb = block_keys.shape[0] if n_blocks is None else n_blocks
+    if nb > block_keys.shape[0]:
+        raise ValueError("n_blocks exceeds the block-key table")
+    dev = q.device
+    if out_idx is None:
+        out_idx = torch.empty((rows, top_k), dtype=torch.int32, device=dev)
+    if with_scores and out_scores is None:
+        out_scores = torch.empty((rows, top_k), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(qsa_score_select_f16_workspace_size(rows, nb, top_k), 256), dtype=torch.uint8,
+                                device=dev)
+    check(_lib.load().qsa_score_select_f16(_ptr(q), _ptr(block_keys), rows, nb, first_pos, ratio, n_heads, hd, top_k,
+                                           _ptr(out_idx), _ptr(out_scores), _ptr(workspace), workspace.numel(),
+                                           _stream()))
+    return out_idx, out_scores
+
+
 def qsa_score_rows(q, block_keys, *, first_pos: int, ratio: int, n_blocks_max: Optional[int] = None,
                    precision: str = "mfma", out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """scores [rows, n_blocks_max] fp32 with -inf past each row's complete blocks.  fp16 q and

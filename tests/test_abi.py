@@ -156,6 +156,56 @@ def test_qsa_score_topk_argument_checks_without_gpu():
     assert lib.qsa_score_topk(16, 16, 32768, 32, 128, 256, 16, None, 256, 1024, None) == _lib.IDX_ERR_WORKSPACE
 
 
+def test_qsa_score_select_argument_checks_without_gpu():
+    lib = _lib.load()
+    # scores with rows padded to 16 blocks, then the sub-tile maxima (n_blocks <= 32768, top_k <= 512)
+    n = lib.qsa_score_select_f16_workspace_size(2048, 32768, 256)
+    assert n >= 2048 * 32768 * 4 + 2048 * 2048 * 4 and n % 256 == 0
+    assert lib.qsa_score_select_f16_workspace_size(40, 700, 64) >= 40 * 704 * 4 + 40 * 44 * 4
+    assert lib.qsa_score_select_f16_workspace_size(0, 700, 64) == 0
+    assert lib.qsa_score_select_f16_workspace_size(40, 0, 64) == 0
+    assert lib.qsa_score_select_f16_workspace_size(40, 700, 0) == 0
+    # beyond the sub-tile select (top_k > 512): the general select's buffers instead
+    assert lib.qsa_score_select_f16_workspace_size(4, 100000, 2048) > 4 * 100000 * 4
+    def call(q=16, keys=16, rows=40, nb=700, ratio=16, nh=32, hd=128, k=64, idx=16, ws=256, wsb=1 << 30):
+        return lib.qsa_score_select_f16(q, keys, rows, nb, 0, ratio, nh, hd, k, idx, None, ws, wsb, None)
+    assert call(q=None) == _lib.IDX_ERR_NULL
+    assert call(idx=None) == _lib.IDX_ERR_NULL
+    assert call(hd=256) == _lib.IDX_ERR_UNSUPPORTED
+    assert call(nh=48) == _lib.IDX_ERR_UNSUPPORTED
+    assert call(ratio=0) == _lib.IDX_ERR_SHAPE
+    assert call(k=0) == _lib.IDX_ERR_UNSUPPORTED
+    assert call(q=17) == _lib.IDX_ERR_SHAPE
+    # a workspace too small: rejected before any HIP call
+    assert call(wsb=1024) == _lib.IDX_ERR_WORKSPACE
+    assert call(ws=None) == _lib.IDX_ERR_WORKSPACE
+    assert call(ws=264) == _lib.IDX_ERR_SHAPE
+    assert call(rows=0) == _lib.IDX_OK
+
+
+def test_qsa_score_tmax_and_tile_select_argument_checks_without_gpu():
+    lib = _lib.load()
+    def score(q=16, keys=16, sc=16, tm=16, rows=4, nb=700, stride=704, tstride=44, ratio=16, nh=32, hd=128):
+        return lib.qsa_score_rows_f16_tmax(q, keys, sc, tm, rows, nb, 0, stride, tstride, ratio, nh, hd, None)
+    assert score(tm=None) == _lib.IDX_ERR_NULL
+    assert score(tstride=43) == _lib.IDX_ERR_SHAPE          # fewer than ceil(700 / 16) sub-tiles
+    assert score(stride=699) == _lib.IDX_ERR_SHAPE
+    assert score(hd=256) == _lib.IDX_ERR_UNSUPPORTED
+    assert score(ratio=0) == _lib.IDX_ERR_SHAPE
+    assert score(rows=0) == _lib.IDX_OK
+    def sel(sc=16, stride=704, tm=16, tstride=44, ratio=16, rows=4, n=700, k=64, idx=16):
+        return lib.qsa_select_tiles(sc, stride, tm, tstride, 0, ratio, rows, n, k, idx, None, None)
+    assert sel(idx=None) == _lib.IDX_ERR_NULL
+    assert sel(tm=None) == _lib.IDX_ERR_NULL
+    assert sel(ratio=0) == _lib.IDX_ERR_SHAPE              # the causal count only
+    assert sel(k=513) == _lib.IDX_ERR_UNSUPPORTED          # past the sub-tile select
+    assert sel(n=40000, stride=40000, tstride=2500) == _lib.IDX_ERR_UNSUPPORTED
+    assert sel(stride=700) == _lib.IDX_ERR_SHAPE           # rows must hold whole sub-tiles
+    assert sel(sc=20) == _lib.IDX_ERR_SHAPE                # 16-byte aligned rows
+    assert sel(tstride=40) == _lib.IDX_ERR_SHAPE
+    assert sel(rows=0) == _lib.IDX_OK
+
+
 def test_qsa_fp16_storage_argument_checks_without_gpu():
     lib = _lib.load()
     assert lib.qsa_block_pool_f16(None, 16, 32, 0, 1, 16, 128, 64, 1e4, 1e-6, None) == _lib.IDX_ERR_NULL

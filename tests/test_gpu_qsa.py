@@ -201,6 +201,82 @@ def test_score_topk_is_score_then_select_bit_for_bit(nb):
         ws.fill_(0xA5)
 
 
+# (rows, n_blocks, first_pos, ratio, n_heads, hd, top_k, keys): valid counts below and
+# above top_k, fewer sub-tiles than top_k, top_k at the sub-tile select's limit (512) and
+# past it (600: the general select), n_blocks not a multiple of 16, and rows of equal
+# scores (every block key the same vector: the candidate list overflows and the select
+# falls back to passes over the whole row)
+_SCORE_SELECT = [
+    (300, 300, 0, 1, 16, 64, 64, "normal"),
+    (300, 2300, 2000, 1, 16, 64, 64, "normal"),
+    (260, 5003, 4700, 1, 64, 128, 512, "normal"),
+    (64, 32768, 40000, 1, 64, 128, 512, "normal"),
+    (64, 3000, 2900, 1, 32, 128, 600, "normal"),
+    (300, 4000, 3800, 1, 16, 64, 256, "equal"),
+    (50, 2000, 31000, 16, 32, 128, 256, "normal"),
+]
+
+
+@pytest.mark.parametrize("rows,nb,first_pos,ratio,n_heads,hd,k,keys", _SCORE_SELECT)
+def test_score_select_is_score_rows_then_select_bit_for_bit(rows, nb, first_pos, ratio, n_heads, hd, k, keys):
+    """qsa_score_select_f16 gives the indices and scores of qsa_score_rows (fp16 inputs) then
+    indexer_topk_select with the causal count, bit for bit, from a workspace full of
+    garbage, twice in a row."""
+    rng = np.random.default_rng(rows * 7 + nb + k)
+    q = torch.from_numpy(rng.standard_normal((rows, n_heads, hd)).astype(np.float16)).cuda()
+    if keys == "equal":
+        kv = rng.standard_normal((1, hd)).astype(np.float16)
+        kb = torch.from_numpy(np.repeat(kv, nb, axis=0)).cuda()
+    else:
+        kb = torch.from_numpy(rng.standard_normal((nb, hd)).astype(np.float16)).cuda()
+    scores = salb.qsa_score_rows(q, kb, first_pos=first_pos, ratio=ratio)
+    idx_ref, val_ref = salb.indexer_topk_select(scores, k, first_pos=first_pos, ratio=ratio, with_scores=True)
+    ws = torch.full((salb.qsa_score_select_f16_workspace_size(rows, nb, k),), 0xFF, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        idx, val = salb.qsa_score_select_f16(q, kb, k, first_pos=first_pos, ratio=ratio, with_scores=True,
+                                             workspace=ws)
+        assert torch.equal(idx, idx_ref)
+        assert torch.equal(val.view(torch.int32), val_ref.view(torch.int32))
+    # the two halves: the same scores, and (where the sub-tile select takes the shape) the
+    # same selection
+    sc, tm = salb.qsa_score_rows_f16_tmax(q, kb, first_pos=first_pos, ratio=ratio)
+    assert torch.equal(sc[:, :nb].view(torch.int32), scores.view(torch.int32))
+    ref_max = torch.full((rows, (nb + 15) // 16 * 16), -float("inf"), device="cuda")
+    ref_max[:, :nb] = scores
+    keys_u = ref_max.view(torch.int32).to(torch.int64) & 0xFFFFFFFF
+    neg = keys_u >= 0x80000000
+    ok = torch.where(neg, 0xFFFFFFFF - keys_u, keys_u | 0x80000000)     # order keys (no NaN, no -0 here)
+    ok[:, nb:] = 0
+    want = ok.view(rows, -1, 16).amax(dim=2)
+    assert torch.equal(tm.to(torch.int64) & 0xFFFFFFFF, want)
+    if k <= 512:
+        idx2, val2 = salb.qsa_select_tiles(sc, tm, k, n_cols=nb, first_pos=first_pos, ratio=ratio, with_scores=True)
+        assert torch.equal(idx2, idx_ref)
+        assert torch.equal(val2.view(torch.int32), val_ref.view(torch.int32))
+
+
+def test_score_select_full_size_matches_the_two_calls():
+    """The QSA prefill (2048 rows x 32768 blocks, top_k 256, fp16 storage): the fused call's
+    selection equals the two calls' for every row."""
+    w = make(5)
+    raw = _bf16(w.raw_keys).cuda()
+    kw = torch.from_numpy(w.k_norm_w).cuda()
+    keys = torch.empty((w.n_blocks, w.hd), dtype=torch.float16, device="cuda")
+    salb.qsa_block_pool(raw, kw, keys, first_block=0, n_new=w.n_blocks, ratio=w.ratio, rot=w.rot, theta=w.theta,
+                        eps=w.eps)
+    qk = _bf16(w.qk).cuda()
+    qw = torch.from_numpy(w.q_norm_w).cuda()
+    q = salb.qsa_qprep_rows(qk, qw, n_heads=w.n_heads, hd=w.hd, first_pos=w.first_pos, rot=w.rot, theta=w.theta,
+                            eps=w.eps, dtype=torch.float16)
+    scores = salb.qsa_score_rows(q, keys, first_pos=w.first_pos, ratio=w.ratio)
+    idx_ref, val_ref = salb.indexer_topk_select(scores, w.top_k, first_pos=w.first_pos, ratio=w.ratio,
+                                                with_scores=True)
+    del scores
+    idx, val = salb.qsa_score_select_f16(q, keys, w.top_k, first_pos=w.first_pos, ratio=w.ratio, with_scores=True)
+    assert torch.equal(idx, idx_ref)
+    assert torch.equal(val.view(torch.int32), val_ref.view(torch.int32))
+
+
 @pytest.mark.parametrize("precision", ["fp32", "mfma"])
 def test_score_rows_and_topk_reduced(precision):
     """Scores from the GPU's own pooled keys and prepared queries (the same fp32 inputs on
