@@ -240,8 +240,14 @@ def run_qsa(args, w):
     sdt = torch.float16 if mfma else torch.float32
     keys = torch.empty((w.n_blocks, w.hd), dtype=sdt, device=dev)
     q = torch.empty((w.rows, w.n_heads, w.hd), dtype=sdt, device=dev)
-    scores = torch.empty((w.rows, w.n_blocks), dtype=torch.float32, device=dev)
     idx = torch.empty((w.rows, w.top_k), dtype=torch.int32, device=dev)
+    # the matrix-core path scores with the 16-block sub-tile maxima and selects from the
+    # sub-tiles that can hold a winner (qsa_score_select_f16 as its two halves); the FP32
+    # path scores whole rows and runs the general select
+    tiles = mfma and w.n_blocks <= 32768 and w.top_k <= 512
+    s16 = (w.n_blocks + 15) // 16 * 16
+    scores = torch.empty((w.rows, s16 if tiles else w.n_blocks), dtype=torch.float32, device=dev)
+    tmax = torch.empty((w.rows, s16 // 16), dtype=torch.int32, device=dev) if tiles else None
     ws = torch.zeros(max(1, salb.indexer_topk_workspace_size(w.rows, w.n_blocks, w.top_k)), dtype=torch.uint8,
                      device=dev)
 
@@ -252,10 +258,18 @@ def run_qsa(args, w):
                             eps=w.eps, out=q)
 
     def score():
-        salb.qsa_score_rows(q, keys, first_pos=w.first_pos, ratio=w.ratio, precision=args.precision, out=scores)
+        if tiles:
+            salb.qsa_score_rows_f16_tmax(q, keys, first_pos=w.first_pos, ratio=w.ratio, out=scores, tile_max=tmax)
+        else:
+            salb.qsa_score_rows(q, keys, first_pos=w.first_pos, ratio=w.ratio, precision=args.precision, out=scores)
 
     def select():
-        salb.indexer_topk_select(scores, w.top_k, first_pos=w.first_pos, ratio=w.ratio, workspace=ws, out_idx=idx)
+        if tiles:
+            salb.qsa_select_tiles(scores, tmax, w.top_k, n_cols=w.n_blocks, first_pos=w.first_pos, ratio=w.ratio,
+                                  out_idx=idx)
+        else:
+            salb.indexer_topk_select(scores, w.top_k, first_pos=w.first_pos, ratio=w.ratio, workspace=ws,
+                                     out_idx=idx)
 
     stages = [prep, score, select]
     for _ in range(args.warmup):
@@ -290,6 +304,7 @@ def run_qsa(args, w):
         "config": {"workload": w.name, "rows": w.rows, "heads": w.n_heads, "hd": w.hd, "raw_keys": w.n_blocks * w.ratio,
                    "ratio": w.ratio, "blocks": w.n_blocks, "top_k": w.top_k, "pairs": pairs,
                    "precision": args.precision, "storage": "f16" if mfma else "f32",
+                   "select": "sub-tile" if tiles else "rows",
                    "launch": "hip_graph" if args.graph else "eager"},
         "step_ms": {"p50": float(np.median(prep_ms + score_ms + select_ms))},
         "stage_ms": {"pool_and_qprep": prep_avg, "score": score_avg, "select": select_avg},

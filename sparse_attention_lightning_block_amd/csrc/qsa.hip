@@ -465,11 +465,13 @@ __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const InT* 
   // per row of the wave: its output row (a row past the last one writes nothing) and
   // the end of its valid keys relative to the chunk start, key offsets are 32-bit
   float* orow[RPW];
+  uint32_t* trow[RPW];  // with TMAX: the row's sub-tile maxima from the chunk start on
   int vrel[RPW];
 #pragma unroll
   for (int rr = 0; rr < RPW; ++rr) {
     const int r = r0 + wave * RPW + rr;
     orow[rr] = r < (int)rows ? scores + (int64_t)r * stride + c0 : nullptr;
+    trow[rr] = TMAX && r < (int)rows ? tmax + (int64_t)r * tstride + (c0 >> 4) : nullptr;  // c0: a multiple of 64
     vrel[rr] = r < (int)rows ? (int)(valid_of(r) - c0) : 0;
   }
   const int crel = (int)(c1 - c0);
@@ -548,11 +550,14 @@ __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const InT* 
       const float sv = key < vrel[rr] ? v * out_scale : -INFINITY;
       if (orow[rr] != nullptr && key < crel) orow[rr][key] = sv;
       if constexpr (TMAX) {
+        // the order key of the stored score: a score here is +0 or more, or NaN (only from
+        // non-finite inputs: key 0), or the -inf of a masked block (key ~bits(-inf))
+        const uint32_t sb = __float_as_uint(sv);
+        const uint32_t k = key >= vrel[rr] ? ~0xff800000u : sb > 0x7f800000u ? 0u : (sb | 0x80000000u);
         // sub-tile (k0 + 16 quarter) / 16 of the row; its last lane (col 15) stores
-        const uint32_t m = row_max_last(orow[rr] != nullptr && key < crel ? ord_key(sv) : 0u);
+        const uint32_t m = row_max_last(trow[rr] != nullptr && key < crel ? k : 0u);
         const int st0 = (int)(k0 - c0) + 16 * quarter;  // its first block, relative to c0
-        if (col == 15 && orow[rr] != nullptr && st0 < crel)
-          tmax[(int64_t)(r0 + wave * RPW + rr) * tstride + (uint32_t)((c0 + st0) >> 4)] = m;
+        if (col == 15 && trow[rr] != nullptr && st0 < crel) trow[rr][st0 >> 4] = m;
       }
     }
   };

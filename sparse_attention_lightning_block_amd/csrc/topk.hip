@@ -851,20 +851,30 @@ __global__ __launch_bounds__(NT) void select_tiles_kernel(SelArgs a, int rows) {
     }
     __syncthreads();
     const int ct = (int)s_tiles;
-    // their entries at or above T: four lanes per sub-tile, 16 bytes each; the count runs
-    // on past the list's capacity, the writes stop at it
-    for (int w0 = 0; w0 < 4 * ct; w0 += NT) {
-      const int w = w0 + tid;
-      float4v x = {0.f, 0.f, 0.f, 0.f};
-      int e0 = 0;
-      if (w < 4 * ct) {
-        e0 = 16 * (int)tlist[w >> 2] + 4 * (w & 3);
-        x = *reinterpret_cast<const float4v*>(src + e0);
+    // their entries at or above T: four lanes per sub-tile, 16 bytes each, LB passes of the
+    // workgroup's loads in flight at once; the count runs on past the list's capacity, the
+    // writes stop at it
+    constexpr int LB = 8;
+    for (int w0 = 0; w0 < 4 * ct; w0 += LB * NT) {
+      float4v xs[LB];
+      int es[LB];
+#pragma unroll
+      for (int b = 0; b < LB; ++b) {
+        const int w = w0 + b * NT + tid;
+        xs[b] = float4v{0.f, 0.f, 0.f, 0.f};
+        es[b] = 0;
+        if (w < 4 * ct) {
+          es[b] = 16 * (int)tlist[w >> 2] + 4 * (w & 3);
+          xs[b] = *reinterpret_cast<const float4v*>(src + es[b]);
+        }
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = e0 + q;
-        const uint32_t key = ord_key(x[q]);
+      for (int bq = 0; bq < 4 * LB; ++bq) {
+        const int b = bq >> 2, q = bq & 3;
+        if (w0 + b * NT >= 4 * ct) break;  // uniform: the passes past the list hold nothing
+        const int w = w0 + b * NT + tid;
+        const int e = es[b] + q;
+        const uint32_t key = ord_key(xs[b][q]);
         const bool pick = w < 4 * ct && e < n && key >= T;
         const uint64_t m = __ballot(pick);
         if (m != 0ull) {
