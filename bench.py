@@ -73,7 +73,7 @@ SCORER_TRAFFIC = {   # workload: (sources, sha, FETCH_SIZE KiB, WRITE_SIZE KiB p
     "decode_T8_S65536": ("csa", "2dba759cfc17e677", 3552.0, 2048.0),
     "long_decode_T32_S262144": ("csa", "2dba759cfc17e677", 33760.1, 32776.0),
     "prefill_T4096": ("csa", "2dba759cfc17e677", 35446.6, 65690.6),
-    "qsa_prefill": ("qsa", "5e1f6904c0c9ea7b", 81958.7, 262424.2),
+    "qsa_prefill": ("qsa", "2f36886fab1bdedb", 81970.9, 278873.5),
     "qsa_decode": ("qsa", "5e1f6904c0c9ea7b", 8280.0, 231.3),
     "hbm_true_T32_S262144": ("csa", "2dba759cfc17e677", 229531.2, 32776.1),
 }
