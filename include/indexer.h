@@ -348,9 +348,12 @@ int qsa_score(const float* q, const float* block_keys, float* scores, uint32_t n
 /*
  * qsa_score_topk -- qsa_score of one decode query over n_blocks blocks, then the top_k
  * of those scores as indexer_topk_select of one row with every block valid: the same
- * indices and scores, bit for bit, as the two calls.  The scores live in the workspace
- * and the score launch also clears the select's counters, so the call takes one launch
- * fewer than the two.  top_k slots past n_blocks get -1 (and -inf).
+ * indices and scores, bit for bit, as the two calls.  The scores live in the workspace.
+ * On the matrix-core scorer (16..64 heads in steps of 16, hd 64 or 128) with n_blocks <=
+ * 32768 and top_k <= 512, the score launch also records the largest order key of every
+ * 16-block sub-tile and one select launch reads only the sub-tiles that can hold a winner
+ * (as qsa_select_tiles); otherwise the score launch clears the general select's counters.
+ * top_k slots past n_blocks get -1 (and -inf).
  *  workspace  >= qsa_score_topk_workspace_size(n_blocks, top_k) bytes, 256-byte aligned,
  *             any contents (NULL allowed when the size is 0)
  * Errors as qsa_score and indexer_topk_select; IDX_ERR_WORKSPACE when it is too small.

@@ -506,11 +506,20 @@ int qsa_score(const float* q, const float* block_keys, float* scores, uint32_t n
   return ok();
 }
 
+// qsa_score_topk's workspace: the scores then the general select's buffers, or (on the
+// matrix-core scorer, when the sub-tile select takes the shape) the scores padded to whole
+// 16-block sub-tiles then the sub-tile maxima.  The size covers both.
+static size_t decode_tiles_bytes(uint32_t n_blocks) {
+  return round_up((size_t)((n_blocks + 15) & ~15u) * 4, 256) + round_up((size_t)((n_blocks + 15) / 16) * 4, 256);
+}
+
 size_t qsa_score_topk_workspace_size(uint32_t n_blocks, int top_k) {
   if (n_blocks == 0 || n_blocks > 0x7fffffffu || top_k <= 0) return 0;
   salb::SelectPlan p;
   if (!salb::plan_select(1, (int)n_blocks, top_k, &p)) return 0;
-  return round_up((size_t)n_blocks * 4, 256) + p.bytes;
+  const size_t rows_path = round_up((size_t)n_blocks * 4, 256) + p.bytes;
+  const size_t tiles_path = salb::tile_select_fits((int)n_blocks, top_k) ? decode_tiles_bytes(n_blocks) : 0;
+  return rows_path > tiles_path ? rows_path : tiles_path;
 }
 
 int qsa_score_topk(const float* q, const float* block_keys, uint32_t n_blocks, uint32_t n_heads, uint32_t hd,
@@ -527,6 +536,22 @@ int qsa_score_topk(const float* q, const float* block_keys, uint32_t n_blocks, u
   if (n_blocks == 0) {  // no block: every slot is padding (the select alone writes it)
     return indexer_topk_select(nullptr, 0, nullptr, 0, 0, 1, 0, top_k, topk_idx, topk_scores, workspace,
                                workspace_bytes, stream);
+  }
+  if (salb::qsa_decode_uses_mfma(n_heads, hd) && salb::tile_select_fits((int)n_blocks, top_k)) {
+    // the scorer records the 16-block sub-tile maxima; the sub-tile select reads only the
+    // sub-tiles that can hold a winner (one launch for the select, no counters to clear)
+    const size_t need = decode_tiles_bytes(n_blocks);
+    if (!workspace || workspace_bytes < need)
+      return fail(IDX_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace_bytes);
+    if (!aligned(workspace, 256)) return fail(IDX_ERR_SHAPE, "workspace must be 256-byte aligned");
+    const uint32_t s16 = (n_blocks + 15) & ~15u;
+    float* sc = static_cast<float*>(workspace);
+    uint32_t* tm = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(workspace) + round_up((size_t)s16 * 4, 256));
+    hipError_t e = salb::launch_qsa_decode_score(q, block_keys, sc, n_blocks, n_heads, hd, nullptr, 0, stream, tm);
+    if (e != hipSuccess) return hip_fail(e, "QSA decode score launch");
+    e = salb::launch_select_tiles(sc, s16, tm, s16 / 16, 0, 0, 1, (int)n_blocks, top_k, topk_idx, topk_scores, stream);
+    if (e != hipSuccess) return hip_fail(e, "select kernel launch");
+    return ok();
   }
   salb::SelectPlan p;
   if (!salb::plan_select(1, (int)n_blocks, top_k, &p)) return fail(IDX_ERR_UNSUPPORTED, "top_k %d is not supported", top_k);

@@ -110,8 +110,11 @@ hipError_t launch_qsa_score_f16(const _Float16* q, const _Float16* keys, float* 
                                 hipStream_t st, uint32_t* tmax = nullptr, uint32_t tstride = 0);
 bool qsa_score_uses_mfma(int precision, uint32_t n_heads, uint32_t hd);
 // zero_ptr / zero_n16: 16-byte words the launch also zeroes (0 words: none)
+// Whether the decode scores run on the fp32 matrix cores (the kernel that can also write
+// the 16-block sub-tile maxima).
+bool qsa_decode_uses_mfma(uint32_t n_heads, uint32_t hd);
 hipError_t launch_qsa_decode_score(const float* q, const float* keys, float* scores, uint32_t nb, uint32_t n_heads,
-                                   uint32_t hd, uint4* zero_ptr, int64_t zero_n16, hipStream_t st);
+                                   uint32_t hd, uint4* zero_ptr, int64_t zero_n16, hipStream_t st, uint32_t* tmax = nullptr);
 hipError_t launch_qsa_score(const float* q, const float* keys, float* scores, uint32_t rows, uint32_t nb,
                             uint32_t first_pos, uint32_t stride, uint32_t ratio, uint32_t n_heads, uint32_t hd,
                             int precision, hipStream_t st);

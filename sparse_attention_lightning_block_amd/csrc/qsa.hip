@@ -666,7 +666,7 @@ __global__ __launch_bounds__(256) void qsa_decode_score_mfma_kernel(const float*
                                                                     const float* __restrict__ keys,
                                                                     float* __restrict__ scores, uint32_t nb,
                                                                     float out_scale, uint4* __restrict__ zero_ptr,
-                                                                    int64_t zero_n16) {
+                                                                    int64_t zero_n16, uint32_t* __restrict__ tmax) {
   zero_words(zero_ptr, zero_n16);
   constexpr int KS = HD / 4;  // MFMA steps = dims per lane group
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -717,6 +717,10 @@ __global__ __launch_bounds__(256) void qsa_decode_score_mfma_kernel(const float*
     part = row_sum4(part);
     const uint32_t b = (u0 + u) * 16 + c;
     if (g == 0 && b < nb) scores[b] = part * out_scale;
+    if (tmax != nullptr) {  // uniform: the unit's largest order key (every 16-lane row holds the unit)
+      const uint32_t m = row_max_last(b < nb ? ord_key(part * out_scale) : 0u);
+      if (lane == 15 && (u0 + u) * 16 < nb) tmax[u0 + u] = m;
+    }
   }
 }
 
@@ -834,17 +838,17 @@ static hipError_t launch_qsa_mfma(const InT* q, const InT* keys, float* scores, 
 
 template <int HD, int MT>
 static hipError_t launch_decode_mfma(const float* q, const float* keys, float* scores, uint32_t nb, float sc,
-                                     uint4* zero_ptr, int64_t zero_n16, hipStream_t st) {
+                                     uint4* zero_ptr, int64_t zero_n16, uint32_t* tmax, hipStream_t st) {
   // two 16-block units per wave once that still leaves a wave per SIMD (1024 SIMDs)
   const uint32_t units = (nb + 15) / 16;
   if (units >= 2048) {
     const dim3 grid((units + 7) / 8);
     hipLaunchKernelGGL((qsa_decode_score_mfma_kernel<HD, MT, 2>), grid, dim3(256), 0, st, q, keys, scores, nb, sc,
-                       zero_ptr, zero_n16);
+                       zero_ptr, zero_n16, tmax);
   } else {
     const dim3 grid((units + 3) / 4);
     hipLaunchKernelGGL((qsa_decode_score_mfma_kernel<HD, MT, 1>), grid, dim3(256), 0, st, q, keys, scores, nb, sc,
-                       zero_ptr, zero_n16);
+                       zero_ptr, zero_n16, tmax);
   }
   return hipGetLastError();
 }
@@ -854,23 +858,24 @@ bool qsa_decode_uses_mfma(uint32_t n_heads, uint32_t hd) {
 }
 
 hipError_t launch_qsa_decode_score(const float* q, const float* keys, float* scores, uint32_t nb, uint32_t n_heads,
-                                   uint32_t hd, uint4* zero_ptr, int64_t zero_n16, hipStream_t st) {
+                                   uint32_t hd, uint4* zero_ptr, int64_t zero_n16, hipStream_t st, uint32_t* tmax) {
+  if (tmax != nullptr && !qsa_decode_uses_mfma(n_heads, hd)) return hipErrorInvalidValue;  // maxima: matrix-core kernel only
   const float sc = 1.0f / sqrtf((float)hd);
   if (qsa_decode_uses_mfma(n_heads, hd)) {
     const uint32_t mt = n_heads / 16;
     if (hd == 64) {
       switch (mt) {
-        case 1: return launch_decode_mfma<64, 1>(q, keys, scores, nb, sc, zero_ptr, zero_n16, st);
-        case 2: return launch_decode_mfma<64, 2>(q, keys, scores, nb, sc, zero_ptr, zero_n16, st);
-        case 3: return launch_decode_mfma<64, 3>(q, keys, scores, nb, sc, zero_ptr, zero_n16, st);
-        default: return launch_decode_mfma<64, 4>(q, keys, scores, nb, sc, zero_ptr, zero_n16, st);
+        case 1: return launch_decode_mfma<64, 1>(q, keys, scores, nb, sc, zero_ptr, zero_n16, tmax, st);
+        case 2: return launch_decode_mfma<64, 2>(q, keys, scores, nb, sc, zero_ptr, zero_n16, tmax, st);
+        case 3: return launch_decode_mfma<64, 3>(q, keys, scores, nb, sc, zero_ptr, zero_n16, tmax, st);
+        default: return launch_decode_mfma<64, 4>(q, keys, scores, nb, sc, zero_ptr, zero_n16, tmax, st);
       }
     }
     switch (mt) {
-      case 1: return launch_decode_mfma<128, 1>(q, keys, scores, nb, sc, zero_ptr, zero_n16, st);
-      case 2: return launch_decode_mfma<128, 2>(q, keys, scores, nb, sc, zero_ptr, zero_n16, st);
-      case 3: return launch_decode_mfma<128, 3>(q, keys, scores, nb, sc, zero_ptr, zero_n16, st);
-      default: return launch_decode_mfma<128, 4>(q, keys, scores, nb, sc, zero_ptr, zero_n16, st);
+      case 1: return launch_decode_mfma<128, 1>(q, keys, scores, nb, sc, zero_ptr, zero_n16, tmax, st);
+      case 2: return launch_decode_mfma<128, 2>(q, keys, scores, nb, sc, zero_ptr, zero_n16, tmax, st);
+      case 3: return launch_decode_mfma<128, 3>(q, keys, scores, nb, sc, zero_ptr, zero_n16, tmax, st);
+      default: return launch_decode_mfma<128, 4>(q, keys, scores, nb, sc, zero_ptr, zero_n16, tmax, st);
     }
   }
   const dim3 grid((nb + 63) / 64);

@@ -277,6 +277,23 @@ def test_score_select_full_size_matches_the_two_calls():
     assert torch.equal(val.view(torch.int32), val_ref.view(torch.int32))
 
 
+@pytest.mark.parametrize("n_heads,hd,nb,k", [(64, 128, 32768, 512), (48, 128, 5000, 256), (32, 128, 40001, 256),
+                                             (16, 64, 3000, 600), (32, 64, 20000, 1)])
+def test_score_topk_shapes_bit_for_bit(n_heads, hd, nb, k):
+    """qsa_score_topk on the sub-tile select (matrix-core scorer, <= 32768 blocks, top_k <=
+    512) and off it (48 heads: the vector scorer; 40001 blocks; top_k 600): the indices and
+    scores of qsa_score then indexer_topk_select, bit for bit."""
+    rng = np.random.default_rng(n_heads + hd + nb + k)
+    q = torch.from_numpy(rng.standard_normal((n_heads, hd)).astype(np.float32)).cuda()
+    keys = torch.from_numpy(rng.standard_normal((nb, hd)).astype(np.float32)).cuda()
+    ws = torch.full((max(256, salb.qsa_score_topk_workspace_size(nb, k)),), 0x5A, dtype=torch.uint8, device="cuda")
+    a_idx, a_val = salb.qsa_score_topk(q, keys, k, with_scores=True, workspace=ws)
+    sc = salb.qsa_score(q, keys)
+    b_idx, b_val = salb.indexer_topk_select(sc.view(1, nb), k, with_scores=True)
+    assert torch.equal(a_idx, b_idx[0])
+    assert torch.equal(a_val.view(torch.int32), b_val[0].view(torch.int32))
+
+
 @pytest.mark.parametrize("precision", ["fp32", "mfma"])
 def test_score_rows_and_topk_reduced(precision):
     """Scores from the GPU's own pooled keys and prepared queries (the same fp32 inputs on
