@@ -69,13 +69,13 @@ COLD_SPAN_BYTES = 2 * 256 * 2**20
 TRAFFIC_COPY_FACTOR = {"FETCH_SIZE": 1.9998, "WRITE_SIZE": 1.0}
 SCORER_SOURCES = {"csa": ['score.hip', 'nvfp4.hpp', 'common.hpp', 'internal.hpp'], "qsa": ['qsa.hip', 'common.hpp', 'internal.hpp']}
 SCORER_TRAFFIC = {   # workload: (sources, sha, FETCH_SIZE KiB, WRITE_SIZE KiB per dispatch)
-    "tiny_decode": ("csa", "c6de6a85a7789694", 81.7, 16.0),
-    "decode_T8_S65536": ("csa", "c6de6a85a7789694", 3551.9, 2048.0),
-    "long_decode_T32_S262144": ("csa", "c6de6a85a7789694", 33752.8, 32776.0),
-    "prefill_T4096": ("csa", "c6de6a85a7789694", 35440.5, 65692.6),
-    "qsa_prefill": ("qsa", "2f36886fab1bdedb", 81970.9, 278873.5),
-    "qsa_decode": ("qsa", "2f36886fab1bdedb", 8283.5, 231.7),
-    "hbm_true_T32_S262144": ("csa", "c6de6a85a7789694", 229536.5, 32776.1),
+    "tiny_decode": ("csa", "1a53394b857b3ffd", 81.7, 16.0),
+    "decode_T8_S65536": ("csa", "1a53394b857b3ffd", 3552.0, 2048.0),
+    "long_decode_T32_S262144": ("csa", "1a53394b857b3ffd", 33796.7, 32776.0),
+    "prefill_T4096": ("csa", "1a53394b857b3ffd", 35444.1, 65690.8),
+    "qsa_prefill": ("qsa", "9dd33e1c6ddc3eae", 81969.4, 278863.0),
+    "qsa_decode": ("qsa", "9dd33e1c6ddc3eae", 8279.9, 141.5),
+    "hbm_true_T32_S262144": ("csa", "1a53394b857b3ffd", 229530.6, 32776.1),
 }
 
 
