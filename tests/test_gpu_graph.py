@@ -91,6 +91,48 @@ def test_qsa_graph_replays_match_eager():
         torch.cuda.synchronize()
 
 
+def test_qsa_fp16_score_select_graph_replays_match_eager():
+    """The QSA prefill on fp16 storage with the fused score + sub-tile select captured once:
+    every replay (workspace and outputs overwritten between replays, eager work between
+    them) equals the eager call bit for bit."""
+    w = make(5, reduced=1)
+    raw = torch.from_numpy(w.raw_keys.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    kw = torch.from_numpy(w.k_norm_w).cuda()
+    qk = torch.from_numpy(w.qk.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    qw = torch.from_numpy(w.q_norm_w).cuda()
+    keys = torch.empty((w.n_blocks, w.hd), dtype=torch.float16, device="cuda")
+    q = torch.empty((w.rows, w.n_heads, w.hd), dtype=torch.float16, device="cuda")
+    idx = torch.empty((w.rows, w.top_k), dtype=torch.int32, device="cuda")
+    val = torch.empty((w.rows, w.top_k), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(salb.qsa_score_select_f16_workspace_size(w.rows, w.n_blocks, w.top_k), dtype=torch.uint8,
+                     device="cuda")
+
+    def path():
+        salb.qsa_block_pool(raw, kw, keys, first_block=0, n_new=w.n_blocks, ratio=w.ratio, rot=w.rot, theta=w.theta,
+                            eps=w.eps)
+        salb.qsa_qprep_rows(qk, qw, n_heads=w.n_heads, hd=w.hd, first_pos=w.first_pos, rot=w.rot, theta=w.theta,
+                            eps=w.eps, out=q)
+        salb.qsa_score_select_f16(q, keys, w.top_k, first_pos=w.first_pos, ratio=w.ratio, workspace=ws,
+                                  out_idx=idx, out_scores=val)
+
+    path()
+    torch.cuda.synchronize()
+    ref_i, ref_v = idx.clone(), val.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        path()
+    for rep in range(3):
+        ws.fill_(0xFF)
+        idx.fill_(-7)
+        val.fill_(1.5)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref_i), rep
+        assert torch.equal(val.view(torch.int32), ref_v.view(torch.int32)), rep
+        path()  # eager work between replays
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("cfg,reduced", [(2, 0), (3, 1)])
 def test_fused_entry_graph_replays_match_eager(cfg, reduced):
     """indexer_score_topk captured whole (scorer, select stages; the scorer launch zeroes
