@@ -73,8 +73,8 @@ SCORER_TRAFFIC = {   # workload: (sources, sha, FETCH_SIZE KiB, WRITE_SIZE KiB p
     "decode_T8_S65536": ("csa", "1a53394b857b3ffd", 3552.0, 2048.0),
     "long_decode_T32_S262144": ("csa", "1a53394b857b3ffd", 33796.7, 32776.0),
     "prefill_T4096": ("csa", "1a53394b857b3ffd", 35444.1, 65690.8),
-    "qsa_prefill": ("qsa", "9dd33e1c6ddc3eae", 81969.4, 278863.0),
-    "qsa_decode": ("qsa", "9dd33e1c6ddc3eae", 8279.9, 141.5),
+    "qsa_prefill": ("qsa", "ec667992117eed46", 81970.8, 278861.5),
+    "qsa_decode": ("qsa", "ec667992117eed46", 8279.1, 141.5),
     "hbm_true_T32_S262144": ("csa", "1a53394b857b3ffd", 229530.6, 32776.1),
 }
 

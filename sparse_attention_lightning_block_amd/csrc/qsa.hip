@@ -380,6 +380,20 @@ __device__ __forceinline__ uint32_t row_max_last(uint32_t x) {
   return x;
 }
 
+// row_max_last of N values, the N chains interleaved step by step (each DPP read then
+// follows its source's write by N - 1 independent instructions instead of wait states).
+template <int N>
+__device__ __forceinline__ void row_max_last_n(uint32_t (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = max(x[i], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x[i], 0x111, 0xf, 0xf, false));
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = max(x[i], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x[i], 0x112, 0xf, 0xf, false));
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = max(x[i], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x[i], 0x114, 0xf, 0xf, false));
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = max(x[i], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x[i], 0x118, 0xf, 0xf, false));
+}
+
 template <int HD, int NH, typename InT, bool TMAX>
 __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const InT* __restrict__ q,
                                                                      const InT* __restrict__ keys,
@@ -534,6 +548,7 @@ __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const InT* 
     // the quarters so that quarter q keeps N tile q: lane (quarter, col) ends with key
     // 16 * quarter + col of the tile, for each row.
     const int key = (int)(k0 - c0) + 16 * quarter + col;
+    uint32_t tk[RPW];  // with TMAX: each row's order key of its stored score
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
       float x[4];
@@ -554,10 +569,18 @@ __global__ __launch_bounds__(kQsaThreads) void qsa_score_mfma_kernel(const InT* 
         // non-finite inputs: key 0), or the -inf of a masked block (key ~bits(-inf))
         const uint32_t sb = __float_as_uint(sv);
         const uint32_t k = key >= vrel[rr] ? ~0xff800000u : sb > 0x7f800000u ? 0u : (sb | 0x80000000u);
-        // sub-tile (k0 + 16 quarter) / 16 of the row; its last lane (col 15) stores
-        const uint32_t m = row_max_last(trow[rr] != nullptr && key < crel ? k : 0u);
-        const int st0 = (int)(k0 - c0) + 16 * quarter;  // its first block, relative to c0
-        if (col == 15 && trow[rr] != nullptr && st0 < crel) trow[rr][st0 >> 4] = m;
+        tk[rr] = trow[rr] != nullptr && key < crel ? k : 0u;
+      }
+    }
+    if constexpr (TMAX) {
+      // the maximum of sub-tile (k0 + 16 quarter) / 16 of each row, in the last lane
+      // (col 15) of the quarter, which stores all of the wave's rows in one branch
+      row_max_last_n<RPW>(tk);
+      const int st0 = (int)(k0 - c0) + 16 * quarter;  // the sub-tile's first block, relative to c0
+      if (col == 15 && st0 < crel) {
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr)
+          if (trow[rr] != nullptr) trow[rr][st0 >> 4] = tk[rr];
       }
     }
   };
