@@ -14,9 +14,12 @@ def pytest_terminal_summary(terminalreporter):
     """Top-k checks whose set differences reached past one score tolerance (all are still
     within two: see tests/parity.py)."""
     parity = sys.modules.get("tests.parity")
-    beyond = getattr(parity, "BEYOND_TAU", None)
     if parity is None:
         return
-    n_checks = len(beyond)
-    terminalreporter.write_line(f"top-k set differences beyond one tolerance: {sum(beyond.values())} entries "
-                                f"in {n_checks} row checks" + (f": {dict(list(beyond.items())[:20])}" if beyond else ""))
+    beyond = parity.BEYOND_TAU
+    c = parity.TOPK_CHECKS
+    terminalreporter.write_line(
+        f"top-k row checks against the oracle: {c['rows']}; rows whose set differs: {c['rows_differing']} "
+        f"({c['entries_differing']} entries, all within two tolerances of the K-th score); entries beyond one "
+        f"tolerance: {sum(beyond.values())} in {len(beyond)} checks" +
+        (f": {dict(list(beyond.items())[:20])}" if beyond else ""))

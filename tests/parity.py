@@ -69,6 +69,9 @@ def check_scores(got_row, ref, amag, precision, what=""):
 # score, per check label; printed by tests that run with -s and summarised in the
 # design notes.
 BEYOND_TAU = {}
+# Every top-k row check of the session: rows checked, rows whose set differs from the
+# oracle's, and the differing entries (a differing pair counts twice: one in, one out).
+TOPK_CHECKS = {"rows": 0, "rows_differing": 0, "entries_differing": 0}
 
 
 def check_topk(gpu_idx, gpu_val, ref, amag, k, precision, what="", tol=None):
@@ -89,6 +92,7 @@ def check_topk(gpu_idx, gpu_val, ref, amag, k, precision, what="", tol=None):
     assert len(set(g.tolist())) == K, f"{what}: duplicates"
     assert np.all((g >= 0) & (g < n)), f"{what}: index out of [0, valid)"
     if K == 0:
+        TOPK_CHECKS["rows"] += 1
         return 0, 0
     o_idx, o_val = indexer.topk(ref, k)
     vk = o_val[K - 1]
@@ -104,6 +108,9 @@ def check_topk(gpu_idx, gpu_val, ref, amag, k, precision, what="", tol=None):
         beyond += abs(ref[s] - vk) > t
     if beyond:
         BEYOND_TAU[what] = beyond
+    TOPK_CHECKS["rows"] += 1
+    TOPK_CHECKS["rows_differing"] += bool(diff)
+    TOPK_CHECKS["entries_differing"] += len(diff)
     if gpu_val is not None:
         v = np.asarray(gpu_val[:K], dtype=np.float64)
         assert np.all(np.isneginf(np.asarray(gpu_val[K:]))), f"{what}: score padding"
