@@ -490,23 +490,36 @@ __global__ __launch_bounds__(NT, (NT == kRowThreads && PER <= 16) ? 5 : 1) void 
   // entry of register i, and the first entry any thread holds in register i
   auto ent = [&](int i) { return VEC ? 4 * ((i >> 2) * NT + tid) + (i & 3) : i * NT + tid; };
   auto ent0 = [](int i) { return VEC ? 4 * (i >> 2) * NT : i * NT; };
+  // all loads unconditional inside one row-uniform branch, so that they are in flight
+  // together: positions past n re-read the row's last quad (or entry), keys 0
   uint32_t key[PER];
-  if constexpr (VEC) {
-    static_assert(PER % 4 == 0, "vector rows");
+  if (n > 0) {
+    if constexpr (VEC) {
+      static_assert(PER % 4 == 0, "vector rows");
+      const int last = (n - 1) & ~3;  // rows and n_cols are 16-byte aligned
+      float4v x[PER / 4];
 #pragma unroll
-    for (int j = 0; j < PER / 4; ++j) {
-      const int v = j * NT + tid;
-      float4v x = {0.f, 0.f, 0.f, 0.f};
-      if (4 * v < n) x = *reinterpret_cast<const float4v*>(src + 4 * v);
+      for (int j = 0; j < PER / 4; ++j) {
+        const int e0 = 4 * (j * NT + tid);
+        x[j] = *reinterpret_cast<const float4v*>(src + (e0 < n ? e0 : last));
+      }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) key[4 * j + q] = 4 * v + q < n ? ord_key(x[q]) : 0u;
+      for (int j = 0; j < PER / 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) key[4 * j + q] = 4 * (j * NT + tid) + q < n ? ord_key(x[j][q]) : 0u;
+    } else {
+      float x[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = i * NT + tid;
+        x[i] = src[e < n ? e : n - 1];
+      }
+#pragma unroll
+      for (int i = 0; i < PER; ++i) key[i] = i * NT + tid < n ? ord_key(x[i]) : 0u;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = i * NT + tid;
-      key[i] = e < n ? ord_key(src[e]) : 0u;
-    }
+    for (int i = 0; i < PER; ++i) key[i] = 0u;
   }
   // registers past the row's last entry are skipped on a wave-uniform branch: a short
   // row costs passes over its own length, not over the workgroup's capacity
@@ -937,24 +950,40 @@ __device__ __forceinline__ int chunk_ent(int lo, int i) {
   return VEC ? lo + 4 * ((i >> 2) * NT + (int)threadIdx.x) + (i & 3) : lo + i * NT + (int)threadIdx.x;
 }
 
+// Every load is unconditional, so that all of them are in flight together (a load in a
+// branch gets its own wait before the next one is issued): positions past n re-read the
+// row's last entry (or quad), and entry 0 when n is 0 (a chunked row is never empty of
+// columns), and their keys are 0.
 template <int PER, bool VEC>
 __device__ __forceinline__ void load_chunk(const float* src, int lo, int n, uint32_t (&key)[PER]) {
   constexpr int NT = kChunkThreads;
   if constexpr (VEC) {
     static_assert(PER % 4 == 0, "vector chunks");
+    const int last = n > 0 ? ((n - 1) & ~3) : 0;  // 16-byte aligned: rows and n_cols are
+    float4v x[PER / 4];
 #pragma unroll
     for (int j = 0; j < PER / 4; ++j) {
       const int e0 = lo + 4 * (j * NT + (int)threadIdx.x);
-      float4v x = {0.f, 0.f, 0.f, 0.f};
-      if (e0 < n) x = *reinterpret_cast<const float4v*>(src + e0);
+      x[j] = *reinterpret_cast<const float4v*>(src + (e0 < n ? e0 : last));
+    }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) key[4 * j + q] = e0 + q < n ? ord_key(x[q]) : 0u;
+    for (int j = 0; j < PER / 4; ++j) {
+      const int e0 = lo + 4 * (j * NT + (int)threadIdx.x);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) key[4 * j + q] = e0 + q < n ? ord_key(x[j][q]) : 0u;
     }
   } else {
+    const int last = n > 0 ? n - 1 : 0;
+    float x[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = lo + i * NT + (int)threadIdx.x;
-      key[i] = e < n ? ord_key(src[e]) : 0u;
+      x[i] = src[e < n ? e : last];
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lo + i * NT + (int)threadIdx.x;
+      key[i] = e < n ? ord_key(x[i]) : 0u;
     }
   }
 }
